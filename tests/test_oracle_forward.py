@@ -1,0 +1,302 @@
+"""Pins of the oracle's span forward.
+
+Copy-as-Decode Appendix K: a span forward over N tokens advances positions exactly as N
+decode steps would, so it must reproduce them.  SwitchSD block verify: each candidate sees
+the prefix and its own earlier tokens only, so a block forward equals W independent causal
+forwards.  PLD page: greedy verification emits exactly what plain greedy decoding emits."""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+from spec_verify_cad_amd import synth
+from spec_verify_cad_amd.configs import CONFIGS, SMALL, TINY
+from spec_verify_cad_amd.synth import LayerShape
+
+from helpers import oracle_layer, small_layer
+
+MINI = LayerShape(hidden=128, n_q_heads=4, n_kv_heads=2, head_dim=32, ffn=192, vocab=211)
+MINI_F32 = LayerShape(hidden=128, n_q_heads=4, n_kv_heads=2, head_dim=32, ffn=192, vocab=211, dtype="f32")
+
+
+@pytest.fixture(scope="module")
+def mini():
+    return small_layer(MINI, 7)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = CONFIGS["tiny_f32"]
+    w, L = small_layer(TINY, wl.seed)
+    cache = O.cache_from_hidden(L, synth.hidden_states(wl.seed, wl.cache_len, TINY.hidden), 160)
+    return L, cache
+
+
+def _same(a, b):
+    for key in ("hidden_out", "logits", "argmax"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+@pytest.mark.parametrize("shape", [MINI, MINI_F32])
+def test_span_equals_sequential_decode(shape):
+    w, L = small_layer(shape, 11)
+    ctx = synth.uniform_tokens(11, 40, shape.vocab)
+    span = synth.uniform_tokens(11, 13, shape.vocab, stream=1)
+    c1 = O.cache_from_tokens(L, ctx, 64)
+    c2 = c1.copy()
+    s = O.span_forward(L, c1, span)
+    steps = [O.decode_one(L, c2, t) for t in span]
+    for key in ("hidden_out", "logits", "argmax"):
+        np.testing.assert_array_equal(s[key], np.concatenate([d[key] for d in steps]), err_msg=key)
+    assert c1.length == c2.length == 53
+    np.testing.assert_array_equal(c1.K, c2.K)
+    np.testing.assert_array_equal(c1.V, c2.V)
+
+
+def test_tiny_config_span_equals_8_decode_steps(tiny):
+    L, cache = tiny
+    span = synth.uniform_tokens(CONFIGS["tiny_f32"].seed, 8, TINY.vocab, stream=1)
+    c1, c2 = cache.copy(), cache.copy()
+    s = O.span_forward(L, c1, span)
+    d = [O.decode_one(L, c2, t) for t in span]
+    _same(s, {k: np.concatenate([x[k] for x in d]) for k in ("hidden_out", "logits", "argmax")})
+    np.testing.assert_array_equal(s["positions"], np.arange(128, 136))
+
+
+def test_span_in_chunks_equals_one_span(mini):
+    _, L = mini
+    ctx = synth.uniform_tokens(3, 30, MINI.vocab)
+    span = synth.uniform_tokens(3, 12, MINI.vocab, stream=1)
+    c1 = O.cache_from_tokens(L, ctx, 48)
+    c2 = c1.copy()
+    a = O.span_forward(L, c1, span)
+    b1 = O.span_forward(L, c2, span[:5])
+    b2 = O.span_forward(L, c2, span[5:])
+    for key in ("hidden_out", "logits", "argmax"):
+        np.testing.assert_array_equal(a[key], np.concatenate([b1[key], b2[key]]))
+
+
+def test_prefill_cache_equals_decoding_the_prefix(mini):
+    # The K/V-only prefill must store what full decode steps store.
+    _, L = mini
+    ctx = synth.uniform_tokens(5, 20, MINI.vocab)
+    c1 = O.cache_from_tokens(L, ctx, 24)
+    c2 = O.Cache(L.n_kv_heads, 24, L.head_dim)
+    for t in ctx:
+        O.decode_one(L, c2, t)
+    np.testing.assert_array_equal(c1.K, c2.K)
+    np.testing.assert_array_equal(c1.V, c2.V)
+
+
+def test_block_equals_independent_causal_spans(mini):
+    _, L = mini
+    W, D = 3, 5
+    ctx = synth.uniform_tokens(9, 33, MINI.vocab)
+    cands = synth.uniform_tokens(9, W * D, MINI.vocab, stream=2)
+    base = O.cache_from_tokens(L, ctx, 64)
+    blk = O.span_forward(L, base.copy(), cands, mode="block", W=W, D=D, commit=False)
+    for w in range(W):
+        c = O.span_forward(L, base.copy(), cands[w * D:(w + 1) * D], mode="causal", commit=False)
+        for key in ("hidden_out", "logits", "argmax"):
+            np.testing.assert_array_equal(blk[key][w * D:(w + 1) * D], c[key], err_msg=f"{key} w={w}")
+    one = O.span_forward(L, base.copy(), cands[:D], mode="block", W=1, D=D, commit=False)
+    cau = O.span_forward(L, base.copy(), cands[:D], mode="causal", commit=False)
+    _same(one, cau)
+
+
+def test_block_positions_and_slots():
+    slots, pos, mask = O.span_layout(10, 6, "block", W=2, D=3)
+    np.testing.assert_array_equal(slots, np.arange(10, 16))
+    np.testing.assert_array_equal(pos, [10, 11, 12, 10, 11, 12])
+    assert mask[4, :10].all() and mask[4, 13] and mask[4, 14] and not mask[4, 15]
+    assert not mask[4, 10:13].any()
+
+
+def test_gqa_equals_replicated_mha():
+    # Query head h reads KV head h // (Hq/Hkv): replicate each KV head's weights over its
+    # group and the MHA layer must give the same result.
+    shp = LayerShape(hidden=64, n_q_heads=6, n_kv_heads=2, head_dim=16, ffn=96, vocab=97)
+    w = synth.layer_weights(shp, 21)
+    L = oracle_layer(shp, w)
+    qd, kd = 6 * 16, 2 * 16
+    qkv = w["w_qkv"]
+    k_rows = qkv[qd:qd + kd].reshape(2, 16, 64)
+    v_rows = qkv[qd + kd:].reshape(2, 16, 64)
+    rep = lambda r: np.repeat(r, 3, axis=0).reshape(6 * 16, 64)
+    w2 = dict(w, w_qkv=np.concatenate([qkv[:qd], rep(k_rows), rep(v_rows)]))
+    mha = LayerShape(hidden=64, n_q_heads=6, n_kv_heads=6, head_dim=16, ffn=96, vocab=97)
+    L2 = oracle_layer(mha, w2)
+    ctx = synth.uniform_tokens(21, 17, 97)
+    span = synth.uniform_tokens(21, 6, 97, stream=1)
+    a = O.span_forward(L, O.cache_from_tokens(L, ctx, 30), span)
+    b = O.span_forward(L2, O.cache_from_tokens(L2, ctx, 30), span)
+    np.testing.assert_allclose(a["logits"], b["logits"], rtol=0, atol=1e-6)
+    np.testing.assert_array_equal(a["argmax"], b["argmax"])
+
+
+def test_attention_matches_sdpa(mini):
+    # The attention step alone against torch's scaled_dot_product_attention (fp64, GQA).
+    _, L = mini
+    ctx = synth.uniform_tokens(13, 25, MINI.vocab)
+    span = synth.uniform_tokens(13, 7, MINI.vocab, stream=1)
+    c = O.cache_from_tokens(L, ctx, 40)
+    out = O.span_forward(L, c, span)
+    S = 32
+    q = torch.from_numpy(out["q"]).permute(1, 0, 2)[None]              # [1, Hq, n, d]
+    k = torch.from_numpy(c.K[:, :S])[None]
+    v = torch.from_numpy(c.V[:, :S])[None]
+    mask = torch.ones(7, S, dtype=torch.bool).tril(diagonal=25)
+    ref = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, enable_gqa=True)
+    ref = ref[0].permute(1, 0, 2).reshape(7, -1).numpy()
+    got = out["o"]
+    ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
+    assert np.all(np.abs(got - ref) <= ulp), np.max(np.abs(got - ref) / ulp)
+
+
+def test_one_visible_key_returns_its_value(mini):
+    # The first row of a forward over an empty cache sees only itself: o == v.
+    _, L = mini
+    c = O.Cache(L.n_kv_heads, 8, L.head_dim)
+    out = O.span_forward(L, c, [5, 9, 2])
+    v0 = out["v"][0]                                   # [Hkv, d]
+    want = np.concatenate([v0[O.kv_group(L, h)] for h in range(L.n_q_heads)])
+    np.testing.assert_array_equal(out["o"][0], want)
+
+
+def test_equal_scores_average_values():
+    # With W_q = 0 all scores tie, so every output is the plain mean of the visible values.
+    shp = MINI
+    w = synth.layer_weights(shp, 31)
+    qkv = w["w_qkv"].copy()
+    qkv[: shp.n_q_heads * shp.head_dim] = 0
+    L = oracle_layer(shp, dict(w, w_qkv=qkv))
+    c = O.cache_from_tokens(L, synth.uniform_tokens(31, 10, shp.vocab), 16)
+    out = O.span_forward(L, c, [1, 2, 3])
+    for j in range(3):
+        for h in range(shp.n_q_heads):
+            g = O.kv_group(L, h)
+            want = np.mean(c.V[g, : 10 + j + 1], axis=0)
+            got = out["o"][j, h * shp.head_dim:(h + 1) * shp.head_dim]
+            # got must be a nearest bf16 value of the exact mean (either side of an exact tie)
+            half_ulp = 2.0 ** (np.floor(np.log2(np.abs(want))) - 8)
+            assert np.all(np.abs(got - want) <= half_ulp * (1 + 1e-9))
+
+
+def test_planted_lm_head_row_forces_argmax(mini):
+    w, L = mini
+    ctx = synth.uniform_tokens(17, 12, MINI.vocab)
+    span = [3, 4, 5]
+    c = O.cache_from_tokens(L, ctx, 20)
+    base = O.span_forward(L, c.copy(), span)
+    target = 123
+    wl = L.wlm.copy()
+    wl[target] = base["u3"][1]                          # logit = |u3|^2 ~ hidden for row 1
+    L2 = O.Layer(**{**L.__dict__, "wlm": wl})
+    out = O.span_forward(L2, c.copy(), span)
+    assert out["argmax"][1] == target
+    assert out["logits"][1, target] == pytest.approx(float(np.sum(base["u3"][1] ** 2)), rel=1e-6)
+
+
+def test_copy_span_commit_then_decode_matches_pure_decode(mini):
+    # A copy span committed in one forward leaves the cache exactly as decoding would,
+    # so the next generated token is the same.
+    _, L = mini
+    ctx = synth.uniform_tokens(19, 20, MINI.vocab)
+    span = synth.uniform_tokens(19, 9, MINI.vocab, stream=1)
+    c1 = O.cache_from_tokens(L, ctx, 40)
+    c2 = c1.copy()
+    O.span_forward(L, c1, span)
+    for t in span:
+        O.decode_one(L, c2, t)
+    a = O.decode_one(L, c1, 77)
+    b = O.decode_one(L, c2, 77)
+    _same(a, b)
+
+
+def _greedy(L, cache, g, count):
+    toks = []
+    for _ in range(count):
+        g = int(O.decode_one(L, cache, g)["argmax"][0])
+        toks.append(g)
+    return toks
+
+
+def test_pld_verify_loop_emits_plain_greedy_stream(mini):
+    # PLD page: greedy verification is exact.  Drafts are the greedy continuation with a
+    # random corruption (or none) and a random length; every round must emit the greedy
+    # tokens, a accepted + 1 bonus, and leave the cache consistent.
+    _, L = mini
+    rng = np.random.default_rng(23)
+    ctx = synth.uniform_tokens(23, 30, MINI.vocab)
+    c0 = O.cache_from_tokens(L, ctx[:-1], 120)
+    g0 = int(ctx[-1])
+    greedy = _greedy(L, c0.copy(), g0, 60)
+    c, g, out, k = c0.copy(), g0, [], 6
+    while len(out) < 40:
+        p = len(out)
+        dl = int(rng.integers(0, k + 1))
+        draft = np.array(greedy[p:p + k] + [0] * k)[:k]
+        if dl and rng.random() < 0.6:
+            draft[int(rng.integers(0, dl))] += 1
+        draft[dl:] = 0
+        fw = O.span_forward(L, c, [g] + list(draft), commit=False)
+        a, em = O.accept_causal(draft, dl, fw["argmax"])
+        assert len(em) == a + 1
+        assert em == greedy[p:p + a + 1]
+        c.length += a + 1
+        out += em
+        g = em[-1]
+    assert out == greedy[:len(out)]
+
+
+def test_block_verify_emits_plain_greedy_stream(mini):
+    _, L = mini
+    rng = np.random.default_rng(29)
+    W, D = 3, 4
+    ctx = synth.uniform_tokens(29, 25, MINI.vocab)
+    c0 = O.cache_from_tokens(L, ctx[:-1], 120)
+    greedy = _greedy(L, c0.copy(), int(ctx[-1]), 60)
+    c = c0.copy()
+    first_pred = int(O.decode_one(L, c, int(ctx[-1]))["argmax"][0])   # anchor cached
+    out = [first_pred]
+    assert out == greedy[:1]
+    for _ in range(8):
+        p = len(out) - 1                                              # greedy[p] == first_pred
+        drafts = rng.integers(0, MINI.vocab, size=(W, D))
+        good = int(rng.integers(0, W))
+        drafts[good] = greedy[p:p + D]
+        if rng.random() < 0.5:
+            drafts[good, int(rng.integers(0, D))] += 1
+        lens = np.full(W, D)
+        fw = O.span_forward(L, c, drafts.reshape(-1), mode="block", W=W, D=D, commit=False)
+        a, w, em, _ = O.accept_block(drafts, lens, fw["argmax"], first_pred, D)
+        assert em == greedy[p:p + a + 1]
+        O.commit_block(c, w, a, D)
+        # cache the bonus token as the next anchor with one decode step
+        first_pred = int(O.decode_one(L, c, em[-1])["argmax"][0])
+        out = out[:-1] + em + [first_pred]
+        assert out == greedy[:len(out)]
+
+
+def test_tiny_config_corrupted_draft_accepts_four(tiny):
+    # Config: draft = the oracle's own argmax with position 5 corrupted -> a = 4.
+    L, cache = tiny
+    span = synth.uniform_tokens(CONFIGS["tiny_f32"].seed, 8, TINY.vocab, stream=1)
+    fw = O.span_forward(L, cache.copy(), span, commit=False)
+    pred = fw["argmax"]
+    draft = pred[:8].copy()
+    draft[4] = (draft[4] + 1) % TINY.vocab                              # d_5 (1-based)
+    a, em = O.accept_causal(draft, 8, pred)
+    assert a == 4 and em == list(pred[:5])
+    # end to end: greedy-decode 8 tokens, corrupt d_5, verify [g, d_1..d_8]
+    c = cache.copy()
+    g = int(span[0])
+    greedy = _greedy(L, c.copy(), g, 9)
+    draft = np.array(greedy[:8])
+    draft[4] = (draft[4] + 1) % TINY.vocab
+    fw = O.span_forward(L, c, [g] + list(draft), commit=False)
+    a, em = O.accept_causal(draft, 8, fw["argmax"])
+    assert a == 4 and em == greedy[:5]
