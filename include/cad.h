@@ -1,0 +1,197 @@
+/*
+ * cad.h — C ABI of the MI355X (gfx950) span-commit / verify library, libcad.so.
+ *
+ * One data-parallel hot path, in three calls:
+ *   cad_ngram_lookup  — prompt-lookup draft search over int32 token histories
+ *                       (PLD page, "The n-gram match, precisely"; SwitchSD's kappa-gram gate
+ *                       and recency-ranked candidate retrieval);
+ *   cad_span_forward  — one parallel forward of a decoder layer + LM head over Nq new tokens
+ *                       per sequence, appending their K/V to the cache (Copy-as-Decode §2.4,
+ *                       copy-span splicing via parallel prefill; the same forward is the
+ *                       speculative verifier), with a causal-span or a block-triangular
+ *                       multi-candidate mask (SwitchSD, block-triangular verification);
+ *   cad_accept_scan   — greedy left-to-right acceptance of drafts against the forward's argmax
+ *                       (PLD page, "Verification in a single parallel pass"; SwitchSD's
+ *                       longest validated continuation), with KV-length update.
+ *
+ * Conventions for every call
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library never
+ *     allocates, frees or synchronizes; all work is enqueued on `stream` in order.
+ *   - Return value: CAD_OK (0) or a negative CAD_E* code.  Argument errors are detected on
+ *     the host and returned before anything is enqueued.  No exception crosses the ABI.
+ *   - Conditions only the device can see (a sequence whose cache or history would overflow)
+ *     are reported per sequence in `err[b]` (when given) and make that sequence's work a
+ *     no-op: nothing is written for it and its lengths stay unchanged.
+ *   - Layouts are dense row-major with the shapes given; no strides except where named.
+ *   - The first call on a device compiles nothing and allocates nothing; calls on one
+ *     stream are ordered, calls on different streams that share buffers race.
+ */
+#ifndef CAD_H
+#define CAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define CAD_OK            0
+#define CAD_EINVAL       -1   /* null pointer, non-positive size, inconsistent arguments      */
+#define CAD_EUNSUPPORTED -2   /* shape outside what the kernels handle (see each call)        */
+#define CAD_ECAPACITY    -3   /* device-side: len + Nq > cap, or history overflow            */
+#define CAD_EHIP         -4   /* a HIP launch failed                                          */
+#define CAD_EWORKSPACE   -5   /* workspace missing or smaller than cad_span_forward_workspace */
+
+/* storage format of weights, cache and activations */
+#define CAD_DTYPE_BF16    0   /* bf16 storage, fp32 accumulation                              */
+#define CAD_DTYPE_F32     1   /* fp32 storage and accumulation                                */
+
+/* attention mask of a span forward */
+#define CAD_MASK_CAUSAL_SPAN 0  /* row i at slot/position len+i sees slots [0, len+i]           */
+#define CAD_MASK_BLOCK_TRI   1  /* Nq = W*D; row (w,j) at slot len+w*D+j, position len+j, sees
+                                   [0,len) and slots len+w*D+j' for j' <= j                    */
+
+/* span-forward flags */
+#define CAD_COMMIT_ALL   1    /* len += Nq at the end of the forward (a copy span: acceptance 1) */
+#define CAD_KV_ONLY      2    /* stop after appending K/V (prefill of a cache); no outputs     */
+
+/*
+ * A pre-norm decoder layer with grouped-query attention and a SwiGLU MLP, followed by a
+ * final RMSNorm and an untied LM head.  RMSNorm gains are 1, there are no biases, RoPE is the
+ * half-split form (element i pairs with i + head_dim/2) at absolute positions with angles
+ * p * rope_base^(-2i/head_dim).  Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ * All matrices are row-major [out, in] in `dtype`:
+ *   embed     [vocab, hidden]
+ *   w_qkv     [(n_q_heads + 2*n_kv_heads) * head_dim, hidden]   rows: Q heads, K heads, V heads
+ *   w_o       [hidden, n_q_heads * head_dim]
+ *   w_gate_up [2 * ffn, hidden]                                rows: gate, then up
+ *   w_down    [hidden, ffn]
+ *   w_lm      [vocab, hidden]
+ * Supported: hidden, head_dim*n_q_heads and ffn multiples of 8; head_dim in {32, 64, 128};
+ * n_q_heads a multiple of n_kv_heads.
+ */
+typedef struct {
+    int hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+    int dtype;                 /* CAD_DTYPE_BF16 or CAD_DTYPE_F32 */
+    float rms_eps;             /* added to mean(x^2) before the inverse square root */
+    double rope_base;
+    const void *embed, *w_qkv, *w_o, *w_gate_up, *w_down, *w_lm;
+} cad_layer_desc;
+
+/*
+ * KV cache of B sequences.  k, v: [B, n_kv_heads, cap, head_dim] in `dtype`, slot s of
+ * sequence b holding the key/value of the token at position s (after acceptance).
+ * len: [B] int32, device-resident current lengths.  err: [B] int32, nullable; set to
+ * CAD_ECAPACITY for a sequence whose operation would overflow (never cleared by the library).
+ * n_kv_heads, head_dim and dtype must match the layer the cache is used with.
+ */
+typedef struct {
+    void *k, *v;
+    int32_t *len;
+    int32_t *err;
+    int B, cap;
+    int n_kv_heads, head_dim, dtype;
+} cad_kv_desc;
+
+/*
+ * cad_ngram_lookup — most-recent-first suffix match (PLD page, "The n-gram match,
+ * precisely"; SwitchSD, candidate retrieval ranked by recency).
+ *
+ *   ctx        [B, ctx_stride] int32 histories; sequence b uses ctx[b*ctx_stride + 0 .. len-1]
+ *   ctx_len    [B] int32 device lengths (len)
+ *   n, W, D    suffix length (>= 1), candidates kept (1..8), draft length (1..64)
+ *   with_current 0 or 1.  Row layout of `draft` for sequence b is
+ *                [with_current ? ctx[len-1] : nothing, cand_0[0..D-1], ..., cand_{W-1}[0..D-1]]
+ *                so with_current=1 gives directly the token rows [g, d_1..d_D] of a causal
+ *                verify forward, and with_current=0 the W*D rows of a block verify.
+ *   draft      [B, with_current + W*D] int32 out; entries past a candidate's length are 0
+ *   draft_len  [B, W] int32 out; min(D, len - (j + n)) for a hit at start j, else 0
+ *   match_pos  [B, W] int32 out, nullable; the start j of each hit, -1 where none
+ *
+ * The suffix is ctx[len-n .. len-1]; candidate starts are j = len-n-1 down to 0 (at least one
+ * continuation token, the suffix never matching itself, overlap allowed), the first W hits
+ * are kept in that order.  len < n+1 gives no hit.  Lengths outside [0, ctx_stride] are
+ * clamped for the scan.  Errors: CAD_EINVAL, CAD_EUNSUPPORTED (W > 8, D > 64, n > 64).
+ */
+int cad_ngram_lookup(const int32_t *ctx, int64_t ctx_stride, const int32_t *ctx_len, int B,
+                     int n, int W, int D, int with_current,
+                     int32_t *draft, int32_t *draft_len, int32_t *match_pos,
+                     hipStream_t stream);
+
+/*
+ * cad_span_forward — one parallel forward of Nq new tokens per sequence (Copy-as-Decode §2.4
+ * and Appendix K; SwitchSD block-triangular verification).
+ *
+ *   tokens      [B, Nq] int32 token ids (must be < vocab)
+ *   mask_mode   CAD_MASK_CAUSAL_SPAN, or CAD_MASK_BLOCK_TRI with Nq == W*D
+ *   flags       CAD_COMMIT_ALL and/or CAD_KV_ONLY
+ *   argmax_out  [B, Nq] int32 out: LM-head argmax per row, ties to the lowest id (nullable
+ *               only with CAD_KV_ONLY)
+ *   hidden_out  [B*Nq, hidden] dtype out, nullable: the layer output (residual stream)
+ *   logits_out  [B*Nq, vocab] fp32 out, nullable (debug; costs a full logits write)
+ *   workspace   device scratch of at least cad_span_forward_workspace(...) bytes, 256-aligned
+ *
+ * Every row first appends its K/V at slot len+i (RoPE at the row's position), then attends
+ * to the cached prefix and the span rows its mask allows (append-then-attend: a row reads
+ * its own key as stored).  Rounding points (bf16 round-to-nearest-even for a bf16 layer):
+ * normed input, rotated q, stored k and v, attention output, second normed input, SwiGLU
+ * product, hidden_out, final normed input; the residual stream and logits are fp32.
+ * Errors: CAD_EINVAL, CAD_EUNSUPPORTED, CAD_EWORKSPACE, CAD_EHIP; per sequence
+ * CAD_ECAPACITY in kv->err when len + Nq > cap.
+ */
+int cad_span_forward(const cad_layer_desc *layer, const cad_kv_desc *kv,
+                     const int32_t *tokens, int B, int Nq,
+                     int mask_mode, int W, int D, int flags,
+                     int32_t *argmax_out, void *hidden_out, float *logits_out,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace cad_span_forward needs for these arguments and flags (0 on invalid
+ * arguments).  A CAD_KV_ONLY forward needs far less than a full one. */
+size_t cad_span_forward_workspace(const cad_layer_desc *layer, int B, int Nq, int mask_mode,
+                                  int W, int D, int cap, int flags);
+
+/*
+ * cad_accept_scan — greedy acceptance and commit (PLD page, "Verification in a single
+ * parallel pass"; SwitchSD, longest validated continuation).
+ *
+ *   draft, with_current, draft_len : as written by cad_ngram_lookup (same W, D)
+ *   pred        causal: [B, 1+D] argmax of the verify forward over [g, d_1..d_D];
+ *               block:  [B, W*D] argmax of the block forward over the W candidates
+ *   first_pred  block: [B] the target's prediction at the cached anchor; NULL in causal mode
+ *   mask_mode   CAD_MASK_CAUSAL_SPAN (W must be 1, with_current 1) or CAD_MASK_BLOCK_TRI
+ *               (with_current 0)
+ *   accepted    [B] out: a (causal) or a* (block)
+ *   best_w      [B] out, nullable: winning candidate (0 in causal mode)
+ *   emitted     [B, D+1] out: the a accepted draft tokens then the bonus token; rest 0
+ *   n_emitted   [B] out: a + 1
+ *   ctx, ctx_stride, ctx_len, ctx_cap : nullable history; when given the emitted tokens are
+ *               appended at ctx_len[b] and ctx_len[b] grows by a+1 (if ctx_len+a+1 > ctx_cap the
+ *               sequence is flagged CAD_ECAPACITY in kv->err and nothing is appended)
+ *   kv          nullable; when given, causal: len += a+1 (g and the accepted drafts are now
+ *               cached); block: the winner's first a* rows move from slot len+w*D+j to len+j
+ *               and len += a*.
+ * Causal: a = number of leading i < draft_len with d_{i+1} == pred[i]; bonus = pred[a].
+ * Block: a_w = leading run of candidate w checked against first_pred, then against
+ * pred[w*D + j - 1]; the largest a_w wins, ties to the lowest w; bonus = first_pred when a* = 0,
+ * else pred[w*D + a* - 1].  Errors: CAD_EINVAL, CAD_EUNSUPPORTED (W > 8, D > 64).
+ */
+int cad_accept_scan(const int32_t *draft, int with_current, const int32_t *draft_len,
+                    const int32_t *pred, const int32_t *first_pred,
+                    int B, int W, int D, int mask_mode,
+                    int32_t *accepted, int32_t *best_w, int32_t *emitted, int32_t *n_emitted,
+                    int32_t *ctx, int64_t ctx_stride, int32_t *ctx_len, int ctx_cap,
+                    const cad_kv_desc *kv, hipStream_t stream);
+
+/* Static description of a status code. */
+const char *cad_status_string(int status);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int cad_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CAD_H */

@@ -1,0 +1,222 @@
+// C ABI of libcad: host-side argument checks, workspace sizing/carving and the launch
+// sequence of the span forward.  Nothing here allocates, frees or synchronizes.
+#include <cstring>
+
+#include "cad_internal.h"
+
+namespace {
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool layer_ok(const cad_layer_desc* L) {
+    if (!L) return false;
+    if (L->hidden <= 0 || L->n_q_heads <= 0 || L->n_kv_heads <= 0 || L->head_dim <= 0 || L->ffn <= 0 ||
+        L->vocab <= 0)
+        return false;
+    if (L->dtype != CAD_DTYPE_BF16 && L->dtype != CAD_DTYPE_F32) return false;
+    return true;
+}
+
+bool layer_supported(const cad_layer_desc* L) {
+    if (L->n_q_heads % L->n_kv_heads) return false;
+    if (L->head_dim != 32 && L->head_dim != 64 && L->head_dim != 128) return false;
+    if (L->hidden % 8 || L->ffn % 8 || (L->n_q_heads * L->head_dim) % 8) return false;
+    return true;
+}
+
+// attention launch geometry of the bf16 MFMA kernel
+void attn_plan(FwdDims* fd) {
+    const int G = fd->Hq / fd->Hkv, Rg = fd->Nq * G;
+    fd->attn_rows_per_wg = Rg > 64 ? 128 : 64;
+    fd->attn_row_tiles = (Rg + fd->attn_rows_per_wg - 1) / fd->attn_rows_per_wg;
+    const long units = (long)fd->B * fd->Hkv * fd->attn_row_tiles;
+    const long want = 1024;                                  // about 4 workgroups per CU
+    long splits = (want + units - 1) / units;
+    const long maxkeys = fd->cap;                            // len + Nq <= cap for every live sequence
+    long chunk = (maxkeys + splits - 1) / splits;
+    chunk = chunk < 128 ? 128 : chunk;
+    chunk = (chunk + 63) / 64 * 64;
+    fd->attn_chunk = (int)chunk;
+    fd->attn_splits = (int)((maxkeys + chunk - 1) / chunk);
+}
+
+}  // namespace
+
+bool fwd_dims(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, int cap, FwdDims* fd) {
+    if (!layer_ok(L) || B <= 0 || Nq <= 0 || cap <= 0) return false;
+    if (mode != CAD_MASK_CAUSAL_SPAN && mode != CAD_MASK_BLOCK_TRI) return false;
+    if (mode == CAD_MASK_BLOCK_TRI && (W <= 0 || D <= 0 || (long)W * D != Nq)) return false;
+    std::memset(fd, 0, sizeof(*fd));
+    fd->B = B; fd->Nq = Nq; fd->M = B * Nq;
+    fd->h = L->hidden; fd->Hq = L->n_q_heads; fd->Hkv = L->n_kv_heads; fd->d = L->head_dim;
+    fd->ffn = L->ffn; fd->V = L->vocab; fd->cap = cap; fd->mode = mode;
+    fd->Dblk = mode == CAD_MASK_BLOCK_TRI ? D : 1;
+    fd->dtype = L->dtype; fd->esz = L->dtype == CAD_DTYPE_F32 ? 4 : 2;
+    fd->qkv_n = (fd->Hq + 2 * fd->Hkv) * fd->d;
+    fd->lm_tiles = gemm_plan(fd->dtype, fd->M, fd->V, false).nnt;
+    attn_plan(fd);
+    return true;
+}
+
+FwdBufs fwd_carve(const FwdDims& fd, void* base, bool kv_only) {
+    FwdBufs w;
+    std::memset(&w, 0, sizeof(w));
+    char* p = (char*)base;
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> void* {
+        void* r = p ? p + off : nullptr;
+        off += al256(bytes);
+        return r;
+    };
+    const size_t M = fd.M, h = fd.h, e = fd.esz, qd = (size_t)fd.Hq * fd.d;
+    w.len_snap = (int32_t*)take(fd.B * sizeof(int32_t));
+    w.u = take(M * h * e);
+    if (!kv_only) {
+        w.x = (float*)take(M * h * 4);
+        w.q = take(M * qd * e);
+        w.o = take(M * qd * e);
+        if (fd.dtype == CAD_DTYPE_BF16 && (fd.d == 64 || fd.d == 128)) {
+            w.part_o = (float*)take(M * fd.Hq * (size_t)fd.attn_splits * fd.d * 4);
+            w.part_ml = (float*)take(M * fd.Hq * (size_t)fd.attn_splits * 2 * 4);
+        }
+        w.h1 = (float*)take(M * h * 4);
+        w.u2 = take(M * h * e);
+        w.act = take(M * (size_t)fd.ffn * e);
+        w.h2 = (float*)take(M * h * 4);
+        w.u3 = take(M * h * e);
+        w.amax_part = (float2*)take(M * (size_t)fd.lm_tiles * sizeof(float2));
+    }
+    w.total = off;
+    return w;
+}
+
+extern "C" {
+
+const char* cad_status_string(int st) {
+    switch (st) {
+        case CAD_OK: return "ok";
+        case CAD_EINVAL: return "invalid argument";
+        case CAD_EUNSUPPORTED: return "unsupported shape";
+        case CAD_ECAPACITY: return "capacity exceeded";
+        case CAD_EHIP: return "HIP launch failed";
+        case CAD_EWORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+int cad_version(void) { return 100; }
+
+size_t cad_span_forward_workspace(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, int cap,
+                                  int flags) {
+    FwdDims fd;
+    if (!fwd_dims(L, B, Nq, mode, W, D, cap, &fd)) return 0;
+    return fwd_carve(fd, nullptr, (flags & CAD_KV_ONLY) != 0).total;
+}
+
+int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
+                     int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!L || !kv || !tokens) return CAD_EINVAL;
+    if (flags & ~(CAD_COMMIT_ALL | CAD_KV_ONLY)) return CAD_EINVAL;
+    const bool kv_only = (flags & CAD_KV_ONLY) != 0;
+    if (!kv->k || !kv->v || !kv->len || kv->B != B) return CAD_EINVAL;
+    FwdDims fd;
+    if (!fwd_dims(L, B, Nq, mode, W, D, kv->cap, &fd)) return CAD_EINVAL;
+    if (kv->n_kv_heads != L->n_kv_heads || kv->head_dim != L->head_dim || kv->dtype != L->dtype) return CAD_EINVAL;
+    if (!L->embed || !L->w_qkv) return CAD_EINVAL;
+    if (!kv_only && (!L->w_o || !L->w_gate_up || !L->w_down || !L->w_lm || !argmax_out)) return CAD_EINVAL;
+    if (!layer_supported(L)) return CAD_EUNSUPPORTED;
+    if ((long)fd.M * fd.h > (1L << 31) || (long)fd.M * fd.ffn > (1L << 31)) return CAD_EUNSUPPORTED;
+    const bool simple_attn = fd.dtype == CAD_DTYPE_F32 || (fd.d != 64 && fd.d != 128);
+    if (!kv_only && simple_attn && (size_t)(fd.cap + fd.Nq) * 4 > 64 * 1024) return CAD_EUNSUPPORTED;
+    const FwdBufs wb = fwd_carve(fd, workspace, kv_only);
+    if (!workspace || workspace_bytes < wb.total || ((uintptr_t)workspace & 255)) return CAD_EWORKSPACE;
+
+    hipError_t e = launch_embed_norm(fd, tokens, L->embed, L->rms_eps, kv->len, kv->err, wb, stream);
+    if (e != hipSuccess) return CAD_EHIP;
+
+    EpiParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.M = fd.M; p.len_snap = wb.len_snap; p.Nq = fd.Nq; p.cap = fd.cap;
+    p.q_out = wb.q; p.kc = kv->k; p.vc = kv->v;
+    p.Hq = fd.Hq; p.Hkv = fd.Hkv; p.d = fd.d; p.mode = mode; p.Dblk = fd.Dblk; p.rope_base = L->rope_base;
+    const size_t h = fd.h;
+    // QKV projection + RoPE + K/V append (K/V rows only for a cache prefill)
+    {
+        EpiParams pq = p;
+        const char* w = (const char*)L->w_qkv;
+        int N = fd.qkv_n;
+        if (kv_only) {
+            pq.f_off = fd.Hq * fd.d;
+            w += (size_t)pq.f_off * h * fd.esz;
+            N = 2 * fd.Hkv * fd.d;
+        }
+        pq.N = N;
+        if (launch_gemm(fd.dtype, EPI_QKV, wb.u, w, fd.M, N, fd.h, pq, stream) != hipSuccess) return CAD_EHIP;
+    }
+    if (!kv_only) {
+        if (launch_attention(fd, wb, kv->k, kv->v, stream) != hipSuccess) return CAD_EHIP;
+        EpiParams po = p;
+        po.N = fd.h; po.resid = wb.x; po.out_f32 = wb.h1; po.out_t = nullptr;
+        if (launch_gemm(fd.dtype, EPI_RESID, wb.o, L->w_o, fd.M, fd.h, fd.Hq * fd.d, po, stream) != hipSuccess)
+            return CAD_EHIP;
+        if (launch_rmsnorm(fd, wb.h1, wb.u2, L->rms_eps, wb.len_snap, stream) != hipSuccess) return CAD_EHIP;
+        EpiParams pg = p;
+        pg.N = 2 * fd.ffn; pg.act = wb.act; pg.ffn = fd.ffn;
+        if (launch_gemm(fd.dtype, EPI_SWIGLU, wb.u2, L->w_gate_up, fd.M, 2 * fd.ffn, fd.h, pg, stream) != hipSuccess)
+            return CAD_EHIP;
+        EpiParams pd = p;
+        pd.N = fd.h; pd.resid = wb.h1; pd.out_f32 = wb.h2; pd.out_t = hidden_out;
+        if (launch_gemm(fd.dtype, EPI_RESID, wb.act, L->w_down, fd.M, fd.h, fd.ffn, pd, stream) != hipSuccess)
+            return CAD_EHIP;
+        if (launch_rmsnorm(fd, wb.h2, wb.u3, L->rms_eps, wb.len_snap, stream) != hipSuccess) return CAD_EHIP;
+        EpiParams pl = p;
+        pl.N = fd.V; pl.part = wb.amax_part; pl.ntiles = fd.lm_tiles; pl.logits = logits_out;
+        if (launch_gemm(fd.dtype, EPI_ARGMAX, wb.u3, L->w_lm, fd.M, fd.V, fd.h, pl, stream) != hipSuccess)
+            return CAD_EHIP;
+        if (launch_argmax_final(fd, wb, argmax_out, stream) != hipSuccess) return CAD_EHIP;
+    }
+    if (flags & CAD_COMMIT_ALL)
+        if (launch_commit(fd, wb, kv->len, stream) != hipSuccess) return CAD_EHIP;
+    return CAD_OK;
+}
+
+int cad_ngram_lookup(const int32_t* ctx, int64_t ctx_stride, const int32_t* ctx_len, int B, int n, int W, int D,
+                     int with_current, int32_t* draft, int32_t* draft_len, int32_t* match_pos, hipStream_t stream) {
+    if (!ctx || !ctx_len || !draft || !draft_len) return CAD_EINVAL;
+    if (B <= 0 || n <= 0 || W <= 0 || D <= 0 || ctx_stride <= 0) return CAD_EINVAL;
+    if (with_current != 0 && with_current != 1) return CAD_EINVAL;
+    if (W > 8 || D > 64 || n > 64 || ctx_stride > 0x7fffffff) return CAD_EUNSUPPORTED;
+    return launch_ngram(ctx, ctx_stride, ctx_len, B, n, W, D, with_current, draft, draft_len, match_pos, stream) ==
+                   hipSuccess
+               ? CAD_OK
+               : CAD_EHIP;
+}
+
+int cad_accept_scan(const int32_t* draft, int with_current, const int32_t* draft_len, const int32_t* pred,
+                    const int32_t* first_pred, int B, int W, int D, int mode, int32_t* accepted, int32_t* best_w,
+                    int32_t* emitted, int32_t* n_emitted, int32_t* ctx, int64_t ctx_stride, int32_t* ctx_len,
+                    int ctx_cap, const cad_kv_desc* kv, hipStream_t stream) {
+    if (!draft || !draft_len || !pred || !accepted || !emitted || !n_emitted) return CAD_EINVAL;
+    if (B <= 0 || W <= 0 || D <= 0) return CAD_EINVAL;
+    if (mode == CAD_MASK_CAUSAL_SPAN) {
+        if (W != 1 || with_current != 1) return CAD_EINVAL;
+    } else if (mode == CAD_MASK_BLOCK_TRI) {
+        if (!first_pred || with_current != 0) return CAD_EINVAL;
+    } else {
+        return CAD_EINVAL;
+    }
+    if (ctx && (!ctx_len || ctx_stride <= 0 || ctx_cap <= 0 || ctx_cap > ctx_stride)) return CAD_EINVAL;
+    if (kv && (!kv->len || kv->B != B)) return CAD_EINVAL;
+    if (kv && mode == CAD_MASK_BLOCK_TRI &&
+        (!kv->k || !kv->v || kv->n_kv_heads <= 0 || (kv->head_dim != 32 && kv->head_dim != 64 &&
+                                                      kv->head_dim != 128)))
+        return CAD_EINVAL;
+    if (W > 8 || D > 64) return CAD_EUNSUPPORTED;
+    return launch_accept(draft, with_current, draft_len, pred, first_pred, B, W, D, mode, accepted, best_w, emitted,
+                         n_emitted, ctx, ctx_stride, ctx_len, ctx_cap, kv, stream) == hipSuccess
+               ? CAD_OK
+               : CAD_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// Integer kernels around the span forward.
+//
+// k_ngram: prompt-lookup draft search (PLD page, "The n-gram match, precisely"; SwitchSD's
+// kappa-gram gate with recency-ranked candidates).  One workgroup per sequence scans the
+// candidate starts newest-first in chunks of 256 (one start per thread, the chunk's token
+// window staged in LDS so the loads are coalesced), ranks the hits of a chunk by wave ballots
+// and stops as soon as W hits are known.
+//
+// k_accept: greedy left-to-right acceptance (PLD page, "Verification in a single parallel
+// pass") or the longest validated candidate of a block verify (SwitchSD), then the commit:
+// emitted tokens appended to the history, cache length advanced, and in block mode the
+// winner's accepted K/V rows moved down to the slots right after the prefix.
+#include "cad_device.h"
+
+namespace {
+
+constexpr int CH = 256;          // candidate starts per scan chunk
+constexpr int MAXN = 64;
+
+__global__ __launch_bounds__(CH) void k_ngram(const int32_t* __restrict__ ctx, int64_t stride,
+                                              const int32_t* __restrict__ ctx_len, int n, int W, int D,
+                                              int with_current, int32_t* __restrict__ draft,
+                                              int32_t* __restrict__ draft_len, int32_t* __restrict__ match_pos) {
+    __shared__ int32_t win[CH + MAXN];
+    __shared__ int32_t suf[MAXN];
+    __shared__ int wcount[CH / 64];
+    __shared__ int found_s;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t* c = ctx + (size_t)b * stride;
+    int len = ctx_len[b];
+    len = len < 0 ? 0 : (len > stride ? (int)stride : len);
+    const int rowlen = with_current + W * D;
+    int32_t* drow = draft + (size_t)b * rowlen;
+    for (int e = tid; e < rowlen; e += CH) drow[e] = (e == 0 && with_current) ? (len > 0 ? c[len - 1] : 0) : 0;
+    for (int w = tid; w < W; w += CH) {
+        draft_len[b * W + w] = 0;
+        if (match_pos) match_pos[b * W + w] = -1;
+    }
+    if (len < n + 1) return;
+    for (int k = tid; k < n; k += CH) suf[k] = c[len - n + k];
+    if (tid == 0) found_s = 0;
+    __syncthreads();
+    int found = 0;
+    for (int hi = len - n - 1; hi >= 0 && found < W; hi -= CH) {
+        const int lo = hi - CH + 1;                      // window covers starts lo..hi and their n tokens
+        for (int e = tid; e < CH + n - 1; e += CH) {
+            const int p = lo + e;
+            win[e] = p >= 0 ? c[p] : -1;
+        }
+        __syncthreads();
+        const int j = hi - tid;
+        bool hit = j >= 0;
+        for (int k = 0; k < n && hit; ++k) hit = win[j - lo + k] == suf[k];
+        const unsigned long long bal = __ballot(hit);
+        if (lane == 0) wcount[wave] = __popcll(bal);
+        __syncthreads();
+        int before = found;
+        for (int w = 0; w < wave; ++w) before += wcount[w];
+        const int rank = before + __popcll(bal & ((1ull << lane) - 1ull));
+        if (hit && rank < W) {
+            const int dl = min(D, len - (j + n));
+            int32_t* dst = drow + with_current + rank * D;
+            for (int e = 0; e < dl; ++e) dst[e] = c[j + n + e];
+            draft_len[b * W + rank] = dl;
+            if (match_pos) match_pos[b * W + rank] = j;
+        }
+        if (tid == 0) found_s = found + wcount[0] + wcount[1] + wcount[2] + wcount[3];
+        __syncthreads();
+        found = found_s;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draft, int with_current,
+                                                const int32_t* __restrict__ draft_len, const int32_t* __restrict__ pred,
+                                                const int32_t* __restrict__ first_pred, int W, int D, int mode,
+                                                int32_t* __restrict__ accepted, int32_t* __restrict__ best_w,
+                                                int32_t* __restrict__ emitted, int32_t* __restrict__ n_emitted,
+                                                int32_t* __restrict__ ctx, int64_t ctx_stride,
+                                                int32_t* __restrict__ ctx_len, int ctx_cap, void* kc, void* vc,
+                                                int32_t* __restrict__ kv_len, int32_t* __restrict__ kv_err,
+                                                int Hkv, int d, int esz, int cap) {
+    __shared__ int sa, sw, sctx, slen, sskip;
+    __shared__ int32_t em[65];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int rowlen = with_current + W * D;
+    const int32_t* drow = draft + (size_t)b * rowlen + with_current;
+    if (tid == 0) {
+        int skip = kv_err && kv_err[b] != 0;
+        int a_best = 0, w_best = 0;
+        if (mode == CAD_MASK_CAUSAL_SPAN) {
+            const int32_t* pr = pred + (size_t)b * (1 + D);
+            const int dl = draft_len[b];
+            int a = 0;
+            while (a < dl && drow[a] == pr[a]) ++a;
+            a_best = a;
+            for (int e = 0; e < a; ++e) em[e] = drow[e];
+            em[a] = pr[a];
+        } else {
+            const int32_t* pr = pred + (size_t)b * W * D;
+            const int fp = first_pred[b];
+            for (int w = 0; w < W; ++w) {
+                const int dl = draft_len[b * W + w];
+                int a = 0;
+                while (a < dl && drow[w * D + a] == (a == 0 ? fp : pr[w * D + a - 1])) ++a;
+                if (a > a_best) { a_best = a; w_best = w; }
+            }
+            for (int e = 0; e < a_best; ++e) em[e] = drow[w_best * D + e];
+            em[a_best] = a_best == 0 ? fp : pr[w_best * D + a_best - 1];
+        }
+        const int cl = ctx_len ? ctx_len[b] : 0;
+        if (!skip && ctx && (cl < 0 || cl + a_best + 1 > ctx_cap)) {
+            skip = 1;
+            if (kv_err) kv_err[b] = CAD_ECAPACITY;
+        }
+        const int kl = kv_len ? kv_len[b] : 0;
+        // the verify forward wrote rows kl .. kl+rows-1: refuse a length that could not hold them
+        const int rows = mode == CAD_MASK_CAUSAL_SPAN ? 1 + D : W * D;
+        if (!skip && kv_len && (kl < 0 || kl + rows > cap)) {
+            skip = 1;
+            if (kv_err) kv_err[b] = CAD_ECAPACITY;
+        }
+        sa = a_best; sw = w_best; sctx = cl; sskip = skip;
+        slen = kl;
+    }
+    __syncthreads();
+    const int a = sa, w = sw;
+    if (sskip) return;
+    for (int e = tid; e <= D; e += 256) emitted[(size_t)b * (D + 1) + e] = e <= a ? em[e] : 0;
+    if (ctx)
+        for (int e = tid; e <= a; e += 256) ctx[(size_t)b * ctx_stride + sctx + e] = em[e];
+    if (mode == CAD_MASK_BLOCK_TRI && kc && w > 0 && a > 0) {
+        // move rows len + w*D + j -> len + j (j < a); source and destination never overlap (w*D >= D >= a)
+        const int len = slen;
+        const int per_row = d * esz / 16;                         // 16-byte chunks per row
+        const int total = 2 * Hkv * a * per_row;
+        for (int e = tid; e < total; e += 256) {
+            const int which = e / (Hkv * a * per_row);
+            const int rem = e % (Hkv * a * per_row);
+            const int g = rem / (a * per_row), j = (rem / per_row) % a, ck = rem % per_row;
+            uint4* base = (uint4*)(which ? vc : kc);
+            const size_t head = ((size_t)b * Hkv + g) * cap;
+            const size_t rowc = (size_t)d * esz / 16;
+            base[(head + len + j) * rowc + ck] = base[(head + len + (size_t)w * D + j) * rowc + ck];
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        accepted[b] = a;
+        if (best_w) best_w[b] = w;
+        n_emitted[b] = a + 1;
+        if (ctx) ctx_len[b] = sctx + a + 1;
+        if (kv_len) kv_len[b] = slen + (mode == CAD_MASK_CAUSAL_SPAN ? a + 1 : a);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ngram(const int32_t* ctx, int64_t stride, const int32_t* ctx_len, int B, int n, int W, int D,
+                        int with_current, int32_t* draft, int32_t* draft_len, int32_t* match_pos, hipStream_t s) {
+    hipLaunchKernelGGL(k_ngram, dim3(B), dim3(CH), 0, s, ctx, stride, ctx_len, n, W, D, with_current, draft,
+                       draft_len, match_pos);
+    return hipGetLastError();
+}
+
+hipError_t launch_accept(const int32_t* draft, int with_current, const int32_t* draft_len, const int32_t* pred,
+                         const int32_t* first_pred, int B, int W, int D, int mode, int32_t* accepted,
+                         int32_t* best_w, int32_t* emitted, int32_t* n_emitted, int32_t* ctx, int64_t ctx_stride,
+                         int32_t* ctx_len, int ctx_cap, const cad_kv_desc* kv, hipStream_t s) {
+    const int esz = kv && kv->dtype == CAD_DTYPE_F32 ? 4 : 2;
+    hipLaunchKernelGGL(k_accept, dim3(B), dim3(256), 0, s, draft, with_current, draft_len, pred, first_pred, W, D,
+                       mode, accepted, best_w, emitted, n_emitted, ctx, ctx_stride, ctx_len, ctx_cap,
+                       kv ? kv->k : nullptr, kv ? kv->v : nullptr, kv ? kv->len : nullptr, kv ? kv->err : nullptr,
+                       kv ? kv->n_kv_heads : 0, kv ? kv->head_dim : 0, esz, kv ? kv->cap : 0);
+    return hipGetLastError();
+}
