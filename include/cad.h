@@ -185,6 +185,19 @@ int cad_accept_scan(const int32_t *draft, int with_current, const int32_t *draft
                     int32_t *ctx, int64_t ctx_stride, int32_t *ctx_len, int ctx_cap,
                     const cad_kv_desc *kv, hipStream_t stream);
 
+/*
+ * Diagnostics: per-stage GPU time of cad_span_forward.  While enabled, every forward records a
+ * HIP event on its stream before and after each kernel stage (the events come from a pool the
+ * library creates on first use; no device memory is allocated).  cad_profile_read waits for the
+ * recorded events, adds each stage's elapsed milliseconds into ms_sum[stage] and its launch count
+ * into count[stage] (arrays of max_stages, zero them first), clears the record and returns the
+ * number of stages.  cad_profile_stage_name names a stage.  Single-threaded use only; not for
+ * use under graph capture.
+ */
+int cad_profile_enable(int on);
+int cad_profile_read(int max_stages, double *ms_sum, int *count);
+const char *cad_profile_stage_name(int stage);
+
 /* Static description of a status code. */
 const char *cad_status_string(int status);
 

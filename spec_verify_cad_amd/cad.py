@@ -61,6 +61,12 @@ def lib() -> ctypes.CDLL:
     L.cad_status_string.argtypes = [i32]
     L.cad_status_string.restype = ctypes.c_char_p
     L.cad_version.restype = i32
+    L.cad_profile_enable.argtypes = [i32]
+    L.cad_profile_enable.restype = i32
+    L.cad_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    L.cad_profile_read.restype = i32
+    L.cad_profile_stage_name.argtypes = [i32]
+    L.cad_profile_stage_name.restype = ctypes.c_char_p
     _lib = L
     return L
 
@@ -121,15 +127,19 @@ class DeviceLayer:
 
 
 class DeviceCache:
-    """KV cache of B sequences: k, v [B, Hkv, cap, d], len [B], err [B]."""
+    """KV cache of B sequences: k, v [B, Hkv, cap, d], len [B], err [B].
 
-    def __init__(self, shape, B: int, cap: int, device="cuda"):
+    `len_tensor` may supply the int32 [B] length tensor (e.g. a view of a larger one, so the
+    lengths of several caches can be reset by one fill)."""
+
+    def __init__(self, shape, B: int, cap: int, device="cuda", len_tensor=None):
         import torch
         dt = torch.int16 if shape.dtype == "bf16" else torch.float32
         self.shape, self.B, self.cap = shape, B, cap
         self.k = torch.zeros((B, shape.n_kv_heads, cap, shape.head_dim), dtype=dt, device=device)
         self.v = torch.zeros_like(self.k)
-        self.len = torch.zeros(B, dtype=torch.int32, device=device)
+        self.len = torch.zeros(B, dtype=torch.int32, device=device) if len_tensor is None else len_tensor
+        assert self.len.dtype == torch.int32 and self.len.numel() == B and self.len.is_contiguous()
         self.err = torch.zeros(B, dtype=torch.int32, device=device)
         self.desc = KVDesc(self.k.data_ptr(), self.v.data_ptr(), self.len.data_ptr(), self.err.data_ptr(), B, cap,
                            shape.n_kv_heads, shape.head_dim, DTYPE_BF16 if shape.dtype == "bf16" else DTYPE_F32)
@@ -176,3 +186,22 @@ def accept_scan(draft, with_current: int, draft_len, pred, first_pred, B: int, W
                                  mode, _ptr(accepted), _ptr(best_w), _ptr(emitted), _ptr(n_emitted), _ptr(ctx),
                                  ctx.stride(0) if ctx is not None else 0, _ptr(ctx_len), ctx_cap, kvp,
                                  _stream(stream)), "cad_accept_scan")
+
+
+# ---------------------------------------------------------------------------------------
+# diagnostics
+# ---------------------------------------------------------------------------------------
+
+def profile_enable(on: bool = True):
+    _check(lib().cad_profile_enable(1 if on else 0), "cad_profile_enable")
+
+
+def profile_read() -> dict:
+    """Per-stage (total ms, launches) recorded since the last read; waits for the events."""
+    n = 32
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    st = lib().cad_profile_read(n, ms, cnt)
+    if st < 0:
+        raise CadError(st, "cad_profile_read")
+    return {lib().cad_profile_stage_name(i).decode(): (ms[i], cnt[i]) for i in range(st) if cnt[i]}

@@ -300,8 +300,14 @@ hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc
     if (fd.d == 128) { if (two) CAD_ATTN(128, 2); else CAD_ATTN(128, 1); }
     else { if (two) CAD_ATTN(64, 2); else CAD_ATTN(64, 1); }
 #undef CAD_ATTN
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+bool attention_uses_merge(const FwdDims& fd) {
+    return !(fd.dtype == CAD_DTYPE_F32 || (fd.d != 64 && fd.d != 128));
+}
+
+hipError_t launch_attention_merge(const FwdDims& fd, const FwdBufs& wb, hipStream_t s) {
     hipLaunchKernelGGL((k_attn_merge<uint16_t>), dim3(fd.M * fd.Hq), dim3(64), 0, s, wb.part_o, wb.part_ml,
                        wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.d, fd.cap, fd.attn_splits, (uint16_t*)wb.o);
     return hipGetLastError();

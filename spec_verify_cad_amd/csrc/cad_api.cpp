@@ -1,10 +1,50 @@
 // C ABI of libcad: host-side argument checks, workspace sizing/carving and the launch
 // sequence of the span forward.  Nothing here allocates, frees or synchronizes.
 #include <cstring>
+#include <vector>
 
 #include "cad_internal.h"
 
 namespace {
+
+// ---- opt-in per-stage profiler (diagnostics) ----
+enum Stage {
+    ST_EMBED_NORM, ST_QKV, ST_ATTN, ST_ATTN_MERGE, ST_O_PROJ, ST_NORM2, ST_GATE_UP, ST_DOWN, ST_NORM3, ST_LM_HEAD,
+    ST_ARGMAX, ST_COMMIT, ST_COUNT
+};
+const char* kStageNames[ST_COUNT] = {"embed_norm", "qkv_rope_append", "attention", "attention_merge", "o_proj_resid",
+                                     "rmsnorm_2", "gate_up_swiglu", "down_resid", "rmsnorm_final",
+                                     "lm_head_argmax", "argmax_final", "commit"};
+struct ProfRec { int stage; hipEvent_t a, b; };
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+size_t g_used = 0;
+
+hipEvent_t prof_event() {
+    if (g_used == g_pool.size()) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        g_pool.push_back(e);
+    }
+    return g_pool[g_used++];
+}
+
+// Run one launch, bracketed by events when profiling is on.
+template <class F>
+hipError_t stage(int id, hipStream_t s, F&& launch) {
+    hipEvent_t a = nullptr;
+    if (g_prof && (a = prof_event())) (void)hipEventRecord(a, s);
+    const hipError_t e = launch();
+    if (g_prof && a) {
+        hipEvent_t b = prof_event();
+        if (b) {
+            (void)hipEventRecord(b, s);
+            g_recs.push_back({id, a, b});
+        }
+    }
+    return e;
+}
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -106,6 +146,34 @@ const char* cad_status_string(int st) {
 
 int cad_version(void) { return 100; }
 
+int cad_profile_enable(int on) {
+    g_prof = on != 0;
+    return CAD_OK;
+}
+
+int cad_profile_read(int max_stages, double* ms_sum, int* count) {
+    if (!ms_sum || !count || max_stages <= 0) return CAD_EINVAL;
+    int st = CAD_OK;
+    for (const ProfRec& r : g_recs) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+            st = CAD_EHIP;
+            continue;
+        }
+        if (r.stage < max_stages) {
+            ms_sum[r.stage] += ms;
+            count[r.stage] += 1;
+        }
+    }
+    g_recs.clear();
+    g_used = 0;
+    return st == CAD_OK ? ST_COUNT : st;
+}
+
+const char* cad_profile_stage_name(int stage) {
+    return stage >= 0 && stage < ST_COUNT ? kStageNames[stage] : "unknown";
+}
+
 size_t cad_span_forward_workspace(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, int cap,
                                   int flags) {
     FwdDims fd;
@@ -132,8 +200,10 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
     const FwdBufs wb = fwd_carve(fd, workspace, kv_only);
     if (!workspace || workspace_bytes < wb.total || ((uintptr_t)workspace & 255)) return CAD_EWORKSPACE;
 
-    hipError_t e = launch_embed_norm(fd, tokens, L->embed, L->rms_eps, kv->len, kv->err, wb, stream);
-    if (e != hipSuccess) return CAD_EHIP;
+    if (stage(ST_EMBED_NORM, stream, [&] {
+            return launch_embed_norm(fd, tokens, L->embed, L->rms_eps, kv->len, kv->err, wb, stream);
+        }) != hipSuccess)
+        return CAD_EHIP;
 
     EpiParams p;
     std::memset(&p, 0, sizeof(p));
@@ -152,32 +222,52 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
             N = 2 * fd.Hkv * fd.d;
         }
         pq.N = N;
-        if (launch_gemm(fd.dtype, EPI_QKV, wb.u, w, fd.M, N, fd.h, pq, stream) != hipSuccess) return CAD_EHIP;
+        if (stage(ST_QKV, stream, [&] { return launch_gemm(fd.dtype, EPI_QKV, wb.u, w, fd.M, N, fd.h, pq, stream); }) !=
+            hipSuccess)
+            return CAD_EHIP;
     }
     if (!kv_only) {
-        if (launch_attention(fd, wb, kv->k, kv->v, stream) != hipSuccess) return CAD_EHIP;
+        if (stage(ST_ATTN, stream, [&] { return launch_attention(fd, wb, kv->k, kv->v, stream); }) != hipSuccess)
+            return CAD_EHIP;
+        if (attention_uses_merge(fd) &&
+            stage(ST_ATTN_MERGE, stream, [&] { return launch_attention_merge(fd, wb, stream); }) != hipSuccess)
+            return CAD_EHIP;
         EpiParams po = p;
         po.N = fd.h; po.resid = wb.x; po.out_f32 = wb.h1; po.out_t = nullptr;
-        if (launch_gemm(fd.dtype, EPI_RESID, wb.o, L->w_o, fd.M, fd.h, fd.Hq * fd.d, po, stream) != hipSuccess)
+        if (stage(ST_O_PROJ, stream, [&] {
+                return launch_gemm(fd.dtype, EPI_RESID, wb.o, L->w_o, fd.M, fd.h, fd.Hq * fd.d, po, stream);
+            }) != hipSuccess)
             return CAD_EHIP;
-        if (launch_rmsnorm(fd, wb.h1, wb.u2, L->rms_eps, wb.len_snap, stream) != hipSuccess) return CAD_EHIP;
+        if (stage(ST_NORM2, stream, [&] { return launch_rmsnorm(fd, wb.h1, wb.u2, L->rms_eps, wb.len_snap, stream); }) !=
+            hipSuccess)
+            return CAD_EHIP;
         EpiParams pg = p;
         pg.N = 2 * fd.ffn; pg.act = wb.act; pg.ffn = fd.ffn;
-        if (launch_gemm(fd.dtype, EPI_SWIGLU, wb.u2, L->w_gate_up, fd.M, 2 * fd.ffn, fd.h, pg, stream) != hipSuccess)
+        if (stage(ST_GATE_UP, stream, [&] {
+                return launch_gemm(fd.dtype, EPI_SWIGLU, wb.u2, L->w_gate_up, fd.M, 2 * fd.ffn, fd.h, pg, stream);
+            }) != hipSuccess)
             return CAD_EHIP;
         EpiParams pd = p;
         pd.N = fd.h; pd.resid = wb.h1; pd.out_f32 = wb.h2; pd.out_t = hidden_out;
-        if (launch_gemm(fd.dtype, EPI_RESID, wb.act, L->w_down, fd.M, fd.h, fd.ffn, pd, stream) != hipSuccess)
+        if (stage(ST_DOWN, stream, [&] {
+                return launch_gemm(fd.dtype, EPI_RESID, wb.act, L->w_down, fd.M, fd.h, fd.ffn, pd, stream);
+            }) != hipSuccess)
             return CAD_EHIP;
-        if (launch_rmsnorm(fd, wb.h2, wb.u3, L->rms_eps, wb.len_snap, stream) != hipSuccess) return CAD_EHIP;
+        if (stage(ST_NORM3, stream, [&] { return launch_rmsnorm(fd, wb.h2, wb.u3, L->rms_eps, wb.len_snap, stream); }) !=
+            hipSuccess)
+            return CAD_EHIP;
         EpiParams pl = p;
         pl.N = fd.V; pl.part = wb.amax_part; pl.ntiles = fd.lm_tiles; pl.logits = logits_out;
-        if (launch_gemm(fd.dtype, EPI_ARGMAX, wb.u3, L->w_lm, fd.M, fd.V, fd.h, pl, stream) != hipSuccess)
+        if (stage(ST_LM_HEAD, stream, [&] {
+                return launch_gemm(fd.dtype, EPI_ARGMAX, wb.u3, L->w_lm, fd.M, fd.V, fd.h, pl, stream);
+            }) != hipSuccess)
             return CAD_EHIP;
-        if (launch_argmax_final(fd, wb, argmax_out, stream) != hipSuccess) return CAD_EHIP;
+        if (stage(ST_ARGMAX, stream, [&] { return launch_argmax_final(fd, wb, argmax_out, stream); }) != hipSuccess)
+            return CAD_EHIP;
     }
     if (flags & CAD_COMMIT_ALL)
-        if (launch_commit(fd, wb, kv->len, stream) != hipSuccess) return CAD_EHIP;
+        if (stage(ST_COMMIT, stream, [&] { return launch_commit(fd, wb, kv->len, stream); }) != hipSuccess)
+            return CAD_EHIP;
     return CAD_OK;
 }
 

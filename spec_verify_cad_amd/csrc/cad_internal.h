@@ -58,6 +58,8 @@ hipError_t launch_gemm(int dtype, int kind, const void* A, const void* W, int M,
                        const EpiParams& p, hipStream_t s);
 hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc, const void* vc,
                             hipStream_t s);
+hipError_t launch_attention_merge(const FwdDims& fd, const FwdBufs& wb, hipStream_t s);
+bool attention_uses_merge(const FwdDims& fd);
 hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, int32_t* argmax_out, hipStream_t s);
 hipError_t launch_commit(const FwdDims& fd, const FwdBufs& wb, int32_t* kv_len, hipStream_t s);
 hipError_t launch_ngram(const int32_t* ctx, int64_t stride, const int32_t* ctx_len, int B, int n, int W,
