@@ -104,57 +104,78 @@ def main():
     outs = [torch.empty((1, N), dtype=torch.int32, device=dev) for N in spans]
     wss = [cad.alloc_workspace(cad.span_forward_workspace(lay0, 1, N, cad.MASK_CAUSAL, 1, 1, cap, cad.COMMIT_ALL))
            for N in spans]
-    stream = torch.cuda.current_stream()
+    ar_tok = torch.from_numpy(doc[L0:L0 + a.ar_steps].astype(np.int32).reshape(-1, 1)).to(dev)
+    ar_out = torch.empty((1, 1), dtype=torch.int32, device=dev)
+    ar_ws = cad.alloc_workspace(cad.span_forward_workspace(lay0, 1, 1, cad.MASK_CAUSAL, 1, 1, cap, cad.COMMIT_ALL))
 
-    counter = [0]
-
-    def forward(j):
-        lay = layers[counter[0] & 1]
-        counter[0] += 1
-        cad.span_forward(lay, caches[j], toks[j], spans[j], flags=cad.COMMIT_ALL, argmax_out=outs[j],
+    def forward(j, copy, stream):
+        """One copy-span commit of spans[j] from a cache of exactly L0 positions."""
+        lens[j:j + 1].fill_(L0)
+        cad.span_forward(layers[copy], caches[j], toks[j], spans[j], flags=cad.COMMIT_ALL, argmax_out=outs[j],
                          workspace=wss[j], stream=stream)
 
-    def step():
-        lens.fill_(L0)
+    def ar_run(stream, copy0=0):
+        lens[0:1].fill_(L0)
+        for i in range(a.ar_steps):
+            cad.span_forward(layers[(copy0 + i) & 1], caches[0], ar_tok[i:i + 1], 1, flags=cad.COMMIT_ALL,
+                             argmax_out=ar_out, workspace=ar_ws, stream=stream)
+
+    # eager warm-up of every launch configuration (first calls query occupancy), then capture:
+    # the forwards are replayed from HIP graphs, so the timing is of the GPU work, not of the
+    # host's launch rate.  Every replay runs every kernel of the forward.
+    for _ in range(2):
         for j in range(len(spans)):
-            forward(j)
+            forward(j, j & 1, torch.cuda.current_stream())
+        ar_run(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(torch.cuda.current_stream())
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            fn(torch.cuda.current_stream())
+        return g
+
+    # sweep step graphs: one commit of every N, weight copies alternating forward to forward
+    step_graphs = [capture(lambda st, c=c: [forward(j, (j + c) & 1, st) for j in range(len(spans))]) for c in (0, 1)]
+    per_n_graphs = [[capture(lambda st, j=j, c=c: forward(j, c, st)) for c in (0, 1)] for j in range(len(spans))]
+    ar_graphs = [capture(lambda st, c=c: ar_run(st, c)) for c in (0, 1)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(graphs, reps):
+        for i in range(3):
+            graphs[i & 1].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            graphs[i & 1].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps        # ms per replay
 
     # ---- timed region: K steps of the whole sweep
-    for _ in range(a.warmup):
-        step()
+    for i in range(a.warmup):
+        step_graphs[i & 1].replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(a.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    ms_step = timed(step_graphs, a.steps)
     wall = time.perf_counter() - wall0
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / a.steps
     tokens_step = sum(spans)
     value = tokens_step / (ms_step * 1e-3)
     log(f"sweep step {ms_step * 1e3:.1f} us -> {value:.0f} committed tok/s (wall {wall * 1e3 / a.steps:.1f} us/step)")
+    # check: the replayed commits left the caches at L0 + N and produced argmax ids
+    assert all(int(lens[j]) == L0 + N for j, N in enumerate(spans))
 
     # ---- per-N: forward time (length restore included), and per-kernel times from the profiler
     per_n = []
     for j, N in enumerate(spans):
-        for _ in range(3):
-            lens.fill_(L0)
-            forward(j)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(a.steps):
-            lens.fill_(L0)
-            forward(j)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / a.steps
+        us = timed(per_n_graphs[j], a.steps) * 1e3
         cad.profile_enable(True)
-        for _ in range(a.steps):
-            lens.fill_(L0)
-            forward(j)
+        for i in range(a.steps):
+            forward(j, i & 1, stream)
         torch.cuda.synchronize()
         prof = cad.profile_read()
         cad.profile_enable(False)
@@ -178,23 +199,7 @@ def main():
             f"({floor / us * 100:.1f}%), lm_head {lm_us} us")
 
     # ---- autoregressive baseline: single-token teacher-forced forwards
-    j0 = 0
-    lens.fill_(L0)
-    ar_tok = torch.from_numpy(doc[L0:L0 + a.ar_steps].astype(np.int32).reshape(-1, 1)).to(dev)
-    ar_out = torch.empty((1, 1), dtype=torch.int32, device=dev)
-    ar_ws = cad.alloc_workspace(cad.span_forward_workspace(lay0, 1, 1, cad.MASK_CAUSAL, 1, 1, cap, cad.COMMIT_ALL))
-    for i in range(4):
-        cad.span_forward(layers[i & 1], caches[j0], ar_tok[i:i + 1], 1, flags=cad.COMMIT_ALL, argmax_out=ar_out,
-                         workspace=ar_ws, stream=stream)
-    lens.fill_(L0)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(a.ar_steps):
-        cad.span_forward(layers[i & 1], caches[j0], ar_tok[i:i + 1], 1, flags=cad.COMMIT_ALL, argmax_out=ar_out,
-                         workspace=ar_ws, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ar_us = e0.elapsed_time(e1) * 1e3 / a.ar_steps
+    ar_us = timed(ar_graphs, max(2, a.steps // 4)) * 1e3 / a.ar_steps
     for r in per_n:
         r["speedup_vs_ar"] = round(r["N"] * ar_us / r["us"], 2)
     ar_floor, _ = R.floor_us(R.forward_bytes(shp, 1, 1, L0), R.forward_flops(shp, 1, 1, L0))

@@ -12,9 +12,9 @@ enum Stage {
     ST_EMBED_NORM, ST_QKV, ST_ATTN, ST_ATTN_MERGE, ST_O_PROJ, ST_NORM2, ST_GATE_UP, ST_DOWN, ST_NORM3, ST_LM_HEAD,
     ST_ARGMAX, ST_COMMIT, ST_COUNT
 };
-const char* kStageNames[ST_COUNT] = {"embed_norm", "qkv_rope_append", "attention", "attention_merge", "o_proj_resid",
-                                     "rmsnorm_2", "gate_up_swiglu", "down_resid", "rmsnorm_final",
-                                     "lm_head_argmax", "argmax_final", "commit"};
+const char* kStageNames[ST_COUNT] = {"embed_norm", "qkv_rope_append", "attention", "attention_merge", "o_proj",
+                                     "resid_rmsnorm_2", "gate_up_swiglu", "down_proj", "resid_rmsnorm_final",
+                                     "lm_head_argmax", "argmax_final_commit", "commit"};
 struct ProfRec { int stage; hipEvent_t a, b; };
 bool g_prof = false;
 std::vector<ProfRec> g_recs;
@@ -93,7 +93,8 @@ bool fwd_dims(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, in
     fd->Dblk = mode == CAD_MASK_BLOCK_TRI ? D : 1;
     fd->dtype = L->dtype; fd->esz = L->dtype == CAD_DTYPE_F32 ? 4 : 2;
     fd->qkv_n = (fd->Hq + 2 * fd->Hkv) * fd->d;
-    fd->lm_tiles = gemm_plan(fd->dtype, fd->M, fd->V, false).nnt;
+    fd->o_slices = gemm_partial_slices(fd->dtype, fd->M, fd->h, fd->Hq * fd->d);
+    fd->down_slices = gemm_partial_slices(fd->dtype, fd->M, fd->h, fd->ffn);
     attn_plan(fd);
     return true;
 }
@@ -110,8 +111,11 @@ FwdBufs fwd_carve(const FwdDims& fd, void* base, bool kv_only) {
     };
     const size_t M = fd.M, h = fd.h, e = fd.esz, qd = (size_t)fd.Hq * fd.d;
     w.len_snap = (int32_t*)take(fd.B * sizeof(int32_t));
+    w.rope_cs = (float2*)take(M * (size_t)(fd.d / 2) * sizeof(float2));
     w.u = take(M * h * e);
     if (!kv_only) {
+        w.amax_slots = gemm_argmax_slots(fd.dtype, fd.M, fd.V, fd.h);
+        w.amax_part = (float2*)take(M * (size_t)w.amax_slots * sizeof(float2));
         w.x = (float*)take(M * h * 4);
         w.q = take(M * qd * e);
         w.o = take(M * qd * e);
@@ -124,10 +128,23 @@ FwdBufs fwd_carve(const FwdDims& fd, void* base, bool kv_only) {
         w.act = take(M * (size_t)fd.ffn * e);
         w.h2 = (float*)take(M * h * 4);
         w.u3 = take(M * h * e);
-        w.amax_part = (float2*)take(M * (size_t)fd.lm_tiles * sizeof(float2));
+        const int S = fd.o_slices > fd.down_slices ? fd.o_slices : fd.down_slices;
+        w.part = (float*)take((size_t)S * M * h * 4);
     }
     w.total = off;
     return w;
+}
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 extern "C" {
@@ -201,7 +218,7 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
     if (!workspace || workspace_bytes < wb.total || ((uintptr_t)workspace & 255)) return CAD_EWORKSPACE;
 
     if (stage(ST_EMBED_NORM, stream, [&] {
-            return launch_embed_norm(fd, tokens, L->embed, L->rms_eps, kv->len, kv->err, wb, stream);
+            return launch_embed_norm(fd, tokens, L->embed, L->rms_eps, L->rope_base, kv->len, kv->err, wb, stream);
         }) != hipSuccess)
         return CAD_EHIP;
 
@@ -209,7 +226,7 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
     std::memset(&p, 0, sizeof(p));
     p.M = fd.M; p.len_snap = wb.len_snap; p.Nq = fd.Nq; p.cap = fd.cap;
     p.q_out = wb.q; p.kc = kv->k; p.vc = kv->v;
-    p.Hq = fd.Hq; p.Hkv = fd.Hkv; p.d = fd.d; p.mode = mode; p.Dblk = fd.Dblk; p.rope_base = L->rope_base;
+    p.Hq = fd.Hq; p.Hkv = fd.Hkv; p.d = fd.d; p.rope_cs = wb.rope_cs;
     const size_t h = fd.h;
     // QKV projection + RoPE + K/V append (K/V rows only for a cache prefill)
     {
@@ -217,57 +234,70 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
         const char* w = (const char*)L->w_qkv;
         int N = fd.qkv_n;
         if (kv_only) {
-            pq.f_off = fd.Hq * fd.d;
-            w += (size_t)pq.f_off * h * fd.esz;
+            pq.head_off = fd.Hq;
+            w += (size_t)fd.Hq * fd.d * h * fd.esz;
             N = 2 * fd.Hkv * fd.d;
         }
         pq.N = N;
-        if (stage(ST_QKV, stream, [&] { return launch_gemm(fd.dtype, EPI_QKV, wb.u, w, fd.M, N, fd.h, pq, stream); }) !=
-            hipSuccess)
+        if (stage(ST_QKV, stream, [&] {
+                return launch_gemm(fd.dtype, EPI_QKV, wb.u, w, fd.M, N, fd.h, 1, pq, stream);
+            }) != hipSuccess)
             return CAD_EHIP;
     }
-    if (!kv_only) {
-        if (stage(ST_ATTN, stream, [&] { return launch_attention(fd, wb, kv->k, kv->v, stream); }) != hipSuccess)
+    if (kv_only) {
+        if ((flags & CAD_COMMIT_ALL) &&
+            stage(ST_COMMIT, stream, [&] { return launch_commit(fd, wb, kv->len, stream); }) != hipSuccess)
             return CAD_EHIP;
-        if (attention_uses_merge(fd) &&
-            stage(ST_ATTN_MERGE, stream, [&] { return launch_attention_merge(fd, wb, stream); }) != hipSuccess)
-            return CAD_EHIP;
-        EpiParams po = p;
-        po.N = fd.h; po.resid = wb.x; po.out_f32 = wb.h1; po.out_t = nullptr;
-        if (stage(ST_O_PROJ, stream, [&] {
-                return launch_gemm(fd.dtype, EPI_RESID, wb.o, L->w_o, fd.M, fd.h, fd.Hq * fd.d, po, stream);
-            }) != hipSuccess)
-            return CAD_EHIP;
-        if (stage(ST_NORM2, stream, [&] { return launch_rmsnorm(fd, wb.h1, wb.u2, L->rms_eps, wb.len_snap, stream); }) !=
-            hipSuccess)
-            return CAD_EHIP;
-        EpiParams pg = p;
-        pg.N = 2 * fd.ffn; pg.act = wb.act; pg.ffn = fd.ffn;
-        if (stage(ST_GATE_UP, stream, [&] {
-                return launch_gemm(fd.dtype, EPI_SWIGLU, wb.u2, L->w_gate_up, fd.M, 2 * fd.ffn, fd.h, pg, stream);
-            }) != hipSuccess)
-            return CAD_EHIP;
-        EpiParams pd = p;
-        pd.N = fd.h; pd.resid = wb.h1; pd.out_f32 = wb.h2; pd.out_t = hidden_out;
-        if (stage(ST_DOWN, stream, [&] {
-                return launch_gemm(fd.dtype, EPI_RESID, wb.act, L->w_down, fd.M, fd.h, fd.ffn, pd, stream);
-            }) != hipSuccess)
-            return CAD_EHIP;
-        if (stage(ST_NORM3, stream, [&] { return launch_rmsnorm(fd, wb.h2, wb.u3, L->rms_eps, wb.len_snap, stream); }) !=
-            hipSuccess)
-            return CAD_EHIP;
-        EpiParams pl = p;
-        pl.N = fd.V; pl.part = wb.amax_part; pl.ntiles = fd.lm_tiles; pl.logits = logits_out;
-        if (stage(ST_LM_HEAD, stream, [&] {
-                return launch_gemm(fd.dtype, EPI_ARGMAX, wb.u3, L->w_lm, fd.M, fd.V, fd.h, pl, stream);
-            }) != hipSuccess)
-            return CAD_EHIP;
-        if (stage(ST_ARGMAX, stream, [&] { return launch_argmax_final(fd, wb, argmax_out, stream); }) != hipSuccess)
-            return CAD_EHIP;
+        return CAD_OK;
     }
-    if (flags & CAD_COMMIT_ALL)
-        if (stage(ST_COMMIT, stream, [&] { return launch_commit(fd, wb, kv->len, stream); }) != hipSuccess)
-            return CAD_EHIP;
+    if (stage(ST_ATTN, stream, [&] { return launch_attention(fd, wb, kv->k, kv->v, stream); }) != hipSuccess)
+        return CAD_EHIP;
+    if (attention_uses_merge(fd) &&
+        stage(ST_ATTN_MERGE, stream, [&] { return launch_attention_merge(fd, wb, stream); }) != hipSuccess)
+        return CAD_EHIP;
+    // O projection (K-slice partials) -> h1 = x + o.Wo^T, u2 = RMSNorm(h1)
+    EpiParams po = p;
+    po.N = fd.h; po.part = wb.part;
+    if (stage(ST_O_PROJ, stream, [&] {
+            return launch_gemm(fd.dtype, EPI_PARTIAL, wb.o, L->w_o, fd.M, fd.h, fd.Hq * fd.d, fd.o_slices, po,
+                               stream);
+        }) != hipSuccess)
+        return CAD_EHIP;
+    if (stage(ST_NORM2, stream, [&] {
+            return launch_resid_norm(fd, wb.x, wb.part, fd.o_slices, wb.h1, nullptr, wb.u2, L->rms_eps, wb.len_snap,
+                                     stream);
+        }) != hipSuccess)
+        return CAD_EHIP;
+    EpiParams pg = p;
+    pg.N = 2 * fd.ffn; pg.act = wb.act; pg.ffn = fd.ffn;
+    if (stage(ST_GATE_UP, stream, [&] {
+            return launch_gemm(fd.dtype, EPI_SWIGLU, wb.u2, L->w_gate_up, fd.M, 2 * fd.ffn, fd.h, 1, pg, stream);
+        }) != hipSuccess)
+        return CAD_EHIP;
+    // down projection (K-slice partials) -> h2 = h1 + act.Wd^T, hidden_out = rnd(h2), u3 = RMSNorm(h2)
+    EpiParams pd = p;
+    pd.N = fd.h; pd.part = wb.part;
+    if (stage(ST_DOWN, stream, [&] {
+            return launch_gemm(fd.dtype, EPI_PARTIAL, wb.act, L->w_down, fd.M, fd.h, fd.ffn, fd.down_slices, pd,
+                               stream);
+        }) != hipSuccess)
+        return CAD_EHIP;
+    if (stage(ST_NORM3, stream, [&] {
+            return launch_resid_norm(fd, wb.h1, wb.part, fd.down_slices, wb.h2, hidden_out, wb.u3, L->rms_eps,
+                                     wb.len_snap, stream);
+        }) != hipSuccess)
+        return CAD_EHIP;
+    // LM head + argmax partials, then the per-row reduction (+ commit of the cache lengths)
+    EpiParams pl = p;
+    pl.N = fd.V; pl.amax_part = wb.amax_part; pl.amax_slots = wb.amax_slots; pl.logits = logits_out;
+    if (stage(ST_LM_HEAD, stream, [&] {
+            return launch_gemm(fd.dtype, EPI_ARGMAX, wb.u3, L->w_lm, fd.M, fd.V, fd.h, 1, pl, stream);
+        }) != hipSuccess)
+        return CAD_EHIP;
+    if (stage(ST_ARGMAX, stream, [&] {
+            return launch_argmax_final(fd, wb, argmax_out, (flags & CAD_COMMIT_ALL) ? kv->len : nullptr, stream);
+        }) != hipSuccess)
+        return CAD_EHIP;
     return CAD_OK;
 }
 

@@ -31,6 +31,14 @@ template <> struct Elt<float> {
     static __device__ __forceinline__ float rnd(float v) { return v; }
 };
 
+// four consecutive values -> four consecutive stored elements (8 bytes of bf16 / 16 of fp32)
+__device__ __forceinline__ void st4(uint16_t* p, f32x4_t v) {
+    uint2 w;
+    w.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *(uint2*)p = w;
+}
+
 // ---- wavefront reductions (64 lanes) ------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -7,60 +7,80 @@
 #include "cad.h"
 
 // Epilogue kinds of the projection GEMMs.
-enum EpiKind { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+//   EPI_QKV     RoPE at the row's absolute position; q -> workspace, k/v appended to the cache
+//   EPI_SWIGLU  act = rnd(silu(gate) * up); a tile holds matching gate and up features
+//   EPI_ARGMAX  LM head: per-row (max, lowest index) partials, one slot per workgroup (or per
+//               column tile); a small row kernel reduces the slots and commits the cache length
+//   EPI_PARTIAL fp32 partial sums of one K slice, part[slice][row][feature]; the next row
+//               kernel adds the slices (in slice order) to the residual stream
+enum EpiKind { EPI_QKV = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2, EPI_PARTIAL = 3 };
 
 // Everything a GEMM epilogue needs.  Unused fields are ignored by the other kinds.
 struct EpiParams {
-    int M, N;                       // output rows (tokens) and logical output columns
-    const int32_t* len_snap;        // [B] cache length captured at the start of the forward
+    int M, N;                       // output rows (tokens) and logical output features
+    const int32_t* len_snap;        // [B] cache length captured by the first kernel of the forward
     int Nq, cap;
-    // EPI_QKV: RoPE + q write + K/V append
+    // EPI_QKV
     void* q_out; void* kc; void* vc;
-    int Hq, Hkv, d, mode, Dblk, f_off;
-    double rope_base;
-    // EPI_RESID: out = resid + acc (fp32), optional rounded copy
-    const float* resid; float* out_f32; void* out_t;
-    // EPI_SWIGLU: act = rnd(silu(gate) * up)
+    int Hq, Hkv, d, head_off;       // head_off: first head the GEMM produces (Hq for a K/V-only pass)
+    const float2* rope_cs;          // [M, d/2] (cos, sin) of each row's position
+    // EPI_SWIGLU
     void* act; int ffn;
-    // EPI_ARGMAX: per-(row, column tile) (max, index) partials, optional logits
-    float2* part; int ntiles; float* logits;
+    // EPI_ARGMAX
+    float2* amax_part;              // [M, slots] (max, index bits)
+    int amax_slots;
+    float* logits;                  // nullable debug output [M, N]
+    // EPI_PARTIAL
+    float* part;                    // [S, M, N]
+    int k_slice;                    // elements of K per slice (multiple of 64)
 };
-
-// Tile plan of a projection GEMM (shared by workspace sizing and launch).
-struct GemmPlan { int BM, BN, nmt, nnt, grid; };
-GemmPlan gemm_plan(int dtype, int M, int N, bool swiglu);
 
 // Per-forward derived sizes.
 struct FwdDims {
     int B, Nq, M, h, Hq, Hkv, d, ffn, V, cap, mode, Dblk, dtype, esz;
-    int qkv_n, lm_tiles, attn_splits, attn_chunk, attn_rows_per_wg, attn_row_tiles;
+    int qkv_n;
+    int attn_splits, attn_chunk, attn_rows_per_wg, attn_row_tiles;
+    int o_slices, down_slices;      // K slices of the O and down projections (partials)
 };
 
 // Workspace carve-up (offsets are 256-byte aligned).
 struct FwdBufs {
     int32_t* len_snap;
+    float2* amax_part; int amax_slots;
+    float2* rope_cs;
     float* x; void* u; void* q; void* o;
     float* part_o; float* part_ml;
     float* h1; void* u2; void* act; float* h2; void* u3;
-    float2* amax_part;
+    float* part;                    // K-slice partials of the O and down projections
     size_t total;
 };
 
 bool fwd_dims(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, int cap, FwdDims* fd);
 FwdBufs fwd_carve(const FwdDims& fd, void* base, bool kv_only);
 
+// number of compute units of the current device (cached per device)
+int device_cu_count();
+
 // Launchers: each returns hipSuccess or the launch error.
 hipError_t launch_embed_norm(const FwdDims& fd, const int32_t* tokens, const void* embed, float eps,
-                             const int32_t* kv_len, int32_t* err, const FwdBufs& wb, hipStream_t s);
-hipError_t launch_rmsnorm(const FwdDims& fd, const float* in, void* out, float eps, const int32_t* len_snap,
-                          hipStream_t s);
-hipError_t launch_gemm(int dtype, int kind, const void* A, const void* W, int M, int N, int K,
-                       const EpiParams& p, hipStream_t s);
+                             double rope_base, const int32_t* kv_len, int32_t* err, const FwdBufs& wb,
+                             hipStream_t s);
+hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, int32_t* argmax_out, int32_t* kv_len,
+                               hipStream_t s);
+hipError_t launch_resid_norm(const FwdDims& fd, const float* base, const float* part, int slices, float* out_f32,
+                             void* out_t, void* normed, float eps, const int32_t* len_snap, hipStream_t s);
+// Projection GEMM Y[M, N] = A[M, K] . W[N, K]^T with a fused epilogue; picks the kernel
+// (weight-streaming for few rows, LDS-tiled MFMA otherwise) and its K slicing.  For
+// EPI_PARTIAL `slices` gives the number of K slices (p.k_slice is filled in).
+hipError_t launch_gemm(int dtype, int kind, const void* A, const void* W, int M, int N, int K, int slices,
+                       EpiParams p, hipStream_t s);
+int gemm_partial_slices(int dtype, int M, int N, int K);
+// (max, index) partial slots per row written by an EPI_ARGMAX launch of this shape
+int gemm_argmax_slots(int dtype, int M, int N, int K);
 hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc, const void* vc,
                             hipStream_t s);
 hipError_t launch_attention_merge(const FwdDims& fd, const FwdBufs& wb, hipStream_t s);
 bool attention_uses_merge(const FwdDims& fd);
-hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, int32_t* argmax_out, hipStream_t s);
 hipError_t launch_commit(const FwdDims& fd, const FwdBufs& wb, int32_t* kv_len, hipStream_t s);
 hipError_t launch_ngram(const int32_t* ctx, int64_t stride, const int32_t* ctx_len, int B, int n, int W,
                         int D, int with_current, int32_t* draft, int32_t* draft_len, int32_t* match_pos,

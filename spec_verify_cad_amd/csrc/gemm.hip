@@ -1,15 +1,24 @@
-// Projection GEMMs of the span forward: Y[M, N] = A[M, K] . W[N, K]^T, where A holds the
-// M = B*Nq token rows of the forward (activations) and W is a row-major [out, in] weight.
-// The bf16 kernel runs on gfx950 MFMA (v_mfma_f32_16x16x32_bf16) with LDS-staged A and W
-// tiles; the fp32 kernel (for an fp32 layer) uses plain FMA.  Both stage the fp32
-// accumulator tile in LDS and finish with one of four fused epilogues:
-//   EPI_QKV    RoPE at the row's absolute position, q -> workspace, k/v appended to the cache
-//              (Copy-as-Decode Appendix K: positions advance exactly as in decode steps);
-//   EPI_RESID  residual add into the fp32 residual stream (+ optional rounded copy);
-//   EPI_SWIGLU silu(gate) * up, the tile holding matching gate and up columns;
-//   EPI_ARGMAX per-(row, column-tile) max with the lowest index among ties (LM head), so
-//              the logits never reach memory unless a debug buffer is given.
+// LDS-tiled projection GEMMs of the span forward for many token rows: Y[M, N] = A[M, K] . W[N, K]^T,
+// where A holds the M = B*Nq token rows of the forward (activations) and W is a row-major
+// [out, in] weight.  The bf16 kernel runs on gfx950 MFMA (v_mfma_f32_16x16x32_bf16) with
+// LDS-staged A and W tiles; the fp32 kernel (for an fp32 layer) uses plain FMA.  Both stage the
+// fp32 accumulator tile in LDS and finish with one of the fused epilogues (EpiKind):
+//   EPI_QKV     RoPE at the row's absolute position, q -> workspace, k/v appended to the cache
+//               (Copy-as-Decode, Appendix K: positions advance exactly as in decode steps);
+//   EPI_SWIGLU  silu(gate) * up, the tile holding matching gate and up columns;
+//   EPI_ARGMAX  per-(row, column-tile) max with the lowest index among ties (LM head), so the
+//               logits never reach memory unless a debug buffer is given;
+//   EPI_PARTIAL fp32 partial sums of one K slice (O and down projections; the residual add
+//               and the following RMSNorm happen in the next row kernel).
+// A launch may split K into slices (units = tiles x slices) so that narrow projections still
+// fill the chip.  Few-row launches go to the weight-streaming kernel instead.
 #include "cad_device.h"
+
+hipError_t launch_skinny(int kind, const void* A, const void* W, int M, int N, int K, const EpiParams& p,
+                         hipStream_t s);
+bool skinny_supports(int kind, int M, int K);
+int skinny_partial_slices(int K);
+int skinny_argmax_slots(int M, int N, int K);
 
 namespace {
 
@@ -18,106 +27,75 @@ constexpr int LPAD = 8;          // bf16 elements of padding per LDS row (16 byt
 constexpr int LDK = BK + LPAD;   // LDS row pitch in elements
 
 // ---------------------------------------------------------------------------------------
-// epilogues (run by all 256 threads on the fp32 tile C[BM][ldc] in LDS, token-major)
+// epilogues on the fp32 tile C[BM][ldc] in LDS (token-major), run by all 256 threads
 // ---------------------------------------------------------------------------------------
-
-template <typename T>
-__device__ void epi_qkv(const float* C, int ldc, int m0, int n0, int BM, int BN, const EpiParams& p) {
-    const int half = p.d / 2;
-    for (int idx = threadIdx.x; idx < BM * BN; idx += blockDim.x) {
-        const int r = idx / BN, f = idx % BN;
-        const int row = m0 + r, F = n0 + f;
-        if (row >= p.M || F >= p.N) continue;
-        const int b = row / p.Nq, it = row % p.Nq;
-        if (!seq_ok(p.len_snap, b, p.Nq, p.cap)) continue;
-        const int len = p.len_snap[b];
-        const int Fg = F + p.f_off;
-        const int head = Fg / p.d, i = Fg % p.d;
-        const size_t slot = (size_t)len + it;
-        if (head >= p.Hq + p.Hkv) {                                   // V: stored as is
-            const int g = head - p.Hq - p.Hkv;
-            Elt<T>::st((T*)p.vc, (((size_t)b * p.Hkv + g) * p.cap + slot) * p.d + i, C[r * ldc + f]);
-            continue;
-        }
-        if (i >= half) continue;                                      // the partner thread rotates the pair
-        const float a = C[r * ldc + f], bb = C[r * ldc + f + half];
-        const int pos = len + (p.mode == CAD_MASK_BLOCK_TRI ? it % p.Dblk : it);
-        const double ang = (double)pos * pow(p.rope_base, -2.0 * (double)i / (double)p.d);
-        const float c = (float)cos(ang), s = (float)sin(ang);
-        const float y0 = a * c - bb * s, y1 = bb * c + a * s;
-        if (head < p.Hq) {
-            T* q = (T*)p.q_out + ((size_t)row * p.Hq + head) * p.d;
-            Elt<T>::st(q, i, y0);
-            Elt<T>::st(q, i + half, y1);
-        } else {
-            const int g = head - p.Hq;
-            T* k = (T*)p.kc + (((size_t)b * p.Hkv + g) * p.cap + slot) * p.d;
-            Elt<T>::st(k, i, y0);
-            Elt<T>::st(k, i + half, y1);
-        }
-    }
-}
-
-template <typename T>
-__device__ void epi_resid(const float* C, int ldc, int m0, int n0, int BM, int BN, const EpiParams& p) {
-    for (int idx = threadIdx.x; idx < BM * BN; idx += blockDim.x) {
-        const int r = idx / BN, f = idx % BN;
-        const int row = m0 + r, F = n0 + f;
-        if (row >= p.M || F >= p.N) continue;
-        if (!seq_ok(p.len_snap, row / p.Nq, p.Nq, p.cap)) continue;
-        const size_t o = (size_t)row * p.N + F;
-        const float v = p.resid[o] + C[r * ldc + f];
-        p.out_f32[o] = v;
-        if (p.out_t) Elt<T>::st((T*)p.out_t, o, v);
-    }
-}
-
-template <typename T>
-__device__ void epi_swiglu(const float* C, int ldc, int m0, int n0, int BM, int BN, const EpiParams& p) {
-    const int hb = BN / 2, f0 = n0 / 2;      // the tile holds gate cols [0,hb) and up cols [hb,BN)
-    for (int idx = threadIdx.x; idx < BM * hb; idx += blockDim.x) {
-        const int r = idx / hb, j = idx % hb;
-        const int row = m0 + r, F = f0 + j;
-        if (row >= p.M || F >= p.ffn) continue;
-        if (!seq_ok(p.len_snap, row / p.Nq, p.Nq, p.cap)) continue;
-        const float g = C[r * ldc + j], u = C[r * ldc + hb + j];
-        const float sg = g / (1.0f + __expf(-g));
-        Elt<T>::st((T*)p.act, (size_t)row * p.ffn + F, sg * u);
-    }
-}
-
-__device__ void epi_argmax(const float* C, int ldc, int m0, int n0, int BM, int BN, int tile_n,
-                           const EpiParams& p) {
-    const int tpr = blockDim.x / BM;         // threads per row (power of two, <= 64)
-    const int r = threadIdx.x / tpr, sub = threadIdx.x % tpr;
-    const int row = m0 + r;
-    float best = -INFINITY;
-    int bi = 0x7fffffff;
-    const bool live = row < p.M && seq_ok(p.len_snap, row / p.Nq, p.Nq, p.cap);
-    if (live) {
-        for (int f = sub; f < BN; f += tpr) {
-            const int F = n0 + f;
-            if (F >= p.N) break;
-            const float v = C[r * ldc + f];
-            if (v > best) { best = v; bi = F; }                      // increasing F: first max kept
-            if (p.logits) p.logits[(size_t)row * p.N + F] = v;
-        }
-    }
-    for (int o = tpr / 2; o > 0; o >>= 1) {
-        const float v2 = __shfl_xor(best, o, 64);
-        const int i2 = __shfl_xor(bi, o, 64);
-        argmax_merge(best, bi, v2, i2);
-    }
-    if (live && sub == 0) p.part[(size_t)row * p.ntiles + tile_n] = make_float2(best, __int_as_float(bi));
-}
-
 template <typename T, int KIND>
-__device__ __forceinline__ void run_epilogue(const float* C, int ldc, int m0, int n0, int BM, int BN, int tile_n,
-                                             const EpiParams& p) {
-    if constexpr (KIND == EPI_QKV) epi_qkv<T>(C, ldc, m0, n0, BM, BN, p);
-    else if constexpr (KIND == EPI_RESID) epi_resid<T>(C, ldc, m0, n0, BM, BN, p);
-    else if constexpr (KIND == EPI_SWIGLU) epi_swiglu<T>(C, ldc, m0, n0, BM, BN, p);
-    else epi_argmax(C, ldc, m0, n0, BM, BN, tile_n, p);
+__device__ void tile_epilogue(const float* C, int ldc, int m0, int n0, int BM, int BN, int ks, const EpiParams& p) {
+    if constexpr (KIND == EPI_QKV) {
+        const int half = p.d / 2, npair = BN / 2;
+        for (int idx = threadIdx.x; idx < BM * npair; idx += blockDim.x) {
+            const int r = idx / npair, q = idx % npair;
+            const int f1 = (q / half) * p.d + q % half, i = q % half;
+            const int row = m0 + r, F1 = n0 + f1;
+            if (row >= p.M || F1 >= p.N) continue;
+            const int b = row / p.Nq, it = row % p.Nq;
+            if (!seq_ok(p.len_snap, b, p.Nq, p.cap)) continue;
+            const int head = F1 / p.d + p.head_off;
+            const size_t slot = (size_t)p.len_snap[b] + it;
+            const float x1 = C[r * ldc + f1], x2 = C[r * ldc + f1 + half];
+            if (head >= p.Hq + p.Hkv) {
+                T* v = (T*)p.vc + (((size_t)b * p.Hkv + (head - p.Hq - p.Hkv)) * p.cap + slot) * p.d;
+                Elt<T>::st(v, i, x1);
+                Elt<T>::st(v, i + half, x2);
+                continue;
+            }
+            const float2 cs = p.rope_cs[(size_t)row * half + i];
+            const float y1 = x1 * cs.x - x2 * cs.y, y2 = x2 * cs.x + x1 * cs.y;
+            T* dst = head < p.Hq ? (T*)p.q_out + ((size_t)row * p.Hq + head) * p.d
+                                 : (T*)p.kc + (((size_t)b * p.Hkv + (head - p.Hq)) * p.cap + slot) * p.d;
+            Elt<T>::st(dst, i, y1);
+            Elt<T>::st(dst, i + half, y2);
+        }
+    } else if constexpr (KIND == EPI_SWIGLU) {
+        const int hb = BN / 2, f0 = n0 / 2;      // the tile holds gate cols [0,hb) and up cols [hb,BN)
+        for (int idx = threadIdx.x; idx < BM * hb; idx += blockDim.x) {
+            const int r = idx / hb, j = idx % hb;
+            const int row = m0 + r, F = f0 + j;
+            if (row >= p.M || F >= p.ffn) continue;
+            if (!seq_ok(p.len_snap, row / p.Nq, p.Nq, p.cap)) continue;
+            const float g = C[r * ldc + j], u = C[r * ldc + hb + j];
+            Elt<T>::st((T*)p.act, (size_t)row * p.ffn + F, g / (1.0f + __expf(-g)) * u);
+        }
+    } else if constexpr (KIND == EPI_PARTIAL) {
+        for (int idx = threadIdx.x; idx < BM * BN; idx += blockDim.x) {
+            const int r = idx / BN, f = idx % BN;
+            const int row = m0 + r, F = n0 + f;
+            if (row >= p.M || F >= p.N) continue;
+            p.part[((size_t)ks * p.M + row) * p.N + F] = C[r * ldc + f];
+        }
+    } else {                                     // EPI_ARGMAX
+        const int tpr = blockDim.x / BM;         // threads per row (power of two, <= 64)
+        const int r = threadIdx.x / tpr, sub = threadIdx.x % tpr;
+        const int row = m0 + r;
+        float best = -INFINITY;
+        int bi = 0x7fffffff;
+        const bool live = row < p.M && seq_ok(p.len_snap, row / p.Nq, p.Nq, p.cap);
+        if (live) {
+            for (int f = sub; f < BN; f += tpr) {
+                const int F = n0 + f;
+                if (F >= p.N) break;
+                const float v = C[r * ldc + f];
+                if (v > best) { best = v; bi = F; }                      // increasing F: first max kept
+                if (p.logits) p.logits[(size_t)row * p.N + F] = v;
+            }
+        }
+        for (int o = tpr / 2; o > 0; o >>= 1) {
+            const float v2 = __shfl_xor(best, o, 64);
+            const int i2 = __shfl_xor(bi, o, 64);
+            argmax_merge(best, bi, v2, i2);
+        }
+        if (live && sub == 0) p.amax_part[(size_t)row * p.amax_slots + n0 / BN] = make_float2(best, __int_as_float(bi));
+    }
 }
 
 // W row read by tile row `tr` of column tile `nt`.  For SwiGLU the first half of the tile
@@ -133,9 +111,9 @@ __device__ __forceinline__ int w_row(int tr, int nt, int BN, int N, int ffn, boo
     return tr < hb ? F : ffn + F;
 }
 
-// XCD-aware tile id: workgroups are dealt round-robin over the 8 XCDs, so give each XCD a
-// contiguous run of tiles (neighbouring row tiles of one column tile share its W in L2).
-__device__ __forceinline__ int xcd_tile(int bid, int grid) {
+// XCD-aware unit id: workgroups are dealt round-robin over the 8 XCDs, so give each XCD a
+// contiguous run of units (neighbouring row tiles of one column tile share its W in L2).
+__device__ __forceinline__ int xcd_unit(int bid, int grid) {
     return (bid % 8) * (grid / 8) + bid / 8;
 }
 
@@ -145,7 +123,8 @@ __device__ __forceinline__ int xcd_tile(int bid, int grid) {
 // ---------------------------------------------------------------------------------------
 template <int KIND, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                                                   int M, int N, int K, int nmt, int total, int ffn, EpiParams p) {
+                                                   int M, int N, int K, int nmt, int nnt, int S, int ffn,
+                                                   EpiParams p) {
     constexpr int FT = BN / WN / 16, TT = BM / WM / 16;
     constexpr int WCH = BN * (BK / 8) / 256;                     // 16-byte W chunks per thread
     constexpr int ACH = (BM * (BK / 8) + 255) / 256;             // 16-byte A chunks per thread
@@ -156,96 +135,99 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ 
     uint16_t* Ws = (uint16_t*)smem;
     uint16_t* As = Ws + BN * LDK;
 
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    if (tile >= total) return;
-    const int mt = tile % nmt, nt = tile / nmt;
-    const int m0 = mt * BM;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int l16 = lane & 15, g4 = lane >> 4;
+    const int total = nmt * nnt * S;
+    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    if (unit < total) {
+        const int ks = unit % S, tile = unit / S;
+        const int mt = tile % nmt, nt = tile / nmt;
+        const int m0 = mt * BM;
+        const int kbeg = ks * p.k_slice, kend = min(K, kbeg + p.k_slice);
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int wm = wave / WN, wn = wave % WN;
+        const int l16 = lane & 15, g4 = lane >> 4;
 
-    // global -> register prefetch of one BK stage
-    uint4 wreg[WCH], areg[ACH];
-    const uint16_t* wsrc[WCH];
-    bool wval[WCH];
-#pragma unroll
-    for (int c = 0; c < WCH; ++c) {
-        const int ch = tid + c * 256, tr = ch / (BK / 8);
-        bool v;
-        const int r = w_row(tr, nt, BN, N, ffn, v);
-        wval[c] = v;
-        wsrc[c] = W + (size_t)(v ? r : 0) * K + (ch % (BK / 8)) * 8;
-    }
-    auto load_stage = [&](int k0) {
+        // global -> register prefetch of one BK stage
+        uint4 wreg[WCH], areg[ACH];
+        const uint16_t* wsrc[WCH];
+        bool wval[WCH];
 #pragma unroll
         for (int c = 0; c < WCH; ++c) {
-            const int kk = k0 + ((tid + c * 256) % (BK / 8)) * 8;
-            wreg[c] = (wval[c] && kk < K) ? *(const uint4*)(wsrc[c] + k0) : make_uint4(0, 0, 0, 0);
+            const int ch = tid + c * 256, tr = ch / (BK / 8);
+            bool v;
+            const int r = w_row(tr, nt, BN, N, ffn, v);
+            wval[c] = v;
+            wsrc[c] = W + (size_t)(v ? r : 0) * K + (ch % (BK / 8)) * 8;
         }
+        auto load_stage = [&](int k0) {
 #pragma unroll
-        for (int c = 0; c < ACH; ++c) {
-            const int ch = tid + c * 256;
-            const int r = ch / (BK / 8), kk = k0 + (ch % (BK / 8)) * 8;
-            const bool v = ch < BM * (BK / 8) && m0 + r < M && kk < K;
-            areg[c] = v ? *(const uint4*)(A + (size_t)(m0 + r) * K + kk) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_stage = [&]() {
+            for (int c = 0; c < WCH; ++c) {
+                const int kk = k0 + ((tid + c * 256) % (BK / 8)) * 8;
+                wreg[c] = (wval[c] && kk < kend) ? *(const uint4*)(wsrc[c] + k0) : make_uint4(0, 0, 0, 0);
+            }
 #pragma unroll
-        for (int c = 0; c < WCH; ++c) {
-            const int ch = tid + c * 256;
-            *(uint4*)(Ws + (ch / (BK / 8)) * LDK + (ch % (BK / 8)) * 8) = wreg[c];
-        }
+            for (int c = 0; c < ACH; ++c) {
+                const int ch = tid + c * 256;
+                const int r = ch / (BK / 8), kk = k0 + (ch % (BK / 8)) * 8;
+                const bool v = ch < BM * (BK / 8) && m0 + r < M && kk < kend;
+                areg[c] = v ? *(const uint4*)(A + (size_t)(m0 + r) * K + kk) : make_uint4(0, 0, 0, 0);
+            }
+        };
+        auto store_stage = [&]() {
 #pragma unroll
-        for (int c = 0; c < ACH; ++c) {
-            const int ch = tid + c * 256;
-            if (ch < BM * (BK / 8)) *(uint4*)(As + (ch / (BK / 8)) * LDK + (ch % (BK / 8)) * 8) = areg[c];
-        }
-    };
+            for (int c = 0; c < WCH; ++c) {
+                const int ch = tid + c * 256;
+                *(uint4*)(Ws + (ch / (BK / 8)) * LDK + (ch % (BK / 8)) * 8) = wreg[c];
+            }
+#pragma unroll
+            for (int c = 0; c < ACH; ++c) {
+                const int ch = tid + c * 256;
+                if (ch < BM * (BK / 8)) *(uint4*)(As + (ch / (BK / 8)) * LDK + (ch % (BK / 8)) * 8) = areg[c];
+            }
+        };
 
-    f32x4_t acc[FT][TT];
+        f32x4_t acc[FT][TT];
 #pragma unroll
-    for (int i = 0; i < FT; ++i)
+        for (int i = 0; i < FT; ++i)
 #pragma unroll
-        for (int j = 0; j < TT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < TT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = (K + BK - 1) / BK;
-    load_stage(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        __syncthreads();
-        store_stage();
-        __syncthreads();
-        if (kt + 1 < nk) load_stage((kt + 1) * BK);
+        load_stage(kbeg);
+        for (int k0 = kbeg; k0 < kend; k0 += BK) {
+            __syncthreads();
+            store_stage();
+            __syncthreads();
+            if (k0 + BK < kend) load_stage(k0 + BK);
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            bf16x8_t af[FT], bfr[TT];
+            for (int kq = 0; kq < BK / 32; ++kq) {
+                bf16x8_t af[FT], bfr[TT];
 #pragma unroll
-            for (int ft = 0; ft < FT; ++ft)
-                af[ft] = *(const bf16x8_t*)(Ws + (wn * FT * 16 + ft * 16 + l16) * LDK + ks * 32 + g4 * 8);
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-                bfr[tt] = *(const bf16x8_t*)(As + (wm * TT * 16 + tt * 16 + l16) * LDK + ks * 32 + g4 * 8);
-#pragma unroll
-            for (int ft = 0; ft < FT; ++ft)
+                for (int ft = 0; ft < FT; ++ft)
+                    af[ft] = *(const bf16x8_t*)(Ws + (wn * FT * 16 + ft * 16 + l16) * LDK + kq * 32 + g4 * 8);
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt)
-                    acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ft], bfr[tt], acc[ft][tt], 0, 0, 0);
+                    bfr[tt] = *(const bf16x8_t*)(As + (wm * TT * 16 + tt * 16 + l16) * LDK + kq * 32 + g4 * 8);
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                    for (int tt = 0; tt < TT; ++tt)
+                        acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ft], bfr[tt], acc[ft][tt], 0, 0, 0);
+            }
         }
+        __syncthreads();
+        // accumulators -> LDS tile C[token][feature]; lane holds features 4*g4..+3 of token l16
+        float* C = (float*)smem;
+        constexpr int ldc = BN + 4;
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const int tok = wm * TT * 16 + tt * 16 + l16;
+                const int fea = wn * FT * 16 + ft * 16 + g4 * 4;
+                *(f32x4_t*)(C + tok * ldc + fea) = acc[ft][tt];
+            }
+        __syncthreads();
+        tile_epilogue<uint16_t, KIND>(C, ldc, m0, nt * BN, BM, BN, ks, p);
     }
-    __syncthreads();
-    // accumulators -> LDS tile C[token][feature]; lane holds features 4*g4..+3 of token l16
-    float* C = (float*)smem;
-    constexpr int ldc = BN + 4;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            const int tok = wm * TT * 16 + tt * 16 + l16;
-            const int fea = wn * FT * 16 + ft * 16 + g4 * 4;
-            *(f32x4_t*)(C + tok * ldc + fea) = acc[ft][tt];
-        }
-    __syncthreads();
-    run_epilogue<uint16_t, KIND>(C, ldc, m0, nt * BN, BM, BN, nt, p);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -253,96 +235,118 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ 
 // ---------------------------------------------------------------------------------------
 template <int KIND>
 __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, const float* __restrict__ W,
-                                                  int M, int N, int K, int nmt, int total, int ffn, EpiParams p) {
+                                                  int M, int N, int K, int nmt, int nnt, int S, int ffn,
+                                                  EpiParams p) {
     constexpr int BM = 16, BN = 128, BKF = 32;
     __shared__ float As[BM][BKF + 1];
     __shared__ float Ws[BN][BKF + 1];
     __shared__ float C[BM * (BN + 4)];
-    const int tile = blockIdx.x;
-    if (tile >= total) return;
-    const int mt = tile % nmt, nt = tile / nmt, m0 = mt * BM;
-    const int tid = threadIdx.x;
-    const int r = tid / 16, fc = tid % 16;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int k0 = 0; k0 < K; k0 += BKF) {
-        for (int e = tid; e < BM * BKF; e += 256) {
-            const int rr = e / BKF, kk = e % BKF;
-            As[rr][kk] = (m0 + rr < M && k0 + kk < K) ? A[(size_t)(m0 + rr) * K + k0 + kk] : 0.f;
-        }
-        for (int e = tid; e < BN * BKF; e += 256) {
-            const int tr = e / BKF, kk = e % BKF;
-            bool v;
-            const int wr = w_row(tr, nt, BN, N, ffn, v);
-            Ws[tr][kk] = (v && k0 + kk < K) ? W[(size_t)wr * K + k0 + kk] : 0.f;
-        }
-        __syncthreads();
-        for (int kk = 0; kk < BKF; ++kk) {
-            const float a = As[r][kk];
+    const int unit = blockIdx.x;
+    if (unit < nmt * nnt * S) {
+        const int ks = unit % S, tile = unit / S;
+        const int mt = tile % nmt, nt = tile / nmt, m0 = mt * BM;
+        const int kbeg = ks * p.k_slice, kend = min(K, kbeg + p.k_slice);
+        const int tid = threadIdx.x;
+        const int r = tid / 16, fc = tid % 16;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int k0 = kbeg; k0 < kend; k0 += BKF) {
+            for (int e = tid; e < BM * BKF; e += 256) {
+                const int rr = e / BKF, kk = e % BKF;
+                As[rr][kk] = (m0 + rr < M && k0 + kk < kend) ? A[(size_t)(m0 + rr) * K + k0 + kk] : 0.f;
+            }
+            for (int e = tid; e < BN * BKF; e += 256) {
+                const int tr = e / BKF, kk = e % BKF;
+                bool v;
+                const int wr = w_row(tr, nt, BN, N, ffn, v);
+                Ws[tr][kk] = (v && k0 + kk < kend) ? W[(size_t)wr * K + k0 + kk] : 0.f;
+            }
+            __syncthreads();
+            for (int kk = 0; kk < BKF; ++kk) {
+                const float a = As[r][kk];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] += a * Ws[fc + 16 * j][kk];
+                for (int j = 0; j < 8; ++j) acc[j] += a * Ws[fc + 16 * j][kk];
+            }
+            __syncthreads();
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) C[r * (BN + 4) + fc + 16 * j] = acc[j];
         __syncthreads();
+        tile_epilogue<float, KIND>(C, BN + 4, m0, nt * BN, BM, BN, ks, p);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) C[r * (BN + 4) + fc + 16 * j] = acc[j];
-    __syncthreads();
-    run_epilogue<float, KIND>(C, BN + 4, m0, nt * BN, BM, BN, nt, p);
+}
+
+struct TilePlan { int BM, BN, nmt, nnt, S, k_slice, grid; };
+
+TilePlan tile_plan(int dtype, int kind, int M, int N, int K, int slices) {
+    TilePlan t;
+    t.BN = 128;
+    if (dtype == CAD_DTYPE_F32) t.BM = 16;
+    else t.BM = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+    t.nmt = (M + t.BM - 1) / t.BM;
+    // SwiGLU tiles cover BN/2 gate columns and the matching BN/2 up columns (N = 2*ffn)
+    t.nnt = kind == EPI_SWIGLU ? (N / 2 + t.BN / 2 - 1) / (t.BN / 2) : (N + t.BN - 1) / t.BN;
+    t.S = kind == EPI_PARTIAL ? slices : 1;
+    const int kstep = dtype == CAD_DTYPE_F32 ? 32 : BK;
+    t.k_slice = ((K + t.S - 1) / t.S + kstep - 1) / kstep * kstep;
+    const int total = t.nmt * t.nnt * t.S;
+    t.grid = dtype == CAD_DTYPE_F32 ? total : (total + 7) / 8 * 8;
+    return t;
 }
 
 template <int KIND, int BM, int BN, int WM, int WN>
-hipError_t go_bf16(const void* A, const void* W, int M, int N, int K, int ffn, const GemmPlan& pl,
+hipError_t go_bf16(const void* A, const void* W, int M, int N, int K, int ffn, const TilePlan& t,
                    const EpiParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((k_gemm_bf16<KIND, BM, BN, WM, WN>), dim3(pl.grid), dim3(256), 0, s,
-                       (const uint16_t*)A, (const uint16_t*)W, M, N, K, pl.nmt, pl.nmt * pl.nnt, ffn, p);
+    hipLaunchKernelGGL((k_gemm_bf16<KIND, BM, BN, WM, WN>), dim3(t.grid), dim3(256), 0, s, (const uint16_t*)A,
+                       (const uint16_t*)W, M, N, K, t.nmt, t.nnt, t.S, ffn, p);
     return hipGetLastError();
 }
 
 template <int KIND>
-hipError_t dispatch_bf16(const void* A, const void* W, int M, int N, int K, int ffn, const GemmPlan& pl,
-                         const EpiParams& p, hipStream_t s) {
-    switch (pl.BM) {
-        case 16: return go_bf16<KIND, 16, 128, 1, 4>(A, W, M, N, K, ffn, pl, p, s);
-        case 32: return go_bf16<KIND, 32, 128, 2, 2>(A, W, M, N, K, ffn, pl, p, s);
-        case 64: return go_bf16<KIND, 64, 128, 2, 2>(A, W, M, N, K, ffn, pl, p, s);
-        default: return go_bf16<KIND, 128, 128, 2, 2>(A, W, M, N, K, ffn, pl, p, s);
-    }
-}
-
-template <int KIND>
-hipError_t dispatch(int dtype, const void* A, const void* W, int M, int N, int K, const EpiParams& p,
+hipError_t dispatch(int dtype, const void* A, const void* W, int M, int N, int K, int slices, EpiParams p,
                     hipStream_t s) {
-    const bool sw = KIND == EPI_SWIGLU;
-    const GemmPlan pl = gemm_plan(dtype, M, N, sw);
-    const int ffn = sw ? p.ffn : 0;
+    const int ffn = KIND == EPI_SWIGLU ? p.ffn : 0;
+    const TilePlan t = tile_plan(dtype, KIND, M, N, K, slices);
+    p.k_slice = t.k_slice;
     if (dtype == CAD_DTYPE_F32) {
-        hipLaunchKernelGGL((k_gemm_f32<KIND>), dim3(pl.grid), dim3(256), 0, s, (const float*)A, (const float*)W,
-                           M, N, K, pl.nmt, pl.nmt * pl.nnt, ffn, p);
+        hipLaunchKernelGGL((k_gemm_f32<KIND>), dim3(t.grid), dim3(256), 0, s, (const float*)A, (const float*)W, M, N,
+                           K, t.nmt, t.nnt, t.S, ffn, p);
         return hipGetLastError();
     }
-    return dispatch_bf16<KIND>(A, W, M, N, K, ffn, pl, p, s);
+    switch (t.BM) {
+        case 16: return go_bf16<KIND, 16, 128, 1, 4>(A, W, M, N, K, ffn, t, p, s);
+        case 32: return go_bf16<KIND, 32, 128, 2, 2>(A, W, M, N, K, ffn, t, p, s);
+        case 64: return go_bf16<KIND, 64, 128, 2, 2>(A, W, M, N, K, ffn, t, p, s);
+        default: return go_bf16<KIND, 128, 128, 2, 2>(A, W, M, N, K, ffn, t, p, s);
+    }
 }
 
 }  // namespace
 
-GemmPlan gemm_plan(int dtype, int M, int N, bool swiglu) {
-    GemmPlan pl;
-    pl.BN = 128;
-    if (dtype == CAD_DTYPE_F32) pl.BM = 16;
-    else pl.BM = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
-    pl.nmt = (M + pl.BM - 1) / pl.BM;
-    // SwiGLU tiles cover BN/2 gate columns and the matching BN/2 up columns (N = 2*ffn)
-    pl.nnt = swiglu ? (N / 2 + pl.BN / 2 - 1) / (pl.BN / 2) : (N + pl.BN - 1) / pl.BN;
-    const int total = pl.nmt * pl.nnt;
-    pl.grid = dtype == CAD_DTYPE_F32 ? total : (total + 7) / 8 * 8;
-    return pl;
+// K slices of an EPI_PARTIAL launch (the O and down projections); the workspace holds
+// slices x M x N fp32 partials.
+int gemm_argmax_slots(int dtype, int M, int N, int K) {
+    if (dtype == CAD_DTYPE_BF16 && skinny_supports(EPI_ARGMAX, M, K)) return skinny_argmax_slots(M, N, K);
+    return tile_plan(dtype, EPI_ARGMAX, M, N, K, 1).nnt;
 }
 
-hipError_t launch_gemm(int dtype, int kind, const void* A, const void* W, int M, int N, int K, const EpiParams& p,
-                       hipStream_t s) {
+int gemm_partial_slices(int dtype, int M, int N, int K) {
+    if (dtype == CAD_DTYPE_BF16 && skinny_supports(EPI_PARTIAL, M, K)) return skinny_partial_slices(K);
+    const TilePlan t = tile_plan(dtype, EPI_PARTIAL, M, N, K, 1);
+    const int tiles = t.nmt * t.nnt;
+    const int want = 2 * device_cu_count();
+    int S = (want + tiles - 1) / tiles;
+    const int smax = K / 256 > 1 ? K / 256 : 1;                  // at least 256 of K per slice
+    S = S < 1 ? 1 : (S > smax ? smax : S);
+    return S;
+}
+
+hipError_t launch_gemm(int dtype, int kind, const void* A, const void* W, int M, int N, int K, int slices,
+                       EpiParams p, hipStream_t s) {
+    if (dtype == CAD_DTYPE_BF16 && skinny_supports(kind, M, K)) return launch_skinny(kind, A, W, M, N, K, p, s);
     switch (kind) {
-        case EPI_QKV: return dispatch<EPI_QKV>(dtype, A, W, M, N, K, p, s);
-        case EPI_RESID: return dispatch<EPI_RESID>(dtype, A, W, M, N, K, p, s);
-        case EPI_SWIGLU: return dispatch<EPI_SWIGLU>(dtype, A, W, M, N, K, p, s);
-        default: return dispatch<EPI_ARGMAX>(dtype, A, W, M, N, K, p, s);
+        case EPI_QKV: return dispatch<EPI_QKV>(dtype, A, W, M, N, K, 1, p, s);
+        case EPI_SWIGLU: return dispatch<EPI_SWIGLU>(dtype, A, W, M, N, K, 1, p, s);
+        case EPI_ARGMAX: return dispatch<EPI_ARGMAX>(dtype, A, W, M, N, K, 1, p, s);
+        default: return dispatch<EPI_PARTIAL>(dtype, A, W, M, N, K, slices, p, s);
     }
 }

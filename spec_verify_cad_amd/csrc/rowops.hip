@@ -1,6 +1,17 @@
-// Row-wise kernels of the span forward: embedding gather + RMSNorm (which also captures the
-// per-sequence cache length the rest of the forward uses), RMSNorm of the residual stream,
-// the LM-head argmax finalisation over column-tile partials, and the length commit.
+// Row-wise kernels of the span forward.
+//
+// k_embed_norm  first kernel of every forward: captures the per-sequence cache length the
+//               rest of the forward uses (flagging sequences that would overflow), gathers the
+//               embedding rows, applies RMSNorm and tabulates the (cos, sin) of each row's rotary angles
+//               p * base^(-2i/d), computed in double (Copy-as-Decode, Appendix K: the rows
+//               take the absolute positions N sequential decode steps would have).
+// k_resid_norm  residual add of the K-slice partial sums of a projection (in slice order,
+//               so the result does not depend on scheduling), optional rounded copy, and the
+//               RMSNorm that feeds the next projection.
+// k_argmax_final reduces the LM head's (max, index) slots of each row (ties to the lowest
+//               index) and, for a committing forward, advances the cache length: the last
+//               kernel of a full forward.
+// k_commit      len += Nq for a K/V-only forward.
 #include "cad_device.h"
 
 namespace {
@@ -18,10 +29,11 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 template <typename T>
 __global__ __launch_bounds__(NT) void k_embed_norm(const int32_t* __restrict__ tokens, const T* __restrict__ embed,
-                                                   int h, int vocab, int Nq, int cap, float eps,
-                                                   const int32_t* __restrict__ kv_len, int32_t* __restrict__ err,
-                                                   int32_t* __restrict__ len_snap, float* __restrict__ x,
-                                                   T* __restrict__ u) {
+                                                   int h, int vocab, int Nq, int cap, float eps, int mode, int Dblk,
+                                                   int half, double rope_base, const int32_t* __restrict__ kv_len,
+                                                   int32_t* __restrict__ err, int32_t* __restrict__ len_snap,
+                                                   float2* __restrict__ rope_cs,
+                                                   float* __restrict__ x, T* __restrict__ u) {
     __shared__ float red[4];
     const int r = blockIdx.x, b = r / Nq, it = r % Nq;
     const int len = kv_len[b];
@@ -31,6 +43,13 @@ __global__ __launch_bounds__(NT) void k_embed_norm(const int32_t* __restrict__ t
         if (!ok && err) err[b] = CAD_ECAPACITY;
     }
     if (!ok) return;
+    if (rope_cs) {
+        const int pos = len + (mode == CAD_MASK_BLOCK_TRI ? it % Dblk : it);
+        for (int i = threadIdx.x; i < half; i += NT) {
+            const double ang = (double)pos * pow(rope_base, -(double)i / (double)half);
+            rope_cs[(size_t)r * half + i] = make_float2((float)cos(ang), (float)sin(ang));
+        }
+    }
     int t = tokens[r];
     t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
     const T* e = embed + (size_t)t * h;
@@ -48,29 +67,41 @@ __global__ __launch_bounds__(NT) void k_embed_norm(const int32_t* __restrict__ t
     }
 }
 
+// out = base + sum_s part[s] (fp32); out_t = rnd(out) if given; normed = rnd(RMSNorm(out)).
 template <typename T>
-__global__ __launch_bounds__(NT) void k_rmsnorm(const float* __restrict__ in, T* __restrict__ out, int h, int Nq,
-                                                int cap, float eps, const int32_t* __restrict__ len_snap) {
+__global__ __launch_bounds__(NT) void k_resid_norm(const float* __restrict__ base, const float* __restrict__ part,
+                                                   int slices, int M, int h, int Nq, int cap, float eps,
+                                                   const int32_t* __restrict__ len_snap, float* __restrict__ out,
+                                                   T* __restrict__ out_t, T* __restrict__ normed) {
     __shared__ float red[4];
+    extern __shared__ float rowbuf[];            // [h]
     const int r = blockIdx.x;
     if (!seq_ok(len_snap, r / Nq, Nq, cap)) return;
-    const float* p = in + (size_t)r * h;
     float ss = 0.f;
-    for (int j = threadIdx.x; j < h; j += NT) ss += p[j] * p[j];
+    for (int j = threadIdx.x; j < h; j += NT) {
+        float v = 0.f;
+        for (int s = 0; s < slices; ++s) v += part[((size_t)s * M + r) * h + j];
+        v = base[(size_t)r * h + j] + v;
+        rowbuf[j] = v;
+        out[(size_t)r * h + j] = v;
+        if (out_t) Elt<T>::st(out_t, (size_t)r * h + j, v);
+        ss += v * v;
+    }
     ss = block_sum(ss, red);
     const float scale = 1.0f / sqrtf(ss / (float)h + eps);
-    for (int j = threadIdx.x; j < h; j += NT) Elt<T>::st(out, (size_t)r * h + j, p[j] * scale);
+    for (int j = threadIdx.x; j < h; j += NT) Elt<T>::st(normed, (size_t)r * h + j, rowbuf[j] * scale);
 }
 
-// One wave per row: reduce the (max, index) partials of all column tiles.
-__global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ part, int ntiles, int Nq, int cap,
-                                                     const int32_t* __restrict__ len_snap, int32_t* __restrict__ out) {
-    const int r = blockIdx.x;
-    if (!seq_ok(len_snap, r / Nq, Nq, cap)) return;
+// One wave per row.  Row r of sequence b = r / Nq; the wave of the sequence's first row commits.
+__global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ part, int slots, int Nq, int cap,
+                                                     const int32_t* __restrict__ len_snap, int32_t* __restrict__ out,
+                                                     int32_t* __restrict__ kv_len) {
+    const int r = blockIdx.x, b = r / Nq;
+    if (!seq_ok(len_snap, b, Nq, cap)) return;
     float best = -INFINITY;
     int bi = 0x7fffffff;
-    for (int t = threadIdx.x; t < ntiles; t += 64) {
-        const float2 pv = part[(size_t)r * ntiles + t];
+    for (int t = threadIdx.x; t < slots; t += 64) {
+        const float2 pv = part[(size_t)r * slots + t];
         argmax_merge(best, bi, pv.x, __float_as_int(pv.y));
     }
 #pragma unroll
@@ -79,7 +110,10 @@ __global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ 
         const int i2 = __shfl_xor(bi, o, 64);
         argmax_merge(best, bi, v2, i2);
     }
-    if (threadIdx.x == 0) out[r] = bi;
+    if (threadIdx.x == 0) {
+        out[r] = bi;
+        if (kv_len && r % Nq == 0) kv_len[b] = len_snap[b] + Nq;
+    }
 }
 
 __global__ void k_commit(const int32_t* __restrict__ len_snap, int B, int Nq, int cap, int32_t* __restrict__ kv_len) {
@@ -90,30 +124,36 @@ __global__ void k_commit(const int32_t* __restrict__ len_snap, int B, int Nq, in
 }  // namespace
 
 hipError_t launch_embed_norm(const FwdDims& fd, const int32_t* tokens, const void* embed, float eps,
-                             const int32_t* kv_len, int32_t* err, const FwdBufs& wb, hipStream_t s) {
+                             double rope_base, const int32_t* kv_len, int32_t* err, const FwdBufs& wb,
+                             hipStream_t s) {
+    const int half = fd.d / 2;
     if (fd.dtype == CAD_DTYPE_F32)
         hipLaunchKernelGGL(k_embed_norm<float>, dim3(fd.M), dim3(NT), 0, s, tokens, (const float*)embed, fd.h, fd.V,
-                           fd.Nq, fd.cap, eps, kv_len, err, wb.len_snap, wb.x, (float*)wb.u);
+                           fd.Nq, fd.cap, eps, fd.mode, fd.Dblk, half, rope_base, kv_len, err, wb.len_snap,
+                           wb.rope_cs, wb.x, (float*)wb.u);
     else
         hipLaunchKernelGGL(k_embed_norm<uint16_t>, dim3(fd.M), dim3(NT), 0, s, tokens, (const uint16_t*)embed, fd.h,
-                           fd.V, fd.Nq, fd.cap, eps, kv_len, err, wb.len_snap, wb.x, (uint16_t*)wb.u);
+                           fd.V, fd.Nq, fd.cap, eps, fd.mode, fd.Dblk, half, rope_base, kv_len, err, wb.len_snap,
+                           wb.rope_cs, wb.x, (uint16_t*)wb.u);
     return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(const FwdDims& fd, const float* in, void* out, float eps, const int32_t* len_snap,
-                          hipStream_t s) {
+hipError_t launch_resid_norm(const FwdDims& fd, const float* base, const float* part, int slices, float* out_f32,
+                             void* out_t, void* normed, float eps, const int32_t* len_snap, hipStream_t s) {
+    const size_t smem = (size_t)fd.h * sizeof(float);
     if (fd.dtype == CAD_DTYPE_F32)
-        hipLaunchKernelGGL(k_rmsnorm<float>, dim3(fd.M), dim3(NT), 0, s, in, (float*)out, fd.h, fd.Nq, fd.cap, eps,
-                           len_snap);
+        hipLaunchKernelGGL(k_resid_norm<float>, dim3(fd.M), dim3(NT), smem, s, base, part, slices, fd.M, fd.h, fd.Nq,
+                           fd.cap, eps, len_snap, out_f32, (float*)out_t, (float*)normed);
     else
-        hipLaunchKernelGGL(k_rmsnorm<uint16_t>, dim3(fd.M), dim3(NT), 0, s, in, (uint16_t*)out, fd.h, fd.Nq, fd.cap,
-                           eps, len_snap);
+        hipLaunchKernelGGL(k_resid_norm<uint16_t>, dim3(fd.M), dim3(NT), smem, s, base, part, slices, fd.M, fd.h,
+                           fd.Nq, fd.cap, eps, len_snap, out_f32, (uint16_t*)out_t, (uint16_t*)normed);
     return hipGetLastError();
 }
 
-hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, int32_t* argmax_out, hipStream_t s) {
-    hipLaunchKernelGGL(k_argmax_final, dim3(fd.M), dim3(64), 0, s, wb.amax_part, fd.lm_tiles, fd.Nq, fd.cap,
-                       wb.len_snap, argmax_out);
+hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, int32_t* argmax_out, int32_t* kv_len,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(k_argmax_final, dim3(fd.M), dim3(64), 0, s, wb.amax_part, wb.amax_slots, fd.Nq, fd.cap,
+                       wb.len_snap, argmax_out, kv_len);
     return hipGetLastError();
 }
 
