@@ -82,8 +82,12 @@ typedef struct {
 } cad_layer_desc;
 
 /*
- * KV cache of B sequences.  k, v: [B, n_kv_heads, cap, head_dim] in `dtype`, slot s of
- * sequence b holding the key/value of the token at position s (after acceptance).
+ * KV cache of B sequences, in `dtype`:
+ *   k: [B, n_kv_heads, cap, head_dim]  slot-major: k[b][g][s][i]
+ *   v: [B, n_kv_heads, head_dim, cap]  dim-major:  v[b][g][i][s]
+ * Slot s of sequence b holds the key/value of the token at position s (after acceptance).  The
+ * value cache is stored transposed so that attention reads, for one dimension, a contiguous run
+ * of slots (the operand layout of the value product).  cap must be a multiple of 4.
  * len: [B] int32, device-resident current lengths.  err: [B] int32, nullable; set to
  * CAD_ECAPACITY for a sequence whose operation would overflow (never cleared by the library).
  * n_kv_heads, head_dim and dtype must match the layer the cache is used with.
@@ -139,8 +143,8 @@ int cad_ngram_lookup(const int32_t *ctx, int64_t ctx_stride, const int32_t *ctx_
  * its own key as stored).  Rounding points (bf16 round-to-nearest-even for a bf16 layer):
  * normed input, rotated q, stored k and v, attention output, second normed input, SwiGLU
  * product, hidden_out, final normed input; the residual stream and logits are fp32.
- * Errors: CAD_EINVAL, CAD_EUNSUPPORTED, CAD_EWORKSPACE, CAD_EHIP; per sequence
- * CAD_ECAPACITY in kv->err when len + Nq > cap.
+ * Errors: CAD_EINVAL, CAD_EUNSUPPORTED (also: cap not a multiple of 4), CAD_EWORKSPACE, CAD_EHIP;
+ * per sequence CAD_ECAPACITY in kv->err when len + Nq > cap.
  */
 int cad_span_forward(const cad_layer_desc *layer, const cad_kv_desc *kv,
                      const int32_t *tokens, int B, int Nq,
@@ -171,8 +175,8 @@ size_t cad_span_forward_workspace(const cad_layer_desc *layer, int B, int Nq, in
  *               appended at ctx_len[b] and ctx_len[b] grows by a+1 (if ctx_len+a+1 > ctx_cap the
  *               sequence is flagged CAD_ECAPACITY in kv->err and nothing is appended)
  *   kv          nullable; when given, causal: len += a+1 (g and the accepted drafts are now
- *               cached); block: the winner's first a* rows move from slot len+w*D+j to len+j
- *               and len += a*.
+ *               cached); block: the winner's first a* slots move from slot len+w*D+j to len+j
+ *               (keys and values) and len += a*.
  * Causal: a = number of leading i < draft_len with d_{i+1} == pred[i]; bonus = pred[a].
  * Block: a_w = leading run of candidate w checked against first_pred, then against
  * pred[w*D + j - 1]; the largest a_w wins, ties to the lowest w; bonus = first_pred when a* = 0,

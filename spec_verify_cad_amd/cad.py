@@ -127,7 +127,7 @@ class DeviceLayer:
 
 
 class DeviceCache:
-    """KV cache of B sequences: k, v [B, Hkv, cap, d], len [B], err [B].
+    """KV cache of B sequences: k [B, Hkv, cap, d], v [B, Hkv, d, cap] (dim-major), len [B], err [B].
 
     `len_tensor` may supply the int32 [B] length tensor (e.g. a view of a larger one, so the
     lengths of several caches can be reset by one fill)."""
@@ -137,7 +137,7 @@ class DeviceCache:
         dt = torch.int16 if shape.dtype == "bf16" else torch.float32
         self.shape, self.B, self.cap = shape, B, cap
         self.k = torch.zeros((B, shape.n_kv_heads, cap, shape.head_dim), dtype=dt, device=device)
-        self.v = torch.zeros_like(self.k)
+        self.v = torch.zeros((B, shape.n_kv_heads, shape.head_dim, cap), dtype=dt, device=device)
         self.len = torch.zeros(B, dtype=torch.int32, device=device) if len_tensor is None else len_tensor
         assert self.len.dtype == torch.int32 and self.len.numel() == B and self.len.is_contiguous()
         self.err = torch.zeros(B, dtype=torch.int32, device=device)

@@ -2,22 +2,27 @@
 // rows their mask allows (causal span, or SwitchSD's block-triangular candidate mask), with
 // grouped-query heads sharing one K/V stream.
 //
-// bf16 path (gfx950 MFMA, head_dim 64 or 128): split-L flash decoding.  A workgroup owns one
-// (sequence, KV head, key chunk, query-row tile); the query rows of a tile are the
-// (token, q head) pairs of the GQA group, so every K/V tile is read from HBM once per
-// group.  Per 64-key tile: S^T = K . Q^T on MFMA (each lane then holds the scores of ONE
-// query), online softmax with exp2, O^T += V^T . P^T on MFMA with P taken straight from
-// registers (the MFMA k-slots are mapped onto the keys the lane already holds, and V is
-// staged transposed in LDS to match).  P is split into bf16 hi + lo parts, two MFMAs, so
-// the attention output carries fp32-level weights into its bf16 rounding point.  Partial (m, l, O) per chunk go to the workspace and a
-// merge kernel combines them.
+// bf16 path (gfx950 MFMA, head_dim 64 or 128): split-L flash decoding with no LDS.  A
+// workgroup owns one (sequence, KV head, key chunk, 64-row tile); the rows of a tile are the
+// (token, q head) pairs of the GQA group, so every K/V byte of a chunk is fetched from HBM once
+// per group (the four waves of a workgroup share it through L1).  Each wave takes 16 rows and
+// walks its keys 32 at a time, loading MFMA operands straight from the cache:
+//   S^T = K . Q^T   A = 16 keys x 32 dims of the K cache (16 contiguous bytes per lane),
+//                   B = the wave's query fragments (loaded once);
+//   O^T += V^T . P^T  A = 16 dims x 32 keys of the dim-major V cache, B = P^T taken from the
+//                   score registers: the MFMA k-slots 8g+i / 8g+4+i are mapped to keys 4g+i /
+//                   16+4g+i, which are exactly the scores lane (g, r) holds, so P never moves
+//                   between lanes, and V^T is read with the same key order (two 8-byte loads).
+// Online softmax runs in registers with exp2; P enters the PV product as bf16 hi + bf16 lo
+// (the rounding remainder), two MFMAs, so the weights keep about 16 significant bits.  With
+// one key chunk the wave writes the normalised output; otherwise it writes (m, l, O) partials
+// and a merge kernel combines them.
 //
 // fp32 path: one workgroup per (row, q head), plain two-pass softmax over all keys.
 #include "cad_device.h"
 
 namespace {
 
-constexpr int KT = 64;          // keys per LDS tile
 constexpr int WAVES = 4;
 
 __device__ __forceinline__ bool key_allowed(int key, int len, int it, int mode, int Dblk) {
@@ -30,177 +35,162 @@ __device__ __forceinline__ bool key_allowed(int key, int len, int it, int mode, 
     return s <= it;
 }
 
-// RPW = 16-query tiles per wave.  DH = head_dim.
-template <int DH, int RPW>
+// four bf16 of one V row (keys key0..key0+3, key0 a multiple of 4); keys at or past kend read
+// as zero.  Branch-free: a group wholly past kend reads slot 0 instead (cap is a multiple of 4,
+// so a load never crosses the end of a row), so all loads of a step issue back to back.
+__device__ __forceinline__ uint2 v4(const uint16_t* vrow, int key0, int kend) {
+    const int n = kend - key0;                       // valid keys in the group
+    uint2 w = *(const uint2*)(vrow + (n > 0 ? key0 : 0));   // keys key0 .. key0+3, low half first
+    w.x &= n >= 2 ? 0xFFFFFFFFu : (n == 1 ? 0xFFFFu : 0u);
+    w.y &= n >= 4 ? 0xFFFFFFFFu : (n == 3 ? 0xFFFFu : 0u);
+    return w;
+}
+
+template <int DH>
 __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                                    const uint16_t* __restrict__ vc, const int32_t* __restrict__ len_snap,
                                                    int Nq, int Hq, int Hkv, int cap, int mode, int Dblk,
                                                    int chunk, int nsplit, float* __restrict__ part_o,
-                                                   float* __restrict__ part_ml) {
-    constexpr int ROWS = WAVES * RPW * 16;      // query rows per workgroup
-    constexpr int KPAD = 8, VPAD = 8;
+                                                   float* __restrict__ part_ml, uint16_t* __restrict__ o_out) {
     constexpr int DS = DH / 32;                 // MFMA k-steps over head_dim
     constexpr int DB = DH / 16;                 // 16-wide head_dim blocks of the output
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT][DH + KPAD];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[DH][KT + VPAD];
-
     const int split = blockIdx.x, rtile = blockIdx.y;
     const int bg = blockIdx.z, b = bg / Hkv, g = bg % Hkv;
     const int G = Hq / Hkv, Rg = Nq * G;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
 
+    const int wrow0 = rtile * (WAVES * 16) + wave * 16;
+    if (wrow0 >= Rg) return;                    // no rows for this wave (no barriers below)
     const bool ok = seq_ok(len_snap, b, Nq, cap);
     const int len = ok ? len_snap[b] : 0;
-    const int row0 = rtile * ROWS;
-    // rows of this tile cover tokens it in [row0/G, (row0+ROWS-1)/G]: keys beyond len+it_max are masked
-    const int it_max = min(Nq - 1, (row0 + ROWS - 1) / G);
-    const int kend_all = len + Nq;
-    int kbeg = split * chunk;
-    int kend = min(kbeg + chunk, min(kend_all, len + it_max + 1));
-    if (!ok) kend = kbeg;                        // nothing to do: write empty partials
+    const int rho = wrow0 + l16;
+    const bool qlive = rho < Rg;
+    const int it = qlive ? rho / G : 0, hh = qlive ? rho % G : 0;
+    // keys past len + (last token of the wave) are masked for every row of the wave
+    const int it_max = min(Nq - 1, min(wrow0 + 15, Rg - 1) / G);
+    const int kbeg = split * chunk;
+    int kend = min(kbeg + chunk, len + it_max + 1);
+    if (!ok) kend = kbeg;
 
-    // per-wave query fragments (B operand): lane holds Q[row = l16][dim 32*ks + 8*g4 .. +8]
-    bf16x8_t qf[RPW][DS];
-    int q_it[RPW];
-    bool q_live[RPW];
-#pragma unroll
-    for (int rp = 0; rp < RPW; ++rp) {
-        const int rho = row0 + (wave * RPW + rp) * 16 + l16;
-        q_live[rp] = rho < Rg;
-        const int it = q_live[rp] ? rho / G : 0, hh = q_live[rp] ? rho % G : 0;
-        q_it[rp] = it;
+    bf16x8_t qf[DS];
+    {
         const uint16_t* qp = q + (((size_t)b * Nq + it) * Hq + g * G + hh) * DH;
 #pragma unroll
         for (int ks = 0; ks < DS; ++ks) {
-            uint4 v = q_live[rp] && ok ? *(const uint4*)(qp + ks * 32 + g4 * 8) : make_uint4(0, 0, 0, 0);
-            qf[rp][ks] = *(bf16x8_t*)&v;
+            uint4 v = qlive && ok ? *(const uint4*)(qp + ks * 32 + g4 * 8) : make_uint4(0, 0, 0, 0);
+            qf[ks] = *(bf16x8_t*)&v;
         }
     }
 
     const float sl2 = 1.4426950408889634f / sqrtf((float)DH);   // log2(e)/sqrt(d)
-    float m_run[RPW], l_run[RPW];
-    f32x4_t oacc[RPW][DB];
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t oacc[DB];
 #pragma unroll
-    for (int rp = 0; rp < RPW; ++rp) {
-        m_run[rp] = -INFINITY;
-        l_run[rp] = 0.f;
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const size_t head = (size_t)b * Hkv + g;
+    const uint16_t* kbase = kc + head * cap * DH;
+    const uint16_t* vbase = vc + head * DH * cap;          // dim-major: row = one dim over all slots
+
+    for (int k0 = kbeg; k0 < kend; k0 += 32) {
+        // K fragments: lane (key l16, g4) of key block kb
+        bf16x8_t kf[2][DS];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[rp][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const size_t head_off = ((size_t)b * Hkv + g) * cap * DH;
-    const uint16_t* kbase = kc + head_off;
-    const uint16_t* vbase = vc + head_off;
-
-    for (int k0 = kbeg; k0 < kend; k0 += KT) {
-        __syncthreads();
-        // stage K [KT][DH] (row-major) and V^T [DH][KT]
-        for (int c = tid; c < KT * DH / 8; c += 256) {
-            const int kr = c / (DH / 8), dc = (c % (DH / 8)) * 8;
-            const int key = k0 + kr;
-            uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-            if (key < kend) {
-                kv = *(const uint4*)(kbase + (size_t)key * DH + dc);
-                vv = *(const uint4*)(vbase + (size_t)key * DH + dc);
+        for (int kb = 0; kb < 2; ++kb) {
+            const int key = k0 + kb * 16 + l16;
+            const uint16_t* kp = kbase + (size_t)(key < kend ? key : kbeg) * DH + g4 * 8;
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) {
+                uint4 v = *(const uint4*)(kp + ks * 32);
+                kf[kb][ks] = *(bf16x8_t*)&v;
             }
-            *(uint4*)&Ks[kr][dc] = kv;
-            const uint16_t* ve = (const uint16_t*)&vv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Vt[dc + e][kr] = ve[e];
         }
-        __syncthreads();
-
+        // V^T fragments: lane (dim db*16 + l16, g4) takes keys 4g4..+3 and 16+4g4..+3
+        bf16x8_t vf[DB];
 #pragma unroll
-        for (int rp = 0; rp < RPW; ++rp) {
-            // S^T[key][query]: 4 key blocks of 16; lane holds keys kb*16 + 4*g4 + i for query l16
-            f32x4_t st[4];
+        for (int db = 0; db < DB; ++db) {
+            const uint16_t* vrow = vbase + (size_t)(db * 16 + l16) * cap;
+            const uint2 lo = v4(vrow, k0 + 4 * g4, kend), hi = v4(vrow, k0 + 16 + 4 * g4, kend);
+            uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            vf[db] = *(bf16x8_t*)&vv;
+        }
+        // S^T[key][query]: lane holds keys kb*16 + 4*g4 + i of query l16
+        f32x4_t st[2];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 2; ++kb) {
+            st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < DS; ++ks) {
-                    const bf16x8_t kf = *(const bf16x8_t*)&Ks[kb * 16 + l16][ks * 32 + g4 * 8];
-                    st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rp][ks], st[kb], 0, 0, 0);
-                }
+            for (int ks = 0; ks < DS; ++ks)
+                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][ks], qf[ks], st[kb], 0, 0, 0);
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = k0 + kb * 16 + g4 * 4 + i;
+                const bool al = qlive && key < kend && key_allowed(key, len, it, mode, Dblk);
+                const float sv = al ? st[kb][i] * sl2 : -INFINITY;
+                st[kb][i] = sv;
+                tmax = fmaxf(tmax, sv);
             }
-            // mask + scale, tile max for this lane's query
-            float tmax = -INFINITY;
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+        float psum = 0.f;
+        // P^T fragment: k-slot 8*g4 + i <- key 4*g4 + i (block 0), 8*g4 + 4 + i <- key 16 + 4*g4 + i
+        bf16x8_t ph, pl;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = k0 + kb * 16 + g4 * 4 + i;
-                    const bool al = q_live[rp] && key < kend && key_allowed(key, len, q_it[rp], mode, Dblk);
-                    const float sv = al ? st[kb][i] * sl2 : -INFINITY;
-                    st[kb][i] = sv;
-                    tmax = fmaxf(tmax, sv);
-                }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float m_new = fmaxf(m_run[rp], tmax);
-            const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run[rp] - m_new);
-            float psum = 0.f;
-            // P enters the PV MFMA as bf16 hi + bf16 lo (the rounding remainder), so the
-            // weights keep about 16 significant bits instead of 8.
-            bf16x8_t pf[2], pl[2];               // PV k-steps over 32 keys each
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pv = m_new == -INFINITY ? 0.f : exp2f(st[kb][i] - m_new);
-                    const uint16_t ph = f32_to_bf16(pv);
-                    const float rem = pv - bf16_to_f32(ph);
-                    const uint16_t plo = f32_to_bf16(rem);
-                    psum += pv;
-                    // k-slot mapping of PV step kb/2: slots 8*g4+i <- key block 2*(kb/2), slots 8*g4+4+i <- the next
-                    ((uint16_t*)&pf[kb >> 1])[(kb & 1) * 4 + i] = ph;
-                    ((uint16_t*)&pl[kb >> 1])[(kb & 1) * 4 + i] = plo;
-                }
-            psum += __shfl_xor(psum, 16, 64);
-            psum += __shfl_xor(psum, 32, 64);
-            l_run[rp] = l_run[rp] * alpha + psum;
-            m_run[rp] = m_new;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[rp][db] *= alpha;
-            // O^T[dim][query] += V^T[dim][keys] . P^T[keys][query]
-#pragma unroll
-            for (int pk = 0; pk < 2; ++pk) {
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const uint16_t* vrow = &Vt[db * 16 + l16][pk * 32];
-                    uint2 lo = *(const uint2*)(vrow + g4 * 4);          // keys 32pk + 4g4 .. +3
-                    uint2 hi = *(const uint2*)(vrow + 16 + g4 * 4);     // keys 32pk + 16 + 4g4 .. +3
-                    uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    const bf16x8_t vf = *(bf16x8_t*)&vv;
-                    oacc[rp][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[pk], oacc[rp][db], 0, 0, 0);
-                    oacc[rp][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[pk], oacc[rp][db], 0, 0, 0);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const float pv = m_new == -INFINITY ? 0.f : exp2f(st[kb][i] - m_new);
+                const uint16_t hb = f32_to_bf16(pv);
+                const uint16_t lb = f32_to_bf16(pv - bf16_to_f32(hb));
+                psum += pv;
+                ((uint16_t*)&ph)[kb * 4 + i] = hb;
+                ((uint16_t*)&pl)[kb * 4 + i] = lb;
             }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            oacc[db] *= alpha;
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], ph, oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pl, oacc[db], 0, 0, 0);
         }
     }
 
-    // partials: lane holds O^T[dim = db*16 + 4*g4 + i][query l16]
+    if (!qlive) return;
+    // lane holds O^T[dim = db*16 + 4*g4 + i][query l16]
+    if (nsplit == 1) {
+        if (!ok) return;
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        uint16_t* op = o_out + (((size_t)b * Nq + it) * Hq + g * G + hh) * DH;
 #pragma unroll
-    for (int rp = 0; rp < RPW; ++rp) {
-        const int rho = row0 + (wave * RPW + rp) * 16 + l16;
-        if (rho >= Rg) continue;
-        const size_t pidx = (((size_t)b * Hkv + g) * Rg + rho) * nsplit + split;
+        for (int db = 0; db < DB; ++db) st4(op + db * 16 + g4 * 4, oacc[db] * inv);
+        return;
+    }
+    const size_t pidx = (head * Rg + rho) * nsplit + split;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            *(f32x4_t*)(part_o + pidx * DH + db * 16 + g4 * 4) = oacc[rp][db];
-        if (g4 == 0) {
-            part_ml[pidx * 2 + 0] = m_run[rp];
-            part_ml[pidx * 2 + 1] = l_run[rp];
-        }
+    for (int db = 0; db < DB; ++db) *(f32x4_t*)(part_o + pidx * DH + db * 16 + g4 * 4) = oacc[db];
+    if (g4 == 0) {
+        part_ml[pidx * 2 + 0] = m_run;
+        part_ml[pidx * 2 + 1] = l_run;
     }
 }
 
-// Combine the split partials of one (row, q head): o = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s.
+// Combine the split partials of one (row, q head): o = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s,
+// summed in split order.  The (m, l) of all splits are fetched in parallel, one per lane.
 template <typename T>
 __global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                    const int32_t* __restrict__ len_snap, int Nq, int Hq, int Hkv,
                                                    int DH, int cap, int nsplit, T* __restrict__ o) {
+    __shared__ float wgt[256];
     const int rowhead = blockIdx.x;                  // (b*Nq + it)*Hq + h
     const int h = rowhead % Hq, row = rowhead / Hq;
     const int b = row / Nq, it = row % Nq;
@@ -209,19 +199,23 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ par
     const int Rg = Nq * G, rho = it * G + hh;
     const size_t p0 = (((size_t)b * Hkv + g) * Rg + rho) * nsplit;
     float m = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_ml[(p0 + s) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
+    for (int s = threadIdx.x; s < nsplit; s += 64) m = fmaxf(m, part_ml[(p0 + s) * 2]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    for (int s = threadIdx.x; s < nsplit; s += 64) {
         const float ms = part_ml[(p0 + s) * 2];
-        if (ms != -INFINITY) L += exp2f(ms - m) * part_ml[(p0 + s) * 2 + 1];
+        wgt[s] = ms == -INFINITY ? 0.f : exp2f(ms - m);
     }
+    __syncthreads();
+    float L = 0.f;                                   // every lane sums the same terms in split order
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) L += wgt[s] * part_ml[(p0 + s) * 2 + 1];
+    const float inv = L > 0.f ? 1.f / L : 0.f;
     for (int dd = threadIdx.x; dd < DH; dd += 64) {
         float acc = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float ms = part_ml[(p0 + s) * 2];
-            if (ms != -INFINITY) acc += exp2f(ms - m) * part_o[(p0 + s) * DH + dd];
-        }
-        Elt<T>::st(o, (size_t)rowhead * DH + dd, acc / L);
+#pragma unroll 8
+        for (int s = 0; s < nsplit; ++s) acc += wgt[s] * part_o[(p0 + s) * DH + dd];
+        Elt<T>::st(o, (size_t)rowhead * DH + dd, acc * inv);
     }
 }
 
@@ -240,7 +234,7 @@ __global__ __launch_bounds__(256) void k_attn_simple(const T* __restrict__ q, co
     const int g = h / (Hq / Hkv);
     const T* qp = q + (size_t)rowhead * DH;
     const T* kb = kc + ((size_t)b * Hkv + g) * cap * DH;
-    const T* vb = vc + ((size_t)b * Hkv + g) * cap * DH;
+    const T* vb = vc + ((size_t)b * Hkv + g) * DH * cap;      // dim-major
     const float scale = 1.0f / sqrtf((float)DH);
     float mx = -INFINITY;
     for (int key = threadIdx.x; key < S; key += 256) {
@@ -271,15 +265,38 @@ __global__ __launch_bounds__(256) void k_attn_simple(const T* __restrict__ q, co
     for (int dd = threadIdx.x; dd < DH; dd += 256) {
         float acc = 0.f;
         for (int key = 0; key < S; ++key)
-            if (sc[key] != 0.f) acc += sc[key] * Elt<T>::ld(vb, (size_t)key * DH + dd);
+            if (sc[key] != 0.f) acc += sc[key] * Elt<T>::ld(vb, (size_t)dd * cap + key);
         Elt<T>::st(o, (size_t)rowhead * DH + dd, acc / sum);
     }
 }
 
+bool mfma_path(const FwdDims& fd) { return !(fd.dtype == CAD_DTYPE_F32 || (fd.d != 64 && fd.d != 128)); }
+
 }  // namespace
 
+// Split plan of the MFMA path: 64-row tiles of each GQA group, key chunks (multiples of 32,
+// at least 64) so that about two workgroups per CU are launched.
+void attention_plan(FwdDims* fd, int cus) {
+    const int G = fd->Hq / fd->Hkv, Rg = fd->Nq * G;
+    fd->attn_rows_per_wg = WAVES * 16;
+    fd->attn_row_tiles = (Rg + fd->attn_rows_per_wg - 1) / fd->attn_rows_per_wg;
+    const long units = (long)fd->B * fd->Hkv * fd->attn_row_tiles;
+    const long want = 2L * cus;
+    long splits = (want + units - 1) / units;
+    long chunk = (fd->cap + splits - 1) / splits;
+    chunk = (chunk + 31) / 32 * 32;
+    if (chunk < 64) chunk = 64;
+    fd->attn_chunk = (int)chunk;
+    fd->attn_splits = (int)((fd->cap + chunk - 1) / chunk);
+    if (fd->attn_splits > 256) {                    // the merge holds at most 256 split weights
+        fd->attn_chunk = (fd->cap + 255) / 256;
+        fd->attn_chunk = (fd->attn_chunk + 31) / 32 * 32;
+        fd->attn_splits = (fd->cap + fd->attn_chunk - 1) / fd->attn_chunk;
+    }
+}
+
 hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc, const void* vc, hipStream_t s) {
-    if (fd.dtype == CAD_DTYPE_F32 || (fd.d != 64 && fd.d != 128)) {
+    if (!mfma_path(fd)) {
         const size_t smem = (size_t)(fd.cap + fd.Nq) * sizeof(float);
         if (fd.dtype == CAD_DTYPE_F32)
             hipLaunchKernelGGL((k_attn_simple<float>), dim3(fd.M * fd.Hq), dim3(256), smem, s, (const float*)wb.q,
@@ -292,20 +309,18 @@ hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc
         return hipGetLastError();
     }
     const dim3 grid(fd.attn_splits, fd.attn_row_tiles, fd.B * fd.Hkv);
-    const bool two = fd.attn_rows_per_wg == 128;
-#define CAD_ATTN(DH, RPW)                                                                                        \
-    hipLaunchKernelGGL((k_attn_bf16<DH, RPW>), grid, dim3(256), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc, \
-                       (const uint16_t*)vc, wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.mode, fd.Dblk,          \
-                       fd.attn_chunk, fd.attn_splits, wb.part_o, wb.part_ml)
-    if (fd.d == 128) { if (two) CAD_ATTN(128, 2); else CAD_ATTN(128, 1); }
-    else { if (two) CAD_ATTN(64, 2); else CAD_ATTN(64, 1); }
-#undef CAD_ATTN
+    if (fd.d == 128)
+        hipLaunchKernelGGL((k_attn_bf16<128>), grid, dim3(WAVES * 64), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc,
+                           (const uint16_t*)vc, wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.mode, fd.Dblk,
+                           fd.attn_chunk, fd.attn_splits, wb.part_o, wb.part_ml, (uint16_t*)wb.o);
+    else
+        hipLaunchKernelGGL((k_attn_bf16<64>), grid, dim3(WAVES * 64), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc,
+                           (const uint16_t*)vc, wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.mode, fd.Dblk,
+                           fd.attn_chunk, fd.attn_splits, wb.part_o, wb.part_ml, (uint16_t*)wb.o);
     return hipGetLastError();
 }
 
-bool attention_uses_merge(const FwdDims& fd) {
-    return !(fd.dtype == CAD_DTYPE_F32 || (fd.d != 64 && fd.d != 128));
-}
+bool attention_uses_merge(const FwdDims& fd) { return mfma_path(fd) && fd.attn_splits > 1; }
 
 hipError_t launch_attention_merge(const FwdDims& fd, const FwdBufs& wb, hipStream_t s) {
     hipLaunchKernelGGL((k_attn_merge<uint16_t>), dim3(fd.M * fd.Hq), dim3(64), 0, s, wb.part_o, wb.part_ml,

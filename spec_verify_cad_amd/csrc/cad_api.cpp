@@ -1,5 +1,6 @@
 // C ABI of libcad: host-side argument checks, workspace sizing/carving and the launch
 // sequence of the span forward.  Nothing here allocates, frees or synchronizes.
+#include <cmath>
 #include <cstring>
 #include <vector>
 
@@ -64,22 +65,6 @@ bool layer_supported(const cad_layer_desc* L) {
     return true;
 }
 
-// attention launch geometry of the bf16 MFMA kernel
-void attn_plan(FwdDims* fd) {
-    const int G = fd->Hq / fd->Hkv, Rg = fd->Nq * G;
-    fd->attn_rows_per_wg = Rg > 64 ? 128 : 64;
-    fd->attn_row_tiles = (Rg + fd->attn_rows_per_wg - 1) / fd->attn_rows_per_wg;
-    const long units = (long)fd->B * fd->Hkv * fd->attn_row_tiles;
-    const long want = 1024;                                  // about 4 workgroups per CU
-    long splits = (want + units - 1) / units;
-    const long maxkeys = fd->cap;                            // len + Nq <= cap for every live sequence
-    long chunk = (maxkeys + splits - 1) / splits;
-    chunk = chunk < 128 ? 128 : chunk;
-    chunk = (chunk + 63) / 64 * 64;
-    fd->attn_chunk = (int)chunk;
-    fd->attn_splits = (int)((maxkeys + chunk - 1) / chunk);
-}
-
 }  // namespace
 
 bool fwd_dims(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, int cap, FwdDims* fd) {
@@ -95,7 +80,7 @@ bool fwd_dims(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, in
     fd->qkv_n = (fd->Hq + 2 * fd->Hkv) * fd->d;
     fd->o_slices = gemm_partial_slices(fd->dtype, fd->M, fd->h, fd->Hq * fd->d);
     fd->down_slices = gemm_partial_slices(fd->dtype, fd->M, fd->h, fd->ffn);
-    attn_plan(fd);
+    attention_plan(fd, device_cu_count());
     return true;
 }
 
@@ -210,15 +195,17 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
     if (kv->n_kv_heads != L->n_kv_heads || kv->head_dim != L->head_dim || kv->dtype != L->dtype) return CAD_EINVAL;
     if (!L->embed || !L->w_qkv) return CAD_EINVAL;
     if (!kv_only && (!L->w_o || !L->w_gate_up || !L->w_down || !L->w_lm || !argmax_out)) return CAD_EINVAL;
-    if (!layer_supported(L)) return CAD_EUNSUPPORTED;
+    if (!layer_supported(L) || kv->cap % 4) return CAD_EUNSUPPORTED;
     if ((long)fd.M * fd.h > (1L << 31) || (long)fd.M * fd.ffn > (1L << 31)) return CAD_EUNSUPPORTED;
     const bool simple_attn = fd.dtype == CAD_DTYPE_F32 || (fd.d != 64 && fd.d != 128);
     if (!kv_only && simple_attn && (size_t)(fd.cap + fd.Nq) * 4 > 64 * 1024) return CAD_EUNSUPPORTED;
     const FwdBufs wb = fwd_carve(fd, workspace, kv_only);
     if (!workspace || workspace_bytes < wb.total || ((uintptr_t)workspace & 255)) return CAD_EWORKSPACE;
 
+    RopeFreqs freqs;
+    for (int i = 0; i < fd.d / 2; ++i) freqs.inv[i] = std::pow(L->rope_base, -2.0 * i / fd.d);
     if (stage(ST_EMBED_NORM, stream, [&] {
-            return launch_embed_norm(fd, tokens, L->embed, L->rms_eps, L->rope_base, kv->len, kv->err, wb, stream);
+            return launch_embed_norm(fd, tokens, L->embed, L->rms_eps, freqs, kv->len, kv->err, wb, stream);
         }) != hipSuccess)
         return CAD_EHIP;
 
@@ -332,7 +319,7 @@ int cad_accept_scan(const int32_t* draft, int with_current, const int32_t* draft
         (!kv->k || !kv->v || kv->n_kv_heads <= 0 || (kv->head_dim != 32 && kv->head_dim != 64 &&
                                                       kv->head_dim != 128)))
         return CAD_EINVAL;
-    if (W > 8 || D > 64) return CAD_EUNSUPPORTED;
+    if (W > 8 || D > 64 || (kv && kv->cap % 4)) return CAD_EUNSUPPORTED;
     return launch_accept(draft, with_current, draft_len, pred, first_pred, B, W, D, mode, accepted, best_w, emitted,
                          n_emitted, ctx, ctx_stride, ctx_len, ctx_cap, kv, stream) == hipSuccess
                ? CAD_OK

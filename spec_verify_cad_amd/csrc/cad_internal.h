@@ -43,6 +43,9 @@ struct FwdDims {
     int o_slices, down_slices;      // K slices of the O and down projections (partials)
 };
 
+// Rotary inverse frequencies base^(-2i/d), i < d/2, computed in double on the host.
+struct RopeFreqs { double inv[64]; };
+
 // Workspace carve-up (offsets are 256-byte aligned).
 struct FwdBufs {
     int32_t* len_snap;
@@ -63,7 +66,7 @@ int device_cu_count();
 
 // Launchers: each returns hipSuccess or the launch error.
 hipError_t launch_embed_norm(const FwdDims& fd, const int32_t* tokens, const void* embed, float eps,
-                             double rope_base, const int32_t* kv_len, int32_t* err, const FwdBufs& wb,
+                             const RopeFreqs& freqs, const int32_t* kv_len, int32_t* err, const FwdBufs& wb,
                              hipStream_t s);
 hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, int32_t* argmax_out, int32_t* kv_len,
                                hipStream_t s);
@@ -77,6 +80,7 @@ hipError_t launch_gemm(int dtype, int kind, const void* A, const void* W, int M,
 int gemm_partial_slices(int dtype, int M, int N, int K);
 // (max, index) partial slots per row written by an EPI_ARGMAX launch of this shape
 int gemm_argmax_slots(int dtype, int M, int N, int K);
+void attention_plan(FwdDims* fd, int cus);
 hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc, const void* vc,
                             hipStream_t s);
 hipError_t launch_attention_merge(const FwdDims& fd, const FwdBufs& wb, hipStream_t s);

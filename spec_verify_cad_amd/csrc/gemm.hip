@@ -43,10 +43,10 @@ __device__ void tile_epilogue(const float* C, int ldc, int m0, int n0, int BM, i
             const int head = F1 / p.d + p.head_off;
             const size_t slot = (size_t)p.len_snap[b] + it;
             const float x1 = C[r * ldc + f1], x2 = C[r * ldc + f1 + half];
-            if (head >= p.Hq + p.Hkv) {
-                T* v = (T*)p.vc + (((size_t)b * p.Hkv + (head - p.Hq - p.Hkv)) * p.cap + slot) * p.d;
-                Elt<T>::st(v, i, x1);
-                Elt<T>::st(v, i + half, x2);
+            if (head >= p.Hq + p.Hkv) {                  // V cache is dim-major [d][cap]
+                T* v = (T*)p.vc + ((size_t)b * p.Hkv + (head - p.Hq - p.Hkv)) * p.d * p.cap + slot;
+                Elt<T>::st(v, (size_t)i * p.cap, x1);
+                Elt<T>::st(v, (size_t)(i + half) * p.cap, x2);
                 continue;
             }
             const float2 cs = p.rope_cs[(size_t)row * half + i];

@@ -155,15 +155,16 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
                                 y[i] = first ? c[i] * t.x - o[i] * t.y : c[i] * t.x + o[i] * t.y;
                             }
                         }
-                        uint16_t* dst;
-                        if (head < p.Hq)
-                            dst = (uint16_t*)p.q_out + ((size_t)tok * p.Hq + head) * p.d + dim;
-                        else if (head < p.Hq + p.Hkv)
-                            dst = (uint16_t*)p.kc + (((size_t)b * p.Hkv + (head - p.Hq)) * p.cap + slot) * p.d + dim;
-                        else
-                            dst = (uint16_t*)p.vc +
-                                  (((size_t)b * p.Hkv + (head - p.Hq - p.Hkv)) * p.cap + slot) * p.d + dim;
-                        st4(dst, y);
+                        if (head < p.Hq) {
+                            st4((uint16_t*)p.q_out + ((size_t)tok * p.Hq + head) * p.d + dim, y);
+                        } else if (head < p.Hq + p.Hkv) {
+                            st4((uint16_t*)p.kc + (((size_t)b * p.Hkv + (head - p.Hq)) * p.cap + slot) * p.d + dim, y);
+                        } else {                                 // V cache is dim-major [d][cap]
+                            uint16_t* vp = (uint16_t*)p.vc +
+                                           (((size_t)b * p.Hkv + (head - p.Hq - p.Hkv)) * p.d + dim) * p.cap + slot;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) vp[(size_t)i * p.cap] = f32_to_bf16(y[i]);
+                        }
                     }
                 }
             }

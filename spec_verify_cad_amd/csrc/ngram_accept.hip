@@ -9,7 +9,7 @@
 // k_accept: greedy left-to-right acceptance (PLD page, "Verification in a single parallel
 // pass") or the longest validated candidate of a block verify (SwitchSD), then the commit:
 // emitted tokens appended to the history, cache length advanced, and in block mode the
-// winner's accepted K/V rows moved down to the slots right after the prefix.
+// winner's accepted K/V entries moved down to the slots right after the prefix.
 #include "cad_device.h"
 
 namespace {
@@ -129,18 +129,26 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
     if (ctx)
         for (int e = tid; e <= a; e += 256) ctx[(size_t)b * ctx_stride + sctx + e] = em[e];
     if (mode == CAD_MASK_BLOCK_TRI && kc && w > 0 && a > 0) {
-        // move rows len + w*D + j -> len + j (j < a); source and destination never overlap (w*D >= D >= a)
+        // move the winner's rows len + w*D + j -> len + j (j < a); source and destination never
+        // overlap (w*D >= D >= a).  K rows are whole [d] rows; V is dim-major, so each of its
+        // d rows per head moves a elements.
         const int len = slen;
-        const int per_row = d * esz / 16;                         // 16-byte chunks per row
-        const int total = 2 * Hkv * a * per_row;
-        for (int e = tid; e < total; e += 256) {
-            const int which = e / (Hkv * a * per_row);
-            const int rem = e % (Hkv * a * per_row);
-            const int g = rem / (a * per_row), j = (rem / per_row) % a, ck = rem % per_row;
-            uint4* base = (uint4*)(which ? vc : kc);
+        const int per_row = d * esz / 16;                         // 16-byte chunks per K row
+        const int ktotal = Hkv * a * per_row;
+        for (int e = tid; e < ktotal; e += 256) {
+            const int g = e / (a * per_row), j = (e / per_row) % a, ck = e % per_row;
+            uint4* base = (uint4*)kc;
             const size_t head = ((size_t)b * Hkv + g) * cap;
-            const size_t rowc = (size_t)d * esz / 16;
-            base[(head + len + j) * rowc + ck] = base[(head + len + (size_t)w * D + j) * rowc + ck];
+            base[(head + len + j) * per_row + ck] = base[(head + len + (size_t)w * D + j) * per_row + ck];
+        }
+        const int vtotal = Hkv * d * a;
+        for (int e = tid; e < vtotal; e += 256) {
+            const int g = e / (d * a), dim = (e / a) % d, j = e % a;
+            const size_t row = (((size_t)b * Hkv + g) * d + dim) * cap;
+            if (esz == 2)
+                ((uint16_t*)vc)[row + len + j] = ((const uint16_t*)vc)[row + len + (size_t)w * D + j];
+            else
+                ((float*)vc)[row + len + j] = ((const float*)vc)[row + len + (size_t)w * D + j];
         }
     }
     __syncthreads();

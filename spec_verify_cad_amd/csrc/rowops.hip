@@ -2,9 +2,11 @@
 //
 // k_embed_norm  first kernel of every forward: captures the per-sequence cache length the
 //               rest of the forward uses (flagging sequences that would overflow), gathers the
-//               embedding rows, applies RMSNorm and tabulates the (cos, sin) of each row's rotary angles
-//               p * base^(-2i/d), computed in double (Copy-as-Decode, Appendix K: the rows
-//               take the absolute positions N sequential decode steps would have).
+//               embedding rows, applies RMSNorm and tabulates the (cos, sin) of each row's
+//               rotary angles p * base^(-2i/d) (Copy-as-Decode, Appendix K: the rows take the
+//               absolute positions N sequential decode steps would have).  The angle is formed
+//               and reduced modulo 2*pi in double, so positions in the tens of thousands keep
+//               full fp32 accuracy in cos and sin.
 // k_resid_norm  residual add of the K-slice partial sums of a projection (in slice order,
 //               so the result does not depend on scheduling), optional rounded copy, and the
 //               RMSNorm that feeds the next projection.
@@ -30,7 +32,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 template <typename T>
 __global__ __launch_bounds__(NT) void k_embed_norm(const int32_t* __restrict__ tokens, const T* __restrict__ embed,
                                                    int h, int vocab, int Nq, int cap, float eps, int mode, int Dblk,
-                                                   int half, double rope_base, const int32_t* __restrict__ kv_len,
+                                                   int half, RopeFreqs freqs, const int32_t* __restrict__ kv_len,
                                                    int32_t* __restrict__ err, int32_t* __restrict__ len_snap,
                                                    float2* __restrict__ rope_cs,
                                                    float* __restrict__ x, T* __restrict__ u) {
@@ -46,8 +48,13 @@ __global__ __launch_bounds__(NT) void k_embed_norm(const int32_t* __restrict__ t
     if (rope_cs) {
         const int pos = len + (mode == CAD_MASK_BLOCK_TRI ? it % Dblk : it);
         for (int i = threadIdx.x; i < half; i += NT) {
-            const double ang = (double)pos * pow(rope_base, -(double)i / (double)half);
-            rope_cs[(size_t)r * half + i] = make_float2((float)cos(ang), (float)sin(ang));
+            const double ang = (double)pos * freqs.inv[i];
+            const double k = rint(ang * 0.15915494309189535);            // 1 / (2 pi)
+            double red = fma(-k, 6.283185307179586, ang);                 // 2 pi, high part
+            red = fma(-k, 2.4492935982947064e-16, red);                   // 2 pi, low part
+            float sn, cn;
+            sincosf((float)red, &sn, &cn);
+            rope_cs[(size_t)r * half + i] = make_float2(cn, sn);
         }
     }
     int t = tokens[r];
@@ -78,9 +85,11 @@ __global__ __launch_bounds__(NT) void k_resid_norm(const float* __restrict__ bas
     const int r = blockIdx.x;
     if (!seq_ok(len_snap, r / Nq, Nq, cap)) return;
     float ss = 0.f;
+#pragma unroll 2
     for (int j = threadIdx.x; j < h; j += NT) {
         float v = 0.f;
-        for (int s = 0; s < slices; ++s) v += part[((size_t)s * M + r) * h + j];
+#pragma unroll 8
+        for (int s = 0; s < slices; ++s) v += part[((size_t)s * M + r) * h + j];   // slice order
         v = base[(size_t)r * h + j] + v;
         rowbuf[j] = v;
         out[(size_t)r * h + j] = v;
@@ -124,16 +133,16 @@ __global__ void k_commit(const int32_t* __restrict__ len_snap, int B, int Nq, in
 }  // namespace
 
 hipError_t launch_embed_norm(const FwdDims& fd, const int32_t* tokens, const void* embed, float eps,
-                             double rope_base, const int32_t* kv_len, int32_t* err, const FwdBufs& wb,
+                             const RopeFreqs& freqs, const int32_t* kv_len, int32_t* err, const FwdBufs& wb,
                              hipStream_t s) {
     const int half = fd.d / 2;
     if (fd.dtype == CAD_DTYPE_F32)
         hipLaunchKernelGGL(k_embed_norm<float>, dim3(fd.M), dim3(NT), 0, s, tokens, (const float*)embed, fd.h, fd.V,
-                           fd.Nq, fd.cap, eps, fd.mode, fd.Dblk, half, rope_base, kv_len, err, wb.len_snap,
+                           fd.Nq, fd.cap, eps, fd.mode, fd.Dblk, half, freqs, kv_len, err, wb.len_snap,
                            wb.rope_cs, wb.x, (float*)wb.u);
     else
         hipLaunchKernelGGL(k_embed_norm<uint16_t>, dim3(fd.M), dim3(NT), 0, s, tokens, (const uint16_t*)embed, fd.h,
-                           fd.V, fd.Nq, fd.cap, eps, fd.mode, fd.Dblk, half, rope_base, kv_len, err, wb.len_snap,
+                           fd.V, fd.Nq, fd.cap, eps, fd.mode, fd.Dblk, half, freqs, kv_len, err, wb.len_snap,
                            wb.rope_cs, wb.x, (uint16_t*)wb.u);
     return hipGetLastError();
 }

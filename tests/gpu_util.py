@@ -1,7 +1,7 @@
 """Helpers shared by the GPU parity tests: device layers/caches from seeded inputs,
 KV-only prefill through the library, and oracle comparisons (tolerances of the contract:
-bit-exact integers and argmax away from near-ties, max-abs 2e-2 on bf16 hidden outputs,
-1e-2 on fp32 logits)."""
+bit-exact integers, max-abs 2e-2 on bf16 hidden outputs, 1e-2 on fp32 logits, and argmax ids
+bit-exact wherever the oracle's top-2 gap makes them unique given the logit error)."""
 import numpy as np
 import torch
 
@@ -34,17 +34,27 @@ def prefill(layer: cad.DeviceLayer, cache: cad.DeviceCache, tokens: np.ndarray, 
         cad.span_forward(layer, cache, t, t.shape[1], flags=cad.KV_ONLY | cad.COMMIT_ALL)
 
 
+def _device_values(a: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(np.ascontiguousarray(a, dtype=np.float32))   # exact: values are bf16
+        return torch.from_numpy(bits.view(np.int16)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
 def upload_oracle_cache(cache: cad.DeviceCache, b: int, oc: O.Cache, dtype: str):
-    """Copy an oracle cache into sequence b of a device cache (an oracle-made input)."""
+    """Copy an oracle cache into sequence b of a device cache (an oracle-made input).
+    The device value cache is dim-major: v[b, g, dim, slot]."""
     n = oc.length
-    for name, src in (("k", oc.K), ("v", oc.V)):
-        dst = getattr(cache, name)
-        if dtype == "bf16":
-            bits = synth.f32_to_bf16_bits(src[:, :n].astype(np.float32))   # exact: values are bf16
-            dst[b, :, :n] = torch.from_numpy(bits.view(np.int16)).cuda()
-        else:
-            dst[b, :, :n] = torch.from_numpy(src[:, :n].astype(np.float32)).cuda()
+    cache.k[b, :, :n] = _device_values(oc.K[:, :n], dtype)
+    cache.v[b, :, :, :n] = _device_values(oc.V[:, :n].transpose(0, 2, 1), dtype)
     cache.len[b] = n
+
+
+def device_cache_rows(cache: cad.DeviceCache, b: int, lo: int, hi: int, dtype: str):
+    """Slots [lo, hi) of sequence b as (K, V), each [Hkv, slots, d] in fp64."""
+    k = to_f64(cache.k[b, :, lo:hi], dtype)
+    v = to_f64(cache.v[b, :, :, lo:hi], dtype).transpose(0, 2, 1)
+    return k, v
 
 
 def run_forward(layer, cache, tokens: np.ndarray, mode=cad.MASK_CAUSAL, W=1, D=1, flags=0, logits=True):
@@ -61,20 +71,43 @@ def run_forward(layer, cache, tokens: np.ndarray, mode=cad.MASK_CAUSAL, W=1, D=1
             "logits": None if lg is None else lg.cpu().numpy().astype(np.float64)}
 
 
+def argmax_check(g_a, ref: dict, g_l=None, what=""):
+    """Argmax ids against the oracle's.
+
+    Each GPU logit may differ from the oracle's by up to its measured row error e_r (the row's
+    max |logit difference|, or LOGIT_TOL when logits were not written).  An fp32-accumulating
+    forward reaches several 1e-3 of such drift through the bf16 rounding points (see
+    test_tolerance_derivation.py), so the argmax is unique, and must match bit for bit, where
+    the oracle's top-2 gap exceeds both NEAR_TIE and 2*e_r.  Elsewhere the GPU's id must be a
+    valid near-top choice: its oracle logit within 2*e_r of the oracle's maximum."""
+    lg = ref["logits"]
+    e = np.full(len(g_a), LOGIT_TOL) if g_l is None else np.max(np.abs(g_l - lg), axis=1)
+    unique = ref["top2_gap"] > np.maximum(NEAR_TIE, 2 * e)
+    bad = np.nonzero((g_a != ref["argmax"]) & unique)[0]
+    assert bad.size == 0, (f"{what} argmax differs at rows {bad[:10]}: gpu {g_a[bad[:10]]} oracle "
+                           f"{ref['argmax'][bad[:10]]} gap {ref['top2_gap'][bad[:10]]} row err {e[bad[:10]]}")
+    rows = np.arange(len(g_a))
+    ok_id = (g_a >= 0) & (g_a < lg.shape[1])
+    assert ok_id.all(), f"{what} argmax out of range at rows {np.nonzero(~ok_id)[0][:10]}"
+    slack = lg.max(axis=1) - lg[rows, g_a]
+    assert (slack <= 2 * e + 1e-12).all(), f"{what} argmax not a near-top choice at rows {np.nonzero(slack > 2 * e)[0][:10]}"
+    return unique
+
+
 def compare(gpu: dict, ref: dict, rows=None, what=""):
     """GPU forward outputs against an oracle forward (rows: subset of GPU rows to use)."""
     g_h = gpu["hidden"] if rows is None else gpu["hidden"][rows]
     g_a = gpu["argmax"] if rows is None else gpu["argmax"][rows]
     dh = np.max(np.abs(g_h - ref["hidden_out"]))
     assert dh <= HIDDEN_TOL, f"{what} hidden max-abs {dh}"
+    g_l = None
     if gpu["logits"] is not None:
         g_l = gpu["logits"] if rows is None else gpu["logits"][rows]
         dl = np.max(np.abs(g_l - ref["logits"]))
         assert dl <= LOGIT_TOL, f"{what} logits max-abs {dl} (hidden {dh})"
-    log(f"{what} hidden max-abs {dh:.3e}" + (f" logits max-abs {dl:.3e}" if gpu["logits"] is not None else ""))
-    sure = ref["top2_gap"] >= NEAR_TIE
-    bad = np.nonzero((g_a != ref["argmax"]) & sure)[0]
-    assert bad.size == 0, f"{what} argmax differs at rows {bad[:10]}: gpu {g_a[bad[:10]]} oracle {ref['argmax'][bad[:10]]}"
+    unique = argmax_check(g_a, ref, g_l, what)
+    log(f"{what} hidden max-abs {dh:.3e}" + (f" logits max-abs {dl:.3e}" if g_l is not None else "") +
+        f" argmax unique on {int(unique.sum())}/{len(g_a)} rows")
     return dh
 
 
@@ -85,8 +118,8 @@ def compare_cache(cache: cad.DeviceCache, b: int, oc: O.Cache, lo: int, hi: int,
     move by several of its own ulps, so the bound is absolute (the hidden-output tolerance for
     bf16, 1e-5 for fp32) and almost every element must be bit-identical."""
     tol = HIDDEN_TOL if dtype == "bf16" else 1e-5
-    for name, ref in (("k", oc.K), ("v", oc.V)):
-        got = to_f64(getattr(cache, name)[b, :, lo:hi], dtype)
+    gk, gv = device_cache_rows(cache, b, lo, hi, dtype)
+    for name, got, ref in (("k", gk, oc.K), ("v", gv, oc.V)):
         want = ref[:, lo:hi]
         diff = np.abs(got - want)
         assert np.max(diff) <= tol, f"{what} {name} max-abs {np.max(diff)}"

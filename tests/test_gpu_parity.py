@@ -131,7 +131,7 @@ def test_accept_scan_block_with_row_compaction():
         assert cache.len[b].item() == L + a
         want_k, want_v = K0[b].copy(), V0[b].copy()
         want_k[:, L:L + a] = K0[b][:, L + w * D:L + w * D + a]
-        want_v[:, L:L + a] = V0[b][:, L + w * D:L + w * D + a]
+        want_v[:, :, L:L + a] = V0[b][:, :, L + w * D:L + w * D + a]      # v is dim-major [g, d, slot]
         np.testing.assert_array_equal(K1[b], want_k)
         np.testing.assert_array_equal(V1[b], want_v)
 
