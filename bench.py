@@ -60,7 +60,7 @@ def main():
 
     from spec_verify_cad_amd import cad, synth
     from spec_verify_cad_amd import roofline as R
-    from spec_verify_cad_amd.configs import CONFIGS
+    from spec_verify_cad_amd.configs import CONFIGS, copy_sweep_inputs
 
     wl = CONFIGS["qwen15_span"]
     shp = wl.shape
@@ -83,11 +83,7 @@ def main():
     lay1.desc = lay1.make_desc()
     layers = [lay0, lay1]
 
-    doc = synth.uniform_tokens(wl.seed, L0 + 4096, shp.vocab, stream=3)
-    prefix = doc[:L0]
-    rng = np.random.default_rng(wl.seed)
-    srcs = [int(rng.integers(L0, len(doc) - N)) for N in spans]
-    span_toks = [doc[s:s + N] for s, N in zip(srcs, spans)]
+    doc, prefix, span_toks = copy_sweep_inputs(wl, spans)
 
     # one cache per N; their lengths are views of one tensor so a single fill restores them all
     lens = torch.zeros(len(spans), dtype=torch.int32, device=dev)

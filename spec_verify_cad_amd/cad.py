@@ -149,10 +149,15 @@ class DeviceCache:
 # the three calls
 # ---------------------------------------------------------------------------------------
 
+def _row_stride(t) -> int:
+    """Elements between rows of a [B, stride] history (a single row may carry any stride)."""
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
 def ngram_lookup(ctx, ctx_len, n: int, W: int, D: int, with_current: int, draft, draft_len, match_pos=None,
                  stream=None):
     B = ctx.shape[0]
-    _check(lib().cad_ngram_lookup(_ptr(ctx), ctx.stride(0), _ptr(ctx_len), B, n, W, D, with_current, _ptr(draft),
+    _check(lib().cad_ngram_lookup(_ptr(ctx), _row_stride(ctx), _ptr(ctx_len), B, n, W, D, with_current, _ptr(draft),
                                   _ptr(draft_len), _ptr(match_pos), _stream(stream)), "cad_ngram_lookup")
 
 
@@ -184,7 +189,7 @@ def accept_scan(draft, with_current: int, draft_len, pred, first_pred, B: int, W
     kvp = ctypes.byref(cache.desc) if cache is not None else None
     _check(lib().cad_accept_scan(_ptr(draft), with_current, _ptr(draft_len), _ptr(pred), _ptr(first_pred), B, W, D,
                                  mode, _ptr(accepted), _ptr(best_w), _ptr(emitted), _ptr(n_emitted), _ptr(ctx),
-                                 ctx.stride(0) if ctx is not None else 0, _ptr(ctx_len), ctx_cap, kvp,
+                                 _row_stride(ctx) if ctx is not None else 0, _ptr(ctx_len), ctx_cap, kvp,
                                  _stream(stream)), "cad_accept_scan")
 
 

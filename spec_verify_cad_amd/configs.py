@@ -49,3 +49,62 @@ CONFIGS = {
                                  {"B": 64, "ctx_len": 32768, "frac": 0.40, "min_copy": 8, "max_copy": 256,
                                   "zipf_s": 1.1, "n": 3, "k": 10, "rounds": 32}),
 }
+
+
+# ---------------------------------------------------------------------------------------
+# input recipes of the workloads (seeded data only; shared by the benchmark and the tests)
+# ---------------------------------------------------------------------------------------
+
+def copy_sweep_inputs(wl: Workload, spans=None, extra_tail: int = 4096):
+    """Copy-span sweep: a uniform random document whose first cache_len tokens fill the
+    cache, and for each span length N a span copied from a random later place of it.
+    Returns (doc, prefix, [span tokens per N])."""
+    import numpy as np
+    from . import synth
+    spans = wl.spans if spans is None else spans
+    doc = synth.uniform_tokens(wl.seed, wl.cache_len + extra_tail, wl.shape.vocab, stream=3)
+    rng = np.random.default_rng(wl.seed)
+    srcs = [int(rng.integers(wl.cache_len, len(doc) - N)) for N in spans]
+    return doc, doc[:wl.cache_len], [doc[s:s + N] for s, N in zip(srcs, spans)]
+
+
+def block_verify_context(wl: Workload):
+    """Context of the block-triangular verify: uniform background, planted verbatim repeats
+    covering the configured fraction, and the final kappa-gram planted five more times with
+    different continuations (so at least W candidates exist)."""
+    from . import synth
+    e = wl.extra
+    ctx, _ = synth.planted_context(wl.seed, e["ctx_len"], wl.shape.vocab, e["frac"], e["min_copy"], e["max_copy"],
+                                   "uniform")
+    return synth.plant_anchor_repeats(ctx, wl.seed, e["kappa"], 5, e["D"], e["max_copy"])
+
+
+def pld_contexts(wl: Workload, B=None):
+    """Contexts of the batched PLD workload: per-sequence seed streams, bounded Zipf
+    background, planted copies covering the configured fraction, and a final planted copy
+    that runs to the end of the context, so every sequence starts mid-copy (the state prompt
+    lookup targets: the suffix has an earlier occurrence).  Returns [B, ctx_len]."""
+    import numpy as np
+    from . import synth
+    e = wl.extra
+    B = e["B"] if B is None else B
+    out = []
+    for b in range(B):
+        ctx, _ = synth.planted_context(wl.seed, e["ctx_len"], wl.shape.vocab, e["frac"], e["min_copy"],
+                                       e["max_copy"], "zipf", e["zipf_s"], stream=b)
+        rng = np.random.default_rng([wl.seed, 77, b])
+        n = int(rng.integers(e["min_copy"], e["max_copy"] + 1))
+        src = int(rng.integers(0, len(ctx) - 2 * n))
+        ctx[len(ctx) - n:] = ctx[src:src + n]
+        out.append(ctx)
+    return np.stack(out)
+
+
+def cad_program_inputs(wl: Workload):
+    """Document and op schedule of the Copy-as-Decode program workload."""
+    from . import synth
+    e = wl.extra
+    doc = synth.uniform_tokens(wl.seed, e["doc_len"], wl.shape.vocab, stream=5)
+    ops = synth.cad_program(wl.seed, e["doc_len"], e["total_out"], e["median"], e["sigma"], e["max_span"],
+                            e["gen_min"], e["gen_max"])
+    return doc, ops

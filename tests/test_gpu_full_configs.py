@@ -1,0 +1,287 @@
+"""GPU parity at the benchmark configurations' full sizes, against the CPU oracle.
+
+Each test runs a workload at its configured size in the launch configuration bench.py uses
+(same caches, capacities, spans and batch), then checks sampled outputs against the oracle and
+properties that hold at any size:
+  * copy-span sweep, 1.5B-shaped layer, L = 2048, N in {8 .. 512} (every committed row);
+  * block-triangular verify, 7B-shaped layer, L = 4096, W = 4 candidates of D = 8, plus a planted
+    greedy candidate that exercises the acceptance and the K/V compaction;
+  * batched PLD rounds, 1.5B-shaped layer, 64 sequences x 32768-token contexts, 32 rounds with no
+    host sync, two sequences replayed by the oracle round by round;
+  * Copy-as-Decode program, 7B-shaped layer, 4096-token document, 4096 output tokens: the first
+    256 output tokens replayed by the oracle, and the whole 8192-row cache checked against the
+    oracle's K/V of the emitted stream.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from spec_verify_cad_amd import cad, synth
+from spec_verify_cad_amd.configs import (CONFIGS, block_verify_context, cad_program_inputs, copy_sweep_inputs,
+                                         pld_contexts)
+
+from gpu_util import (argmax_check, compare, compare_cache, log, logit_tol, prefill, run_forward)
+from helpers import oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+T32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def _layers(wl):
+    log(f"{wl.name}: generating weights")
+    w = synth.layer_weights(wl.shape, wl.seed)
+    dl = cad.DeviceLayer(wl.shape, w)
+    log(f"{wl.name}: decoding oracle weights")
+    return w, dl, oracle_layer(wl.shape, w)
+
+
+@pytest.fixture(scope="module")
+def qwen15():
+    return _layers(CONFIGS["qwen15_span"])
+
+
+@pytest.fixture(scope="module")
+def qwen7():
+    return _layers(CONFIGS["qwen7_block_verify"])
+
+
+# ---------------------------------------------------------------------------------------------
+# config 2: copy-span sweep (the benchmark's workload)
+# ---------------------------------------------------------------------------------------------
+def test_copy_span_sweep_full_size(qwen15):
+    wl = CONFIGS["qwen15_span"]
+    _, dl, OL = qwen15
+    L0, spans = wl.cache_len, list(wl.spans)
+    cap = L0 + max(spans) + 64 + 8                        # bench.py's capacity
+    doc, prefix, span_toks = copy_sweep_inputs(wl, spans)
+    cache = cad.DeviceCache(wl.shape, 1, cap)
+    log("copy sweep: prefill 2048")
+    cad.span_forward(dl, cache, T32(prefix[None]), L0, flags=cad.KV_ONLY | cad.COMMIT_ALL)
+    torch.cuda.synchronize()
+    oc = O.cache_from_tokens(OL, prefix, cap)
+    rows = np.r_[0:8, 1000:1008, L0 - 8:L0]
+    for lo in rows[::8]:
+        compare_cache(cache, 0, oc, int(lo), int(lo) + 8, "bf16", what=f"prefill rows {lo}")
+    for N, toks in zip(spans, span_toks):
+        log(f"copy sweep N={N}")
+        cache.len.fill_(L0)
+        g = run_forward(dl, cache, toks[None], flags=cad.COMMIT_ALL)
+        assert int(cache.len[0]) == L0 + N
+        ref = O.span_forward(OL, oc.copy(), toks)
+        compare(g, ref, what=f"N={N}")
+        c2 = oc.copy()
+        O.span_forward(OL, c2, toks)
+        compare_cache(cache, 0, c2, L0, L0 + N, "bf16", what=f"N={N} committed rows")
+
+
+# ---------------------------------------------------------------------------------------------
+# config 4: block-triangular multi-candidate verify
+# ---------------------------------------------------------------------------------------------
+def _block_round(dl, OL, cache, oc, hist, cands, dlen, first_pred, W, D, what):
+    """One block verify forward + accept on the GPU, checked against the oracle."""
+    L = int(cache.len[0])
+    g = run_forward(dl, cache, cands.reshape(1, -1), mode=cad.MASK_BLOCK, W=W, D=D)
+    assert int(cache.len[0]) == L                        # a verify forward does not commit
+    ref = O.span_forward(OL, oc.copy(), cands.reshape(-1), mode="block", W=W, D=D, commit=False)
+    compare(g, ref, what=what)
+    pred = g["argmax"]
+    acc, bw, ne = (torch.full((1,), -1, dtype=torch.int32, device="cuda") for _ in range(3))
+    em = torch.full((1, D + 1), -1, dtype=torch.int32, device="cuda")
+    k_before, v_before = cache.k.clone(), cache.v.clone()
+    cad.accept_scan(T32(cands.reshape(1, -1)), 0, T32(dlen[None]), T32(pred[None]), T32([first_pred]), 1, W, D,
+                    cad.MASK_BLOCK, acc, bw, em, ne, cache=cache)
+    torch.cuda.synchronize()
+    a, w, e, _ = O.accept_block(cands, dlen, pred, int(first_pred), D)
+    assert (acc.item(), bw.item(), ne.item()) == (a, w, a + 1), what
+    assert list(em[0, :a + 1].cpu().numpy()) == e
+    assert int(cache.len[0]) == L + a
+    # compaction: the winner's first a slots moved down to L..L+a-1, nothing else changed
+    want_k, want_v = k_before.clone(), v_before.clone()
+    want_k[0, :, L:L + a] = k_before[0, :, L + w * D:L + w * D + a]
+    want_v[0, :, :, L:L + a] = v_before[0, :, :, L + w * D:L + w * D + a]
+    assert torch.equal(cache.k, want_k) and torch.equal(cache.v, want_v), what
+    return ref, a, w
+
+
+def test_block_verify_full_size(qwen7):
+    wl = CONFIGS["qwen7_block_verify"]
+    _, dl, OL = qwen7
+    e = wl.extra
+    W, D, n = e["W"], e["D"], e["kappa"]
+    ctx = block_verify_context(wl)
+    Lc = len(ctx)
+    cap = Lc + W * D + 32
+    cache = cad.DeviceCache(wl.shape, 1, cap)
+    log("block verify: prefill 4095 + anchor")
+    prefill(dl, cache, ctx[None, :Lc - 1])
+    anchor = run_forward(dl, cache, ctx[None, Lc - 1:], flags=cad.COMMIT_ALL, logits=False)
+    first_pred = int(anchor["argmax"][0])
+    oc = O.cache_from_tokens(OL, ctx[:Lc - 1], cap)
+    oa = O.span_forward(OL, oc, ctx[Lc - 1:])
+    argmax_check(anchor["argmax"], oa, what="anchor", tol=logit_tol(wl.shape.hidden))
+    compare_cache(cache, 0, oc, Lc - 64, Lc, "bf16", what="anchor rows")
+    # kappa-gram lookup of W recency-ranked candidates (bit-exact)
+    hist = T32(ctx[None])
+    draft = torch.full((1, W * D), -1, dtype=torch.int32, device="cuda")
+    dlen = torch.full((1, W), -1, dtype=torch.int32, device="cuda")
+    mpos = torch.full((1, W), -1, dtype=torch.int32, device="cuda")
+    cad.ngram_lookup(hist, T32([Lc]), n, W, D, 0, draft, dlen, mpos)
+    torch.cuda.synchronize()
+    od, ol, om = O.ngram_lookup(ctx, Lc, n, W, D)
+    np.testing.assert_array_equal(draft.cpu().numpy().reshape(W, D), od)
+    np.testing.assert_array_equal(dlen.cpu().numpy()[0], ol)
+    np.testing.assert_array_equal(mpos.cpu().numpy()[0], om)
+    assert (ol > 0).sum() == W
+    cands = od.copy()
+    log("block verify: retrieved candidates")
+    _block_round(dl, OL, cache, oc, hist, cands, ol, first_pred, W, D, "block retrieved")
+    # planted agreement: candidate 2 becomes the oracle's greedy continuation from the anchor
+    greedy, c = [first_pred], oc.copy()
+    for _ in range(D - 1):
+        greedy.append(int(O.decode_one(OL, c, greedy[-1])["argmax"][0]))
+    cands[2] = greedy
+    ol2 = ol.copy()
+    ol2[2] = D
+    cache.len.fill_(Lc)                                  # undo the first round's acceptance, if any
+    log("block verify: planted greedy candidate")
+    ref, a, w = _block_round(dl, OL, cache, oc, hist, cands, ol2, first_pred, W, D, "block planted")
+    # the planted candidate is accepted as far as the GPU's argmaxes are determined: its first
+    # token is first_pred, and token j agrees with the oracle's (greedy) argmax of row (2, j-1)
+    unique = ref["top2_gap"][2 * D:2 * D + D - 1] > 2 * logit_tol(wl.shape.hidden)
+    lead = int(np.argmin(unique)) if not unique.all() else D - 1
+    assert a >= 1 + lead, (a, w, unique)
+    if unique.all():
+        assert (a, w) == (D, 2)
+
+
+# ---------------------------------------------------------------------------------------------
+# config 5: batched PLD rounds, zero host syncs inside the 32 rounds
+# ---------------------------------------------------------------------------------------------
+def test_pld_batch_rounds_full_size(qwen15):
+    wl = CONFIGS["qwen15_pld_batch"]
+    _, dl, OL = qwen15
+    e = wl.extra
+    B, Lc, n, k, R = e["B"], e["ctx_len"], e["n"], e["k"], e["rounds"]
+    log("pld: contexts")
+    ctxs = pld_contexts(wl)
+    stride = Lc + R * (k + 1) + 8
+    cap = stride
+    hist_np = np.zeros((B, stride), dtype=np.int32)
+    hist_np[:, :Lc] = ctxs
+    hist, hlen = T32(hist_np), T32(np.full(B, Lc))
+    cache = cad.DeviceCache(wl.shape, B, cap)
+    log("pld: prefill 64 x 32767")
+    prefill(dl, cache, ctxs[:, :Lc - 1], chunk=2048)
+    torch.cuda.synchronize()
+    assert (cache.len.cpu().numpy() == Lc - 1).all()
+    rows = torch.zeros((B, 1 + k), dtype=torch.int32, device="cuda")
+    dlen = torch.zeros((B, 1), dtype=torch.int32, device="cuda")
+    am = torch.zeros((B, 1 + k), dtype=torch.int32, device="cuda")
+    acc, ne = torch.zeros(B, dtype=torch.int32, device="cuda"), torch.zeros(B, dtype=torch.int32, device="cuda")
+    em = torch.zeros((B, k + 1), dtype=torch.int32, device="cuda")
+    rec_rows = torch.zeros((R, B, 1 + k), dtype=torch.int32, device="cuda")
+    rec_dlen = torch.zeros((R, B), dtype=torch.int32, device="cuda")
+    rec_pred = torch.zeros((R, B, 1 + k), dtype=torch.int32, device="cuda")
+    rec_acc = torch.zeros((R, B), dtype=torch.int32, device="cuda")
+    ws = cad.alloc_workspace(cad.span_forward_workspace(dl, B, 1 + k, cad.MASK_CAUSAL, 1, 1, cap, 0))
+    log("pld: 32 rounds")
+    for r in range(R):
+        cad.ngram_lookup(hist, hlen, n, 1, k, 1, rows, dlen)
+        cad.span_forward(dl, cache, rows, 1 + k, argmax_out=am, workspace=ws)
+        cad.accept_scan(rows, 1, dlen, am, None, B, 1, k, cad.MASK_CAUSAL, acc, None, em, ne, ctx=hist, ctx_len=hlen,
+                        ctx_cap=stride, cache=cache)
+        rec_rows[r].copy_(rows)
+        rec_dlen[r].copy_(dlen[:, 0])
+        rec_pred[r].copy_(am)
+        rec_acc[r].copy_(acc)
+    torch.cuda.synchronize()
+    rows_h, dlen_h, pred_h, acc_h = (t.cpu().numpy() for t in (rec_rows, rec_dlen, rec_pred, rec_acc))
+    hist_h, hlen_h, kv_h = hist.cpu().numpy(), hlen.cpu().numpy(), cache.len.cpu().numpy()
+    assert (hlen_h == Lc + (acc_h + 1).sum(0)).all() and (kv_h == hlen_h - 1).all()
+    assert (dlen_h[0] > 0).all()                         # every sequence starts mid-copy
+    # the oracle replays two sequences round by round, following the GPU's stream where an
+    # argmax was not determined (its choice is then checked to be a near-top one)
+    for b in (0, 41):
+        log(f"pld: oracle replay of sequence {b}")
+        oc = O.cache_from_tokens(OL, ctxs[b][:Lc - 1], cap)
+        h = list(ctxs[b])
+        for r in range(R):
+            d, l, _ = O.ngram_lookup(np.array(h), len(h), n, 1, k)
+            assert rows_h[r, b, 0] == h[-1] and list(rows_h[r, b, 1:]) == list(d[0]) and dlen_h[r, b] == l[0], (b, r)
+            ref = O.span_forward(OL, oc, [h[-1]] + list(d[0]), commit=False)
+            argmax_check(pred_h[r, b], ref, None, what=f"pld b={b} r={r}", tol=logit_tol(wl.shape.hidden))
+            a, emitted = O.accept_causal(d[0], int(l[0]), pred_h[r, b])
+            assert a == acc_h[r, b], (b, r)
+            h += emitted
+            oc.length += a + 1
+        np.testing.assert_array_equal(hist_h[b, :len(h)], h)
+
+
+# ---------------------------------------------------------------------------------------------
+# config 3: a Copy-as-Decode program (copy spans and greedy gen segments)
+# ---------------------------------------------------------------------------------------------
+def test_cad_program_full_size(qwen7):
+    wl = CONFIGS["qwen7_cad_program"]
+    _, dl, OL = qwen7
+    doc, ops = cad_program_inputs(wl)
+    Ld, T = len(doc), wl.extra["total_out"]
+    cap = Ld + T + 8
+    cache = cad.DeviceCache(wl.shape, 1, cap)
+    log("cad program: prefill document")
+    prefill(dl, cache, doc[None])
+    # every forward writes its argmax rows into one device buffer; a gen forward reads its input
+    # token straight from the previous forward's last argmax (no host sync in the program)
+    total_rows = sum(o[2] if o[0] == "copy" else o[1] for o in ops)
+    preds = torch.full((total_rows + 1,), -1, dtype=torch.int32, device="cuda")
+    doc_t = T32(doc)
+    ws = {}
+    pos, last = 0, None            # rows written so far; pointer of the last forward's final row
+    stream_src = []                 # per output token: ("doc", index) or ("gen", pred row)
+    log(f"cad program: {len(ops)} ops")
+    for op in ops:
+        if op[0] == "copy":
+            _, src, N = op
+            toks = doc_t[src:src + N].view(1, N)
+            stream_src += [("doc", src + i) for i in range(N)]
+        else:
+            N = 1
+        for rep in range(1 if op[0] == "copy" else op[1]):
+            if op[0] == "gen":
+                toks = preds[last:last + 1].view(1, 1)
+                stream_src.append(("gen", last))
+            if N not in ws:
+                ws[N] = cad.alloc_workspace(cad.span_forward_workspace(dl, 1, N, cad.MASK_CAUSAL, 1, 1, cap,
+                                                                       cad.COMMIT_ALL))
+            cad.span_forward(dl, cache, toks, N, flags=cad.COMMIT_ALL, argmax_out=preds[pos:pos + N].view(1, N),
+                             workspace=ws[N])
+            pos += N
+            last = pos - 1
+    torch.cuda.synchronize()
+    assert int(cache.len[0]) == Ld + T
+    pred_h = preds.cpu().numpy()
+    stream = np.array([doc[i] if kind == "doc" else pred_h[i] for kind, i in stream_src])
+    assert len(stream) == T
+    # the whole cache against the oracle's K/V of document + emitted stream (a one-layer
+    # model's cached K/V depend only on token and position)
+    log("cad program: oracle K/V of 8192 rows")
+    full = np.concatenate([doc, stream])
+    oc_all = O.cache_from_tokens(OL, full, cap)
+    for lo in range(0, Ld + T, 512):
+        compare_cache(cache, 0, oc_all, lo, min(lo + 512, Ld + T), "bf16", what=f"cache rows {lo}")
+    # the first 256 output tokens replayed by the oracle, forward by forward
+    log("cad program: oracle replay of the first 256 output tokens")
+    oc = O.cache_from_tokens(OL, doc, cap)
+    row, out = 0, 0
+    for op in ops:
+        if out >= 256:
+            break
+        N, reps = (op[2], 1) if op[0] == "copy" else (1, op[1])
+        for _ in range(reps):
+            toks = stream[out:out + N]
+            ref = O.span_forward(OL, oc, toks)
+            argmax_check(pred_h[row:row + N], ref, None, what=f"cad forward at output {out}",
+                         tol=logit_tol(wl.shape.hidden))
+            row += N
+            out += N

@@ -276,3 +276,44 @@ def test_forward_is_deterministic(small):
         outs.append(run_forward(dl, c, span))
     for k in ("argmax", "hidden", "logits"):
         np.testing.assert_array_equal(outs[0][k], outs[1][k])
+
+
+def test_forward_replays_from_a_hip_graph(small):
+    # bench.py replays forwards from HIP graphs: every replay must reproduce the eager result,
+    # with the program's own eager work and synchronisations between replays
+    w, dl, OL = small
+    log("graph replay")
+    L0, N, cap = 120, 21, 200
+    ctx = synth.uniform_tokens(43, L0, SMALL.vocab)[None]
+    span = torch.from_numpy(synth.uniform_tokens(44, N, SMALL.vocab)[None].astype(np.int32)).cuda()
+    cache = cad.DeviceCache(SMALL, 1, cap)
+    prefill(dl, cache, ctx)
+    am = torch.zeros((1, N), dtype=torch.int32, device="cuda")
+    hid = torch.zeros((N, SMALL.hidden), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((N, SMALL.vocab), dtype=torch.float32, device="cuda")
+    ws = cad.alloc_workspace(cad.span_forward_workspace(dl, 1, N, cad.MASK_CAUSAL, 1, 1, cap, cad.COMMIT_ALL))
+
+    def fwd(stream):
+        cache.len.fill_(L0)
+        cad.span_forward(dl, cache, span, N, flags=cad.COMMIT_ALL, argmax_out=am, hidden_out=hid, logits_out=lg,
+                         workspace=ws, stream=stream)
+
+    fwd(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (am, hid, lg, cache.k, cache.v)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        fwd(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (am, hid, lg):
+            t.zero_()
+        cache.len.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((am, hid, lg, cache.k, cache.v), eager):
+            assert torch.equal(a, b), f"replay {rep}"
+        assert int(cache.len[0]) == L0 + N

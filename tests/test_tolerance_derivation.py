@@ -1,12 +1,19 @@
-"""Why the argmax check uses the measured logit error, not a fixed 1e-3 near-tie margin.
+"""Why the argmax check uses the measured logit error, not a fixed 1e-3 near-tie margin, and why
+the logit and hidden bounds of the full-size tests grow with the layer's width.
 
 The oracle accumulates in fp64; any GPU forward accumulates in fp32.  Both round to bf16 at the
 same eight points, but wherever an fp32 sum lands within its own rounding error of a bf16
 rounding boundary the two sides round differently, and the differences cascade through the
 following RMSNorms and projections.  This test re-runs the oracle's arithmetic with fp32 matrix
 products (numpy, test-side code that shares nothing with the HIP library) and measures the
-drift: it stays inside the contract's logit tolerance (1e-2) but is several times 1e-3, so an
-argmax is only determined where the top-2 gap exceeds twice the row's logit error."""
+drift: on the small test layer (hidden 512) it stays inside the contract's logit tolerance (1e-2)
+but is several times 1e-3, so an argmax is only determined where the top-2 gap exceeds twice the
+row's logit error.  On the 1.5B-shaped layer the same ideal fp32 pipeline already exceeds 1e-2
+(1.0e-2 to 1.2e-2 measured; 1.6e-2 on the 7B shape, whose hidden outputs move by up to 6.25e-2):
+each bf16 flip of the final normed input adds +-w*ulp to a logit, and each flip of the SwiGLU
+product adds +-w*ulp to the residual stream, so the drift grows with the square root of the
+LM head's input width and of the FFN width respectively.  The full-size bounds are the contract's
+values scaled that way (gpu_util.logit_tol, gpu_util.hidden_tol)."""
 import numpy as np
 
 import oracle as O
@@ -14,6 +21,7 @@ from spec_verify_cad_amd import synth
 from spec_verify_cad_amd.configs import SMALL
 
 from helpers import oracle_layer
+from gpu_util import hidden_tol, logit_tol
 
 LOGIT_TOL, HIDDEN_TOL, NEAR_TIE = 1e-2, 2e-2, 1e-3
 
@@ -71,3 +79,18 @@ def test_fp32_accumulation_drift_needs_measured_argmax_margin():
     am = np.argmax(got["logits"], axis=1)
     assert (am[unique] == ref["argmax"][unique]).all()
     assert unique.mean() > 0.8
+
+
+def test_fp32_drift_at_the_1p5b_shape_fits_the_width_scaled_bounds():
+    from spec_verify_cad_amd.configs import CONFIGS, copy_sweep_inputs
+    wl = CONFIGS["qwen15_span"]
+    w = synth.layer_weights(wl.shape, wl.seed)
+    L = oracle_layer(wl.shape, w)
+    _, prefix, (span,) = copy_sweep_inputs(wl, (8,))
+    cache = O.cache_from_tokens(L, prefix, wl.cache_len + 16)
+    ref = O.span_forward(L, cache.copy(), span)
+    got = fp32_forward(L, cache, span)
+    dl = np.abs(got["logits"] - ref["logits"])
+    assert (np.abs(got["hidden_out"] - ref["hidden_out"]) <= hidden_tol(ref["hidden_out"], wl.shape.ffn)).all()
+    assert dl.max() <= logit_tol(wl.shape.hidden)
+    assert dl.max() > LOGIT_TOL * 0.8             # the contract's fixed 1e-2 is (nearly) used up
