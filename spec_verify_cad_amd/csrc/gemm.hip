@@ -1,8 +1,9 @@
-// LDS-tiled projection GEMMs of the span forward for many token rows: Y[M, N] = A[M, K] . W[N, K]^T,
-// where A holds the M = B*Nq token rows of the forward (activations) and W is a row-major
-// [out, in] weight.  The bf16 kernel runs on gfx950 MFMA (v_mfma_f32_16x16x32_bf16) with
-// LDS-staged A and W tiles; the fp32 kernel (for an fp32 layer) uses plain FMA.  Both stage the
-// fp32 accumulator tile in LDS and finish with one of the fused epilogues (EpiKind):
+// Projection GEMMs of the span forward: Y[M, N] = A[M, K] . W[N, K]^T, where A holds the
+// M = B*Nq token rows of the forward (activations) and W is a row-major [out, in] weight.
+// bf16 layers run on gfx950 MFMA: few-row launches on the weight-streaming kernel
+// (gemm_skinny.hip), the others on the LDS-tiled kernel (gemm_big.hip).  This file holds the
+// dispatch and the plain-FMA kernel of an fp32 layer, which stages its fp32 tile in LDS and
+// finishes with one of the fused epilogues (EpiKind):
 //   EPI_QKV     RoPE at the row's absolute position, q -> workspace, k/v appended to the cache
 //               (Copy-as-Decode, Appendix K: positions advance exactly as in decode steps);
 //   EPI_SWIGLU  silu(gate) * up, the tile holding matching gate and up columns;
@@ -10,8 +11,6 @@
 //               logits never reach memory unless a debug buffer is given;
 //   EPI_PARTIAL fp32 partial sums of one K slice (O and down projections; the residual add
 //               and the following RMSNorm happen in the next row kernel).
-// A launch may split K into slices (units = tiles x slices) so that narrow projections still
-// fill the chip.  Few-row launches go to the weight-streaming kernel instead.
 #include "cad_device.h"
 
 hipError_t launch_skinny(int kind, const void* A, const void* W, int M, int N, int K, const EpiParams& p,
@@ -19,12 +18,12 @@ hipError_t launch_skinny(int kind, const void* A, const void* W, int M, int N, i
 bool skinny_supports(int kind, int M, int K);
 int skinny_partial_slices(int K);
 int skinny_argmax_slots(int M, int N, int K);
+hipError_t launch_big(int kind, const void* A, const void* W, int M, int N, int K, int slices, const EpiParams& p,
+                      hipStream_t s);
+int big_slots(int kind, int M, int N, int K);
+int big_partial_slices(int M, int N, int K, int cus);
 
 namespace {
-
-constexpr int BK = 64;           // k-extent of one LDS stage (bf16 kernel)
-constexpr int LPAD = 8;          // bf16 elements of padding per LDS row (16 bytes)
-constexpr int LDK = BK + LPAD;   // LDS row pitch in elements
 
 // ---------------------------------------------------------------------------------------
 // epilogues on the fp32 tile C[BM][ldc] in LDS (token-major), run by all 256 threads
@@ -111,125 +110,6 @@ __device__ __forceinline__ int w_row(int tr, int nt, int BN, int N, int ffn, boo
     return tr < hb ? F : ffn + F;
 }
 
-// XCD-aware unit id: workgroups are dealt round-robin over the 8 XCDs, so give each XCD a
-// contiguous run of units (neighbouring row tiles of one column tile share its W in L2).
-__device__ __forceinline__ int xcd_unit(int bid, int grid) {
-    return (bid % 8) * (grid / 8) + bid / 8;
-}
-
-// ---------------------------------------------------------------------------------------
-// bf16 MFMA kernel.  WG = 4 waves arranged WM x WN; wave tile (BM/WM) x (BN/WN).
-// MFMA roles: A operand = W rows (output features), B operand = token rows.
-// ---------------------------------------------------------------------------------------
-template <int KIND, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void k_gemm_bf16(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                                                   int M, int N, int K, int nmt, int nnt, int S, int ffn,
-                                                   EpiParams p) {
-    constexpr int FT = BN / WN / 16, TT = BM / WM / 16;
-    constexpr int WCH = BN * (BK / 8) / 256;                     // 16-byte W chunks per thread
-    constexpr int ACH = (BM * (BK / 8) + 255) / 256;             // 16-byte A chunks per thread
-    constexpr int STAGE_BYTES = (BN + BM) * LDK * 2;
-    constexpr int CT_BYTES = BM * (BN + 4) * 4;
-    constexpr int SMEM = STAGE_BYTES > CT_BYTES ? STAGE_BYTES : CT_BYTES;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-    uint16_t* Ws = (uint16_t*)smem;
-    uint16_t* As = Ws + BN * LDK;
-
-    const int total = nmt * nnt * S;
-    const int unit = xcd_unit(blockIdx.x, gridDim.x);
-    if (unit < total) {
-        const int ks = unit % S, tile = unit / S;
-        const int mt = tile % nmt, nt = tile / nmt;
-        const int m0 = mt * BM;
-        const int kbeg = ks * p.k_slice, kend = min(K, kbeg + p.k_slice);
-        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-        const int wm = wave / WN, wn = wave % WN;
-        const int l16 = lane & 15, g4 = lane >> 4;
-
-        // global -> register prefetch of one BK stage
-        uint4 wreg[WCH], areg[ACH];
-        const uint16_t* wsrc[WCH];
-        bool wval[WCH];
-#pragma unroll
-        for (int c = 0; c < WCH; ++c) {
-            const int ch = tid + c * 256, tr = ch / (BK / 8);
-            bool v;
-            const int r = w_row(tr, nt, BN, N, ffn, v);
-            wval[c] = v;
-            wsrc[c] = W + (size_t)(v ? r : 0) * K + (ch % (BK / 8)) * 8;
-        }
-        auto load_stage = [&](int k0) {
-#pragma unroll
-            for (int c = 0; c < WCH; ++c) {
-                const int kk = k0 + ((tid + c * 256) % (BK / 8)) * 8;
-                wreg[c] = (wval[c] && kk < kend) ? *(const uint4*)(wsrc[c] + k0) : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int c = 0; c < ACH; ++c) {
-                const int ch = tid + c * 256;
-                const int r = ch / (BK / 8), kk = k0 + (ch % (BK / 8)) * 8;
-                const bool v = ch < BM * (BK / 8) && m0 + r < M && kk < kend;
-                areg[c] = v ? *(const uint4*)(A + (size_t)(m0 + r) * K + kk) : make_uint4(0, 0, 0, 0);
-            }
-        };
-        auto store_stage = [&]() {
-#pragma unroll
-            for (int c = 0; c < WCH; ++c) {
-                const int ch = tid + c * 256;
-                *(uint4*)(Ws + (ch / (BK / 8)) * LDK + (ch % (BK / 8)) * 8) = wreg[c];
-            }
-#pragma unroll
-            for (int c = 0; c < ACH; ++c) {
-                const int ch = tid + c * 256;
-                if (ch < BM * (BK / 8)) *(uint4*)(As + (ch / (BK / 8)) * LDK + (ch % (BK / 8)) * 8) = areg[c];
-            }
-        };
-
-        f32x4_t acc[FT][TT];
-#pragma unroll
-        for (int i = 0; i < FT; ++i)
-#pragma unroll
-            for (int j = 0; j < TT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-        load_stage(kbeg);
-        for (int k0 = kbeg; k0 < kend; k0 += BK) {
-            __syncthreads();
-            store_stage();
-            __syncthreads();
-            if (k0 + BK < kend) load_stage(k0 + BK);
-#pragma unroll
-            for (int kq = 0; kq < BK / 32; ++kq) {
-                bf16x8_t af[FT], bfr[TT];
-#pragma unroll
-                for (int ft = 0; ft < FT; ++ft)
-                    af[ft] = *(const bf16x8_t*)(Ws + (wn * FT * 16 + ft * 16 + l16) * LDK + kq * 32 + g4 * 8);
-#pragma unroll
-                for (int tt = 0; tt < TT; ++tt)
-                    bfr[tt] = *(const bf16x8_t*)(As + (wm * TT * 16 + tt * 16 + l16) * LDK + kq * 32 + g4 * 8);
-#pragma unroll
-                for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-                    for (int tt = 0; tt < TT; ++tt)
-                        acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ft], bfr[tt], acc[ft][tt], 0, 0, 0);
-            }
-        }
-        __syncthreads();
-        // accumulators -> LDS tile C[token][feature]; lane holds features 4*g4..+3 of token l16
-        float* C = (float*)smem;
-        constexpr int ldc = BN + 4;
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                const int tok = wm * TT * 16 + tt * 16 + l16;
-                const int fea = wn * FT * 16 + ft * 16 + g4 * 4;
-                *(f32x4_t*)(C + tok * ldc + fea) = acc[ft][tt];
-            }
-        __syncthreads();
-        tile_epilogue<uint16_t, KIND>(C, ldc, m0, nt * BN, BM, BN, ks, p);
-    }
-}
-
 // ---------------------------------------------------------------------------------------
 // fp32 kernel (fp32 layers): tile 16 tokens x 128 features, plain FMA.
 // ---------------------------------------------------------------------------------------
@@ -277,47 +157,27 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 
 struct TilePlan { int BM, BN, nmt, nnt, S, k_slice, grid; };
 
-TilePlan tile_plan(int dtype, int kind, int M, int N, int K, int slices) {
+TilePlan tile_plan(int kind, int M, int N, int K, int slices) {
     TilePlan t;
     t.BN = 128;
-    if (dtype == CAD_DTYPE_F32) t.BM = 16;
-    else t.BM = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+    t.BM = 16;
     t.nmt = (M + t.BM - 1) / t.BM;
     // SwiGLU tiles cover BN/2 gate columns and the matching BN/2 up columns (N = 2*ffn)
     t.nnt = kind == EPI_SWIGLU ? (N / 2 + t.BN / 2 - 1) / (t.BN / 2) : (N + t.BN - 1) / t.BN;
     t.S = kind == EPI_PARTIAL ? slices : 1;
-    const int kstep = dtype == CAD_DTYPE_F32 ? 32 : BK;
-    t.k_slice = ((K + t.S - 1) / t.S + kstep - 1) / kstep * kstep;
-    const int total = t.nmt * t.nnt * t.S;
-    t.grid = dtype == CAD_DTYPE_F32 ? total : (total + 7) / 8 * 8;
+    t.k_slice = ((K + t.S - 1) / t.S + 31) / 32 * 32;
+    t.grid = t.nmt * t.nnt * t.S;
     return t;
 }
 
-template <int KIND, int BM, int BN, int WM, int WN>
-hipError_t go_bf16(const void* A, const void* W, int M, int N, int K, int ffn, const TilePlan& t,
-                   const EpiParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((k_gemm_bf16<KIND, BM, BN, WM, WN>), dim3(t.grid), dim3(256), 0, s, (const uint16_t*)A,
-                       (const uint16_t*)W, M, N, K, t.nmt, t.nnt, t.S, ffn, p);
-    return hipGetLastError();
-}
-
 template <int KIND>
-hipError_t dispatch(int dtype, const void* A, const void* W, int M, int N, int K, int slices, EpiParams p,
-                    hipStream_t s) {
+hipError_t dispatch_f32(const void* A, const void* W, int M, int N, int K, int slices, EpiParams p, hipStream_t s) {
     const int ffn = KIND == EPI_SWIGLU ? p.ffn : 0;
-    const TilePlan t = tile_plan(dtype, KIND, M, N, K, slices);
+    const TilePlan t = tile_plan(KIND, M, N, K, slices);
     p.k_slice = t.k_slice;
-    if (dtype == CAD_DTYPE_F32) {
-        hipLaunchKernelGGL((k_gemm_f32<KIND>), dim3(t.grid), dim3(256), 0, s, (const float*)A, (const float*)W, M, N,
-                           K, t.nmt, t.nnt, t.S, ffn, p);
-        return hipGetLastError();
-    }
-    switch (t.BM) {
-        case 16: return go_bf16<KIND, 16, 128, 1, 4>(A, W, M, N, K, ffn, t, p, s);
-        case 32: return go_bf16<KIND, 32, 128, 2, 2>(A, W, M, N, K, ffn, t, p, s);
-        case 64: return go_bf16<KIND, 64, 128, 2, 2>(A, W, M, N, K, ffn, t, p, s);
-        default: return go_bf16<KIND, 128, 128, 2, 2>(A, W, M, N, K, ffn, t, p, s);
-    }
+    hipLaunchKernelGGL((k_gemm_f32<KIND>), dim3(t.grid), dim3(256), 0, s, (const float*)A, (const float*)W, M, N, K,
+                       t.nmt, t.nnt, t.S, ffn, p);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -325,28 +185,35 @@ hipError_t dispatch(int dtype, const void* A, const void* W, int M, int N, int K
 // K slices of an EPI_PARTIAL launch (the O and down projections); the workspace holds
 // slices x M x N fp32 partials.
 int gemm_argmax_slots(int dtype, int M, int N, int K) {
-    if (dtype == CAD_DTYPE_BF16 && skinny_supports(EPI_ARGMAX, M, K)) return skinny_argmax_slots(M, N, K);
-    return tile_plan(dtype, EPI_ARGMAX, M, N, K, 1).nnt;
+    if (dtype == CAD_DTYPE_F32) return tile_plan(EPI_ARGMAX, M, N, K, 1).nnt;
+    if (skinny_supports(EPI_ARGMAX, M, K)) return skinny_argmax_slots(M, N, K);
+    return big_slots(EPI_ARGMAX, M, N, K);
 }
 
+// K slices of an EPI_PARTIAL launch (the O and down projections); the workspace holds
+// slices x M x N fp32 partials.
 int gemm_partial_slices(int dtype, int M, int N, int K) {
-    if (dtype == CAD_DTYPE_BF16 && skinny_supports(EPI_PARTIAL, M, K)) return skinny_partial_slices(K);
-    const TilePlan t = tile_plan(dtype, EPI_PARTIAL, M, N, K, 1);
-    const int tiles = t.nmt * t.nnt;
-    const int want = 2 * device_cu_count();
-    int S = (want + tiles - 1) / tiles;
-    const int smax = K / 256 > 1 ? K / 256 : 1;                  // at least 256 of K per slice
-    S = S < 1 ? 1 : (S > smax ? smax : S);
-    return S;
+    if (dtype == CAD_DTYPE_F32) {
+        const TilePlan t = tile_plan(EPI_PARTIAL, M, N, K, 1);
+        const int tiles = t.nmt * t.nnt;
+        int S = (2 * device_cu_count() + tiles - 1) / tiles;
+        const int smax = K / 256 > 1 ? K / 256 : 1;
+        return S < 1 ? 1 : (S > smax ? smax : S);
+    }
+    if (skinny_supports(EPI_PARTIAL, M, K)) return skinny_partial_slices(K);
+    return big_partial_slices(M, N, K, device_cu_count());
 }
 
 hipError_t launch_gemm(int dtype, int kind, const void* A, const void* W, int M, int N, int K, int slices,
                        EpiParams p, hipStream_t s) {
-    if (dtype == CAD_DTYPE_BF16 && skinny_supports(kind, M, K)) return launch_skinny(kind, A, W, M, N, K, p, s);
+    if (dtype == CAD_DTYPE_BF16) {
+        if (skinny_supports(kind, M, K)) return launch_skinny(kind, A, W, M, N, K, p, s);
+        return launch_big(kind, A, W, M, N, K, slices, p, s);
+    }
     switch (kind) {
-        case EPI_QKV: return dispatch<EPI_QKV>(dtype, A, W, M, N, K, 1, p, s);
-        case EPI_SWIGLU: return dispatch<EPI_SWIGLU>(dtype, A, W, M, N, K, 1, p, s);
-        case EPI_ARGMAX: return dispatch<EPI_ARGMAX>(dtype, A, W, M, N, K, 1, p, s);
-        default: return dispatch<EPI_PARTIAL>(dtype, A, W, M, N, K, slices, p, s);
+        case EPI_QKV: return dispatch_f32<EPI_QKV>(A, W, M, N, K, 1, p, s);
+        case EPI_SWIGLU: return dispatch_f32<EPI_SWIGLU>(A, W, M, N, K, 1, p, s);
+        case EPI_ARGMAX: return dispatch_f32<EPI_ARGMAX>(A, W, M, N, K, 1, p, s);
+        default: return dispatch_f32<EPI_PARTIAL>(A, W, M, N, K, slices, p, s);
     }
 }

@@ -1,0 +1,390 @@
+// Projection GEMM for many token rows (M > 32): Y[M, N] = A[M, K] . W[N, K]^T on gfx950 MFMA.
+//
+// A workgroup of WN x WM waves computes a BN (features) x BM (tokens) tile; wave (wn, wm) owns a
+// (BN/WN) x (BM/WM) sub-tile held as FT x TT accumulators of v_mfma_f32_16x16x32_bf16 (A operand
+// = W rows, B operand = token rows; lane (r, g) holds features 4g..4g+3 of token r of each block).
+// K advances 64 at a time through two LDS buffers: while the waves multiply out of one buffer,
+// the next stage sits in registers on its way to the other and the stage after that is being
+// fetched from HBM, so there is one barrier per stage.  Eight waves share a tile, two per SIMD,
+// so one wave's LDS and MFMA latencies hide behind the other's work.  Every epilogue runs from
+// registers:
+//   QKV     the wave's features are whole heads, a rotation pair (i, i + d/2) sits in the same
+//           lane (blocks fb and fb + d/32), RoPE from the per-row (cos, sin) table; q to the
+//           workspace, k to its cache row, v to the dim-major cache;
+//   SWIGLU  the wave's first FT/2 blocks are gate rows and the last FT/2 the matching up rows;
+//   ARGMAX  per-token max over the wave's features (lane values, then the 4 lanes of a token),
+//           merged over the WN waves through LDS into one (max, index) slot per column tile;
+//   PARTIAL fp32 partial sums of one K slice, 16 bytes per lane store.
+// Workgroups are dealt to XCDs round-robin; the unit order gives each XCD a contiguous run, and
+// consecutive units are the row tiles (then K slices) of one column tile, so they share its W in L2.
+#include "cad_device.h"
+
+namespace {
+
+constexpr int BK64 = 64;
+
+template <int KIND, int BN, int BM, int WN, int WM, int BK>
+struct BigCfg {
+    static constexpr int LDK = BK + 8;                        // LDS row pitch: 16 bytes of padding
+    static constexpr int WTN = BN / WN, WTM = BM / WM;        // wave tile (features, tokens)
+    static constexpr int FT = WTN / 16, TT = WTM / 16;
+    static constexpr int NT = WN * WM * 64;                   // threads
+    static constexpr int WCH = BN * (BK / 8) / NT;            // 16-byte W chunks per thread per stage
+    static constexpr int ACH = BM * (BK / 8) / NT;            // 16-byte A chunks per thread per stage
+    static constexpr int STAGE = (BN + BM) * LDK;             // elements per LDS stage
+    static constexpr size_t SMEM = (size_t)2 * STAGE * sizeof(uint16_t);
+};
+
+// W row of tile row tr (0..BN-1) of column tile nt.  SwiGLU: within each wave's WTN rows the
+// first half are gate rows and the second half the matching up rows.
+template <int KIND, int BN, int WTN>
+__device__ __forceinline__ int big_w_row(int tr, int nt, int N, int ffn, bool& valid) {
+    if constexpr (KIND == EPI_SWIGLU) {
+        const int wn = tr / WTN, f = tr % WTN, half = WTN / 2;
+        const int F = nt * (BN / 2) + wn * half + (f % half);
+        valid = F < ffn;
+        return f < half ? F : ffn + F;
+    } else {
+        const int r = nt * BN + tr;
+        valid = r < N;
+        return r;
+    }
+}
+
+__device__ __forceinline__ int xcd_unit(int bid, int grid) { return (bid % 8) * (grid / 8) + bid / 8; }
+
+// QKV epilogue of one wave: blocks ft with (ft mod 2*HALF) < HALF hold first-half dims of a head,
+// their rotation partners sit in block ft + HALF of the same lane.
+template <int FT, int TT, int HALF>
+__device__ __forceinline__ void qkv_epilogue(const f32x4_t (&acc)[FT][TT], const EpiParams& p, int t0, int fbase,
+                                             int M, int N, int l16, int g4) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const int tok = t0 + tt * 16 + l16;
+        if (tok >= M) continue;
+        const int b = tok / p.Nq, it = tok % p.Nq;
+        if (!seq_ok(p.len_snap, b, p.Nq, p.cap)) continue;
+        const size_t slot = (size_t)p.len_snap[b] + it;
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+            if ((ft % (2 * HALF)) >= HALF) continue;         // handled with its first-half partner
+            const int n1 = fbase + ft * 16 + g4 * 4;         // feature of element 0 (first half)
+            if (n1 >= N) continue;
+            const int head = n1 / p.d + p.head_off, i0 = n1 % p.d;
+            const f32x4_t x1 = acc[ft][tt], x2 = acc[ft + HALF][tt];
+            if (head >= p.Hq + p.Hkv) {                      // V: dim-major cache, stored unrotated
+                uint16_t* vp = (uint16_t*)p.vc +
+                               (((size_t)b * p.Hkv + (head - p.Hq - p.Hkv)) * p.d + i0) * p.cap + slot;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vp[(size_t)i * p.cap] = f32_to_bf16(x1[i]);
+                    vp[(size_t)(i + p.d / 2) * p.cap] = f32_to_bf16(x2[i]);
+                }
+                continue;
+            }
+            const float2* cs = p.rope_cs + (size_t)tok * (p.d / 2) + i0;
+            f32x4_t y1, y2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float2 t = cs[i];
+                y1[i] = x1[i] * t.x - x2[i] * t.y;
+                y2[i] = x2[i] * t.x + x1[i] * t.y;
+            }
+            uint16_t* dst = head < p.Hq
+                                ? (uint16_t*)p.q_out + ((size_t)tok * p.Hq + head) * p.d
+                                : (uint16_t*)p.kc + (((size_t)b * p.Hkv + (head - p.Hq)) * p.cap + slot) * p.d;
+            st4(dst + i0, y1);
+            st4(dst + i0 + p.d / 2, y2);
+        }
+    }
+}
+
+template <int KIND, int BN, int BM, int WN, int WM, int BK, int RS>
+__global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                                     int M, int N, int K, int nmt, int nnt, int S, int ffn,
+                                                     EpiParams p) {
+    using C = BigCfg<KIND, BN, BM, WN, WM, BK>;
+    constexpr int LDK = C::LDK;
+    constexpr int FT = C::FT, TT = C::TT, WCH = C::WCH, ACH = C::ACH, NT = C::NT;
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // 2 stages of [BN + BM][LDK]
+
+    const int total = nmt * nnt * S;
+    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    if (unit >= total) return;
+    const int ks = unit % S, tile = unit / S;
+    const int mt = tile % nmt, nt = tile / nmt;
+    const int m0 = mt * BM;
+    const int kbeg = ks * p.k_slice, kend = min(K, kbeg + p.k_slice);
+    const int nk = (kend - kbeg + BK - 1) / BK;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % WN, wm = wave / WN;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    // per-thread global sources as 32-bit element offsets (row base + chunk offset); invalid rows
+    // read row 0 and are zeroed.  (Every operand here has fewer than 2^31 elements.)
+    uint32_t woff[WCH], aoff[ACH];
+    uint32_t wmask = 0, amask = 0;
+#pragma unroll
+    for (int c = 0; c < WCH; ++c) {
+        const int ch = tid + c * NT, tr = ch / (BK / 8);
+        bool v;
+        const int r = big_w_row<KIND, BN, C::WTN>(tr, nt, N, ffn, v);
+        wmask |= (uint32_t)v << c;
+        woff[c] = (uint32_t)(v ? r : 0) * (uint32_t)K + (ch % (BK / 8)) * 8;
+    }
+#pragma unroll
+    for (int c = 0; c < ACH; ++c) {
+        const int ch = tid + c * NT, r = ch / (BK / 8);
+        const bool v = m0 + r < M;
+        amask |= (uint32_t)v << c;
+        aoff[c] = (uint32_t)(v ? m0 + r : 0) * (uint32_t)K + (ch % (BK / 8)) * 8;
+    }
+    const int kchunk = (tid % (BK / 8)) * 8;                  // same k offset for every chunk of a thread
+    // A stage in registers: raw loads plus their validity bits.  Every load is unconditional from
+    // a valid address (no load sits in a branch, so the wait counts stay exact) and the masking
+    // happens when the stage is written to LDS, so the loads of a stage stay in flight until then.
+    struct Stage { uint4 w[WCH], a[ACH]; uint32_t wok, aok; };
+    auto load_g = [&](int k0, Stage& r) {
+        const bool kin = k0 + kchunk < kend;
+        r.wok = kin ? wmask : 0u;
+        r.aok = kin ? amask : 0u;
+#pragma unroll
+        for (int c = 0; c < WCH; ++c) r.w[c] = *(const uint4*)(W + woff[c] + (((r.wok >> c) & 1) ? k0 : 0));
+#pragma unroll
+        for (int c = 0; c < ACH; ++c) r.a[c] = *(const uint4*)(A + aoff[c] + (((r.aok >> c) & 1) ? k0 : 0));
+    };
+    auto masked = [](uint4 t, uint32_t ok) {
+        const uint32_t m = 0u - ok;
+        return make_uint4(t.x & m, t.y & m, t.z & m, t.w & m);
+    };
+    auto store_lds = [&](int buf, const Stage& r) {
+        uint16_t* Ws = smem + buf * C::STAGE;
+        uint16_t* As = Ws + BN * LDK;
+#pragma unroll
+        for (int c = 0; c < WCH; ++c) {
+            const int ch = tid + c * NT;
+            *(uint4*)(Ws + (ch / (BK / 8)) * LDK + (ch % (BK / 8)) * 8) = masked(r.w[c], (r.wok >> c) & 1);
+        }
+#pragma unroll
+        for (int c = 0; c < ACH; ++c) {
+            const int ch = tid + c * NT;
+            *(uint4*)(As + (ch / (BK / 8)) * LDK + (ch % (BK / 8)) * 8) = masked(r.a[c], (r.aok >> c) & 1);
+        }
+    };
+
+    f32x4_t acc[FT][TT];
+#pragma unroll
+    for (int i = 0; i < FT; ++i)
+#pragma unroll
+        for (int j = 0; j < TT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int buf) {
+        const uint16_t* Ws = smem + buf * C::STAGE;
+        const uint16_t* As = Ws + BN * LDK;
+        __builtin_amdgcn_iglp_opt(0);
+#pragma unroll
+        for (int kq = 0; kq < BK / 32; ++kq) {
+            bf16x8_t af[FT], bfr[TT];
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft)
+                af[ft] = *(const bf16x8_t*)(Ws + (wn * C::WTN + ft * 16 + l16) * LDK + kq * 32 + g4 * 8);
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                bfr[tt] = *(const bf16x8_t*)(As + (wm * C::WTM + tt * 16 + l16) * LDK + kq * 32 + g4 * 8);
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt)
+                    acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ft], bfr[tt], acc[ft][tt], 0, 0, 0);
+        }
+    };
+
+    if constexpr (RS == 1) {
+        // one register stage: the loads of stage kt+2 fly while stage kt is multiplied
+        Stage r;
+        if (nk > 0) {
+            load_g(kbeg, r);
+            store_lds(0, r);
+            if (nk > 1) load_g(kbeg + BK, r);
+        }
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            compute(kt & 1);
+            if (kt + 1 < nk) store_lds((kt + 1) & 1, r);
+            if (kt + 2 < nk) load_g(kbeg + (kt + 2) * BK, r);
+            __syncthreads();
+        }
+    } else {
+        // two register stages (small tiles, whose K loop is latency-bound): every load has two
+        // stages of multiplies to arrive
+        Stage r0, r1;
+        if (nk > 0) load_g(kbeg, r0);
+        if (nk > 1) load_g(kbeg + BK, r1);
+        if (nk > 0) store_lds(0, r0);
+        if (nk > 2) load_g(kbeg + 2 * BK, r0);
+        __syncthreads();
+        for (int kt = 0; kt < nk; kt += 2) {
+            compute(0);                                     // stage kt, buffer 0
+            if (kt + 1 < nk) store_lds(1, r1);              // stage kt+1
+            if (kt + 3 < nk) load_g(kbeg + (kt + 3) * BK, r1);
+            __syncthreads();
+            if (kt + 1 >= nk) break;
+            compute(1);                                     // stage kt+1, buffer 1
+            if (kt + 2 < nk) store_lds(0, r0);              // stage kt+2
+            if (kt + 4 < nk) load_g(kbeg + (kt + 4) * BK, r0);
+            __syncthreads();
+        }
+    }
+
+    // ---------------------------------------------------------------- epilogues from registers
+    const int fbase = nt * BN + wn * C::WTN;                 // first feature (plain layouts)
+    if constexpr (KIND == EPI_PARTIAL) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const int tok = m0 + wm * C::WTM + tt * 16 + l16;
+            if (tok >= M) continue;
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) {
+                const int n = fbase + ft * 16 + g4 * 4;
+                if (n < N) *(f32x4_t*)(p.part + ((size_t)ks * M + tok) * N + n) = acc[ft][tt];
+            }
+        }
+    } else if constexpr (KIND == EPI_SWIGLU) {
+        constexpr int H = FT / 2;
+        const int F0 = nt * (BN / 2) + wn * (C::WTN / 2);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const int tok = m0 + wm * C::WTM + tt * 16 + l16;
+            if (tok >= M || !seq_ok(p.len_snap, tok / p.Nq, p.Nq, p.cap)) continue;
+#pragma unroll
+            for (int ft = 0; ft < H; ++ft) {
+                const int F = F0 + ft * 16 + g4 * 4;
+                if (F >= ffn) continue;
+                f32x4_t a;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float g = acc[ft][tt][i];
+                    a[i] = g / (1.0f + __expf(-g)) * acc[ft + H][tt][i];
+                }
+                st4((uint16_t*)p.act + (size_t)tok * ffn + F, a);
+            }
+        }
+    } else if constexpr (KIND == EPI_QKV) {
+        // the pair offset d/32 (blocks) must be a compile-time index into acc
+        if (p.d == 128) qkv_epilogue<FT, TT, 4>(acc, p, m0 + wm * C::WTM, fbase, M, N, l16, g4);
+        else if (p.d == 64) qkv_epilogue<FT, TT, 2>(acc, p, m0 + wm * C::WTM, fbase, M, N, l16, g4);
+        else qkv_epilogue<FT, TT, 1>(acc, p, m0 + wm * C::WTM, fbase, M, N, l16, g4);
+    } else {                                                 // EPI_ARGMAX
+        __shared__ float2 red[WN][BM];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const int tok = m0 + wm * C::WTM + tt * 16 + l16;
+            float best = -INFINITY;
+            int bi = 0x7fffffff;
+            if (tok < M) {
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int n = fbase + ft * 16 + g4 * 4 + i;       // increasing along the lane
+                        if (n < N) {
+                            const float v = acc[ft][tt][i];
+                            if (v > best) { best = v; bi = n; }
+                            if (p.logits) p.logits[(size_t)tok * N + n] = v;
+                        }
+                    }
+            }
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) {
+                const float v2 = __shfl_xor(best, o, 64);
+                const int i2 = __shfl_xor(bi, o, 64);
+                argmax_merge(best, bi, v2, i2);
+            }
+            if (g4 == 0) red[wn][wm * C::WTM + tt * 16 + l16] = make_float2(best, __int_as_float(bi));
+        }
+        __syncthreads();
+        for (int r = tid; r < BM; r += NT) {
+            const int tok = m0 + r;
+            if (tok >= M || !seq_ok(p.len_snap, tok / p.Nq, p.Nq, p.cap)) continue;
+            float best = red[0][r].x;
+            int bi = __float_as_int(red[0][r].y);
+#pragma unroll
+            for (int w = 1; w < WN; ++w) argmax_merge(best, bi, red[w][r].x, __float_as_int(red[w][r].y));
+            p.amax_part[(size_t)tok * p.amax_slots + nt] = make_float2(best, __int_as_float(bi));
+        }
+    }
+}
+
+struct BigPlan { int BN, BM, nmt, nnt, S, k_slice, grid; };
+
+template <int KIND, int BN, int BM, int WN, int WM, int BK, int RS>
+hipError_t go_big(const void* A, const void* W, int M, int N, int K, int ffn, const BigPlan& t, const EpiParams& p,
+                  hipStream_t s) {
+    auto kern = k_gemm_big<KIND, BN, BM, WN, WM, BK, RS>;
+    constexpr size_t smem = BigCfg<KIND, BN, BM, WN, WM, BK>::SMEM;
+    static bool attr = false;
+    if (!attr) {
+        const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)smem);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(t.grid), dim3(WN * WM * 64), smem, s, (const uint16_t*)A, (const uint16_t*)W, M, N, K,
+                       t.nmt, t.nnt, t.S, ffn, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile choice: 256 features per workgroup tile (two waves of 128 across it); 64, 128 or 256
+// tokens.  The narrow QKV projection takes 128 x 64 tiles (one wave of 128 features, so a wave
+// holds whole heads of up to 128 dims) to spread over more workgroups.
+BigPlan big_plan(int kind, int M, int N, int K, int slices) {
+    BigPlan t;
+    t.BN = 256;
+    t.BM = M <= 64 ? 64 : M <= 128 ? 128 : 256;
+    if (kind == EPI_QKV) {              // narrow output: one head per wave, more workgroups
+        t.BN = 128;
+        t.BM = 64;
+    }
+    t.nmt = (M + t.BM - 1) / t.BM;
+    t.nnt = kind == EPI_SWIGLU ? (N / 2 + t.BN / 2 - 1) / (t.BN / 2) : (N + t.BN - 1) / t.BN;
+    t.S = kind == EPI_PARTIAL ? slices : 1;
+    t.k_slice = ((K + t.S - 1) / t.S + BK64 - 1) / BK64 * BK64;
+    const int total = t.nmt * t.nnt * t.S;
+    t.grid = (total + 7) / 8 * 8;
+    return t;
+}
+
+int big_slots(int kind, int M, int N, int K) { return big_plan(kind, M, N, K, 1).nnt; }
+
+int big_partial_slices(int M, int N, int K, int cus) {
+    const BigPlan t = big_plan(EPI_PARTIAL, M, N, K, 1);
+    const int tiles = t.nmt * t.nnt;
+    int S = (cus + tiles - 1) / tiles;                       // about one workgroup per CU
+    const int smax = K / 256 > 1 ? K / 256 : 1;              // at least 256 of K per slice
+    return S < 1 ? 1 : (S > smax ? smax : S);
+}
+
+template <int KIND>
+hipError_t big_dispatch(const void* A, const void* W, int M, int N, int K, int slices, EpiParams p, hipStream_t s) {
+    const BigPlan t = big_plan(KIND, M, N, K, slices);
+    p.k_slice = t.k_slice;
+    const int ffn = KIND == EPI_SWIGLU ? p.ffn : 0;
+    if (t.BN == 128) return go_big<KIND, 128, 64, 1, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
+    switch (t.BM) {
+        case 64: return go_big<KIND, 256, 64, 2, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
+        case 128: return go_big<KIND, 256, 128, 2, 4, 64, 1>(A, W, M, N, K, ffn, t, p, s);
+        default: return go_big<KIND, 256, 256, 2, 4, 64, 1>(A, W, M, N, K, ffn, t, p, s);
+    }
+}
+
+hipError_t launch_big(int kind, const void* A, const void* W, int M, int N, int K, int slices, const EpiParams& p,
+                      hipStream_t s) {
+    switch (kind) {
+        case EPI_QKV: return big_dispatch<EPI_QKV>(A, W, M, N, K, 1, p, s);
+        case EPI_SWIGLU: return big_dispatch<EPI_SWIGLU>(A, W, M, N, K, 1, p, s);
+        case EPI_ARGMAX: return big_dispatch<EPI_ARGMAX>(A, W, M, N, K, 1, p, s);
+        default: return big_dispatch<EPI_PARTIAL>(A, W, M, N, K, slices, p, s);
+    }
+}
