@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--ar-steps", type=int, default=64)
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="no timing: a few N = ROOF_N forwards and plain copies of a known size, for a "
+                         "hardware-counter run that calibrates and measures the LM head's HBM traffic")
     return ap.parse_args()
 
 
@@ -84,6 +87,9 @@ def main():
     layers = [lay0, lay1]
 
     doc, prefix, span_toks = copy_sweep_inputs(wl, spans)
+    if a.pmc_pass:
+        pmc_pass(a, shp, layers, prefix, span_toks, spans, L0, cap, dev)
+        return
 
     # one cache per N; their lengths are views of one tensor so a single fill restores them all
     lens = torch.zeros(len(spans), dtype=torch.int32, device=dev)
@@ -233,6 +239,35 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+COPY_BYTES = 1 << 29     # plain copy of the counter calibration: reads and writes 512 MiB
+
+
+def pmc_pass(a, shp, layers, prefix, span_toks, spans, L0, cap, dev):
+    """Work for a counter run (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE): four N = ROOF_N
+    commits from the L0-position cache, eager, alternating weight copies, then four device copies
+    of COPY_BYTES.  The copies read and write a known byte count, which scales the counters to bytes."""
+    import numpy as np
+    import torch
+
+    from spec_verify_cad_amd import cad
+    j = spans.index(ROOF_N) if ROOF_N in spans else 0
+    N = spans[j]
+    cache = cad.DeviceCache(shp, 1, cap)
+    ptoks = torch.from_numpy(prefix[None].astype(np.int32)).to(dev)
+    cad.span_forward(layers[0], cache, ptoks, L0, flags=cad.KV_ONLY | cad.COMMIT_ALL)
+    tok = torch.from_numpy(span_toks[j][None].astype(np.int32)).to(dev)
+    out = torch.empty((1, N), dtype=torch.int32, device=dev)
+    for i in range(4):
+        cache.len.fill_(L0)
+        cad.span_forward(layers[i & 1], cache, tok, N, flags=cad.COMMIT_ALL, argmax_out=out)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"pmc pass: 4 forwards of N={N}, 4 copies of {COPY_BYTES} bytes")
 
 
 def cpu_baseline(shp, w, prefix, span_toks, spans, cap, budget_s):

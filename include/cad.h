@@ -70,7 +70,7 @@ extern "C" {
  *   w_gate_up [2 * ffn, hidden]                                rows: gate, then up
  *   w_down    [hidden, ffn]
  *   w_lm      [vocab, hidden]
- * Supported: hidden, head_dim*n_q_heads and ffn multiples of 8; head_dim in {32, 64, 128};
+ * Supported: hidden, head_dim*n_q_heads and ffn multiples of 8, hidden <= 8192; head_dim in {32, 64, 128};
  * n_q_heads a multiple of n_kv_heads.
  */
 typedef struct {

@@ -35,6 +35,16 @@ __device__ __forceinline__ bool key_allowed(int key, int len, int it, int mode, 
     return s <= it;
 }
 
+// Keys per split for a sequence of len cached rows and Nq new rows: the live keys spread
+// evenly over the nsplit splits, in multiples of 32 and at least 64, so splits past the live
+// range get no keys.  Computed on the device from the cache length the forward captured.
+__device__ __forceinline__ int split_chunk(int len, int Nq, int nsplit) {
+    const int S = len + Nq;
+    int c = (S + nsplit - 1) / nsplit;
+    c = (c + 31) & ~31;
+    return c < 64 ? 64 : c;
+}
+
 // four bf16 of one V row (keys key0..key0+3, key0 a multiple of 4); keys at or past kend read
 // as zero.  Branch-free: a group wholly past kend reads slot 0 instead (cap is a multiple of 4,
 // so a load never crosses the end of a row), so all loads of a step issue back to back.
@@ -50,7 +60,7 @@ template <int DH>
 __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                                    const uint16_t* __restrict__ vc, const int32_t* __restrict__ len_snap,
                                                    int Nq, int Hq, int Hkv, int cap, int mode, int Dblk,
-                                                   int chunk, int nsplit, float* __restrict__ part_o,
+                                                   int nsplit, float* __restrict__ part_o,
                                                    float* __restrict__ part_ml, uint16_t* __restrict__ o_out) {
     constexpr int DS = DH / 32;                 // MFMA k-steps over head_dim
     constexpr int DB = DH / 16;                 // 16-wide head_dim blocks of the output
@@ -69,6 +79,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     const int it = qlive ? rho / G : 0, hh = qlive ? rho % G : 0;
     // keys past len + (last token of the wave) are masked for every row of the wave
     const int it_max = min(Nq - 1, min(wrow0 + 15, Rg - 1) / G);
+    const int chunk = split_chunk(len, Nq, nsplit);
     const int kbeg = split * chunk;
     int kend = min(kbeg + chunk, len + it_max + 1);
     if (!ok) kend = kbeg;
@@ -93,28 +104,32 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     const uint16_t* kbase = kc + head * cap * DH;
     const uint16_t* vbase = vc + head * DH * cap;          // dim-major: row = one dim over all slots
 
-    for (int k0 = kbeg; k0 < kend; k0 += 32) {
+    // Operands of one 32-key step.  Keys at or past kend load from slot 0 (always a valid
+    // address) and are masked afterwards, so a step can be fetched before it is known to be
+    // needed: the loop keeps the next step's loads in flight while it computes the current one.
+    struct StepOps { bf16x8_t kf[2][DS]; bf16x8_t vf[DB]; };
+    auto load = [&](int k0, StepOps& op) {
         // K fragments: lane (key l16, g4) of key block kb
-        bf16x8_t kf[2][DS];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int key = k0 + kb * 16 + l16;
-            const uint16_t* kp = kbase + (size_t)(key < kend ? key : kbeg) * DH + g4 * 8;
+            const uint16_t* kp = kbase + (size_t)(key < kend ? key : 0) * DH + g4 * 8;
 #pragma unroll
             for (int ks = 0; ks < DS; ++ks) {
                 uint4 v = *(const uint4*)(kp + ks * 32);
-                kf[kb][ks] = *(bf16x8_t*)&v;
+                op.kf[kb][ks] = *(bf16x8_t*)&v;
             }
         }
         // V^T fragments: lane (dim db*16 + l16, g4) takes keys 4g4..+3 and 16+4g4..+3
-        bf16x8_t vf[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const uint16_t* vrow = vbase + (size_t)(db * 16 + l16) * cap;
             const uint2 lo = v4(vrow, k0 + 4 * g4, kend), hi = v4(vrow, k0 + 16 + 4 * g4, kend);
             uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            vf[db] = *(bf16x8_t*)&vv;
+            op.vf[db] = *(bf16x8_t*)&vv;
         }
+    };
+    auto compute = [&](int k0, const StepOps& op) {
         // S^T[key][query]: lane holds keys kb*16 + 4*g4 + i of query l16
         f32x4_t st[2];
 #pragma unroll
@@ -122,7 +137,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
             st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DS; ++ks)
-                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][ks], qf[ks], st[kb], 0, 0, 0);
+                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kf[kb][ks], qf[ks], st[kb], 0, 0, 0);
         }
         float tmax = -INFINITY;
 #pragma unroll
@@ -160,9 +175,19 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             oacc[db] *= alpha;
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], ph, oacc[db], 0, 0, 0);
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pl, oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.vf[db], ph, oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.vf[db], pl, oacc[db], 0, 0, 0);
         }
+    };
+
+    StepOps opa, opb;
+    load(kbeg, opa);
+    for (int k0 = kbeg; k0 < kend; k0 += 64) {
+        load(k0 + 32, opb);
+        compute(k0, opa);
+        if (k0 + 32 >= kend) break;
+        load(k0 + 64, opa);
+        compute(k0 + 32, opb);
     }
 
     if (!qlive) return;
@@ -184,38 +209,90 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     }
 }
 
-// Combine the split partials of one (row, q head): o = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s,
-// summed in split order.  The (m, l) of all splits are fetched in parallel, one per lane.
-template <typename T>
-__global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+// Combine the split partials of one (row, q head): o = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s.
+// Only splits that held keys for the sequence are read.  The 256 threads form NG groups of DH/4
+// threads (four dims each); group j sums splits j, j + NG, ... in order, and the groups are added
+// in order, so the result does not depend on scheduling.  The O loads of the first SB splits of
+// every group are issued before the weights are known.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                    const int32_t* __restrict__ len_snap, int Nq, int Hq, int Hkv,
-                                                   int DH, int cap, int nsplit, T* __restrict__ o) {
+                                                   int cap, int nsplit, T* __restrict__ o) {
+    constexpr int TPG = DH / 4, NG = 256 / TPG, SB = 8;
     __shared__ float wgt[256];
+    __shared__ float red[2][4];
+    __shared__ float4 gacc[NG][TPG];
     const int rowhead = blockIdx.x;                  // (b*Nq + it)*Hq + h
     const int h = rowhead % Hq, row = rowhead / Hq;
     const int b = row / Nq, it = row % Nq;
     if (!seq_ok(len_snap, b, Nq, cap)) return;
+    const int len = len_snap[b];
+    const int chunk = split_chunk(len, Nq, nsplit);
+    const int live = min(nsplit, (len + Nq + chunk - 1) / chunk);
     const int G = Hq / Hkv, g = h / G, hh = h % G;
     const int Rg = Nq * G, rho = it * G + hh;
     const size_t p0 = (((size_t)b * Hkv + g) * Rg + rho) * nsplit;
+    const int tid = threadIdx.x, grp = tid / TPG, q = tid % TPG;
+    const int lane = tid & 63, wave = tid >> 6;
+
+    float4 ov[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+        const int sp = min(grp + NG * j, live - 1);
+        ov[j] = *(const float4*)(part_o + (p0 + sp) * DH + 4 * q);
+    }
     float m = -INFINITY;
-    for (int s = threadIdx.x; s < nsplit; s += 64) m = fmaxf(m, part_ml[(p0 + s) * 2]);
+    for (int sp = tid; sp < live; sp += 256) m = fmaxf(m, part_ml[(p0 + sp) * 2]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    for (int s = threadIdx.x; s < nsplit; s += 64) {
-        const float ms = part_ml[(p0 + s) * 2];
-        wgt[s] = ms == -INFINITY ? 0.f : exp2f(ms - m);
-    }
+    if (lane == 0) red[0][wave] = m;
     __syncthreads();
-    float L = 0.f;                                   // every lane sums the same terms in split order
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) L += wgt[s] * part_ml[(p0 + s) * 2 + 1];
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int dd = threadIdx.x; dd < DH; dd += 64) {
-        float acc = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < nsplit; ++s) acc += wgt[s] * part_o[(p0 + s) * DH + dd];
-        Elt<T>::st(o, (size_t)rowhead * DH + dd, acc * inv);
+    m = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    float lsum = 0.f;
+    for (int sp = tid; sp < live; sp += 256) {
+        const float2 ml = *(const float2*)(part_ml + (p0 + sp) * 2);
+        const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - m);
+        wgt[sp] = w;
+        lsum += w * ml.y;
+    }
+    lsum = wave_sum(lsum);
+    if (lane == 0) red[1][wave] = lsum;
+    __syncthreads();
+    const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0;; j0 += SB) {
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int sp = grp + NG * (j0 + j);
+            const float w = sp < live ? wgt[sp] : 0.f;
+            acc.x += w * ov[j].x;
+            acc.y += w * ov[j].y;
+            acc.z += w * ov[j].z;
+            acc.w += w * ov[j].w;
+        }
+        if (grp + NG * (j0 + SB) >= live) break;
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int sp = min(grp + NG * (j0 + SB + j), live - 1);
+            ov[j] = *(const float4*)(part_o + (p0 + sp) * DH + 4 * q);
+        }
+    }
+    gacc[grp][q] = acc;
+    __syncthreads();
+    if (tid < TPG) {
+        float4 t = gacc[0][tid];
+#pragma unroll
+        for (int j = 1; j < NG; ++j) {
+            const float4 u = gacc[j][tid];
+            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const size_t ob = (size_t)rowhead * DH + 4 * tid;
+        Elt<T>::st(o, ob + 0, t.x * inv);
+        Elt<T>::st(o, ob + 1, t.y * inv);
+        Elt<T>::st(o, ob + 2, t.z * inv);
+        Elt<T>::st(o, ob + 3, t.w * inv);
     }
 }
 
@@ -274,8 +351,9 @@ bool mfma_path(const FwdDims& fd) { return !(fd.dtype == CAD_DTYPE_F32 || (fd.d 
 
 }  // namespace
 
-// Split plan of the MFMA path: 64-row tiles of each GQA group, key chunks (multiples of 32,
-// at least 64) so that about two workgroups per CU are launched.
+// Split plan of the MFMA path: 64-row tiles of each GQA group and enough key splits for about
+// two workgroups per CU (each split at least 64 keys of a full cache); the keys of a split
+// follow from the sequence's length on the device.
 void attention_plan(FwdDims* fd, int cus) {
     const int G = fd->Hq / fd->Hkv, Rg = fd->Nq * G;
     fd->attn_rows_per_wg = WAVES * 16;
@@ -283,16 +361,12 @@ void attention_plan(FwdDims* fd, int cus) {
     const long units = (long)fd->B * fd->Hkv * fd->attn_row_tiles;
     const long want = 2L * cus;
     long splits = (want + units - 1) / units;
-    long chunk = (fd->cap + splits - 1) / splits;
-    chunk = (chunk + 31) / 32 * 32;
-    if (chunk < 64) chunk = 64;
-    fd->attn_chunk = (int)chunk;
-    fd->attn_splits = (int)((fd->cap + chunk - 1) / chunk);
-    if (fd->attn_splits > 256) {                    // the merge holds at most 256 split weights
-        fd->attn_chunk = (fd->cap + 255) / 256;
-        fd->attn_chunk = (fd->attn_chunk + 31) / 32 * 32;
-        fd->attn_splits = (fd->cap + fd->attn_chunk - 1) / fd->attn_chunk;
-    }
+    const long most = (fd->cap + fd->Nq + 63) / 64;       // splits of at least 64 keys
+    if (splits > most) splits = most;
+    if (splits > 256) splits = 256;                      // the merge holds at most 256 split weights
+    if (splits < 1) splits = 1;
+    fd->attn_splits = (int)splits;
+    fd->attn_chunk = 0;                                  // per sequence, from its length, on the device
 }
 
 hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc, const void* vc, hipStream_t s) {
@@ -312,18 +386,22 @@ hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc
     if (fd.d == 128)
         hipLaunchKernelGGL((k_attn_bf16<128>), grid, dim3(WAVES * 64), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc,
                            (const uint16_t*)vc, wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.mode, fd.Dblk,
-                           fd.attn_chunk, fd.attn_splits, wb.part_o, wb.part_ml, (uint16_t*)wb.o);
+                           fd.attn_splits, wb.part_o, wb.part_ml, (uint16_t*)wb.o);
     else
         hipLaunchKernelGGL((k_attn_bf16<64>), grid, dim3(WAVES * 64), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc,
                            (const uint16_t*)vc, wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.mode, fd.Dblk,
-                           fd.attn_chunk, fd.attn_splits, wb.part_o, wb.part_ml, (uint16_t*)wb.o);
+                           fd.attn_splits, wb.part_o, wb.part_ml, (uint16_t*)wb.o);
     return hipGetLastError();
 }
 
 bool attention_uses_merge(const FwdDims& fd) { return mfma_path(fd) && fd.attn_splits > 1; }
 
 hipError_t launch_attention_merge(const FwdDims& fd, const FwdBufs& wb, hipStream_t s) {
-    hipLaunchKernelGGL((k_attn_merge<uint16_t>), dim3(fd.M * fd.Hq), dim3(64), 0, s, wb.part_o, wb.part_ml,
-                       wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.d, fd.cap, fd.attn_splits, (uint16_t*)wb.o);
+    if (fd.d == 128)
+        hipLaunchKernelGGL((k_attn_merge<uint16_t, 128>), dim3(fd.M * fd.Hq), dim3(256), 0, s, wb.part_o, wb.part_ml,
+                           wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.attn_splits, (uint16_t*)wb.o);
+    else
+        hipLaunchKernelGGL((k_attn_merge<uint16_t, 64>), dim3(fd.M * fd.Hq), dim3(256), 0, s, wb.part_o, wb.part_ml,
+                           wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.attn_splits, (uint16_t*)wb.o);
     return hipGetLastError();
 }

@@ -62,6 +62,7 @@ bool layer_supported(const cad_layer_desc* L) {
     if (L->n_q_heads % L->n_kv_heads) return false;
     if (L->head_dim != 32 && L->head_dim != 64 && L->head_dim != 128) return false;
     if (L->hidden % 8 || L->ffn % 8 || (L->n_q_heads * L->head_dim) % 8) return false;
+    if (L->hidden > 8192) return false;           // row kernels keep a hidden row in registers
     return true;
 }
 

@@ -25,7 +25,11 @@ constexpr int BK64 = 64;
 
 template <int KIND, int BN, int BM, int WN, int WM, int BK>
 struct BigCfg {
-    static constexpr int LDK = BK + 8;                        // LDS row pitch: 16 bytes of padding
+#ifndef BIG_SWZ
+#define BIG_SWZ 1
+#endif
+    static constexpr int SWZ = BIG_SWZ;
+    static constexpr int LDK = SWZ ? BK : BK + 8;             // LDS row pitch: 16 bytes of padding
     static constexpr int WTN = BN / WN, WTM = BM / WM;        // wave tile (features, tokens)
     static constexpr int FT = WTN / 16, TT = WTM / 16;
     static constexpr int NT = WN * WM * 64;                   // threads
@@ -148,10 +152,26 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
         const bool kin = k0 + kchunk < kend;
         r.wok = kin ? wmask : 0u;
         r.aok = kin ? amask : 0u;
+        // With several register stages every load stays in program order (a scheduling barrier
+        // after each): the compiler's wait counts at the loop head merge the loads' issue order
+        // from the prologue and from the previous step, and stay exact only if the orders agree.
 #pragma unroll
-        for (int c = 0; c < WCH; ++c) r.w[c] = *(const uint4*)(W + woff[c] + (((r.wok >> c) & 1) ? k0 : 0));
+        for (int c = 0; c < WCH; ++c) {
+            r.w[c] = *(const uint4*)(W + woff[c] + (((r.wok >> c) & 1) ? k0 : 0));
+            if constexpr (RS > 1) __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-        for (int c = 0; c < ACH; ++c) r.a[c] = *(const uint4*)(A + aoff[c] + (((r.aok >> c) & 1) ? k0 : 0));
+        for (int c = 0; c < ACH; ++c) {
+            r.a[c] = *(const uint4*)(A + aoff[c] + (((r.aok >> c) & 1) ? k0 : 0));
+            if constexpr (RS > 1) __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // 16-byte chunk position of chunk c of tile row r (rows are 16-aligned in every read, so
+    // r mod 16 is all the swizzle needs)
+    auto sw = [](int r, int c) {
+        if constexpr (C::SWZ == 1) return c ^ (r & 7);
+        else if constexpr (C::SWZ == 2) return c ^ ((r >> 1) & 7);
+        else return c;
     };
     auto masked = [](uint4 t, uint32_t ok) {
         const uint32_t m = 0u - ok;
@@ -163,12 +183,12 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
 #pragma unroll
         for (int c = 0; c < WCH; ++c) {
             const int ch = tid + c * NT;
-            *(uint4*)(Ws + (ch / (BK / 8)) * LDK + (ch % (BK / 8)) * 8) = masked(r.w[c], (r.wok >> c) & 1);
+            *(uint4*)(Ws + (ch / (BK / 8)) * LDK + sw(ch / (BK / 8), ch % (BK / 8)) * 8) = masked(r.w[c], (r.wok >> c) & 1);
         }
 #pragma unroll
         for (int c = 0; c < ACH; ++c) {
             const int ch = tid + c * NT;
-            *(uint4*)(As + (ch / (BK / 8)) * LDK + (ch % (BK / 8)) * 8) = masked(r.a[c], (r.aok >> c) & 1);
+            *(uint4*)(As + (ch / (BK / 8)) * LDK + sw(ch / (BK / 8), ch % (BK / 8)) * 8) = masked(r.a[c], (r.aok >> c) & 1);
         }
     };
 
@@ -187,10 +207,10 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
             bf16x8_t af[FT], bfr[TT];
 #pragma unroll
             for (int ft = 0; ft < FT; ++ft)
-                af[ft] = *(const bf16x8_t*)(Ws + (wn * C::WTN + ft * 16 + l16) * LDK + kq * 32 + g4 * 8);
+                af[ft] = *(const bf16x8_t*)(Ws + (wn * C::WTN + ft * 16 + l16) * LDK + sw(l16, kq * 4 + g4) * 8);
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
-                bfr[tt] = *(const bf16x8_t*)(As + (wm * C::WTM + tt * 16 + l16) * LDK + kq * 32 + g4 * 8);
+                bfr[tt] = *(const bf16x8_t*)(As + (wm * C::WTM + tt * 16 + l16) * LDK + sw(l16, kq * 4 + g4) * 8);
 #pragma unroll
             for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
@@ -199,40 +219,27 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
         }
     };
 
-    if constexpr (RS == 1) {
-        // one register stage: the loads of stage kt+2 fly while stage kt is multiplied
-        Stage r;
-        if (nk > 0) {
-            load_g(kbeg, r);
-            store_lds(0, r);
-            if (nk > 1) load_g(kbeg + BK, r);
-        }
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            compute(kt & 1);
-            if (kt + 1 < nk) store_lds((kt + 1) & 1, r);
-            if (kt + 2 < nk) load_g(kbeg + (kt + 2) * BK, r);
+    // RS register stages in a ring: stage kt is loaded into slot kt % RS, RS stages ahead, and
+    // at step kt written to LDS buffer kt & 1, then (after the barrier) multiplied.  Buffer kt & 1
+    // was last read at step kt - 2, and every wave has passed step kt - 1's barrier since, so one
+    // barrier per step suffices.  The loop is unrolled over a multiple of RS and of 2 so every
+    // slot and buffer index is a constant and the oldest loads always sit in the slot written
+    // next; loads are issued unconditionally (a stage past the slice reads valid addresses and
+    // is masked to zero), because a load inside a branch makes the compiler's wait counts at the
+    // join conservative and drains the pipeline before every LDS write.
+    Stage r[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i) load_g(kbeg + i * BK, r[i]);
+    constexpr int UNR = RS % 2 ? 2 * RS : RS;
+    for (int kt0 = 0; kt0 < nk; kt0 += UNR) {
+#pragma unroll
+        for (int j = 0; j < UNR; ++j) {
+            const int kt = kt0 + j;
+            if (kt >= nk) break;
+            store_lds(j & 1, r[j % RS]);
+            load_g(kbeg + (kt + RS) * BK, r[j % RS]);
             __syncthreads();
-        }
-    } else {
-        // two register stages (small tiles, whose K loop is latency-bound): every load has two
-        // stages of multiplies to arrive
-        Stage r0, r1;
-        if (nk > 0) load_g(kbeg, r0);
-        if (nk > 1) load_g(kbeg + BK, r1);
-        if (nk > 0) store_lds(0, r0);
-        if (nk > 2) load_g(kbeg + 2 * BK, r0);
-        __syncthreads();
-        for (int kt = 0; kt < nk; kt += 2) {
-            compute(0);                                     // stage kt, buffer 0
-            if (kt + 1 < nk) store_lds(1, r1);              // stage kt+1
-            if (kt + 3 < nk) load_g(kbeg + (kt + 3) * BK, r1);
-            __syncthreads();
-            if (kt + 1 >= nk) break;
-            compute(1);                                     // stage kt+1, buffer 1
-            if (kt + 2 < nk) store_lds(0, r0);              // stage kt+2
-            if (kt + 4 < nk) load_g(kbeg + (kt + 4) * BK, r0);
-            __syncthreads();
+            compute(j & 1);
         }
     }
 

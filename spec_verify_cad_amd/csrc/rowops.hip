@@ -29,6 +29,17 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return t;
 }
 
+// Four consecutive values to four consecutive stored elements.
+__device__ __forceinline__ void st4v(uint16_t* p, float4 v) { st4(p, f32x4_t{v.x, v.y, v.z, v.w}); }
+__device__ __forceinline__ void st4v(float* p, float4 v) { *(float4*)p = v; }
+// Four consecutive stored elements (8 bytes of bf16 / 16 of fp32) as fp32.
+__device__ __forceinline__ float4 ld4(const uint16_t* p) {
+    const uint2 w = *(const uint2*)p;
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+}
+__device__ __forceinline__ float4 ld4(const float* p) { return *(const float4*)p; }
+
 template <typename T>
 __global__ __launch_bounds__(NT) void k_embed_norm(const int32_t* __restrict__ tokens, const T* __restrict__ embed,
                                                    int h, int vocab, int Nq, int cap, float eps, int mode, int Dblk,
@@ -60,45 +71,86 @@ __global__ __launch_bounds__(NT) void k_embed_norm(const int32_t* __restrict__ t
     int t = tokens[r];
     t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
     const T* e = embed + (size_t)t * h;
+    // the row is read once, four elements per thread per pass, and kept in registers
+    constexpr int QMAX = 8;                        // h <= 4 * NT * QMAX
+    float4 v[QMAX];
     float ss = 0.f;
-    for (int j = threadIdx.x; j < h; j += NT) {
-        const float v = Elt<T>::ld(e, j);
-        ss += v * v;
+#pragma unroll
+    for (int qq = 0; qq < QMAX; ++qq) {
+        const int j = 4 * (threadIdx.x + qq * NT);
+        if (j < h) {
+            v[qq] = ld4(e + j);
+            ss += (v[qq].x * v[qq].x + v[qq].y * v[qq].y) + (v[qq].z * v[qq].z + v[qq].w * v[qq].w);
+        }
     }
     ss = block_sum(ss, red);
     const float scale = 1.0f / sqrtf(ss / (float)h + eps);
-    for (int j = threadIdx.x; j < h; j += NT) {
-        const float v = Elt<T>::ld(e, j);
-        if (x) x[(size_t)r * h + j] = v;
-        Elt<T>::st(u, (size_t)r * h + j, v * scale);
+#pragma unroll
+    for (int qq = 0; qq < QMAX; ++qq) {
+        const int j = 4 * (threadIdx.x + qq * NT);
+        if (j < h) {
+            if (x) *(float4*)(x + (size_t)r * h + j) = v[qq];
+            st4v(u + (size_t)r * h + j, make_float4(v[qq].x * scale, v[qq].y * scale, v[qq].z * scale, v[qq].w * scale));
+        }
     }
 }
 
+
+constexpr int RN_NT = 512;
+
 // out = base + sum_s part[s] (fp32); out_t = rnd(out) if given; normed = rnd(RMSNorm(out)).
-template <typename T>
-__global__ __launch_bounds__(NT) void k_resid_norm(const float* __restrict__ base, const float* __restrict__ part,
-                                                   int slices, int M, int h, int Nq, int cap, float eps,
-                                                   const int32_t* __restrict__ len_snap, float* __restrict__ out,
-                                                   T* __restrict__ out_t, T* __restrict__ normed) {
-    __shared__ float red[4];
-    extern __shared__ float rowbuf[];            // [h]
+// One workgroup per row, four columns per thread.  The partial sums of a column are loaded SB
+// slices at a time, all of a batch in flight together (clamped addresses, unused ones added as
+// zero), and added in slice order, so the result does not depend on scheduling.
+template <typename T, int SB>
+__global__ __launch_bounds__(RN_NT) void k_resid_norm(const float* __restrict__ base, const float* __restrict__ part,
+                                                      int slices, int M, int h, int Nq, int cap, float eps,
+                                                      const int32_t* __restrict__ len_snap, float* __restrict__ out,
+                                                      T* __restrict__ out_t, T* __restrict__ normed) {
+    __shared__ float red[RN_NT / 64];
+    extern __shared__ float4 rowbuf4[];          // [h / 4]
     const int r = blockIdx.x;
     if (!seq_ok(len_snap, r / Nq, Nq, cap)) return;
+    const int h4 = h >> 2;
+    const size_t sstride = (size_t)M * h;
     float ss = 0.f;
-#pragma unroll 2
-    for (int j = threadIdx.x; j < h; j += NT) {
-        float v = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < slices; ++s) v += part[((size_t)s * M + r) * h + j];   // slice order
-        v = base[(size_t)r * h + j] + v;
-        rowbuf[j] = v;
-        out[(size_t)r * h + j] = v;
-        if (out_t) Elt<T>::st(out_t, (size_t)r * h + j, v);
-        ss += v * v;
+    for (int j4 = threadIdx.x; j4 < h4; j4 += RN_NT) {
+        const size_t off = (size_t)r * h + 4 * (size_t)j4;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s0 = 0; s0 < slices; s0 += SB) {
+            float4 v[SB];
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const int sl = min(s0 + i, slices - 1);
+                v[i] = *(const float4*)(part + sl * sstride + off);
+            }
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const bool use = s0 + i < slices;
+                acc.x += use ? v[i].x : 0.f;
+                acc.y += use ? v[i].y : 0.f;
+                acc.z += use ? v[i].z : 0.f;
+                acc.w += use ? v[i].w : 0.f;
+            }
+        }
+        const float4 b = *(const float4*)(base + off);
+        const float4 o = make_float4(b.x + acc.x, b.y + acc.y, b.z + acc.z, b.w + acc.w);
+        rowbuf4[j4] = o;
+        *(float4*)(out + off) = o;
+        if (out_t) st4v(out_t + off, o);
+        ss += (o.x * o.x + o.y * o.y) + (o.z * o.z + o.w * o.w);
     }
-    ss = block_sum(ss, red);
-    const float scale = 1.0f / sqrtf(ss / (float)h + eps);
-    for (int j = threadIdx.x; j < h; j += NT) Elt<T>::st(normed, (size_t)r * h + j, rowbuf[j] * scale);
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < RN_NT / 64; ++w) t += red[w];
+    const float scale = 1.0f / sqrtf(t / (float)h + eps);
+    for (int j4 = threadIdx.x; j4 < h4; j4 += RN_NT) {
+        const float4 o = rowbuf4[j4];
+        st4v(normed + (size_t)r * h + 4 * (size_t)j4, make_float4(o.x * scale, o.y * scale, o.z * scale, o.w * scale));
+    }
 }
 
 // One wave per row.  Row r of sequence b = r / Nq; the wave of the sequence's first row commits.
@@ -147,15 +199,26 @@ hipError_t launch_embed_norm(const FwdDims& fd, const int32_t* tokens, const voi
     return hipGetLastError();
 }
 
+template <typename T, int SB>
+static void resid_norm_go(const FwdDims& fd, const float* base, const float* part, int slices, float* out_f32,
+                          void* out_t, void* normed, float eps, const int32_t* len_snap, hipStream_t s) {
+    const size_t smem = (size_t)fd.h * sizeof(float);
+    hipLaunchKernelGGL((k_resid_norm<T, SB>), dim3(fd.M), dim3(RN_NT), smem, s, base, part, slices, fd.M, fd.h,
+                       fd.Nq, fd.cap, eps, len_snap, out_f32, (T*)out_t, (T*)normed);
+}
+
+template <typename T>
+static void resid_norm_t(const FwdDims& fd, const float* base, const float* part, int slices, float* out_f32,
+                         void* out_t, void* normed, float eps, const int32_t* len_snap, hipStream_t s) {
+    if (slices <= 4) resid_norm_go<T, 4>(fd, base, part, slices, out_f32, out_t, normed, eps, len_snap, s);
+    else if (slices <= 8) resid_norm_go<T, 8>(fd, base, part, slices, out_f32, out_t, normed, eps, len_snap, s);
+    else resid_norm_go<T, 16>(fd, base, part, slices, out_f32, out_t, normed, eps, len_snap, s);
+}
+
 hipError_t launch_resid_norm(const FwdDims& fd, const float* base, const float* part, int slices, float* out_f32,
                              void* out_t, void* normed, float eps, const int32_t* len_snap, hipStream_t s) {
-    const size_t smem = (size_t)fd.h * sizeof(float);
-    if (fd.dtype == CAD_DTYPE_F32)
-        hipLaunchKernelGGL(k_resid_norm<float>, dim3(fd.M), dim3(NT), smem, s, base, part, slices, fd.M, fd.h, fd.Nq,
-                           fd.cap, eps, len_snap, out_f32, (float*)out_t, (float*)normed);
-    else
-        hipLaunchKernelGGL(k_resid_norm<uint16_t>, dim3(fd.M), dim3(NT), smem, s, base, part, slices, fd.M, fd.h,
-                           fd.Nq, fd.cap, eps, len_snap, out_f32, (uint16_t*)out_t, (uint16_t*)normed);
+    if (fd.dtype == CAD_DTYPE_F32) resid_norm_t<float>(fd, base, part, slices, out_f32, out_t, normed, eps, len_snap, s);
+    else resid_norm_t<uint16_t>(fd, base, part, slices, out_f32, out_t, normed, eps, len_snap, s);
     return hipGetLastError();
 }
 
