@@ -211,10 +211,11 @@ def main():
     rn = next(r for r in per_n if r["N"] == ROOF_N) if ROOF_N in spans else per_n[0]
     lm_bytes = R.lm_head_bytes(shp, rn["N"])
     achieved = lm_bytes / (rn["lm_head_us"] * 1e-6) / 1e9
-    roof = {"kernel": "lm_head_argmax (k_gemm_bf16, EPI_ARGMAX)", "N": rn["N"], "bound": "hbm",
+    roof = {"kernel": "lm_head_argmax (k_skinny, EPI_ARGMAX)", "N": rn["N"], "bound": "hbm",
             "achieved": round(achieved, 1), "peak": R.HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / R.HBM_PEAK_GBS, 4), "traffic": None,
-            "alg_bytes_per_launch": int(lm_bytes), "avg_launch_us": rn["lm_head_us"]}
+            "frac": round(achieved / R.HBM_PEAK_GBS, 4), "traffic": lm_traffic() if rn["N"] == 32 else None,
+            "alg_bytes_per_launch": int(lm_bytes), "avg_launch_us": rn["lm_head_us"],
+            "timing": "HIP events around the kernel on its launch stream, eager forwards after the timed graph replays"}
     big = next((r for r in per_n if r["N"] == 512), None)
     if big:
         roof["mfma_at_N512"] = {"achieved_tflops": round(R.lm_head_flops(shp, 512) / (big["lm_head_us"] * 1e-6) / 1e12, 1),
@@ -242,6 +243,21 @@ def main():
 
 
 COPY_BYTES = 1 << 29     # plain copy of the counter calibration: reads and writes 512 MiB
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_argmax_n32_traffic.md")
+
+
+def lm_traffic():
+    """HBM bytes per launch of the N = 32 LM-head kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE of two `--pmc-pass` runs, each scaled by a 512 MiB copy), or None
+    when the kernel's sources have changed since the counters were taken."""
+    import hashlib
+    try:
+        line = next(l for l in open(TRAFFIC_FILE) if l.startswith("traffic_record:"))
+        rec = json.loads(line.split(":", 1)[1])
+        h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])).hexdigest()
+    except (OSError, StopIteration, ValueError, KeyError):
+        return None
+    return int(rec["traffic_bytes_per_launch"]) if h == rec["source_sha256"] else None
 
 
 def pmc_pass(a, shp, layers, prefix, span_toks, spans, L0, cap, dev):
