@@ -2,21 +2,20 @@
 // rows their mask allows (causal span, or SwitchSD's block-triangular candidate mask), with
 // grouped-query heads sharing one K/V stream.
 //
-// bf16 path (gfx950 MFMA, head_dim 64 or 128): split-L flash decoding with no LDS.  A
-// workgroup owns one (sequence, KV head, key chunk, 64-row tile); the rows of a tile are the
-// (token, q head) pairs of the GQA group, so every K/V byte of a chunk is fetched from HBM once
-// per group (the four waves of a workgroup share it through L1).  Each wave takes 16 rows and
-// walks its keys 32 at a time, loading MFMA operands straight from the cache:
-//   S^T = K . Q^T   A = 16 keys x 32 dims of the K cache (16 contiguous bytes per lane),
-//                   B = the wave's query fragments (loaded once);
-//   O^T += V^T . P^T  A = 16 dims x 32 keys of the dim-major V cache, B = P^T taken from the
-//                   score registers: the MFMA k-slots 8g+i / 8g+4+i are mapped to keys 4g+i /
-//                   16+4g+i, which are exactly the scores lane (g, r) holds, so P never moves
-//                   between lanes, and V^T is read with the same key order (two 8-byte loads).
-// Online softmax runs in registers with exp2; P enters the PV product as bf16 hi + bf16 lo
-// (the rounding remainder), two MFMAs, so the weights keep about 16 significant bits.  With
-// one key chunk the wave writes the normalised output; otherwise it writes (m, l, O) partials
-// and a merge kernel combines them.
+// bf16 path (gfx950 MFMA, head_dim 64 or 128): split-L flash decoding with LDS-staged K/V
+// tiles.  A workgroup owns one (sequence, KV head, key split, 64-row tile); the rows of a tile
+// are the (token, q head) pairs of the GQA group, so the K/V of a split is fetched once for all
+// of them.  The 256 threads copy 64-key tiles (K rows, and the dim-major V rows with each
+// lane's 8 keys gathered into one 16-byte chunk) into two swizzled LDS buffers, the next tile
+// in flight while the current one is multiplied; each wave takes 16 rows in 32-key steps:
+//   S^T = K . Q^T   A = 16 keys x 32 dims of the K tile, B = the wave's query fragments;
+//   O^T += V^T . P^T  A = 16 dims x 32 keys of the V tile, B = P^T taken from the score
+//                   registers: MFMA k-slots 8g+i / 8g+4+i carry keys 4g+i / 16+4g+i, exactly
+//                   the scores lane (g, r) holds, so P never moves between lanes.
+// Online softmax runs in registers with exp2 and wavefront max/sum reductions; P enters the PV
+// product as bf16 hi + bf16 lo (the rounding remainder), two MFMAs, so the weights keep about
+// 16 significant bits.  With one split the wave writes the normalised output; otherwise it
+// writes (m, l, O) partials and a merge kernel combines them.
 //
 // fp32 path: one workgroup per (row, q head), plain two-pass softmax over all keys.
 #include "cad_device.h"
@@ -36,25 +35,26 @@ __device__ __forceinline__ bool key_allowed(int key, int len, int it, int mode, 
 }
 
 // Keys per split for a sequence of len cached rows and Nq new rows: the live keys spread
-// evenly over the nsplit splits, in multiples of 32 and at least 64, so splits past the live
-// range get no keys.  Computed on the device from the cache length the forward captured.
+// evenly over the nsplit splits in whole 64-key tiles, so splits past the live range get no
+// keys.  Computed on the device from the cache length the forward captured.
 __device__ __forceinline__ int split_chunk(int len, int Nq, int nsplit) {
     const int S = len + Nq;
     int c = (S + nsplit - 1) / nsplit;
-    c = (c + 31) & ~31;
-    return c < 64 ? 64 : c;
+    return (c + 63) & ~63;
 }
 
-// four bf16 of one V row (keys key0..key0+3, key0 a multiple of 4); keys at or past kend read
-// as zero.  Branch-free: a group wholly past kend reads slot 0 instead (cap is a multiple of 4,
-// so a load never crosses the end of a row), so all loads of a step issue back to back.
-__device__ __forceinline__ uint2 v4(const uint16_t* vrow, int key0, int kend) {
-    const int n = kend - key0;                       // valid keys in the group
-    uint2 w = *(const uint2*)(vrow + (n > 0 ? key0 : 0));   // keys key0 .. key0+3, low half first
-    w.x &= n >= 2 ? 0xFFFFFFFFu : (n == 1 ? 0xFFFFu : 0u);
-    w.y &= n >= 4 ? 0xFFFFFFFFu : (n == 3 ? 0xFFFFu : 0u);
-    return w;
+// Swizzled 16-byte chunk positions in the LDS tiles (reads of 16 consecutive rows at one chunk
+// index, and writes of whole rows, touch every bank once).
+//   K tile [TK keys][DH]: chunk c of key row r; V tile [DH dims][TK keys]: chunk c of dim row r.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int DH>
+__device__ __forceinline__ int swz_k(int r, int c) {
+    if constexpr (DH == 128) return c ^ (r & 15);       // 256-byte rows
+    else return c ^ ((r >> 1) & 7);                     // 128-byte rows
 }
+__device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r >> 1) & 7); }   // 128-byte rows
 
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -64,21 +64,29 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
                                                    float* __restrict__ part_ml, uint16_t* __restrict__ o_out) {
     constexpr int DS = DH / 32;                 // MFMA k-steps over head_dim
     constexpr int DB = DH / 16;                 // 16-wide head_dim blocks of the output
+    constexpr int TK = 64;                      // keys per LDS tile (two 32-key MFMA steps)
+    constexpr int KCH = DH / 8;                 // 16-byte chunks of a K row
+    constexpr int KLD = TK * KCH / 256;         // K chunks each thread copies per tile
+    constexpr int VLD = DH * (TK / 4) / 256;    // 4-key V groups each thread copies per tile
+    __shared__ u32x4_t ks[2][TK * KCH];
+    __shared__ u32x4_t vs[2][DH * (TK / 8)];
+
     const int split = blockIdx.x, rtile = blockIdx.y;
     const int bg = blockIdx.z, b = bg / Hkv, g = bg % Hkv;
     const int G = Hq / Hkv, Rg = Nq * G;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
 
-    const int wrow0 = rtile * (WAVES * 16) + wave * 16;
-    if (wrow0 >= Rg) return;                    // no rows for this wave (no barriers below)
+    const int wg_row0 = rtile * (WAVES * 16);
+    const int wrow0 = wg_row0 + wave * 16;
+    const bool wlive = wrow0 < Rg;              // a wave without rows still copies tiles
     const bool ok = seq_ok(len_snap, b, Nq, cap);
     const int len = ok ? len_snap[b] : 0;
     const int rho = wrow0 + l16;
     const bool qlive = rho < Rg;
     const int it = qlive ? rho / G : 0, hh = qlive ? rho % G : 0;
-    // keys past len + (last token of the wave) are masked for every row of the wave
-    const int it_max = min(Nq - 1, min(wrow0 + 15, Rg - 1) / G);
+    // keys past len + (last token of the workgroup's rows) are masked for all of its rows
+    const int it_max = min(Nq - 1, min(wg_row0 + WAVES * 16 - 1, Rg - 1) / G);
     const int chunk = split_chunk(len, Nq, nsplit);
     const int kbeg = split * chunk;
     int kend = min(kbeg + chunk, len + it_max + 1);
@@ -88,9 +96,9 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     {
         const uint16_t* qp = q + (((size_t)b * Nq + it) * Hq + g * G + hh) * DH;
 #pragma unroll
-        for (int ks = 0; ks < DS; ++ks) {
-            uint4 v = qlive && ok ? *(const uint4*)(qp + ks * 32 + g4 * 8) : make_uint4(0, 0, 0, 0);
-            qf[ks] = *(bf16x8_t*)&v;
+        for (int d = 0; d < DS; ++d) {
+            uint4 v = qlive && ok ? *(const uint4*)(qp + d * 32 + g4 * 8) : make_uint4(0, 0, 0, 0);
+            qf[d] = *(bf16x8_t*)&v;
         }
     }
 
@@ -104,41 +112,57 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     const uint16_t* kbase = kc + head * cap * DH;
     const uint16_t* vbase = vc + head * DH * cap;          // dim-major: row = one dim over all slots
 
-    // Operands of one 32-key step.  Keys at or past kend load from slot 0 (always a valid
-    // address) and are masked afterwards, so a step can be fetched before it is known to be
-    // needed: the loop keeps the next step's loads in flight while it computes the current one.
-    struct StepOps { bf16x8_t kf[2][DS]; bf16x8_t vf[DB]; };
-    auto load = [&](int k0, StepOps& op) {
-        // K fragments: lane (key l16, g4) of key block kb
+    // One tile in registers on its way to LDS.  Every load is issued unconditionally from a valid
+    // address: a K row past kend reads slot 0 (its scores are masked), a V group past kend reads
+    // slot 0 and is zeroed (so masked keys add exactly zero); cap is a multiple of 4, so an 8-byte
+    // V group never crosses the end of a row.
+    struct Tile { u32x4_t k[KLD]; u32x2_t v[VLD]; };
+    auto load = [&](int t0, Tile& r) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int key = k0 + kb * 16 + l16;
-            const uint16_t* kp = kbase + (size_t)(key < kend ? key : 0) * DH + g4 * 8;
-#pragma unroll
-            for (int ks = 0; ks < DS; ++ks) {
-                uint4 v = *(const uint4*)(kp + ks * 32);
-                op.kf[kb][ks] = *(bf16x8_t*)&v;
-            }
+        for (int i = 0; i < KLD; ++i) {
+            const int id = tid + 256 * i, key = t0 + id / KCH;
+            r.k[i] = *(const u32x4_t*)(kbase + (size_t)(key < kend ? key : 0) * DH + (id % KCH) * 8);
         }
-        // V^T fragments: lane (dim db*16 + l16, g4) takes keys 4g4..+3 and 16+4g4..+3
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const uint16_t* vrow = vbase + (size_t)(db * 16 + l16) * cap;
-            const uint2 lo = v4(vrow, k0 + 4 * g4, kend), hi = v4(vrow, k0 + 16 + 4 * g4, kend);
-            uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            op.vf[db] = *(bf16x8_t*)&vv;
+        for (int i = 0; i < VLD; ++i) {
+            const int id = tid + 256 * i, key0 = t0 + 4 * (id % (TK / 4));
+            r.v[i] = *(const u32x2_t*)(vbase + (size_t)(id / (TK / 4)) * cap + (key0 < kend ? key0 : 0));
         }
     };
-    auto compute = [&](int k0, const StepOps& op) {
-        // S^T[key][query]: lane holds keys kb*16 + 4*g4 + i of query l16
+    // V tile layout: the 8 keys an MFMA lane needs (4g..4g+3 and 16+4g..16+4g+3 of a 32-key step)
+    // form one 16-byte chunk, chunk kq*4 + g of the dim row.
+    auto store = [&](int t0, int buf, const Tile& r) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) {
+            const int id = tid + 256 * i, key = id / KCH;
+            ks[buf][key * KCH + swz_k<DH>(key, id % KCH)] = r.k[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) {
+            const int id = tid + 256 * i, row = id / (TK / 4), grp = id % (TK / 4);
+            const int n = kend - (t0 + 4 * grp);                   // valid keys of the group
+            u32x2_t w = r.v[i];
+            w.x &= n >= 2 ? 0xFFFFFFFFu : (n == 1 ? 0xFFFFu : 0u);
+            w.y &= n >= 4 ? 0xFFFFFFFFu : (n == 3 ? 0xFFFFu : 0u);
+            const int kq = grp >> 3, gq = grp & 7;
+            const int c = swz_v(row, kq * 4 + (gq & 3));
+            ((u32x2_t*)vs[buf])[(row * (TK / 8) + c) * 2 + (gq >> 2)] = w;
+        }
+    };
+    // one 32-key step of the wave's 16 rows out of LDS buffer buf (keys k0 .. k0+31, kq = half)
+    auto step = [&](int k0, int buf, int kq) __attribute__((always_inline)) {
         f32x4_t st[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            const int key = kq * 32 + kb * 16 + l16;
             st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < DS; ++ks)
-                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kf[kb][ks], qf[ks], st[kb], 0, 0, 0);
+            for (int d = 0; d < DS; ++d) {
+                const u32x4_t kv = ks[buf][key * KCH + swz_k<DH>(key, d * 4 + g4)];
+                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&kv, qf[d], st[kb], 0, 0, 0);
+            }
         }
+        // S^T[key][query]: lane holds keys kb*16 + 4*g4 + i of query l16
         float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -174,20 +198,26 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
         m_run = m_new;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
+            const int row = db * 16 + l16;
+            const u32x4_t vv = vs[buf][row * (TK / 8) + swz_v(row, kq * 4 + g4)];
             oacc[db] *= alpha;
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.vf[db], ph, oacc[db], 0, 0, 0);
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.vf[db], pl, oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, ph, oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, pl, oacc[db], 0, 0, 0);
         }
     };
 
-    StepOps opa, opb;
-    load(kbeg, opa);
-    for (int k0 = kbeg; k0 < kend; k0 += 64) {
-        load(k0 + 32, opb);
-        compute(k0, opa);
-        if (k0 + 32 >= kend) break;
-        load(k0 + 64, opa);
-        compute(k0 + 32, opb);
+    // tile t is copied to LDS buffer t & 1 at the start of its step (buffer t & 1 was last read
+    // two steps earlier, before the previous barrier), and tile t + 1 is fetched meanwhile
+    Tile r;
+    load(kbeg, r);
+    for (int t0 = kbeg, t = 0; t0 < kend; t0 += TK, ++t) {
+        store(t0, t & 1, r);
+        load(t0 + TK, r);
+        __syncthreads();
+        if (wlive) {
+            step(t0, t & 1, 0);
+            if (t0 + 32 < kend) step(t0 + 32, t & 1, 1);
+        }
     }
 
     if (!qlive) return;
