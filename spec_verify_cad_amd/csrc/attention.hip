@@ -24,14 +24,19 @@ namespace {
 
 constexpr int WAVES = 4;
 
-__device__ __forceinline__ bool key_allowed(int key, int len, int it, int mode, int Dblk) {
+template <int MODE>
+__device__ __forceinline__ bool key_allowed(int key, int len, int it, int Dblk) {
     if (key < len) return true;
     const int s = key - len;
-    if (mode == CAD_MASK_BLOCK_TRI) {
+    if constexpr (MODE == CAD_MASK_BLOCK_TRI) {
         const int w = it / Dblk, j = it % Dblk;
         return s >= w * Dblk && s <= w * Dblk + j;
     }
     return s <= it;
+}
+__device__ __forceinline__ bool key_allowed(int key, int len, int it, int mode, int Dblk) {
+    return mode == CAD_MASK_BLOCK_TRI ? key_allowed<CAD_MASK_BLOCK_TRI>(key, len, it, Dblk)
+                                      : key_allowed<CAD_MASK_CAUSAL_SPAN>(key, len, it, Dblk);
 }
 
 // Keys per split for a sequence of len cached rows and Nq new rows: the live keys spread
@@ -48,6 +53,8 @@ __device__ __forceinline__ int split_chunk(int len, int Nq, int nsplit) {
 //   K tile [TK keys][DH]: chunk c of key row r; V tile [DH dims][TK keys]: chunk c of dim row r.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <int DH>
 __device__ __forceinline__ int swz_k(int r, int c) {
@@ -56,10 +63,10 @@ __device__ __forceinline__ int swz_k(int r, int c) {
 }
 __device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r >> 1) & 7); }   // 128-byte rows
 
-template <int DH>
+template <int DH, int MODE>
 __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                                    const uint16_t* __restrict__ vc, const int32_t* __restrict__ len_snap,
-                                                   int Nq, int Hq, int Hkv, int cap, int mode, int Dblk,
+                                                   int Nq, int Hq, int Hkv, int cap, int Dblk,
                                                    int nsplit, float* __restrict__ part_o,
                                                    float* __restrict__ part_ml, uint16_t* __restrict__ o_out) {
     constexpr int DS = DH / 32;                 // MFMA k-steps over head_dim
@@ -97,13 +104,20 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
         const uint16_t* qp = q + (((size_t)b * Nq + it) * Hq + g * G + hh) * DH;
 #pragma unroll
         for (int d = 0; d < DS; ++d) {
-            uint4 v = qlive && ok ? *(const uint4*)(qp + d * 32 + g4 * 8) : make_uint4(0, 0, 0, 0);
+            // unconditional (a lane without a row reads row 0's q, finite, and writes nothing):
+            // a load inside a branch would make the wait counts of the loop below conservative
+            uint4 v = *(const uint4*)(qp + d * 32 + g4 * 8);
             qf[d] = *(bf16x8_t*)&v;
         }
     }
 
     const float sl2 = 1.4426950408889634f / sqrtf((float)DH);   // log2(e)/sqrt(d)
-    float m_run = -INFINITY, l_run = 0.f;
+    // m_run: the query's reference maximum (log2 units), shared by its 4 lanes; it may trail the
+    // running maximum by up to RESCALE, so weights stay <= 2^RESCALE and the accumulators are
+    // rescaled only when some lane of the wave exceeds that.  l_lane: this lane's share of the
+    // weight sum (its 8 keys of every step), summed over the 4 lanes at the end.
+    constexpr float RESCALE = 8.f;
+    float m_run = -INFINITY, l_lane = 0.f;
     f32x4_t oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -112,8 +126,10 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     const uint16_t* kbase = kc + head * cap * DH;
     const uint16_t* vbase = vc + head * DH * cap;          // dim-major: row = one dim over all slots
 
-    // One tile in registers on its way to LDS.  Every load is issued unconditionally from a valid
-    // address: a K row past kend reads slot 0 (its scores are masked), a V group past kend reads
+    // One tile in registers on its way to LDS.  The loads stay in program order (a scheduling
+    // barrier after each), so the compiler's wait counts at the loop head, which merge the issue
+    // order of the prologue and of the previous step, wait for the oldest tile only.  Every load
+    // is issued unconditionally from a valid address: a K row past kend reads slot 0 (its scores are masked), a V group past kend reads
     // slot 0 and is zeroed (so masked keys add exactly zero); cap is a multiple of 4, so an 8-byte
     // V group never crosses the end of a row.
     struct Tile { u32x4_t k[KLD]; u32x2_t v[VLD]; };
@@ -122,11 +138,13 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
         for (int i = 0; i < KLD; ++i) {
             const int id = tid + 256 * i, key = t0 + id / KCH;
             r.k[i] = *(const u32x4_t*)(kbase + (size_t)(key < kend ? key : 0) * DH + (id % KCH) * 8);
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int id = tid + 256 * i, key0 = t0 + 4 * (id % (TK / 4));
             r.v[i] = *(const u32x2_t*)(vbase + (size_t)(id / (TK / 4)) * cap + (key0 < kend ? key0 : 0));
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     // V tile layout: the 8 keys an MFMA lane needs (4g..4g+3 and 16+4g..16+4g+3 of a 32-key step)
@@ -149,12 +167,13 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
             ((u32x2_t*)vs[buf])[(row * (TK / 8) + c) * 2 + (gq >> 2)] = w;
         }
     };
-    // one 32-key step of the wave's 16 rows out of LDS buffer buf (keys k0 .. k0+31, kq = half)
-    auto step = [&](int k0, int buf, int kq) __attribute__((always_inline)) {
-        f32x4_t st[2];
+    // one 64-key step of the wave's 16 rows out of LDS buffer buf (keys k0 .. k0+63): four
+    // 16-key score blocks, one softmax update, then two 32-key value products
+    auto step = [&](int k0, int buf) __attribute__((always_inline)) {
+        f32x4_t st[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int key = kq * 32 + kb * 16 + l16;
+        for (int kb = 0; kb < 4; ++kb) {
+            const int key = kb * 16 + l16;
             st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int d = 0; d < DS; ++d) {
@@ -162,47 +181,56 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
                 st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&kv, qf[d], st[kb], 0, 0, 0);
             }
         }
-        // S^T[key][query]: lane holds keys kb*16 + 4*g4 + i of query l16
-        float tmax = -INFINITY;
+        // S^T[key][query]: lane holds keys kb*16 + 4*g4 + i of query l16.  A step wholly below
+        // the cached length and kend needs no mask (every cached key is visible to every row).
+        const bool full = k0 + TK <= kend && k0 + TK <= len;
+        float lmax = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = k0 + kb * 16 + g4 * 4 + i;
-                const bool al = qlive && key < kend && key_allowed(key, len, it, mode, Dblk);
+                const bool al = full || (qlive && key < kend && key_allowed<MODE>(key, len, it, Dblk));
                 const float sv = al ? st[kb][i] * sl2 : -INFINITY;
                 st[kb][i] = sv;
-                tmax = fmaxf(tmax, sv);
+                lmax = fmaxf(lmax, sv);
             }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-        float psum = 0.f;
-        // P^T fragment: k-slot 8*g4 + i <- key 4*g4 + i (block 0), 8*g4 + 4 + i <- key 16 + 4*g4 + i
-        bf16x8_t ph, pl;
+        if (__ballot(lmax > m_run + RESCALE) != 0) {      // wave-uniform, rare after the first step
+            float tmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_lane *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            m_run = m_new;
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float pv = m_new == -INFINITY ? 0.f : exp2f(st[kb][i] - m_new);
-                const uint16_t hb = f32_to_bf16(pv);
-                const uint16_t lb = f32_to_bf16(pv - bf16_to_f32(hb));
-                psum += pv;
-                ((uint16_t*)&ph)[kb * 4 + i] = hb;
-                ((uint16_t*)&pl)[kb * 4 + i] = lb;
+        for (int kq = 0; kq < 2; ++kq) {
+            // P^T fragment of keys k0 + 32kq ..: k-slot 8*g4 + i <- key 4*g4 + i (block 2kq),
+            // 8*g4 + 4 + i <- key 16 + 4*g4 + i (block 2kq + 1); each weight as bf16 hi + bf16 lo
+            // (both round to nearest even, two keys per conversion)
+            bf16x8_t ph, pl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int kb = 2 * kq + (j >> 1), i = (j & 1) * 2;
+                const f32x2_t pv = m_run == -INFINITY
+                                       ? f32x2_t{0.f, 0.f}
+                                       : f32x2_t{__builtin_amdgcn_exp2f(st[kb][i] - m_run),
+                                                 __builtin_amdgcn_exp2f(st[kb][i + 1] - m_run)};
+                const bf16x2_t h = __builtin_convertvector(pv, bf16x2_t);
+                const bf16x2_t lo = __builtin_convertvector(pv - __builtin_convertvector(h, f32x2_t), bf16x2_t);
+                l_lane += pv.x + pv.y;
+                ph[2 * j] = h.x; ph[2 * j + 1] = h.y;
+                pl[2 * j] = lo.x; pl[2 * j + 1] = lo.y;
             }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int row = db * 16 + l16;
-            const u32x4_t vv = vs[buf][row * (TK / 8) + swz_v(row, kq * 4 + g4)];
-            oacc[db] *= alpha;
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, ph, oacc[db], 0, 0, 0);
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, pl, oacc[db], 0, 0, 0);
+            for (int db = 0; db < DB; ++db) {
+                const int row = db * 16 + l16;
+                const u32x4_t vv = vs[buf][row * (TK / 8) + swz_v(row, kq * 4 + g4)];
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, ph, oacc[db], 0, 0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, pl, oacc[db], 0, 0, 0);
+            }
         }
     };
 
@@ -214,12 +242,11 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
         store(t0, t & 1, r);
         load(t0 + TK, r);
         __syncthreads();
-        if (wlive) {
-            step(t0, t & 1, 0);
-            if (t0 + 32 < kend) step(t0 + 32, t & 1, 1);
-        }
+        if (wlive) step(t0, t & 1);
     }
 
+    float l_run = l_lane + __shfl_xor(l_lane, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
     if (!qlive) return;
     // lane holds O^T[dim = db*16 + 4*g4 + i][query l16]
     if (nsplit == 1) {
@@ -326,6 +353,57 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
     }
 }
 
+// Merge for few splits (nsplit <= SMAX): DH/4 threads per (row, q head), four dims each, several
+// pairs per workgroup and no LDS.  Every thread loads all the pair's (m, l) and its four dims of
+// each split at once, then combines them in split order with the same weights as k_attn_merge.
+template <typename T, int DH, int SMAX>
+__global__ __launch_bounds__(256) void k_attn_merge_few(const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml,
+                                                        const int32_t* __restrict__ len_snap, int Nq, int Hq, int Hkv,
+                                                        int cap, int nsplit, int pairs, T* __restrict__ o) {
+    constexpr int TPG = DH / 4;
+    const int rowhead = blockIdx.x * (256 / TPG) + threadIdx.x / TPG;   // (b*Nq + it)*Hq + h
+    const int q = threadIdx.x % TPG;
+    if (rowhead >= pairs) return;
+    const int h = rowhead % Hq, row = rowhead / Hq;
+    const int b = row / Nq, it = row % Nq;
+    if (!seq_ok(len_snap, b, Nq, cap)) return;
+    const int len = len_snap[b];
+    const int chunk = split_chunk(len, Nq, nsplit);
+    const int live = min(nsplit, (len + Nq + chunk - 1) / chunk);
+    const int G = Hq / Hkv, g = h / G, hh = h % G;
+    const int Rg = Nq * G, rho = it * G + hh;
+    const size_t p0 = (((size_t)b * Hkv + g) * Rg + rho) * nsplit;
+    float2 ml[SMAX];
+    float4 ov[SMAX];
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) {
+        const int sp = min(j, live - 1);
+        ml[j] = *(const float2*)(part_ml + (p0 + sp) * 2);
+        ov[j] = *(const float4*)(part_o + (p0 + sp) * DH + 4 * q);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) m = j < live ? fmaxf(m, ml[j].x) : m;
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j) {
+        const float w = (j >= live || ml[j].x == -INFINITY) ? 0.f : exp2f(ml[j].x - m);
+        L += w * ml[j].y;
+        acc.x += w * ov[j].x;
+        acc.y += w * ov[j].y;
+        acc.z += w * ov[j].z;
+        acc.w += w * ov[j].w;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const size_t ob = (size_t)rowhead * DH + 4 * q;
+    Elt<T>::st(o, ob + 0, acc.x * inv);
+    Elt<T>::st(o, ob + 1, acc.y * inv);
+    Elt<T>::st(o, ob + 2, acc.z * inv);
+    Elt<T>::st(o, ob + 3, acc.w * inv);
+}
+
 // fp32 (or any dtype) reference-style kernel: one workgroup per (row, q head); scores in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_simple(const T* __restrict__ q, const T* __restrict__ kc,
@@ -413,25 +491,37 @@ hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc
         return hipGetLastError();
     }
     const dim3 grid(fd.attn_splits, fd.attn_row_tiles, fd.B * fd.Hkv);
-    if (fd.d == 128)
-        hipLaunchKernelGGL((k_attn_bf16<128>), grid, dim3(WAVES * 64), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc,
-                           (const uint16_t*)vc, wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.mode, fd.Dblk,
-                           fd.attn_splits, wb.part_o, wb.part_ml, (uint16_t*)wb.o);
-    else
-        hipLaunchKernelGGL((k_attn_bf16<64>), grid, dim3(WAVES * 64), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc,
-                           (const uint16_t*)vc, wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.mode, fd.Dblk,
-                           fd.attn_splits, wb.part_o, wb.part_ml, (uint16_t*)wb.o);
+    const bool tri = fd.mode == CAD_MASK_BLOCK_TRI;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc,
+                           (const uint16_t*)vc, wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.Dblk, fd.attn_splits,
+                           wb.part_o, wb.part_ml, (uint16_t*)wb.o);
+    };
+    if (fd.d == 128) tri ? go(k_attn_bf16<128, CAD_MASK_BLOCK_TRI>) : go(k_attn_bf16<128, CAD_MASK_CAUSAL_SPAN>);
+    else tri ? go(k_attn_bf16<64, CAD_MASK_BLOCK_TRI>) : go(k_attn_bf16<64, CAD_MASK_CAUSAL_SPAN>);
     return hipGetLastError();
 }
 
 bool attention_uses_merge(const FwdDims& fd) { return mfma_path(fd) && fd.attn_splits > 1; }
 
 hipError_t launch_attention_merge(const FwdDims& fd, const FwdBufs& wb, hipStream_t s) {
+    const int pairs = fd.M * fd.Hq;
+    if (fd.attn_splits <= 8) {
+        const int per = 256 / (fd.d / 4);
+        const dim3 grid((pairs + per - 1) / per);
+        if (fd.d == 128)
+            hipLaunchKernelGGL((k_attn_merge_few<uint16_t, 128, 8>), grid, dim3(256), 0, s, wb.part_o, wb.part_ml,
+                               wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.attn_splits, pairs, (uint16_t*)wb.o);
+        else
+            hipLaunchKernelGGL((k_attn_merge_few<uint16_t, 64, 8>), grid, dim3(256), 0, s, wb.part_o, wb.part_ml,
+                               wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.attn_splits, pairs, (uint16_t*)wb.o);
+        return hipGetLastError();
+    }
     if (fd.d == 128)
-        hipLaunchKernelGGL((k_attn_merge<uint16_t, 128>), dim3(fd.M * fd.Hq), dim3(256), 0, s, wb.part_o, wb.part_ml,
+        hipLaunchKernelGGL((k_attn_merge<uint16_t, 128>), dim3(pairs), dim3(256), 0, s, wb.part_o, wb.part_ml,
                            wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.attn_splits, (uint16_t*)wb.o);
     else
-        hipLaunchKernelGGL((k_attn_merge<uint16_t, 64>), dim3(fd.M * fd.Hq), dim3(256), 0, s, wb.part_o, wb.part_ml,
+        hipLaunchKernelGGL((k_attn_merge<uint16_t, 64>), dim3(pairs), dim3(256), 0, s, wb.part_o, wb.part_ml,
                            wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.attn_splits, (uint16_t*)wb.o);
     return hipGetLastError();
 }
