@@ -110,11 +110,15 @@ def main():
     ar_out = torch.empty((1, 1), dtype=torch.int32, device=dev)
     ar_ws = cad.alloc_workspace(cad.span_forward_workspace(lay0, 1, 1, cad.MASK_CAUSAL, 1, 1, cap, cad.COMMIT_ALL))
 
-    def forward(j, copy, stream):
-        """One copy-span commit of spans[j] from a cache of exactly L0 positions."""
+    outs_last = [torch.empty((1,), dtype=torch.int32, device=dev) for _ in spans]
+
+    def forward(j, copy, stream, last=False):
+        """One copy-span commit of spans[j] from a cache of exactly L0 positions (last: copy-commit
+        mode, the LM head only for the span's last row)."""
         lens[j:j + 1].fill_(L0)
-        cad.span_forward(layers[copy], caches[j], toks[j], spans[j], flags=cad.COMMIT_ALL, argmax_out=outs[j],
-                         workspace=wss[j], stream=stream)
+        cad.span_forward(layers[copy], caches[j], toks[j], spans[j],
+                         flags=cad.COMMIT_ALL | (cad.LOGITS_LAST if last else 0),
+                         argmax_out=outs_last[j] if last else outs[j], workspace=wss[j], stream=stream)
 
     def ar_run(stream, copy0=0):
         lens[0:1].fill_(L0)
@@ -128,6 +132,7 @@ def main():
     for _ in range(2):
         for j in range(len(spans)):
             forward(j, j & 1, torch.cuda.current_stream())
+            forward(j, j & 1, torch.cuda.current_stream(), last=True)
         ar_run(torch.cuda.current_stream())
     torch.cuda.synchronize()
     cap_stream = torch.cuda.Stream()
@@ -143,6 +148,10 @@ def main():
     step_graphs = [capture(lambda st, c=c: [forward(j, (j + c) & 1, st) for j in range(len(spans))]) for c in (0, 1)]
     per_n_graphs = [[capture(lambda st, j=j, c=c: forward(j, c, st)) for c in (0, 1)] for j in range(len(spans))]
     ar_graphs = [capture(lambda st, c=c: ar_run(st, c)) for c in (0, 1)]
+    last_step_graphs = [capture(lambda st, c=c: [forward(j, (j + c) & 1, st, last=True) for j in range(len(spans))])
+                        for c in (0, 1)]
+    last_graphs = [[capture(lambda st, j=j, c=c: forward(j, c, st, last=True)) for c in (0, 1)]
+                   for j in range(len(spans))]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -200,6 +209,19 @@ def main():
         log(f"N={N}: {us:.1f} us, {N / (us * 1e-6):.0f} tok/s, {bound} floor {floor:.1f} us "
             f"({floor / us * 100:.1f}%), lm_head {lm_us} us")
 
+    # ---- copy-commit mode (CAD_LOGITS_LAST): inside a copy span only the prediction after the
+    # span is consumed, so the LM head runs for the last row only
+    ms_last = timed(last_step_graphs, a.steps)
+    last_per_n = []
+    for j, N in enumerate(spans):
+        us = timed(last_graphs[j], a.steps) * 1e3
+        last_per_n.append({"N": N, "us": round(us, 2), "committed_tok_s": round(N / (us * 1e-6), 1),
+                           "speedup_vs_full": round(per_n[j]["us"] / us, 3)})
+        log(f"copy-commit N={N}: {us:.1f} us, {N / (us * 1e-6):.0f} tok/s")
+    copy_commit = {"flag": "CAD_LOGITS_LAST", "value": round(tokens_step / (ms_last * 1e-3), 1),
+                   "unit": "committed tokens/s", "ms_per_step": round(ms_last, 4), "per_n": last_per_n}
+    log(f"copy-commit sweep {ms_last * 1e3:.1f} us -> {copy_commit['value']:.0f} committed tok/s")
+
     # ---- autoregressive baseline: single-token teacher-forced forwards
     ar_us = timed(ar_graphs, max(2, a.steps // 4)) * 1e3 / a.ar_steps
     for r in per_n:
@@ -237,6 +259,7 @@ def main():
         "per_n": per_n,
         "ar_baseline": {"us_per_token": round(ar_us, 2), "tok_s": round(1e6 / ar_us, 1), "floor_us": round(ar_floor, 2)},
         "roofline": roof,
+        "copy_commit_mode": copy_commit,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

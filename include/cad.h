@@ -57,6 +57,9 @@ extern "C" {
 /* span-forward flags */
 #define CAD_COMMIT_ALL   1    /* len += Nq at the end of the forward (a copy span: acceptance 1) */
 #define CAD_KV_ONLY      2    /* stop after appending K/V (prefill of a cache); no outputs     */
+#define CAD_LOGITS_LAST  4    /* copy-commit mode: final norm, LM head and argmax only for each
+                                 sequence's last row (inside a copy span only the prediction after
+                                 the span is used); causal-span mask only                     */
 
 /*
  * A pre-norm decoder layer with grouped-query attention and a SwiGLU MLP, followed by a
@@ -131,11 +134,12 @@ int cad_ngram_lookup(const int32_t *ctx, int64_t ctx_stride, const int32_t *ctx_
  *
  *   tokens      [B, Nq] int32 token ids (must be < vocab)
  *   mask_mode   CAD_MASK_CAUSAL_SPAN, or CAD_MASK_BLOCK_TRI with Nq == W*D
- *   flags       CAD_COMMIT_ALL and/or CAD_KV_ONLY
+ *   flags       CAD_COMMIT_ALL, CAD_KV_ONLY, CAD_LOGITS_LAST (or-ed)
  *   argmax_out  [B, Nq] int32 out: LM-head argmax per row, ties to the lowest id (nullable
- *               only with CAD_KV_ONLY)
+ *               only with CAD_KV_ONLY); [B] (the last row's) with CAD_LOGITS_LAST
  *   hidden_out  [B*Nq, hidden] dtype out, nullable: the layer output (residual stream)
- *   logits_out  [B*Nq, vocab] fp32 out, nullable (debug; costs a full logits write)
+ *   logits_out  [B*Nq, vocab] fp32 out, nullable (debug; costs a full logits write);
+ *               [B, vocab] with CAD_LOGITS_LAST
  *   workspace   device scratch of at least cad_span_forward_workspace(...) bytes, 256-aligned
  *
  * Every row first appends its K/V at slot len+i (RoPE at the row's position), then attends
@@ -143,8 +147,12 @@ int cad_ngram_lookup(const int32_t *ctx, int64_t ctx_stride, const int32_t *ctx_
  * its own key as stored).  Rounding points (bf16 round-to-nearest-even for a bf16 layer):
  * normed input, rotated q, stored k and v, attention output, second normed input, SwiGLU
  * product, hidden_out, final normed input; the residual stream and logits are fp32.
- * Errors: CAD_EINVAL, CAD_EUNSUPPORTED (also: cap not a multiple of 4), CAD_EWORKSPACE, CAD_EHIP;
- * per sequence CAD_ECAPACITY in kv->err when len + Nq > cap.
+ * Copy-as-Decode's copy-span commit (§2.4) needs only the prediction after the span:
+ * CAD_LOGITS_LAST runs the final norm, LM head and argmax for row Nq-1 of each sequence; the
+ * cache rows and hidden_out are those of a full forward.
+ * Errors: CAD_EINVAL (also: CAD_LOGITS_LAST with the block mask), CAD_EUNSUPPORTED (also: cap
+ * not a multiple of 4), CAD_EWORKSPACE, CAD_EHIP; per sequence CAD_ECAPACITY in kv->err when
+ * len + Nq > cap.
  */
 int cad_span_forward(const cad_layer_desc *layer, const cad_kv_desc *kv,
                      const int32_t *tokens, int B, int Nq,

@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "cad.h")
 CAD_OK, CAD_EINVAL, CAD_EUNSUPPORTED, CAD_ECAPACITY, CAD_EHIP, CAD_EWORKSPACE = 0, -1, -2, -3, -4, -5
 DTYPE_BF16, DTYPE_F32 = 0, 1
 MASK_CAUSAL, MASK_BLOCK = 0, 1
-COMMIT_ALL, KV_ONLY = 1, 2
+COMMIT_ALL, KV_ONLY, LOGITS_LAST = 1, 2, 4
 
 
 class LayerDesc(ctypes.Structure):

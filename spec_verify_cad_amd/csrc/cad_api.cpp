@@ -1,5 +1,6 @@
 // C ABI of libcad: host-side argument checks, workspace sizing/carving and the launch
 // sequence of the span forward.  Nothing here allocates, frees or synchronizes.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -101,7 +102,9 @@ FwdBufs fwd_carve(const FwdDims& fd, void* base, bool kv_only) {
     w.u = take(M * h * e);
     if (!kv_only) {
         w.amax_slots = gemm_argmax_slots(fd.dtype, fd.M, fd.V, fd.h);
-        w.amax_part = (float2*)take(M * (size_t)w.amax_slots * sizeof(float2));
+        w.amax_slots_last = gemm_argmax_slots(fd.dtype, fd.B, fd.V, fd.h);
+        const size_t sl = std::max(M * (size_t)w.amax_slots, (size_t)fd.B * w.amax_slots_last);
+        w.amax_part = (float2*)take(sl * sizeof(float2));
         w.x = (float*)take(M * h * 4);
         w.q = take(M * qd * e);
         w.o = take(M * qd * e);
@@ -188,8 +191,10 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
                      int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!L || !kv || !tokens) return CAD_EINVAL;
-    if (flags & ~(CAD_COMMIT_ALL | CAD_KV_ONLY)) return CAD_EINVAL;
+    if (flags & ~(CAD_COMMIT_ALL | CAD_KV_ONLY | CAD_LOGITS_LAST)) return CAD_EINVAL;
     const bool kv_only = (flags & CAD_KV_ONLY) != 0;
+    const bool last_only = (flags & CAD_LOGITS_LAST) != 0;
+    if (last_only && mode != CAD_MASK_CAUSAL_SPAN) return CAD_EINVAL;
     if (!kv->k || !kv->v || !kv->len || kv->B != B) return CAD_EINVAL;
     FwdDims fd;
     if (!fwd_dims(L, B, Nq, mode, W, D, kv->cap, &fd)) return CAD_EINVAL;
@@ -252,7 +257,7 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
         }) != hipSuccess)
         return CAD_EHIP;
     if (stage(ST_NORM2, stream, [&] {
-            return launch_resid_norm(fd, wb.x, wb.part, fd.o_slices, wb.h1, nullptr, wb.u2, L->rms_eps, wb.len_snap,
+            return launch_resid_norm(fd, wb.x, wb.part, fd.o_slices, wb.h1, nullptr, wb.u2, false, L->rms_eps, wb.len_snap,
                                      stream);
         }) != hipSuccess)
         return CAD_EHIP;
@@ -271,19 +276,24 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
         }) != hipSuccess)
         return CAD_EHIP;
     if (stage(ST_NORM3, stream, [&] {
-            return launch_resid_norm(fd, wb.h1, wb.part, fd.down_slices, wb.h2, hidden_out, wb.u3, L->rms_eps,
+            return launch_resid_norm(fd, wb.h1, wb.part, fd.down_slices, wb.h2, hidden_out, wb.u3, last_only, L->rms_eps,
                                      wb.len_snap, stream);
         }) != hipSuccess)
         return CAD_EHIP;
-    // LM head + argmax partials, then the per-row reduction (+ commit of the cache lengths)
+    // LM head + argmax partials, then the per-row reduction (+ commit of the cache lengths).
+    // Copy-commit mode: u3 holds one row per sequence (row b = the sequence's last row).
     EpiParams pl = p;
-    pl.N = fd.V; pl.amax_part = wb.amax_part; pl.amax_slots = wb.amax_slots; pl.logits = logits_out;
+    const int lm_rows = last_only ? fd.B : fd.M;
+    pl.M = lm_rows; pl.Nq = last_only ? 1 : fd.Nq;
+    pl.N = fd.V; pl.amax_part = wb.amax_part; pl.amax_slots = last_only ? wb.amax_slots_last : wb.amax_slots;
+    pl.logits = logits_out;
     if (stage(ST_LM_HEAD, stream, [&] {
-            return launch_gemm(fd.dtype, EPI_ARGMAX, wb.u3, L->w_lm, fd.M, fd.V, fd.h, 1, pl, stream);
+            return launch_gemm(fd.dtype, EPI_ARGMAX, wb.u3, L->w_lm, lm_rows, fd.V, fd.h, 1, pl, stream);
         }) != hipSuccess)
         return CAD_EHIP;
     if (stage(ST_ARGMAX, stream, [&] {
-            return launch_argmax_final(fd, wb, argmax_out, (flags & CAD_COMMIT_ALL) ? kv->len : nullptr, stream);
+            return launch_argmax_final(fd, wb, last_only, argmax_out, (flags & CAD_COMMIT_ALL) ? kv->len : nullptr,
+                                       stream);
         }) != hipSuccess)
         return CAD_EHIP;
     return CAD_OK;

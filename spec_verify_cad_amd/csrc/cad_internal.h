@@ -50,6 +50,7 @@ struct RopeFreqs { double inv[64]; };
 struct FwdBufs {
     int32_t* len_snap;
     float2* amax_part; int amax_slots;
+    int amax_slots_last;            // slots per row of an LM head over one row per sequence
     float2* rope_cs;
     float* x; void* u; void* q; void* o;
     float* part_o; float* part_ml;
@@ -68,10 +69,13 @@ int device_cu_count();
 hipError_t launch_embed_norm(const FwdDims& fd, const int32_t* tokens, const void* embed, float eps,
                              const RopeFreqs& freqs, const int32_t* kv_len, int32_t* err, const FwdBufs& wb,
                              hipStream_t s);
-hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, int32_t* argmax_out, int32_t* kv_len,
-                               hipStream_t s);
+// argmax over the LM head's slots of `rows` rows: all M rows, or (last_only) one per sequence
+hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, bool last_only, int32_t* argmax_out,
+                               int32_t* kv_len, hipStream_t s);
+// normed rows are written for every row, or (last_only) compactly for each sequence's last row
 hipError_t launch_resid_norm(const FwdDims& fd, const float* base, const float* part, int slices, float* out_f32,
-                             void* out_t, void* normed, float eps, const int32_t* len_snap, hipStream_t s);
+                             void* out_t, void* normed, bool last_only, float eps, const int32_t* len_snap,
+                             hipStream_t s);
 // Projection GEMM Y[M, N] = A[M, K] . W[N, K]^T with a fused epilogue; picks the kernel
 // (weight-streaming for few rows, LDS-tiled MFMA otherwise) and its K slicing.  For
 // EPI_PARTIAL `slices` gives the number of K slices (p.k_slice is filled in).

@@ -105,8 +105,9 @@ constexpr int RN_NT = 512;
 template <typename T, int SB>
 __global__ __launch_bounds__(RN_NT) void k_resid_norm(const float* __restrict__ base, const float* __restrict__ part,
                                                       int slices, int M, int h, int Nq, int cap, float eps,
-                                                      const int32_t* __restrict__ len_snap, float* __restrict__ out,
-                                                      T* __restrict__ out_t, T* __restrict__ normed) {
+                                                      int last_only, const int32_t* __restrict__ len_snap,
+                                                      float* __restrict__ out, T* __restrict__ out_t,
+                                                      T* __restrict__ normed) {
     __shared__ float red[RN_NT / 64];
     extern __shared__ float4 rowbuf4[];          // [h / 4]
     const int r = blockIdx.x;
@@ -147,17 +148,20 @@ __global__ __launch_bounds__(RN_NT) void k_resid_norm(const float* __restrict__ 
 #pragma unroll
     for (int w = 0; w < RN_NT / 64; ++w) t += red[w];
     const float scale = 1.0f / sqrtf(t / (float)h + eps);
+    if (last_only && r % Nq != Nq - 1) return;
+    const size_t nrow = last_only ? (size_t)(r / Nq) : (size_t)r;   // compact: one row per sequence
     for (int j4 = threadIdx.x; j4 < h4; j4 += RN_NT) {
         const float4 o = rowbuf4[j4];
-        st4v(normed + (size_t)r * h + 4 * (size_t)j4, make_float4(o.x * scale, o.y * scale, o.z * scale, o.w * scale));
+        st4v(normed + nrow * h + 4 * (size_t)j4, make_float4(o.x * scale, o.y * scale, o.z * scale, o.w * scale));
     }
 }
 
-// One wave per row.  Row r of sequence b = r / Nq; the wave of the sequence's first row commits.
-__global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ part, int slots, int Nq, int cap,
-                                                     const int32_t* __restrict__ len_snap, int32_t* __restrict__ out,
-                                                     int32_t* __restrict__ kv_len) {
-    const int r = blockIdx.x, b = r / Nq;
+// One wave per row.  The LM head ran on rps rows per sequence (Nq, or 1 for the last row only):
+// row r belongs to sequence b = r / rps, and the wave of the sequence's first row commits.
+__global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ part, int slots, int rps, int Nq,
+                                                     int cap, const int32_t* __restrict__ len_snap,
+                                                     int32_t* __restrict__ out, int32_t* __restrict__ kv_len) {
+    const int r = blockIdx.x, b = r / rps;
     if (!seq_ok(len_snap, b, Nq, cap)) return;
     float best = -INFINITY;
     int bi = 0x7fffffff;
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ 
     }
     if (threadIdx.x == 0) {
         out[r] = bi;
-        if (kv_len && r % Nq == 0) kv_len[b] = len_snap[b] + Nq;
+        if (kv_len && r % rps == 0) kv_len[b] = len_snap[b] + Nq;
     }
 }
 
@@ -201,30 +205,35 @@ hipError_t launch_embed_norm(const FwdDims& fd, const int32_t* tokens, const voi
 
 template <typename T, int SB>
 static void resid_norm_go(const FwdDims& fd, const float* base, const float* part, int slices, float* out_f32,
-                          void* out_t, void* normed, float eps, const int32_t* len_snap, hipStream_t s) {
+                          void* out_t, void* normed, int last, float eps, const int32_t* len_snap, hipStream_t s) {
     const size_t smem = (size_t)fd.h * sizeof(float);
     hipLaunchKernelGGL((k_resid_norm<T, SB>), dim3(fd.M), dim3(RN_NT), smem, s, base, part, slices, fd.M, fd.h,
-                       fd.Nq, fd.cap, eps, len_snap, out_f32, (T*)out_t, (T*)normed);
+                       fd.Nq, fd.cap, eps, last, len_snap, out_f32, (T*)out_t, (T*)normed);
 }
 
 template <typename T>
 static void resid_norm_t(const FwdDims& fd, const float* base, const float* part, int slices, float* out_f32,
-                         void* out_t, void* normed, float eps, const int32_t* len_snap, hipStream_t s) {
-    if (slices <= 4) resid_norm_go<T, 4>(fd, base, part, slices, out_f32, out_t, normed, eps, len_snap, s);
-    else if (slices <= 8) resid_norm_go<T, 8>(fd, base, part, slices, out_f32, out_t, normed, eps, len_snap, s);
-    else resid_norm_go<T, 16>(fd, base, part, slices, out_f32, out_t, normed, eps, len_snap, s);
+                         void* out_t, void* normed, int last, float eps, const int32_t* len_snap, hipStream_t s) {
+    if (slices <= 4) resid_norm_go<T, 4>(fd, base, part, slices, out_f32, out_t, normed, last, eps, len_snap, s);
+    else if (slices <= 8) resid_norm_go<T, 8>(fd, base, part, slices, out_f32, out_t, normed, last, eps, len_snap, s);
+    else resid_norm_go<T, 16>(fd, base, part, slices, out_f32, out_t, normed, last, eps, len_snap, s);
 }
 
 hipError_t launch_resid_norm(const FwdDims& fd, const float* base, const float* part, int slices, float* out_f32,
-                             void* out_t, void* normed, float eps, const int32_t* len_snap, hipStream_t s) {
-    if (fd.dtype == CAD_DTYPE_F32) resid_norm_t<float>(fd, base, part, slices, out_f32, out_t, normed, eps, len_snap, s);
-    else resid_norm_t<uint16_t>(fd, base, part, slices, out_f32, out_t, normed, eps, len_snap, s);
+                             void* out_t, void* normed, bool last_only, float eps, const int32_t* len_snap,
+                             hipStream_t s) {
+    const int last = last_only ? 1 : 0;
+    if (fd.dtype == CAD_DTYPE_F32)
+        resid_norm_t<float>(fd, base, part, slices, out_f32, out_t, normed, last, eps, len_snap, s);
+    else resid_norm_t<uint16_t>(fd, base, part, slices, out_f32, out_t, normed, last, eps, len_snap, s);
     return hipGetLastError();
 }
 
-hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, int32_t* argmax_out, int32_t* kv_len,
-                               hipStream_t s) {
-    hipLaunchKernelGGL(k_argmax_final, dim3(fd.M), dim3(64), 0, s, wb.amax_part, wb.amax_slots, fd.Nq, fd.cap,
+hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, bool last_only, int32_t* argmax_out,
+                               int32_t* kv_len, hipStream_t s) {
+    const int rps = last_only ? 1 : fd.Nq;
+    const int slots = last_only ? wb.amax_slots_last : wb.amax_slots;
+    hipLaunchKernelGGL(k_argmax_final, dim3(fd.B * rps), dim3(64), 0, s, wb.amax_part, slots, rps, fd.Nq, fd.cap,
                        wb.len_snap, argmax_out, kv_len);
     return hipGetLastError();
 }

@@ -74,6 +74,19 @@ def test_copy_span_sweep_full_size(qwen15):
         c2 = oc.copy()
         O.span_forward(OL, c2, toks)
         compare_cache(cache, 0, c2, L0, L0 + N, "bf16", what=f"N={N} committed rows")
+        # copy-commit mode: the same commit with the LM head for the last row only
+        cache.len.fill_(L0)
+        am = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+        lg = torch.zeros((1, wl.shape.vocab), dtype=torch.float32, device="cuda")
+        cad.span_forward(dl, cache, T32(toks[None]), N, flags=cad.COMMIT_ALL | cad.LOGITS_LAST, argmax_out=am,
+                         logits_out=lg)
+        torch.cuda.synchronize()
+        assert int(cache.len[0]) == L0 + N
+        last = {k: ref[k][N - 1:N] for k in ("logits", "argmax", "top2_gap")}
+        g_l = lg.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(g_l - last["logits"])) <= logit_tol(wl.shape.hidden), f"N={N} copy-commit logits"
+        argmax_check(am.cpu().numpy(), last, g_l, what=f"N={N} copy-commit", tol=logit_tol(wl.shape.hidden))
+        compare_cache(cache, 0, c2, L0, L0 + N, "bf16", what=f"N={N} copy-commit rows")
 
 
 # ---------------------------------------------------------------------------------------------

@@ -8,7 +8,8 @@ from spec_verify_cad_amd import cad, synth
 from spec_verify_cad_amd.configs import CONFIGS, SMALL, TINY
 from spec_verify_cad_amd.synth import LayerShape
 
-from gpu_util import (compare, compare_cache, log, prefill, run_forward, to_f64, upload_oracle_cache)
+from gpu_util import (LOGIT_TOL, argmax_check, compare, compare_cache, hidden_tol, log, prefill, run_forward, to_f64,
+                      upload_oracle_cache)
 from helpers import oracle_layer
 
 pytestmark = pytest.mark.gpu
@@ -215,6 +216,48 @@ def test_small_bf16_span_matches_oracle(small, Nq):
         ref = O.span_forward(OL, oc, span[b])
         compare(g, ref, rows=slice(b * Nq, (b + 1) * Nq), what=f"b={b}")
         compare_cache(cache, b, oc, L0, L0 + Nq, "bf16", what=f"span rows b={b}")
+
+
+@pytest.mark.parametrize("Nq", [1, 13, 40])
+def test_small_bf16_copy_commit_last_row_matches_oracle(small, Nq):
+    """Copy-commit mode (CAD_LOGITS_LAST): the LM head and argmax run for each sequence's last
+    row only; the cache rows, hidden output and commit are those of the full forward."""
+    w, dl, OL = small
+    log(f"small bf16 copy-commit Nq={Nq}")
+    B, L0, cap = 3, 150, 320
+    ctx = np.stack([synth.uniform_tokens(50 + b, L0, SMALL.vocab) for b in range(B)])
+    span = np.stack([synth.uniform_tokens(70 + b, Nq, SMALL.vocab) for b in range(B)])
+    cache = cad.DeviceCache(SMALL, B, cap)
+    prefill(dl, cache, ctx, chunk=64)
+    t = torch.from_numpy(np.ascontiguousarray(span, dtype=np.int32)).cuda()
+    am = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    hid = torch.zeros((B * Nq, SMALL.hidden), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((B, SMALL.vocab), dtype=torch.float32, device="cuda")
+    cad.span_forward(dl, cache, t, Nq, flags=cad.COMMIT_ALL | cad.LOGITS_LAST, argmax_out=am, hidden_out=hid,
+                     logits_out=lg)
+    torch.cuda.synchronize()
+    assert list(cache.len.cpu().numpy()) == [L0 + Nq] * B
+    g_a, g_h, g_l = am.cpu().numpy(), to_f64(hid, "bf16"), lg.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        oc = O.cache_from_tokens(OL, ctx[b], cap)
+        ref = O.span_forward(OL, oc, span[b])
+        rows = slice(b * Nq, (b + 1) * Nq)
+        dh = np.abs(g_h[rows] - ref["hidden_out"])
+        assert (dh <= hidden_tol(ref["hidden_out"], SMALL.ffn)).all(), f"b={b} hidden {dh.max()}"
+        last = {k: ref[k][Nq - 1:Nq] for k in ("logits", "argmax", "top2_gap")}
+        dl_ = np.max(np.abs(g_l[b:b + 1] - last["logits"]))
+        assert dl_ <= LOGIT_TOL, f"b={b} last-row logits {dl_}"
+        argmax_check(g_a[b:b + 1], last, g_l[b:b + 1], what=f"copy-commit b={b}")
+        compare_cache(cache, b, oc, L0, L0 + Nq, "bf16", what=f"copy-commit rows b={b}")
+
+
+def test_copy_commit_mode_rejects_the_block_mask(small):
+    w, dl, OL = small
+    cache = cad.DeviceCache(SMALL, 1, 64)
+    t = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    am = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(cad.CadError):
+        cad.span_forward(dl, cache, t, 8, mode=cad.MASK_BLOCK, W=2, D=4, flags=cad.LOGITS_LAST, argmax_out=am)
 
 
 def test_small_bf16_block_verify_matches_oracle(small):
