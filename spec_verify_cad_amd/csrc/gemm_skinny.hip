@@ -1,4 +1,4 @@
-// Weight-streaming projection GEMM for few token rows (M <= 32): Y[M, N] = A[M, K] . W[N, K]^T.
+// Weight-streaming projection GEMM for few token rows (M <= 64): Y[M, N] = A[M, K] . W[N, K]^T.
 //
 // With a handful of rows every weight is used by at most 32 multiply-adds, so the kernel is a
 // pure stream of W from HBM: nothing of W goes through LDS.  A unit of work is one 16-feature
@@ -239,24 +239,36 @@ hipError_t go(const void* A, const void* W, int M, int N, int K, int ntiles, int
     return hipGetLastError();
 }
 
-// Variant for a full-K epilogue: the K of one unit must cover all of K.
+// Variant for a full-K epilogue: the K of one unit must cover all of K.  With 64 token rows
+// (TT = 4) the token fragments take 4x the registers, so the slice is spread over 8 waves of
+// 3 super-steps (K <= 1536).
 template <int KIND, int TT>
 hipError_t go_full(const void* A, const void* W, int M, int N, int K, int ntiles, const EpiParams& p, hipStream_t s) {
-    if (K <= 4 * 6 * 64) return go<KIND, TT, 6, 4>(A, W, M, N, K, ntiles, 1, p, s);
-    if (K <= 8 * 7 * 64) return go<KIND, TT, 7, 8>(A, W, M, N, K, ntiles, 1, p, s);
-    return hipErrorInvalidValue;
+    if constexpr (TT == 4) {
+        if (K <= 8 * 3 * 64) return go<KIND, 4, 3, 8>(A, W, M, N, K, ntiles, 1, p, s);
+        return hipErrorInvalidValue;
+    } else {
+        if (K <= 4 * 6 * 64) return go<KIND, TT, 6, 4>(A, W, M, N, K, ntiles, 1, p, s);
+        if (K <= 8 * 7 * 64) return go<KIND, TT, 7, 8>(A, W, M, N, K, ntiles, 1, p, s);
+        return hipErrorInvalidValue;
+    }
 }
 
 template <int KIND, int TT>
 int full_grid(int K, int ntiles) {
-    if (K <= 4 * 6 * 64) return skinny_grid<KIND, TT, 6, 4, false>(ntiles, 1);
-    return skinny_grid<KIND, TT, 7, 8, false>(ntiles, 1);
+    if constexpr (TT == 4) {
+        return skinny_grid<KIND, 4, 3, 8, false>(ntiles, 1);
+    } else {
+        if (K <= 4 * 6 * 64) return skinny_grid<KIND, TT, 6, 4, false>(ntiles, 1);
+        return skinny_grid<KIND, TT, 7, 8, false>(ntiles, 1);
+    }
 }
 
 }  // namespace
 
 int skinny_argmax_slots(int M, int N, int K) {
     const int nt = (N + 15) / 16;
+    if (M > 32) return full_grid<EPI_ARGMAX, 4>(K, nt);
     return M > 16 ? full_grid<EPI_ARGMAX, 2>(K, nt) : full_grid<EPI_ARGMAX, 1>(K, nt);
 }
 
@@ -264,34 +276,33 @@ constexpr int kSkinnyPartialSlice = 4 * 3 * 64;   // K per slice of the partial-
 
 int skinny_partial_slices(int K) { return (K + kSkinnyPartialSlice - 1) / kSkinnyPartialSlice; }
 
+// Rows 33..64 take the 8-wave, 3-super-step variant (one workgroup per CU); for the LM head that
+// measured slower than the LDS-tiled kernel, so only the layer's projections use it.
 bool skinny_supports(int kind, int M, int K) {
-    if (M > 32) return false;
+    if (M > 64 || (M > 32 && kind == EPI_ARGMAX)) return false;
     if (kind == EPI_PARTIAL) return true;
-    return K <= 8 * 7 * 64;
+    return K <= (M > 32 ? 8 * 3 * 64 : 8 * 7 * 64);
+}
+
+template <int KIND>
+static hipError_t full_tt(const void* A, const void* W, int M, int N, int K, int nt, const EpiParams& p,
+                          hipStream_t s) {
+    if (M > 32) return go_full<KIND, 4>(A, W, M, N, K, nt, p, s);
+    if (M > 16) return go_full<KIND, 2>(A, W, M, N, K, nt, p, s);
+    return go_full<KIND, 1>(A, W, M, N, K, nt, p, s);
 }
 
 hipError_t launch_skinny(int kind, const void* A, const void* W, int M, int N, int K, const EpiParams& p,
                          hipStream_t s) {
-    const bool two = M > 16;
     switch (kind) {
-        case EPI_QKV: {
-            const int nt = N / 16;
-            return two ? go_full<EPI_QKV, 2>(A, W, M, N, K, nt, p, s) : go_full<EPI_QKV, 1>(A, W, M, N, K, nt, p, s);
-        }
-        case EPI_SWIGLU: {
-            const int nt = (p.ffn + 7) / 8;
-            return two ? go_full<EPI_SWIGLU, 2>(A, W, M, N, K, nt, p, s)
-                       : go_full<EPI_SWIGLU, 1>(A, W, M, N, K, nt, p, s);
-        }
-        case EPI_ARGMAX: {
-            const int nt = (N + 15) / 16;
-            return two ? go_full<EPI_ARGMAX, 2>(A, W, M, N, K, nt, p, s)
-                       : go_full<EPI_ARGMAX, 1>(A, W, M, N, K, nt, p, s);
-        }
+        case EPI_QKV: return full_tt<EPI_QKV>(A, W, M, N, K, N / 16, p, s);
+        case EPI_SWIGLU: return full_tt<EPI_SWIGLU>(A, W, M, N, K, (p.ffn + 7) / 8, p, s);
+        case EPI_ARGMAX: return full_tt<EPI_ARGMAX>(A, W, M, N, K, (N + 15) / 16, p, s);
         default: {
             const int nt = (N + 15) / 16, S = skinny_partial_slices(K);
-            return two ? go<EPI_PARTIAL, 2, 3, 4>(A, W, M, N, K, nt, S, p, s)
-                       : go<EPI_PARTIAL, 1, 3, 4>(A, W, M, N, K, nt, S, p, s);
+            if (M > 32) return go<EPI_PARTIAL, 4, 3, 4>(A, W, M, N, K, nt, S, p, s);
+            if (M > 16) return go<EPI_PARTIAL, 2, 3, 4>(A, W, M, N, K, nt, S, p, s);
+            return go<EPI_PARTIAL, 1, 3, 4>(A, W, M, N, K, nt, S, p, s);
         }
     }
 }
