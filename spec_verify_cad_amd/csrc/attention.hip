@@ -459,19 +459,27 @@ bool mfma_path(const FwdDims& fd) { return !(fd.dtype == CAD_DTYPE_F32 || (fd.d 
 
 }  // namespace
 
-// Split plan of the MFMA path: 64-row tiles of each GQA group and enough key splits for about
-// two workgroups per CU (each split at least 64 keys of a full cache); the keys of a split
-// follow from the sequence's length on the device.
+// Split plan of the MFMA path: 64-row tiles of each GQA group and key splits: with few row tiles
+// enough splits to fill the chip (each at least one 64-key tile of a full cache), otherwise as
+// many as keep every workgroup resident (two per CU), at most 8.  The keys of a split follow
+// from the sequence's length on the device.
 void attention_plan(FwdDims* fd, int cus) {
     const int G = fd->Hq / fd->Hkv, Rg = fd->Nq * G;
     fd->attn_rows_per_wg = WAVES * 16;
     fd->attn_row_tiles = (Rg + fd->attn_rows_per_wg - 1) / fd->attn_rows_per_wg;
     const long units = (long)fd->B * fd->Hkv * fd->attn_row_tiles;
-    const long want = 2L * cus;
-    long splits = (want + units - 1) / units;
-    const long most = (fd->cap + fd->Nq + 63) / 64;       // splits of at least 64 keys
-    if (splits > most) splits = most;
-    if (splits > 256) splits = 256;                      // the merge holds at most 256 split weights
+    const long want = 2L * cus;                          // resident workgroups (two per CU)
+    long splits = want / units;
+    if (splits > 24) {
+        // few row tiles (small spans): as many splits as fill the chip, the merge is cheap
+        splits = (want + units - 1) / units;
+        const long most = (fd->cap + fd->Nq + 63) / 64;  // splits of at least one 64-key tile
+        if (splits > most) splits = most;
+        if (splits > 256) splits = 256;                  // the merge holds at most 256 split weights
+    } else if (splits > 8) {
+        splits = 8;                                      // the merge without LDS takes up to 8
+    }
+    // (never more workgroups than stay resident: a second, nearly empty round costs a whole one)
     if (splits < 1) splits = 1;
     fd->attn_splits = (int)splits;
     fd->attn_chunk = 0;                                  // per sequence, from its length, on the device
