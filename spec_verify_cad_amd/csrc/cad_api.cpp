@@ -12,11 +12,11 @@ namespace {
 // ---- opt-in per-stage profiler (diagnostics) ----
 enum Stage {
     ST_EMBED_NORM, ST_QKV, ST_ATTN, ST_ATTN_MERGE, ST_O_PROJ, ST_NORM2, ST_GATE_UP, ST_DOWN, ST_NORM3, ST_LM_HEAD,
-    ST_ARGMAX, ST_COMMIT, ST_COUNT
+    ST_ARGMAX, ST_COMMIT, ST_QKV_FINISH, ST_COUNT
 };
 const char* kStageNames[ST_COUNT] = {"embed_norm", "qkv_rope_append", "attention", "attention_merge", "o_proj",
                                      "resid_rmsnorm_2", "gate_up_swiglu", "down_proj", "resid_rmsnorm_final",
-                                     "lm_head_argmax", "argmax_final_commit", "commit"};
+                                     "lm_head_argmax", "argmax_final_commit", "commit", "qkv_rope_append_rows"};
 struct ProfRec { int stage; hipEvent_t a, b; };
 bool g_prof = false;
 std::vector<ProfRec> g_recs;
@@ -82,6 +82,10 @@ bool fwd_dims(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, in
     fd->qkv_n = (fd->Hq + 2 * fd->Hkv) * fd->d;
     fd->o_slices = gemm_partial_slices(fd->dtype, fd->M, fd->h, fd->Hq * fd->d);
     fd->down_slices = gemm_partial_slices(fd->dtype, fd->M, fd->h, fd->ffn);
+    if (gemm_qkv_split(fd->dtype, fd->M, fd->h)) {
+        fd->qkv_slices = gemm_partial_slices(fd->dtype, fd->M, fd->qkv_n, fd->h);
+        fd->kv_slices = gemm_partial_slices(fd->dtype, fd->M, 2 * fd->Hkv * fd->d, fd->h);
+    }
     attention_plan(fd, device_cu_count());
     return true;
 }
@@ -100,6 +104,10 @@ FwdBufs fwd_carve(const FwdDims& fd, void* base, bool kv_only) {
     w.len_snap = (int32_t*)take(fd.B * sizeof(int32_t));
     w.rope_cs = (float2*)take(M * (size_t)(fd.d / 2) * sizeof(float2));
     w.u = take(M * h * e);
+    if (fd.qkv_slices) {
+        const size_t full = (size_t)fd.qkv_slices * fd.qkv_n, kv = (size_t)fd.kv_slices * 2 * fd.Hkv * fd.d;
+        w.qkv_part = (float*)take(M * (kv_only ? kv : std::max(full, kv)) * 4);
+    }
     if (!kv_only) {
         w.amax_slots = gemm_argmax_slots(fd.dtype, fd.M, fd.V, fd.h);
         w.amax_slots_last = gemm_argmax_slots(fd.dtype, fd.B, fd.V, fd.h);
@@ -232,10 +240,23 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
             N = 2 * fd.Hkv * fd.d;
         }
         pq.N = N;
-        if (stage(ST_QKV, stream, [&] {
-                return launch_gemm(fd.dtype, EPI_QKV, wb.u, w, fd.M, N, fd.h, 1, pq, stream);
-            }) != hipSuccess)
+        if (fd.qkv_slices) {
+            // split form: K-slice partials, then RoPE + K/V append per row
+            const int S = kv_only ? fd.kv_slices : fd.qkv_slices;
+            pq.part = wb.qkv_part;
+            if (stage(ST_QKV, stream, [&] {
+                    return launch_gemm(fd.dtype, EPI_PARTIAL, wb.u, w, fd.M, N, fd.h, S, pq, stream);
+                }) != hipSuccess)
+                return CAD_EHIP;
+            if (stage(ST_QKV_FINISH, stream, [&] {
+                    return launch_qkv_finish(fd, wb.qkv_part, S, N, pq.head_off, wb, kv->k, kv->v, stream);
+                }) != hipSuccess)
+                return CAD_EHIP;
+        } else if (stage(ST_QKV, stream, [&] {
+                       return launch_gemm(fd.dtype, EPI_QKV, wb.u, w, fd.M, N, fd.h, 1, pq, stream);
+                   }) != hipSuccess) {
             return CAD_EHIP;
+        }
     }
     if (kv_only) {
         if ((flags & CAD_COMMIT_ALL) &&

@@ -41,6 +41,7 @@ struct FwdDims {
     int qkv_n;
     int attn_splits, attn_chunk, attn_rows_per_wg, attn_row_tiles;
     int o_slices, down_slices;      // K slices of the O and down projections (partials)
+    int qkv_slices, kv_slices;      // K slices of a split QKV projection (all heads / K,V heads), 0 if not split
 };
 
 // Rotary inverse frequencies base^(-2i/d), i < d/2, computed in double on the host.
@@ -56,6 +57,7 @@ struct FwdBufs {
     float* part_o; float* part_ml;
     float* h1; void* u2; void* act; float* h2; void* u3;
     float* part;                    // K-slice partials of the O and down projections
+    float* qkv_part;                // K-slice partials of a split QKV projection
     size_t total;
 };
 
@@ -82,6 +84,11 @@ hipError_t launch_resid_norm(const FwdDims& fd, const float* base, const float* 
 hipError_t launch_gemm(int dtype, int kind, const void* A, const void* W, int M, int N, int K, int slices,
                        EpiParams p, hipStream_t s);
 int gemm_partial_slices(int dtype, int M, int N, int K);
+bool gemm_qkv_split(int dtype, int M, int K);
+// RoPE + K/V append from the QKV projection's K-slice partials (the split form of EPI_QKV):
+// row r, produced columns [0, N) = heads head_off .. head_off + N/d - 1
+hipError_t launch_qkv_finish(const FwdDims& fd, const float* part, int slices, int N, int head_off,
+                             const FwdBufs& wb, void* kc, void* vc, hipStream_t s);
 // (max, index) partial slots per row written by an EPI_ARGMAX launch of this shape
 int gemm_argmax_slots(int dtype, int M, int N, int K);
 void attention_plan(FwdDims* fd, int cus);

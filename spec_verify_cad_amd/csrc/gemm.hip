@@ -204,6 +204,12 @@ int gemm_partial_slices(int dtype, int M, int N, int K) {
     return big_partial_slices(M, N, K, device_cu_count());
 }
 
+// A bf16 QKV projection the weight-streaming kernel does not take runs as K-slice partials plus
+// a row kernel for RoPE and the K/V append: its output is too narrow to fill the chip otherwise.
+bool gemm_qkv_split(int dtype, int M, int K) {
+    return dtype == CAD_DTYPE_BF16 && !skinny_supports(EPI_QKV, M, K);
+}
+
 hipError_t launch_gemm(int dtype, int kind, const void* A, const void* W, int M, int N, int K, int slices,
                        EpiParams p, hipStream_t s) {
     if (dtype == CAD_DTYPE_BF16) {

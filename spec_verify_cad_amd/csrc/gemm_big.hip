@@ -346,12 +346,14 @@ hipError_t go_big(const void* A, const void* W, int M, int N, int K, int ffn, co
 // Tile choice: 256 features per workgroup tile (two waves of 128 across it); 64, 128 or 256
 // tokens.  The narrow QKV projection and the K-slice partial projections take 128 x 64 tiles
 // (one wave of 128 features, so a QKV wave holds whole heads of up to 128 dims) to spread over
-// more workgroups.
+// more workgroups; so does the gate/up projection up to 256 rows (measured on the 1.5B shape:
+// 256 x 64 tiles are best up to 128 rows, 128 x 64 up to 256, 256 x 256 beyond).
 BigPlan big_plan(int kind, int M, int N, int K, int slices) {
     BigPlan t;
     t.BN = 256;
     t.BM = M <= 64 ? 64 : M <= 128 ? 128 : 256;
-    if (kind == EPI_QKV || kind == EPI_PARTIAL) {
+    if (kind == EPI_SWIGLU && M <= 128) t.BM = 64;     // more workgroups for the gate/up pairs
+    if (kind == EPI_QKV || kind == EPI_PARTIAL || (kind == EPI_SWIGLU && M > 128 && M <= 256)) {
         // narrow outputs: 128 x 64 tiles give more workgroups (and QKV one head per wave); for the
         // K-slice partials they also mean fewer slices, so less partial traffic for the row
         // kernel that adds them

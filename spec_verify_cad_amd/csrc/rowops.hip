@@ -156,6 +156,56 @@ __global__ __launch_bounds__(RN_NT) void k_resid_norm(const float* __restrict__ 
     }
 }
 
+// The split form of the QKV epilogue: one workgroup per row r (token it of sequence b).  Each
+// thread takes four consecutive rotation pairs (i, i + d/2) of one produced head, adds the K-slice
+// partials in slice order, rotates q and k with the row's (cos, sin) and stores q to the
+// workspace, k to cache slot len + it and v (unrotated) to the dim-major cache.
+__global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ part, int slices, int M, int N,
+                                                    int head_off, int Hq, int Hkv, int d, int Nq, int cap,
+                                                    const int32_t* __restrict__ len_snap,
+                                                    const float2* __restrict__ rope_cs, uint16_t* __restrict__ q_out,
+                                                    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
+    const int r = blockIdx.x, b = r / Nq, it = r % Nq;
+    if (!seq_ok(len_snap, b, Nq, cap)) return;
+    const size_t slot = (size_t)len_snap[b] + it;
+    const int half = d / 2, groups = N / 8;               // 4 pairs per group, N/2 pairs per row
+    const size_t sstride = (size_t)M * N;
+    for (int gi = threadIdx.x; gi < groups; gi += 256) {
+        const int hl = gi / (half / 4), i0 = (gi % (half / 4)) * 4;
+        const size_t c1 = (size_t)r * N + (size_t)hl * d + i0;
+        float4 x1 = make_float4(0.f, 0.f, 0.f, 0.f), x2 = x1;
+        for (int sl = 0; sl < slices; ++sl) {             // slice order
+            const float4 a = *(const float4*)(part + sl * sstride + c1);
+            const float4 c = *(const float4*)(part + sl * sstride + c1 + half);
+            x1.x += a.x; x1.y += a.y; x1.z += a.z; x1.w += a.w;
+            x2.x += c.x; x2.y += c.y; x2.z += c.z; x2.w += c.w;
+        }
+        const int head = hl + head_off;
+        const float v1[4] = {x1.x, x1.y, x1.z, x1.w}, v2[4] = {x2.x, x2.y, x2.z, x2.w};
+        if (head >= Hq + Hkv) {                           // V: dim-major cache, stored unrotated
+            uint16_t* vp = vc + (((size_t)b * Hkv + (head - Hq - Hkv)) * d + i0) * cap + slot;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vp[(size_t)i * cap] = f32_to_bf16(v1[i]);
+                vp[(size_t)(i + half) * cap] = f32_to_bf16(v2[i]);
+            }
+            continue;
+        }
+        const float2* cs = rope_cs + (size_t)r * half + i0;
+        f32x4_t y1, y2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float2 t = cs[i];
+            y1[i] = v1[i] * t.x - v2[i] * t.y;
+            y2[i] = v2[i] * t.x + v1[i] * t.y;
+        }
+        uint16_t* dst = head < Hq ? q_out + ((size_t)r * Hq + head) * d
+                                  : kc + (((size_t)b * Hkv + (head - Hq)) * cap + slot) * d;
+        st4(dst + i0, y1);
+        st4(dst + i0 + half, y2);
+    }
+}
+
 // One wave per row.  The LM head ran on rps rows per sequence (Nq, or 1 for the last row only):
 // row r belongs to sequence b = r / rps, and the wave of the sequence's first row commits.
 __global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ part, int slots, int rps, int Nq,
@@ -240,5 +290,12 @@ hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, bool last_o
 
 hipError_t launch_commit(const FwdDims& fd, const FwdBufs& wb, int32_t* kv_len, hipStream_t s) {
     hipLaunchKernelGGL(k_commit, dim3((fd.B + 255) / 256), dim3(256), 0, s, wb.len_snap, fd.B, fd.Nq, fd.cap, kv_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_qkv_finish(const FwdDims& fd, const float* part, int slices, int N, int head_off,
+                             const FwdBufs& wb, void* kc, void* vc, hipStream_t s) {
+    hipLaunchKernelGGL(k_qkv_finish, dim3(fd.M), dim3(256), 0, s, part, slices, fd.M, N, head_off, fd.Hq, fd.Hkv,
+                       fd.d, fd.Nq, fd.cap, wb.len_snap, wb.rope_cs, (uint16_t*)wb.q, (uint16_t*)kc, (uint16_t*)vc);
     return hipGetLastError();
 }
