@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--ar-steps", type=int, default=64)
+    ap.add_argument("--no-pld", action="store_true", help="skip the batched PLD round measurement")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="no timing: a few N = ROOF_N forwards and plain copies of a known size, for a "
                          "hardware-counter run that calibrates and measures the LM head's HBM traffic")
@@ -222,6 +223,9 @@ def main():
                    "unit": "committed tokens/s", "ms_per_step": round(ms_last, 4), "per_n": last_per_n}
     log(f"copy-commit sweep {ms_last * 1e3:.1f} us -> {copy_commit['value']:.0f} committed tok/s")
 
+    # ---- batched PLD rounds (lookup -> verify forward -> accept, no host sync inside)
+    pld = None if a.no_pld else pld_rounds(a, lay0, dev)
+
     # ---- autoregressive baseline: single-token teacher-forced forwards
     ar_us = timed(ar_graphs, max(2, a.steps // 4)) * 1e3 / a.ar_steps
     for r in per_n:
@@ -260,9 +264,98 @@ def main():
         "ar_baseline": {"us_per_token": round(ar_us, 2), "tok_s": round(1e6 / ar_us, 1), "floor_us": round(ar_floor, 2)},
         "roofline": roof,
         "copy_commit_mode": copy_commit,
+        "pld_rounds": pld,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def pld_rounds(a, layer, dev):
+    """Batched prompt-lookup decoding on the 1.5B-shaped layer: 64 sequences with 32768-token
+    histories (planted copies + Zipf background), 32 rounds of n-gram lookup (n = 3, one
+    candidate of k = 10), an 11-row verify forward over each sequence's cache, and the accept
+    scan that appends a + 1 tokens to the history and commits the cache, all enqueued without
+    a host sync and replayed from a HIP graph.  Reported per round and per second."""
+    import numpy as np
+    import torch
+
+    from spec_verify_cad_amd import cad
+    from spec_verify_cad_amd import roofline as R
+    from spec_verify_cad_amd.configs import CONFIGS, pld_contexts
+
+    wl = CONFIGS["qwen15_pld_batch"]
+    e = wl.extra
+    B, Lc, n, k, rounds = e["B"], e["ctx_len"], e["n"], e["k"], e["rounds"]
+    t0 = time.time()
+    ctxs = pld_contexts(wl)
+    stride = Lc + rounds * (k + 1) + 8
+    hist_np = np.zeros((B, stride), dtype=np.int32)
+    hist_np[:, :Lc] = ctxs
+    hist = torch.from_numpy(hist_np).to(dev)
+    hlen = torch.full((B,), Lc, dtype=torch.int32, device=dev)
+    cache = cad.DeviceCache(wl.shape, B, stride)
+    pre = torch.from_numpy(np.ascontiguousarray(ctxs[:, :Lc - 1])).to(dev)
+    for s0 in range(0, Lc - 1, 2048):
+        blk = pre[:, s0:s0 + 2048].contiguous()
+        cad.span_forward(layer, cache, blk, blk.shape[1], flags=cad.KV_ONLY | cad.COMMIT_ALL)
+    torch.cuda.synchronize()
+    log(f"pld: contexts and 64 x {Lc - 1} prefill in {time.time() - t0:.1f}s")
+    rows = torch.zeros((B, 1 + k), dtype=torch.int32, device=dev)
+    dlen = torch.zeros((B, 1), dtype=torch.int32, device=dev)
+    am = torch.zeros((B, 1 + k), dtype=torch.int32, device=dev)
+    acc, ne = (torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2))
+    em = torch.zeros((B, k + 1), dtype=torch.int32, device=dev)
+    ws = cad.alloc_workspace(cad.span_forward_workspace(layer, B, 1 + k, cad.MASK_CAUSAL, 1, 1, stride, 0))
+
+    def reset(st):
+        hlen.fill_(Lc)
+        cache.len.fill_(Lc - 1)
+
+    def run(st):
+        for _ in range(rounds):
+            cad.ngram_lookup(hist, hlen, n, 1, k, 1, rows, dlen, stream=st)
+            cad.span_forward(layer, cache, rows, 1 + k, argmax_out=am, workspace=ws, stream=st)
+            cad.accept_scan(rows, 1, dlen, am, None, B, 1, k, cad.MASK_CAUSAL, acc, None, em, ne, ctx=hist,
+                            ctx_len=hlen, ctx_cap=stride, cache=cache, stream=st)
+
+    st = torch.cuda.current_stream()
+    reset(st)
+    run(st)                                              # eager warm-up
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(st)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        run(torch.cuda.current_stream())
+    reps, total_ms, committed = 3, 0.0, 0
+    for i in range(reps + 1):
+        reset(st)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        if i:                                            # the first replay is a warm-up
+            total_ms += e0.elapsed_time(e1)
+            committed += int((hlen - Lc).sum())
+    assert int((cache.len - (hlen - 1)).abs().max()) == 0
+    round_us = total_ms * 1e3 / (reps * rounds)
+    Lmid = Lc + rounds * (k + 1) // 2                    # mean cache length over the rounds (a ~ 0)
+    nb = R.pld_round_bytes(wl.shape, B, k, Lmid, Lc)
+    fl = R.pld_round_flops(wl.shape, B, k, Lmid)
+    floor, bound = R.floor_us(nb, fl)
+    res = {"workload": f"batched PLD, 1.5B-shaped layer: {B} sequences x {Lc}-token histories, n = {n}, k = {k}, "
+                       f"{rounds} rounds per replay (lookup + {1 + k}-row verify + accept, no host sync)",
+           "us_per_round": round(round_us, 2),
+           "verified_positions_per_s": round(B * (1 + k) / (round_us * 1e-6), 1),
+           "committed_tokens_per_s": round(committed / (total_ms * 1e-3), 1),
+           "mean_accepted_per_round": round(committed / (reps * rounds * B) - 1, 4),
+           "alg_bytes_per_round": int(nb), "bound": bound, "floor_us": round(floor, 2),
+           "frac_of_roofline": round(floor / round_us, 4)}
+    log(f"pld: {round_us:.1f} us/round, {res['verified_positions_per_s']:.0f} verified positions/s, "
+        f"{bound} floor {floor:.1f} us ({floor / round_us * 100:.1f}%)")
+    return res
 
 
 COPY_BYTES = 1 << 29     # plain copy of the counter calibration: reads and writes 512 MiB

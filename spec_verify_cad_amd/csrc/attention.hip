@@ -63,8 +63,8 @@ __device__ __forceinline__ int swz_k(int r, int c) {
 }
 __device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r >> 1) & 7); }   // 128-byte rows
 
-template <int DH, int MODE>
-__global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+template <int DH, int MODE, int NWV>
+__global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                                    const uint16_t* __restrict__ vc, const int32_t* __restrict__ len_snap,
                                                    int Nq, int Hq, int Hkv, int cap, int Dblk,
                                                    int nsplit, float* __restrict__ part_o,
@@ -73,8 +73,9 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     constexpr int DB = DH / 16;                 // 16-wide head_dim blocks of the output
     constexpr int TK = 64;                      // keys per LDS tile (two 32-key MFMA steps)
     constexpr int KCH = DH / 8;                 // 16-byte chunks of a K row
-    constexpr int KLD = TK * KCH / 256;         // K chunks each thread copies per tile
-    constexpr int VLD = DH * (TK / 4) / 256;    // 4-key V groups each thread copies per tile
+    constexpr int NT = NWV * 64;                // threads; NWV waves of 16 rows each
+    constexpr int KLD = TK * KCH / NT;          // K chunks each thread copies per tile
+    constexpr int VLD = DH * (TK / 4) / NT;     // 4-key V groups each thread copies per tile
     __shared__ u32x4_t ks[2][TK * KCH];
     __shared__ u32x4_t vs[2][DH * (TK / 8)];
 
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
 
-    const int wg_row0 = rtile * (WAVES * 16);
+    const int wg_row0 = rtile * (NWV * 16);
     const int wrow0 = wg_row0 + wave * 16;
     const bool wlive = wrow0 < Rg;              // a wave without rows still copies tiles
     const bool ok = seq_ok(len_snap, b, Nq, cap);
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     const bool qlive = rho < Rg;
     const int it = qlive ? rho / G : 0, hh = qlive ? rho % G : 0;
     // keys past len + (last token of the workgroup's rows) are masked for all of its rows
-    const int it_max = min(Nq - 1, min(wg_row0 + WAVES * 16 - 1, Rg - 1) / G);
+    const int it_max = min(Nq - 1, min(wg_row0 + NWV * 16 - 1, Rg - 1) / G);
     const int chunk = split_chunk(len, Nq, nsplit);
     const int kbeg = split * chunk;
     int kend = min(kbeg + chunk, len + it_max + 1);
@@ -136,13 +137,13 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     auto load = [&](int t0, Tile& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
-            const int id = tid + 256 * i, key = t0 + id / KCH;
+            const int id = tid + NT * i, key = t0 + id / KCH;
             r.k[i] = *(const u32x4_t*)(kbase + (size_t)(key < kend ? key : 0) * DH + (id % KCH) * 8);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
-            const int id = tid + 256 * i, key0 = t0 + 4 * (id % (TK / 4));
+            const int id = tid + NT * i, key0 = t0 + 4 * (id % (TK / 4));
             r.v[i] = *(const u32x2_t*)(vbase + (size_t)(id / (TK / 4)) * cap + (key0 < kend ? key0 : 0));
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -152,12 +153,12 @@ __global__ __launch_bounds__(256) void k_attn_bf16(const uint16_t* __restrict__ 
     auto store = [&](int t0, int buf, const Tile& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
-            const int id = tid + 256 * i, key = id / KCH;
+            const int id = tid + NT * i, key = id / KCH;
             ks[buf][key * KCH + swz_k<DH>(key, id % KCH)] = r.k[i];
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
-            const int id = tid + 256 * i, row = id / (TK / 4), grp = id % (TK / 4);
+            const int id = tid + NT * i, row = id / (TK / 4), grp = id % (TK / 4);
             const int n = kend - (t0 + 4 * grp);                   // valid keys of the group
             u32x2_t w = r.v[i];
             w.x &= n >= 2 ? 0xFFFFFFFFu : (n == 1 ? 0xFFFFu : 0u);
@@ -465,10 +466,13 @@ bool mfma_path(const FwdDims& fd) { return !(fd.dtype == CAD_DTYPE_F32 || (fd.d 
 // from the sequence's length on the device.
 void attention_plan(FwdDims* fd, int cus) {
     const int G = fd->Hq / fd->Hkv, Rg = fd->Nq * G;
-    fd->attn_rows_per_wg = WAVES * 16;
+    // 128-row tiles (8 waves) once a GQA group has more than 64 rows: the K/V of a split is then
+    // fetched for twice the rows (a 66-row group, 6 heads x 11 positions, is one tile, not two)
+    fd->attn_rows_per_wg = Rg > 64 ? 128 : 64;
     fd->attn_row_tiles = (Rg + fd->attn_rows_per_wg - 1) / fd->attn_rows_per_wg;
     const long units = (long)fd->B * fd->Hkv * fd->attn_row_tiles;
-    const long want = 2L * cus;                          // resident workgroups (two per CU)
+    // resident workgroups: two 4-wave or one 8-wave workgroup per CU (registers and LDS)
+    const long want = (fd->attn_rows_per_wg == 128 ? 1L : 2L) * cus;
     long splits = want / units;
     if (splits > 24) {
         // few row tiles (small spans): as many splits as fill the chip, the merge is cheap
@@ -500,13 +504,20 @@ hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc
     }
     const dim3 grid(fd.attn_splits, fd.attn_row_tiles, fd.B * fd.Hkv);
     const bool tri = fd.mode == CAD_MASK_BLOCK_TRI;
+    const int nt = fd.attn_rows_per_wg / 16 * 64;
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc,
+        hipLaunchKernelGGL(kern, grid, dim3(nt), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc,
                            (const uint16_t*)vc, wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.Dblk, fd.attn_splits,
                            wb.part_o, wb.part_ml, (uint16_t*)wb.o);
     };
-    if (fd.d == 128) tri ? go(k_attn_bf16<128, CAD_MASK_BLOCK_TRI>) : go(k_attn_bf16<128, CAD_MASK_CAUSAL_SPAN>);
-    else tri ? go(k_attn_bf16<64, CAD_MASK_BLOCK_TRI>) : go(k_attn_bf16<64, CAD_MASK_CAUSAL_SPAN>);
+    const bool big = fd.attn_rows_per_wg == 128;
+    if (fd.d == 128) {
+        if (tri) big ? go(k_attn_bf16<128, CAD_MASK_BLOCK_TRI, 8>) : go(k_attn_bf16<128, CAD_MASK_BLOCK_TRI, 4>);
+        else big ? go(k_attn_bf16<128, CAD_MASK_CAUSAL_SPAN, 8>) : go(k_attn_bf16<128, CAD_MASK_CAUSAL_SPAN, 4>);
+    } else {
+        if (tri) big ? go(k_attn_bf16<64, CAD_MASK_BLOCK_TRI, 8>) : go(k_attn_bf16<64, CAD_MASK_BLOCK_TRI, 4>);
+        else big ? go(k_attn_bf16<64, CAD_MASK_CAUSAL_SPAN, 8>) : go(k_attn_bf16<64, CAD_MASK_CAUSAL_SPAN, 4>);
+    }
     return hipGetLastError();
 }
 

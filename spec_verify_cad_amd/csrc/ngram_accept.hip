@@ -1,10 +1,10 @@
 // Integer kernels around the span forward.
 //
 // k_ngram: prompt-lookup draft search (PLD page, "The n-gram match, precisely"; SwitchSD's
-// kappa-gram gate with recency-ranked candidates).  One workgroup per sequence scans the
-// candidate starts newest-first in chunks of 256 (one start per thread, the chunk's token
-// window staged in LDS so the loads are coalesced), ranks the hits of a chunk by wave ballots
-// and stops as soon as W hits are known.
+// kappa-gram gate with recency-ranked candidates).  One workgroup of 1024 threads per sequence
+// scans the candidate starts newest-first in chunks of 4096 (four consecutive starts per thread,
+// the chunk's token window staged in LDS so the loads are coalesced), ranks the hits of a chunk
+// by a block-wide prefix count in descending start order and stops as soon as W hits are known.
 //
 // k_accept: greedy left-to-right acceptance (PLD page, "Verification in a single parallel
 // pass") or the longest validated candidate of a block verify (SwitchSD), then the commit:
@@ -14,59 +14,79 @@
 
 namespace {
 
-constexpr int CH = 256;          // candidate starts per scan chunk
+constexpr int NG_NT = 1024;      // threads of the scan workgroup
+constexpr int NG_Q = 4;          // candidate starts per thread per chunk
+constexpr int CH = NG_NT * NG_Q; // candidate starts per scan chunk
 constexpr int MAXN = 64;
 
-__global__ __launch_bounds__(CH) void k_ngram(const int32_t* __restrict__ ctx, int64_t stride,
-                                              const int32_t* __restrict__ ctx_len, int n, int W, int D,
-                                              int with_current, int32_t* __restrict__ draft,
-                                              int32_t* __restrict__ draft_len, int32_t* __restrict__ match_pos) {
+__global__ __launch_bounds__(NG_NT) void k_ngram(const int32_t* __restrict__ ctx, int64_t stride,
+                                                 const int32_t* __restrict__ ctx_len, int n, int W, int D,
+                                                 int with_current, int32_t* __restrict__ draft,
+                                                 int32_t* __restrict__ draft_len, int32_t* __restrict__ match_pos) {
     __shared__ int32_t win[CH + MAXN];
     __shared__ int32_t suf[MAXN];
-    __shared__ int wcount[CH / 64];
-    __shared__ int found_s;
+    __shared__ int wsum[NG_NT / 64];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int32_t* c = ctx + (size_t)b * stride;
     int len = ctx_len[b];
     len = len < 0 ? 0 : (len > stride ? (int)stride : len);
     const int rowlen = with_current + W * D;
     int32_t* drow = draft + (size_t)b * rowlen;
-    for (int e = tid; e < rowlen; e += CH) drow[e] = (e == 0 && with_current) ? (len > 0 ? c[len - 1] : 0) : 0;
-    for (int w = tid; w < W; w += CH) {
+    for (int e = tid; e < rowlen; e += NG_NT) drow[e] = (e == 0 && with_current) ? (len > 0 ? c[len - 1] : 0) : 0;
+    for (int w = tid; w < W; w += NG_NT) {
         draft_len[b * W + w] = 0;
         if (match_pos) match_pos[b * W + w] = -1;
     }
     if (len < n + 1) return;
-    for (int k = tid; k < n; k += CH) suf[k] = c[len - n + k];
-    if (tid == 0) found_s = 0;
-    __syncthreads();
+    for (int k = tid; k < n; k += NG_NT) suf[k] = c[len - n + k];
     int found = 0;
     for (int hi = len - n - 1; hi >= 0 && found < W; hi -= CH) {
         const int lo = hi - CH + 1;                      // window covers starts lo..hi and their n tokens
-        for (int e = tid; e < CH + n - 1; e += CH) {
-            const int p = lo + e;
-            win[e] = p >= 0 ? c[p] : -1;
+        __syncthreads();                                 // the previous chunk's window is no longer read
+        for (int e = tid; e < CH + n - 1; e += NG_NT) {
+            const int pos = lo + e;
+            win[e] = pos >= 0 ? c[pos] : -1;
         }
         __syncthreads();
-        const int j = hi - tid;
-        bool hit = j >= 0;
-        for (int k = 0; k < n && hit; ++k) hit = win[j - lo + k] == suf[k];
-        const unsigned long long bal = __ballot(hit);
-        if (lane == 0) wcount[wave] = __popcll(bal);
+        // thread t takes starts hi - 4t - q, q = 0..3 (descending in thread order, then in q)
+        int hits = 0;
+#pragma unroll
+        for (int q = 0; q < NG_Q; ++q) {
+            const int j = hi - NG_Q * tid - q;
+            bool hit = j >= 0;
+            for (int k = 0; k < n && hit; ++k) hit = win[j - lo + k] == suf[k];
+            hits |= (int)hit << q;
+        }
+        const int cnt = __popc(hits);
+        int incl = cnt;                                  // inclusive scan over the wave's lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += t;
+        }
+        if (lane == 63) wsum[wave] = incl;
         __syncthreads();
         int before = found;
-        for (int w = 0; w < wave; ++w) before += wcount[w];
-        const int rank = before + __popcll(bal & ((1ull << lane) - 1ull));
-        if (hit && rank < W) {
-            const int dl = min(D, len - (j + n));
-            int32_t* dst = drow + with_current + rank * D;
-            for (int e = 0; e < dl; ++e) dst[e] = c[j + n + e];
-            draft_len[b * W + rank] = dl;
-            if (match_pos) match_pos[b * W + rank] = j;
+        int total = found;
+        for (int w = 0; w < NG_NT / 64; ++w) {
+            before += w < wave ? wsum[w] : 0;
+            total += wsum[w];
         }
-        if (tid == 0) found_s = found + wcount[0] + wcount[1] + wcount[2] + wcount[3];
-        __syncthreads();
-        found = found_s;
+        int rank = before + incl - cnt;
+#pragma unroll
+        for (int q = 0; q < NG_Q; ++q) {
+            if (!((hits >> q) & 1)) continue;
+            if (rank < W) {
+                const int j = hi - NG_Q * tid - q;
+                const int dl = min(D, len - (j + n));
+                int32_t* dst = drow + with_current + rank * D;
+                for (int e = 0; e < dl; ++e) dst[e] = c[j + n + e];
+                draft_len[b * W + rank] = dl;
+                if (match_pos) match_pos[b * W + rank] = j;
+            }
+            ++rank;
+        }
+        found = total;                                   // the same value in every thread
     }
 }
 
@@ -165,7 +185,7 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
 
 hipError_t launch_ngram(const int32_t* ctx, int64_t stride, const int32_t* ctx_len, int B, int n, int W, int D,
                         int with_current, int32_t* draft, int32_t* draft_len, int32_t* match_pos, hipStream_t s) {
-    hipLaunchKernelGGL(k_ngram, dim3(B), dim3(CH), 0, s, ctx, stride, ctx_len, n, W, D, with_current, draft,
+    hipLaunchKernelGGL(k_ngram, dim3(B), dim3(NG_NT), 0, s, ctx, stride, ctx_len, n, W, D, with_current, draft,
                        draft_len, match_pos);
     return hipGetLastError();
 }

@@ -60,3 +60,13 @@ def floor_us(nbytes: float, flops: float) -> tuple:
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
     t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6
     return (t_hbm, "hbm") if t_hbm >= t_mfma else (t_mfma, "mfma")
+
+
+def pld_round_bytes(s, B: int, k: int, L: int, ctx_len: int) -> float:
+    """One batched PLD round: the n-gram scan of every history (int32), a verify forward of k + 1
+    rows per sequence over caches of length L, and the accept scan's few bytes per sequence."""
+    return forward_bytes(s, B, k + 1, L) + B * ctx_len * 4 + B * (k + 1) * 4 * 4
+
+
+def pld_round_flops(s, B: int, k: int, L: int) -> float:
+    return forward_flops(s, B, k + 1, L)
