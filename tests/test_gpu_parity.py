@@ -307,6 +307,63 @@ def test_capacity_overflow_flags_and_skips(small):
     assert (g["argmax"][8:] == -7).all()                       # nothing written for the flagged sequence
 
 
+def test_sequence_filled_exactly_to_capacity(small):
+    """len + Nq == cap is accepted and commits; the same span one slot later overflows."""
+    w, dl, OL = small
+    log("exact capacity")
+    B, Nq, cap = 2, 12, 64
+    ctx = np.stack([synth.uniform_tokens(150 + b, cap - Nq, SMALL.vocab) for b in range(B)])
+    span = np.stack([synth.uniform_tokens(160 + b, Nq, SMALL.vocab) for b in range(B)])
+    cache = cad.DeviceCache(SMALL, B, cap)
+    prefill(dl, cache, ctx, chunk=64)
+    g = run_forward(dl, cache, span, flags=cad.COMMIT_ALL)
+    assert list(cache.len.cpu().numpy()) == [cap] * B and not cache.err.any()
+    for b in range(B):
+        oc = O.cache_from_tokens(OL, ctx[b], cap)
+        ref = O.span_forward(OL, oc, span[b])
+        compare(g, ref, rows=slice(b * Nq, (b + 1) * Nq), what=f"full cache b={b}")
+        compare_cache(cache, b, oc, cap - Nq, cap, "bf16", what=f"last rows b={b}")
+    cache.len.fill_(cap - Nq + 1)
+    run_forward(dl, cache, span, flags=cad.COMMIT_ALL)
+    assert list(cache.err.cpu().numpy()) == [cad.CAD_ECAPACITY] * B
+    assert list(cache.len.cpu().numpy()) == [cap - Nq + 1] * B
+
+
+def test_argument_errors_are_reported_before_any_work(small):
+    """Host-visible argument errors return a negative status and enqueue nothing."""
+    w, dl, OL = small
+    log("argument errors")
+    cache = cad.DeviceCache(SMALL, 2, 64)
+    t = torch.zeros((2, 8), dtype=torch.int32, device="cuda")
+    am = torch.zeros((2, 8), dtype=torch.int32, device="cuda")
+    ws = cad.alloc_workspace(cad.span_forward_workspace(dl, 2, 8, cad.MASK_CAUSAL, 1, 1, 64, 0))
+
+    def status(fn):
+        try:
+            fn()
+        except cad.CadError as e:
+            return e.status
+        return cad.CAD_OK
+
+    assert status(lambda: cad.span_forward(dl, cache, t, 0, argmax_out=am, workspace=ws)) == cad.CAD_EINVAL
+    assert status(lambda: cad.span_forward(dl, cache, t, 8, mode=cad.MASK_BLOCK, W=3, D=4, argmax_out=am,
+                                           workspace=ws)) == cad.CAD_EINVAL          # W*D != Nq
+    assert status(lambda: cad.span_forward(dl, cache, t, 8, flags=8, argmax_out=am, workspace=ws)) == cad.CAD_EINVAL
+    assert status(lambda: cad.span_forward(dl, cache, t, 8, workspace=ws)) == cad.CAD_EINVAL   # no argmax_out
+    small_ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    assert status(lambda: cad.span_forward(dl, cache, t, 8, argmax_out=am, workspace=small_ws)) == cad.CAD_EWORKSPACE
+    odd = cad.DeviceCache(SMALL, 2, 66)                                               # cap not a multiple of 4
+    assert status(lambda: cad.span_forward(dl, odd, t, 8, argmax_out=am)) == cad.CAD_EUNSUPPORTED
+    d = torch.zeros((2, 8), dtype=torch.int32, device="cuda")
+    dlen = torch.zeros((2, 1), dtype=torch.int32, device="cuda")
+    ctx = torch.zeros((2, 32), dtype=torch.int32, device="cuda")
+    clen = torch.zeros(2, dtype=torch.int32, device="cuda")
+    assert status(lambda: cad.ngram_lookup(ctx, clen, 0, 1, 8, 0, d, dlen)) == cad.CAD_EINVAL           # n = 0
+    assert status(lambda: cad.ngram_lookup(ctx, clen, 3, 9, 8, 0, d, dlen)) == cad.CAD_EUNSUPPORTED     # W > 8
+    torch.cuda.synchronize()
+    assert not cache.len.any() and not cache.err.any()                                # nothing ran
+
+
 def test_forward_is_deterministic(small):
     w, dl, OL = small
     log("determinism")
