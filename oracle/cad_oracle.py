@@ -395,6 +395,20 @@ def ngram_lookup(ctx, length: int, n: int, W: int, D: int):
     return drafts, dlen, mpos
 
 
+def ngram_lookup_longest(ctx, length: int, n_max: int, n_min: int, W: int, D: int):
+    """Longest-match policy (PLD page, "The n-gram match, precisely": with several matches a
+    common policy prefers the most recent or the longest; n is often 1-3).  Reading: try the
+    suffix lengths n = n_max, n_max-1, ..., n_min in turn and keep the most-recent-first hits of
+    the first length that has any.  Returns drafts, draft_len, match_pos as `ngram_lookup`, and
+    the suffix length used (0 when no length matches)."""
+    for n in range(n_max, n_min - 1, -1):
+        d, l, m = ngram_lookup(ctx, length, n, W, D)
+        if m[0] >= 0:
+            return d, l, m, n
+    d, l, m = ngram_lookup(ctx, length, n_min, W, D)
+    return d, l, m, 0
+
+
 def ngram_lookup_bruteforce(ctx, length: int, n: int, W: int, D: int):
     """Second, independently written lookup used to pin `ngram_lookup` on tiny inputs:
     list every (start, continuation) pair whose n tokens equal the suffix, newest first."""

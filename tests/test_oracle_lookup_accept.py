@@ -127,3 +127,40 @@ def test_pld_worked_example():
             assert f * T / L == c["passes_copied"] and round((1 - f) * T) == c["passes_new"]
             assert round(f * T / L + (1 - f) * T) == c["passes_total_approx"]
             assert abs(T / (f * T / L + (1 - f) * T) - s) < 1e-12
+
+
+def test_ngram_longest_match_hand_case():
+    # history ... 7 1 2 3 | 5 ... 1 2 3 ends: the 3-gram (1, 2, 3) recurs at j = 1; a 4-gram does not
+    ctx = [7, 1, 2, 3, 5, 6, 4, 2, 3, 8, 1, 2, 3]
+    d, l, m, n = O.ngram_lookup_longest(ctx, len(ctx), 4, 1, 1, 3)
+    assert n == 3 and m[0] == 1 and list(d[0]) == [5, 6, 4] and l[0] == 3
+    # with n_max = 2 the most recent 2-gram (2, 3) wins: j = 7, continuation (8, 1, 2)
+    d, l, m, n = O.ngram_lookup_longest(ctx, len(ctx), 2, 1, 1, 3)
+    assert n == 2 and m[0] == 7 and list(d[0]) == [8, 1, 2]
+    d, l, m, n = O.ngram_lookup_longest([1, 2, 3, 4], 4, 3, 1, 2, 2)      # nothing recurs
+    assert n == 0 and (m == -1).all() and (l == 0).all()
+
+
+def test_ngram_longest_match_against_brute_force():
+    """The length used is the largest with any earlier occurrence of the suffix (checked by a
+    direct search), and the hits are those of the plain lookup at that length."""
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        L = int(rng.integers(0, 40))
+        ctx = rng.integers(0, 3, size=L)
+        n_max, n_min = int(rng.integers(1, 6)), 1
+        n_min = int(rng.integers(1, n_max + 1))
+        d, l, m, n = O.ngram_lookup_longest(ctx, L, n_max, n_min, 2, 4)
+        seq = [int(t) for t in ctx]
+
+        def occurs(k):
+            return L >= k + 1 and any(seq[j:j + k] == seq[L - k:] for j in range(0, L - k))
+
+        want = next((k for k in range(n_max, n_min - 1, -1) if occurs(k)), 0)
+        assert n == want
+        if n:
+            b = O.ngram_lookup_bruteforce(ctx, L, n, 2, 4)
+            np.testing.assert_array_equal(d, b[0])
+            np.testing.assert_array_equal(m, b[2])
+        else:
+            assert (m == -1).all()
