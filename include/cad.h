@@ -129,6 +129,22 @@ int cad_ngram_lookup(const int32_t *ctx, int64_t ctx_stride, const int32_t *ctx_
                      hipStream_t stream);
 
 /*
+ * cad_ngram_lookup_longest — the longest-match policy of the same search (PLD page, "The n-gram
+ * match, precisely": with several matches a policy may prefer the longest; n is often 1-3).
+ * Suffix lengths n = n_max, n_max-1, ..., n_min are tried in turn; the hits of the first length
+ * with any hit are kept exactly as cad_ngram_lookup keeps them for that n.
+ *
+ *   n_max, n_min  1 <= n_min <= n_max <= 64
+ *   match_n    [B] int32 out, nullable: the suffix length used, 0 when no length matched
+ *   other arguments, outputs and layouts as for cad_ngram_lookup.
+ * Errors: CAD_EINVAL, CAD_EUNSUPPORTED (W > 8, D > 64, n_max > 64).
+ */
+int cad_ngram_lookup_longest(const int32_t *ctx, int64_t ctx_stride, const int32_t *ctx_len, int B,
+                             int n_max, int n_min, int W, int D, int with_current,
+                             int32_t *draft, int32_t *draft_len, int32_t *match_pos,
+                             int32_t *match_n, hipStream_t stream);
+
+/*
  * cad_span_forward — one parallel forward of Nq new tokens per sequence (Copy-as-Decode §2.4
  * and Appendix K; SwitchSD block-triangular verification).
  *

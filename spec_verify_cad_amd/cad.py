@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     L.cad_ngram_lookup.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
     L.cad_ngram_lookup.restype = i32
+    L.cad_ngram_lookup_longest.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.cad_ngram_lookup_longest.restype = i32
     L.cad_span_forward.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(KVDesc), vp, i32, i32, i32, i32, i32,
                                    i32, vp, vp, vp, vp, sz, vp]
     L.cad_span_forward.restype = i32
@@ -159,6 +161,14 @@ def ngram_lookup(ctx, ctx_len, n: int, W: int, D: int, with_current: int, draft,
     B = ctx.shape[0]
     _check(lib().cad_ngram_lookup(_ptr(ctx), _row_stride(ctx), _ptr(ctx_len), B, n, W, D, with_current, _ptr(draft),
                                   _ptr(draft_len), _ptr(match_pos), _stream(stream)), "cad_ngram_lookup")
+
+
+def ngram_lookup_longest(ctx, ctx_len, n_max: int, n_min: int, W: int, D: int, with_current: int, draft, draft_len,
+                         match_pos=None, match_n=None, stream=None):
+    B = ctx.shape[0]
+    _check(lib().cad_ngram_lookup_longest(_ptr(ctx), _row_stride(ctx), _ptr(ctx_len), B, n_max, n_min, W, D,
+                                          with_current, _ptr(draft), _ptr(draft_len), _ptr(match_pos), _ptr(match_n),
+                                          _stream(stream)), "cad_ngram_lookup_longest")
 
 
 def span_forward_workspace(layer: DeviceLayer, B: int, Nq: int, mode: int = MASK_CAUSAL, W: int = 1, D: int = 1,

@@ -326,8 +326,21 @@ int cad_ngram_lookup(const int32_t* ctx, int64_t ctx_stride, const int32_t* ctx_
     if (B <= 0 || n <= 0 || W <= 0 || D <= 0 || ctx_stride <= 0) return CAD_EINVAL;
     if (with_current != 0 && with_current != 1) return CAD_EINVAL;
     if (W > 8 || D > 64 || n > 64 || ctx_stride > 0x7fffffff) return CAD_EUNSUPPORTED;
-    return launch_ngram(ctx, ctx_stride, ctx_len, B, n, W, D, with_current, draft, draft_len, match_pos, stream) ==
-                   hipSuccess
+    return launch_ngram(ctx, ctx_stride, ctx_len, B, n, n, W, D, with_current, draft, draft_len, match_pos, nullptr,
+                        stream) == hipSuccess
+               ? CAD_OK
+               : CAD_EHIP;
+}
+
+int cad_ngram_lookup_longest(const int32_t* ctx, int64_t ctx_stride, const int32_t* ctx_len, int B, int n_max,
+                             int n_min, int W, int D, int with_current, int32_t* draft, int32_t* draft_len,
+                             int32_t* match_pos, int32_t* match_n, hipStream_t stream) {
+    if (!ctx || !ctx_len || !draft || !draft_len) return CAD_EINVAL;
+    if (B <= 0 || n_min <= 0 || n_max < n_min || W <= 0 || D <= 0 || ctx_stride <= 0) return CAD_EINVAL;
+    if (with_current != 0 && with_current != 1) return CAD_EINVAL;
+    if (W > 8 || D > 64 || n_max > 64 || ctx_stride > 0x7fffffff) return CAD_EUNSUPPORTED;
+    return launch_ngram(ctx, ctx_stride, ctx_len, B, n_max, n_min, W, D, with_current, draft, draft_len, match_pos,
+                        match_n, stream) == hipSuccess
                ? CAD_OK
                : CAD_EHIP;
 }

@@ -97,9 +97,9 @@ hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc
 hipError_t launch_attention_merge(const FwdDims& fd, const FwdBufs& wb, hipStream_t s);
 bool attention_uses_merge(const FwdDims& fd);
 hipError_t launch_commit(const FwdDims& fd, const FwdBufs& wb, int32_t* kv_len, hipStream_t s);
-hipError_t launch_ngram(const int32_t* ctx, int64_t stride, const int32_t* ctx_len, int B, int n, int W,
-                        int D, int with_current, int32_t* draft, int32_t* draft_len, int32_t* match_pos,
-                        hipStream_t s);
+hipError_t launch_ngram(const int32_t* ctx, int64_t stride, const int32_t* ctx_len, int B, int n_hi, int n_lo,
+                        int W, int D, int with_current, int32_t* draft, int32_t* draft_len, int32_t* match_pos,
+                        int32_t* match_n, hipStream_t s);
 hipError_t launch_accept(const int32_t* draft, int with_current, const int32_t* draft_len, const int32_t* pred,
                          const int32_t* first_pred, int B, int W, int D, int mode, int32_t* accepted,
                          int32_t* best_w, int32_t* emitted, int32_t* n_emitted, int32_t* ctx, int64_t ctx_stride,

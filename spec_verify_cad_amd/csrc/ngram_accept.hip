@@ -19,10 +19,13 @@ constexpr int NG_Q = 4;          // candidate starts per thread per chunk
 constexpr int CH = NG_NT * NG_Q; // candidate starts per scan chunk
 constexpr int MAXN = 64;
 
+// Suffix lengths n_hi down to n_lo are tried in turn and the hits of the first length that has
+// any are kept (n_hi == n_lo: the plain lookup); match_n (nullable) gets that length, 0 if none.
 __global__ __launch_bounds__(NG_NT) void k_ngram(const int32_t* __restrict__ ctx, int64_t stride,
-                                                 const int32_t* __restrict__ ctx_len, int n, int W, int D,
-                                                 int with_current, int32_t* __restrict__ draft,
-                                                 int32_t* __restrict__ draft_len, int32_t* __restrict__ match_pos) {
+                                                 const int32_t* __restrict__ ctx_len, int n_hi, int n_lo, int W,
+                                                 int D, int with_current, int32_t* __restrict__ draft,
+                                                 int32_t* __restrict__ draft_len, int32_t* __restrict__ match_pos,
+                                                 int32_t* __restrict__ match_n) {
     __shared__ int32_t win[CH + MAXN];
     __shared__ int32_t suf[MAXN];
     __shared__ int wsum[NG_NT / 64];
@@ -37,7 +40,10 @@ __global__ __launch_bounds__(NG_NT) void k_ngram(const int32_t* __restrict__ ctx
         draft_len[b * W + w] = 0;
         if (match_pos) match_pos[b * W + w] = -1;
     }
-    if (len < n + 1) return;
+    if (match_n && tid == 0) match_n[b] = 0;
+    for (int n = n_hi; n >= n_lo; --n) {
+    if (len < n + 1) continue;
+    __syncthreads();                                     // the previous length's suffix is no longer read
     for (int k = tid; k < n; k += NG_NT) suf[k] = c[len - n + k];
     int found = 0;
     for (int hi = len - n - 1; hi >= 0 && found < W; hi -= CH) {
@@ -87,6 +93,11 @@ __global__ __launch_bounds__(NG_NT) void k_ngram(const int32_t* __restrict__ ctx
             ++rank;
         }
         found = total;                                   // the same value in every thread
+    }
+    if (found > 0) {
+        if (match_n && tid == 0) match_n[b] = n;
+        return;
+    }
     }
 }
 
@@ -183,10 +194,11 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
 
 }  // namespace
 
-hipError_t launch_ngram(const int32_t* ctx, int64_t stride, const int32_t* ctx_len, int B, int n, int W, int D,
-                        int with_current, int32_t* draft, int32_t* draft_len, int32_t* match_pos, hipStream_t s) {
-    hipLaunchKernelGGL(k_ngram, dim3(B), dim3(NG_NT), 0, s, ctx, stride, ctx_len, n, W, D, with_current, draft,
-                       draft_len, match_pos);
+hipError_t launch_ngram(const int32_t* ctx, int64_t stride, const int32_t* ctx_len, int B, int n_hi, int n_lo,
+                        int W, int D, int with_current, int32_t* draft, int32_t* draft_len, int32_t* match_pos,
+                        int32_t* match_n, hipStream_t s) {
+    hipLaunchKernelGGL(k_ngram, dim3(B), dim3(NG_NT), 0, s, ctx, stride, ctx_len, n_hi, n_lo, W, D, with_current,
+                       draft, draft_len, match_pos, match_n);
     return hipGetLastError();
 }
 

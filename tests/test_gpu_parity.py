@@ -59,6 +59,35 @@ def test_ngram_lookup_planted_contexts():
         np.testing.assert_array_equal(d[b, 1:], od[0])
 
 
+@pytest.mark.parametrize("n_max,n_min,W,D,wc", [(3, 1, 1, 10, 1), (4, 2, 3, 5, 0), (6, 1, 8, 8, 0)])
+def test_ngram_lookup_longest_matches_oracle(n_max, n_min, W, D, wc):
+    log(f"ngram longest n={n_max}..{n_min} W={W} D={D}")
+    rng = np.random.default_rng(200 + n_max)
+    ctxs = [rng.integers(0, 4, size=int(rng.integers(0, 900))) for _ in range(40)]
+    ctxs += [np.zeros(0, np.int64), np.array([3]), np.array([1, 2, 3, 4, 5])]
+    ctxs += [synth.planted_context(9, 6000 + 11 * b, 50000, 0.4, 8, 256, "zipf", 1.1, stream=b)[0] for b in range(8)]
+    B = len(ctxs)
+    stride = max(len(c) for c in ctxs)
+    ctx = np.zeros((B, stride), dtype=np.int32)
+    for b, c in enumerate(ctxs):
+        ctx[b, :len(c)] = c
+    tc = torch.from_numpy(ctx).cuda()
+    tl = torch.from_numpy(np.array([len(c) for c in ctxs], dtype=np.int32)).cuda()
+    draft = torch.full((B, wc + W * D), -9, dtype=torch.int32, device="cuda")
+    dlen = torch.full((B, W), -9, dtype=torch.int32, device="cuda")
+    mpos = torch.full((B, W), -9, dtype=torch.int32, device="cuda")
+    mn = torch.full((B,), -9, dtype=torch.int32, device="cuda")
+    cad.ngram_lookup_longest(tc, tl, n_max, n_min, W, D, wc, draft, dlen, mpos, mn)
+    torch.cuda.synchronize()
+    d, l, m, nn = (t.cpu().numpy() for t in (draft, dlen, mpos, mn))
+    for b, c in enumerate(ctxs):
+        od, ol, om, on = O.ngram_lookup_longest(c, len(c), n_max, n_min, W, D)
+        assert nn[b] == on, f"b={b}"
+        np.testing.assert_array_equal(l[b], ol, err_msg=f"b={b}")
+        np.testing.assert_array_equal(m[b], om, err_msg=f"b={b}")
+        np.testing.assert_array_equal(d[b, wc:].reshape(W, D), od, err_msg=f"b={b}")
+
+
 # ------------------------------------------------------------------------- accept scan
 def test_accept_scan_causal_matches_oracle():
     log("accept causal")
