@@ -228,6 +228,33 @@ def top2_gap(logits: np.ndarray) -> np.ndarray:
     return part[..., -1] - part[..., -2]
 
 
+def masked_argmax(logits: np.ndarray, allowed: np.ndarray, vocab: int):
+    """Argmax restricted to an allowed id set per row (Copy-as-Decode §2.3: at decision points
+    the FSM intersects the model's logits with the tokens its state allows).  allowed [rows, A]
+    holds ids; entries outside [0, vocab) are padding.  Ties go to the lowest id.  Returns the
+    chosen id per row (-1 when a row allows nothing), the logits at the allowed slots (-inf for
+    padding) and the gap between the best and second-best distinct allowed ids."""
+    logits = np.asarray(logits, dtype=np.float64)
+    allowed = np.asarray(allowed)
+    rows, A = allowed.shape
+    best = np.full(rows, -1, dtype=np.int64)
+    vals = np.full((rows, A), -np.inf)
+    gap = np.full(rows, np.inf)
+    for r in range(rows):
+        ids = sorted({int(a) for a in allowed[r] if 0 <= a < vocab})
+        for k in range(A):
+            a = int(allowed[r, k])
+            if 0 <= a < vocab:
+                vals[r, k] = logits[r, a]
+        if ids:
+            sub = logits[r, ids]
+            best[r] = ids[int(np.argmax(sub))]                # first maximum = lowest id (ids sorted)
+            if len(ids) > 1:
+                srt = np.sort(sub)
+                gap[r] = srt[-1] - srt[-2]
+    return best, vals, gap
+
+
 def softmax_checked(s: np.ndarray) -> np.ndarray:
     """Softmax over the last axis (entries at -inf get weight 0); rows must sum to 1."""
     m = np.max(s, axis=-1, keepdims=True)

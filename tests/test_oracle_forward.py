@@ -300,3 +300,30 @@ def test_tiny_config_corrupted_draft_accepts_four(tiny):
     fw = O.span_forward(L, c, [g] + list(draft), commit=False)
     a, em = O.accept_causal(draft, 8, fw["argmax"])
     assert a == 4 and em == greedy[:5]
+
+
+def test_masked_argmax_definition():
+    lg = np.array([[0.5, 2.0, 2.0, -1.0, 3.0],
+                   [1.0, 1.0, 1.0, 1.0, 1.0]])
+    allowed = np.array([[3, 2, 1, -1], [4, 2, 7, 2]])
+    best, vals, gap = O.masked_argmax(lg, allowed, 5)
+    assert list(best) == [1, 2]                          # ties to the lowest allowed id
+    assert vals[0, 3] == -np.inf and vals[1, 2] == -np.inf and vals[0, 0] == -1.0
+    assert gap[0] == 0.0 and gap[1] == 0.0
+    none, _, _ = O.masked_argmax(lg[:1], np.array([[-1, 9]]), 5)
+    assert none[0] == -1
+
+
+def test_masked_argmax_over_the_whole_vocab_is_the_argmax():
+    rng = np.random.default_rng(3)
+    lg = rng.normal(size=(20, 37))
+    lg[3, 5] = lg[3, 9] = lg[3].max() + 1                # a tie
+    allowed = np.tile(np.arange(37)[::-1], (20, 1))      # every id, in another order
+    best, _, _ = O.masked_argmax(lg, allowed, 37)
+    np.testing.assert_array_equal(best, O.argmax_lowest(lg))
+    sub = rng.integers(0, 37, size=(20, 6))
+    best, vals, _ = O.masked_argmax(lg, sub, 37)
+    for r in range(20):                                  # brute force over the subset
+        ids = sorted(set(sub[r].tolist()))
+        assert best[r] == min(i for i in ids if lg[r, i] == max(lg[r, j] for j in ids))
+        np.testing.assert_array_equal(vals[r], lg[r, sub[r]])
