@@ -176,6 +176,30 @@ int cad_span_forward(const cad_layer_desc *layer, const cad_kv_desc *kv,
                      int32_t *argmax_out, void *hidden_out, float *logits_out,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * cad_span_forward_allowed — a causal span forward whose argmax is restricted to a per-row set
+ * of allowed token ids (Copy-as-Decode §2.3: at the grammar's decision points the FSM intersects
+ * the model's logits with the ids its state allows, e.g. {<, </} at an op boundary).  Only the
+ * allowed rows of the LM head are read (A of them per row instead of the vocabulary).
+ *
+ *   allowed     [B*Nq, A] int32 ids; entries outside [0, vocab) are padding
+ *   A           1 .. CAD_MAX_ALLOWED
+ *   flags       0 or CAD_COMMIT_ALL
+ *   argmax_out  [B*Nq] int32 out: the allowed id with the largest logit, ties to the lowest id;
+ *               -1 for a row whose set holds no valid id
+ *   logits_out  [B*Nq, A] fp32 out, nullable: the logit at each allowed slot, -inf for padding
+ *   hidden_out, workspace (cad_span_forward_workspace with the same B, Nq), stream: as for
+ *               cad_span_forward; the cache rows are those of a full forward.
+ * Errors: CAD_EINVAL, CAD_EUNSUPPORTED (A out of range, and as cad_span_forward), CAD_EWORKSPACE,
+ * CAD_EHIP; per sequence CAD_ECAPACITY in kv->err when len + Nq > cap.
+ */
+#define CAD_MAX_ALLOWED 16
+int cad_span_forward_allowed(const cad_layer_desc *layer, const cad_kv_desc *kv,
+                             const int32_t *tokens, int B, int Nq, int flags,
+                             const int32_t *allowed, int A,
+                             int32_t *argmax_out, float *logits_out, void *hidden_out,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace cad_span_forward needs for these arguments and flags (0 on invalid
  * arguments).  A CAD_KV_ONLY forward needs far less than a full one. */
 size_t cad_span_forward_workspace(const cad_layer_desc *layer, int B, int Nq, int mask_mode,

@@ -20,6 +20,7 @@ CAD_OK, CAD_EINVAL, CAD_EUNSUPPORTED, CAD_ECAPACITY, CAD_EHIP, CAD_EWORKSPACE = 
 DTYPE_BF16, DTYPE_F32 = 0, 1
 MASK_CAUSAL, MASK_BLOCK = 0, 1
 COMMIT_ALL, KV_ONLY, LOGITS_LAST = 1, 2, 4
+MAX_ALLOWED = 16
 
 
 class LayerDesc(ctypes.Structure):
@@ -55,6 +56,9 @@ def lib() -> ctypes.CDLL:
     L.cad_span_forward.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(KVDesc), vp, i32, i32, i32, i32, i32,
                                    i32, vp, vp, vp, vp, sz, vp]
     L.cad_span_forward.restype = i32
+    L.cad_span_forward_allowed.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(KVDesc), vp, i32, i32, i32, vp,
+                                           i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.cad_span_forward_allowed.restype = i32
     L.cad_span_forward_workspace.argtypes = [ctypes.POINTER(LayerDesc), i32, i32, i32, i32, i32, i32, i32]
     L.cad_span_forward_workspace.restype = sz
     L.cad_accept_scan.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64, vp, i32,
@@ -190,6 +194,19 @@ def span_forward(layer: DeviceLayer, cache: DeviceCache, tokens, Nq: int, mode: 
     _check(lib().cad_span_forward(ctypes.byref(layer.desc), ctypes.byref(cache.desc), _ptr(tokens), B, Nq, mode, W, D,
                                   flags, _ptr(argmax_out), _ptr(hidden_out), _ptr(logits_out), _ptr(workspace),
                                   workspace.numel(), _stream(stream)), "cad_span_forward")
+    return workspace
+
+
+def span_forward_allowed(layer: DeviceLayer, cache: DeviceCache, tokens, Nq: int, allowed, A: int, flags: int = 0,
+                         argmax_out=None, logits_out=None, hidden_out=None, workspace=None, stream=None):
+    """Causal span forward with the argmax restricted to each row's A allowed ids (int32 [B*Nq, A])."""
+    B = cache.B
+    if workspace is None:
+        workspace = alloc_workspace(span_forward_workspace(layer, B, Nq, MASK_CAUSAL, 1, 1, cache.cap, flags))
+    _check(lib().cad_span_forward_allowed(ctypes.byref(layer.desc), ctypes.byref(cache.desc), _ptr(tokens), B, Nq,
+                                          flags, _ptr(allowed), A, _ptr(argmax_out), _ptr(logits_out),
+                                          _ptr(hidden_out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "cad_span_forward_allowed")
     return workspace
 
 

@@ -12,11 +12,12 @@ namespace {
 // ---- opt-in per-stage profiler (diagnostics) ----
 enum Stage {
     ST_EMBED_NORM, ST_QKV, ST_ATTN, ST_ATTN_MERGE, ST_O_PROJ, ST_NORM2, ST_GATE_UP, ST_DOWN, ST_NORM3, ST_LM_HEAD,
-    ST_ARGMAX, ST_COMMIT, ST_QKV_FINISH, ST_COUNT
+    ST_ARGMAX, ST_COMMIT, ST_QKV_FINISH, ST_ALLOWED, ST_COUNT
 };
 const char* kStageNames[ST_COUNT] = {"embed_norm", "qkv_rope_append", "attention", "attention_merge", "o_proj",
                                      "resid_rmsnorm_2", "gate_up_swiglu", "down_proj", "resid_rmsnorm_final",
-                                     "lm_head_argmax", "argmax_final_commit", "commit", "qkv_rope_append_rows"};
+                                     "lm_head_argmax", "argmax_final_commit", "commit", "qkv_rope_append_rows",
+                                     "allowed_ids_argmax_commit"};
 struct ProfRec { int stage; hipEvent_t a, b; };
 bool g_prof = false;
 std::vector<ProfRec> g_recs;
@@ -195,9 +196,13 @@ size_t cad_span_forward_workspace(const cad_layer_desc* L, int B, int Nq, int mo
     return fwd_carve(fd, nullptr, (flags & CAD_KV_ONLY) != 0).total;
 }
 
-int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
-                     int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// The span forward.  allowed == nullptr: the full LM head and argmax (or the last row's, with
+// CAD_LOGITS_LAST); otherwise the argmax over each row's A allowed ids.
+int span_forward_impl(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
+                      int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
+                      const int32_t* allowed, int A, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!L || !kv || !tokens) return CAD_EINVAL;
     if (flags & ~(CAD_COMMIT_ALL | CAD_KV_ONLY | CAD_LOGITS_LAST)) return CAD_EINVAL;
     const bool kv_only = (flags & CAD_KV_ONLY) != 0;
@@ -301,6 +306,15 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
                                      wb.len_snap, stream);
         }) != hipSuccess)
         return CAD_EHIP;
+    if (allowed) {
+        // grammar-masked step: logits of the allowed ids only, argmax, commit
+        if (stage(ST_ALLOWED, stream, [&] {
+                return launch_allowed_argmax(fd, wb, L->w_lm, allowed, A, argmax_out, logits_out,
+                                             (flags & CAD_COMMIT_ALL) ? kv->len : nullptr, stream);
+            }) != hipSuccess)
+            return CAD_EHIP;
+        return CAD_OK;
+    }
     // LM head + argmax partials, then the per-row reduction (+ commit of the cache lengths).
     // Copy-commit mode: u3 holds one row per sequence (row b = the sequence's last row).
     EpiParams pl = p;
@@ -318,6 +332,25 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
         }) != hipSuccess)
         return CAD_EHIP;
     return CAD_OK;
+}
+
+}  // namespace
+
+int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
+                     int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return span_forward_impl(L, kv, tokens, B, Nq, mode, W, D, flags, argmax_out, hidden_out, logits_out, nullptr, 0,
+                             workspace, workspace_bytes, stream);
+}
+
+int cad_span_forward_allowed(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
+                             int flags, const int32_t* allowed, int A, int32_t* argmax_out, float* logits_out,
+                             void* hidden_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!allowed || !argmax_out) return CAD_EINVAL;
+    if (A < 1 || A > CAD_MAX_ALLOWED) return CAD_EUNSUPPORTED;
+    if (flags & ~CAD_COMMIT_ALL) return CAD_EINVAL;
+    return span_forward_impl(L, kv, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, argmax_out, hidden_out,
+                             logits_out, allowed, A, workspace, workspace_bytes, stream);
 }
 
 int cad_ngram_lookup(const int32_t* ctx, int64_t ctx_stride, const int32_t* ctx_len, int B, int n, int W, int D,

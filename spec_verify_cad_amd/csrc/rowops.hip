@@ -206,6 +206,57 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ pa
     }
 }
 
+// Grammar-masked argmax: one workgroup per row.  Each thread accumulates, for every allowed id of
+// the row, its strided share of the dot product of the final normed row with that LM-head row
+// (fp32); the shares are summed per id across the workgroup, then thread 0 takes the largest
+// logit (ties to the lowest id), writes the slot logits and, for the sequence's first row,
+// advances the cache length.
+constexpr int AMAX = 16;
+template <typename T>
+__global__ __launch_bounds__(NT) void k_allowed_argmax(const T* __restrict__ u3, const T* __restrict__ wlm, int h,
+                                                       int V, const int32_t* __restrict__ allowed, int A, int Nq,
+                                                       int cap, const int32_t* __restrict__ len_snap,
+                                                       int32_t* __restrict__ out, float* __restrict__ logits,
+                                                       int32_t* __restrict__ kv_len) {
+    static_assert(NT == 256, "the final sum reads four wave partials");
+    __shared__ float red[NT / 64][AMAX];
+    const int r = blockIdx.x, b = r / Nq;
+    if (!seq_ok(len_snap, b, Nq, cap)) return;
+    int ids[AMAX];
+    float acc[AMAX];
+#pragma unroll
+    for (int a = 0; a < AMAX; ++a) {
+        const int id = a < A ? allowed[(size_t)r * A + a] : -1;
+        ids[a] = (id >= 0 && id < V) ? id : -1;
+        acc[a] = 0.f;
+    }
+    for (int j = threadIdx.x; j < h; j += NT) {
+        const float x = Elt<T>::ld(u3, (size_t)r * h + j);
+#pragma unroll
+        for (int a = 0; a < AMAX; ++a)
+            if (ids[a] >= 0) acc[a] += x * Elt<T>::ld(wlm, (size_t)ids[a] * h + j);
+    }
+#pragma unroll
+    for (int a = 0; a < AMAX; ++a) {
+        const float v = wave_sum(acc[a]);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][a] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    float best = -INFINITY;
+    int bi = -1;
+    for (int a = 0; a < A; ++a) {
+        float v = -INFINITY;
+        if (ids[a] >= 0) {
+            v = (red[0][a] + red[1][a]) + (red[2][a] + red[3][a]);
+            if (bi < 0 || v > best || (v == best && ids[a] < bi)) { best = v; bi = ids[a]; }
+        }
+        if (logits) logits[(size_t)r * A + a] = v;
+    }
+    out[r] = bi;
+    if (kv_len && r % Nq == 0) kv_len[b] = len_snap[b] + Nq;
+}
+
 // One wave per row.  The LM head ran on rps rows per sequence (Nq, or 1 for the last row only):
 // row r belongs to sequence b = r / rps, and the wave of the sequence's first row commits.
 __global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ part, int slots, int rps, int Nq,
@@ -297,5 +348,19 @@ hipError_t launch_qkv_finish(const FwdDims& fd, const float* part, int slices, i
                              const FwdBufs& wb, void* kc, void* vc, hipStream_t s) {
     hipLaunchKernelGGL(k_qkv_finish, dim3(fd.M), dim3(256), 0, s, part, slices, fd.M, N, head_off, fd.Hq, fd.Hkv,
                        fd.d, fd.Nq, fd.cap, wb.len_snap, wb.rope_cs, (uint16_t*)wb.q, (uint16_t*)kc, (uint16_t*)vc);
+    return hipGetLastError();
+}
+
+hipError_t launch_allowed_argmax(const FwdDims& fd, const FwdBufs& wb, const void* w_lm, const int32_t* allowed, int A,
+                                 int32_t* argmax_out, float* logits_out, int32_t* kv_len, hipStream_t s) {
+    if (A < 1 || A > AMAX) return hipErrorInvalidValue;
+    if (fd.dtype == CAD_DTYPE_F32)
+        hipLaunchKernelGGL(k_allowed_argmax<float>, dim3(fd.M), dim3(NT), 0, s, (const float*)wb.u3,
+                           (const float*)w_lm, fd.h, fd.V, allowed, A, fd.Nq, fd.cap, wb.len_snap, argmax_out,
+                           logits_out, kv_len);
+    else
+        hipLaunchKernelGGL(k_allowed_argmax<uint16_t>, dim3(fd.M), dim3(NT), 0, s, (const uint16_t*)wb.u3,
+                           (const uint16_t*)w_lm, fd.h, fd.V, allowed, A, fd.Nq, fd.cap, wb.len_snap, argmax_out,
+                           logits_out, kv_len);
     return hipGetLastError();
 }

@@ -10,7 +10,7 @@ from spec_verify_cad_amd import cad
 def test_header_declares_the_three_calls():
     names = cad.header_functions()
     for n in ("cad_ngram_lookup", "cad_span_forward", "cad_accept_scan", "cad_span_forward_workspace",
-              "cad_status_string", "cad_version"):
+              "cad_span_forward_allowed", "cad_ngram_lookup_longest", "cad_status_string", "cad_version"):
         assert n in names
 
 
@@ -61,6 +61,16 @@ def test_host_argument_errors_return_before_launch():
     # unknown flag, missing argmax output
     assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 8, tok, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
     assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, None, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
+    # grammar-masked forward: null set / output, set size, flags it does not take
+    fa = L.cad_span_forward_allowed
+    assert fa(ctypes.byref(d), ctypes.byref(kv), tok, 1, 1, 0, None, 4, tok, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
+    assert fa(ctypes.byref(d), ctypes.byref(kv), tok, 1, 1, 0, tok, 4, None, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
+    assert fa(ctypes.byref(d), ctypes.byref(kv), tok, 1, 1, 0, tok, 0, tok, None, None, tok, 1 << 30, None) == cad.CAD_EUNSUPPORTED
+    assert fa(ctypes.byref(d), ctypes.byref(kv), tok, 1, 1, 0, tok, cad.MAX_ALLOWED + 1, tok, None, None, tok, 1 << 30,
+              None) == cad.CAD_EUNSUPPORTED
+    assert fa(ctypes.byref(d), ctypes.byref(kv), tok, 1, 1, cad.LOGITS_LAST, tok, 4, tok, None, None, tok, 1 << 30,
+              None) == cad.CAD_EINVAL
+    assert fa(ctypes.byref(d), ctypes.byref(kv), None, 1, 1, 0, tok, 4, tok, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
     # lookup / accept argument errors
     assert L.cad_ngram_lookup(tok, 16, tok, 1, 0, 1, 4, 0, tok, tok, None, None) == cad.CAD_EINVAL
     assert L.cad_ngram_lookup(tok, 16, tok, 1, 3, 9, 4, 0, tok, tok, None, None) == cad.CAD_EUNSUPPORTED

@@ -8,7 +8,7 @@ from spec_verify_cad_amd import cad, synth
 from spec_verify_cad_amd.configs import CONFIGS, SMALL, TINY
 from spec_verify_cad_amd.synth import LayerShape
 
-from gpu_util import (LOGIT_TOL, argmax_check, compare, compare_cache, hidden_tol, log, prefill, run_forward, to_f64,
+from gpu_util import (LOGIT_TOL, NEAR_TIE, argmax_check, compare, compare_cache, hidden_tol, log, prefill, run_forward, to_f64,
                       upload_oracle_cache)
 from helpers import oracle_layer
 
@@ -278,6 +278,102 @@ def test_small_bf16_copy_commit_last_row_matches_oracle(small, Nq):
         assert dl_ <= LOGIT_TOL, f"b={b} last-row logits {dl_}"
         argmax_check(g_a[b:b + 1], last, g_l[b:b + 1], what=f"copy-commit b={b}")
         compare_cache(cache, b, oc, L0, L0 + Nq, "bf16", what=f"copy-commit rows b={b}")
+
+
+def _allowed_sets(seed, rows, A, vocab, full_argmax):
+    """Allowed-id sets of A slots per row: random ids, some padding (-1, vocab + 3), a duplicate,
+    the unrestricted argmax in every third row, and one row that allows nothing."""
+    rng = np.random.default_rng(seed)
+    al = rng.integers(0, vocab, size=(rows, A)).astype(np.int32)
+    for r in range(rows):
+        k = r % 4
+        if k == 1:
+            al[r, -2:] = [-1, vocab + 3][-A:]
+        elif k == 2 and A > 1:
+            al[r, 1] = al[r, 0]
+        if r % 3 == 0:
+            al[r, r % A] = full_argmax[r]
+    al[rows // 2] = -1
+    return al
+
+
+def _check_masked(g_a, g_v, al, ref_logits, vocab, what):
+    best, vals, gap = O.masked_argmax(ref_logits, al, vocab)
+    pad = ~np.isfinite(vals)
+    assert (np.isneginf(g_v[pad])).all(), f"{what} padding slots must read -inf"
+    d = np.where(pad, 0.0, np.abs(np.where(pad, 0.0, g_v) - np.where(pad, 0.0, vals)))
+    e = d.max(axis=1)
+    assert e.max() <= LOGIT_TOL, f"{what} allowed logits off by {e.max()}"
+    none = best < 0
+    assert (g_a[none] == -1).all(), f"{what} empty set must give -1"
+    unique = ~none & (gap > np.maximum(NEAR_TIE, 2 * e))
+    bad = np.nonzero(unique & (g_a != best))[0]
+    assert bad.size == 0, f"{what} masked argmax differs at rows {bad[:10]}: {g_a[bad[:10]]} vs {best[bad[:10]]}"
+    for r in np.nonzero(~none & ~unique)[0]:                  # near ties: a valid near-top allowed id
+        ok = [int(a) for a in al[r] if 0 <= a < vocab]
+        assert int(g_a[r]) in ok, f"{what} row {r} chose {g_a[r]} outside its set"
+        assert ref_logits[r, ok].max() - ref_logits[r, g_a[r]] <= 2 * e[r] + 1e-12
+    return int(unique.sum())
+
+
+@pytest.mark.parametrize("Nq,A,commit", [(1, 12, True), (5, 16, True), (3, 1, False)])
+def test_small_bf16_grammar_masked_argmax_matches_oracle(small, Nq, A, commit):
+    """cad_span_forward_allowed: the argmax over each row's allowed ids equals the oracle's
+    masked argmax on the oracle forward's logits; the cache rows, hidden output and commit are
+    those of the full forward."""
+    w, dl, OL = small
+    log(f"small bf16 masked argmax Nq={Nq} A={A} commit={commit}")
+    B, L0, cap = 3, 150, 320
+    ctx = np.stack([synth.uniform_tokens(50 + b, L0, SMALL.vocab) for b in range(B)])
+    span = np.stack([synth.uniform_tokens(110 + b, Nq, SMALL.vocab) for b in range(B)])
+    ocs = [O.cache_from_tokens(OL, ctx[b], cap) for b in range(B)]
+    refs = [O.span_forward(OL, ocs[b], span[b]) for b in range(B)]       # appends the span rows to ocs[b]
+    ref_logits = np.concatenate([r["logits"] for r in refs])
+    ref_hidden = np.concatenate([r["hidden_out"] for r in refs])
+    al = _allowed_sets(7 * Nq + A, B * Nq, A, SMALL.vocab, np.concatenate([r["argmax"] for r in refs]))
+    cache = cad.DeviceCache(SMALL, B, cap)
+    prefill(dl, cache, ctx, chunk=64)
+    t = torch.from_numpy(np.ascontiguousarray(span, dtype=np.int32)).cuda()
+    ta = torch.from_numpy(al).cuda()
+    am = torch.full((B * Nq,), -7, dtype=torch.int32, device="cuda")
+    lv = torch.zeros((B * Nq, A), dtype=torch.float32, device="cuda")
+    hid = torch.zeros((B * Nq, SMALL.hidden), dtype=torch.int16, device="cuda")
+    cad.span_forward_allowed(dl, cache, t, Nq, ta, A, flags=cad.COMMIT_ALL if commit else 0, argmax_out=am,
+                             logits_out=lv, hidden_out=hid)
+    torch.cuda.synchronize()
+    assert list(cache.len.cpu().numpy()) == [L0 + Nq if commit else L0] * B
+    dh = np.abs(to_f64(hid, "bf16") - ref_hidden)
+    assert (dh <= hidden_tol(ref_hidden, SMALL.ffn)).all(), f"hidden {dh.max()}"
+    n_unique = _check_masked(am.cpu().numpy(), lv.cpu().numpy().astype(np.float64), al, ref_logits, SMALL.vocab,
+                             f"Nq={Nq} A={A}")
+    assert n_unique >= (B * Nq) // 2
+    for b in range(B):
+        compare_cache(cache, b, ocs[b], L0, L0 + Nq, "bf16", what=f"masked rows b={b}")
+
+
+def test_masked_argmax_over_the_top_ids_equals_the_plain_argmax(small):
+    """A set holding the oracle's 16 largest logits of each row (in reverse order) gives the
+    unrestricted argmax wherever that is unique."""
+    w, dl, OL = small
+    B, L0, cap, Nq, A = 2, 90, 128, 4, 16
+    log("small bf16 masked argmax over the top-16 ids")
+    ctx = np.stack([synth.uniform_tokens(30 + b, L0, SMALL.vocab) for b in range(B)])
+    span = np.stack([synth.uniform_tokens(40 + b, Nq, SMALL.vocab) for b in range(B)])
+    refs = [O.span_forward(OL, O.cache_from_tokens(OL, ctx[b], cap), span[b]) for b in range(B)]
+    lg = np.concatenate([r["logits"] for r in refs])
+    top = np.ascontiguousarray(np.argsort(-lg, axis=1, kind="stable")[:, :A][:, ::-1], dtype=np.int32)
+    cache = cad.DeviceCache(SMALL, B, cap)
+    prefill(dl, cache, ctx)
+    t = torch.from_numpy(np.ascontiguousarray(span, dtype=np.int32)).cuda()
+    am = torch.full((B * Nq,), -7, dtype=torch.int32, device="cuda")
+    lv = torch.zeros((B * Nq, A), dtype=torch.float32, device="cuda")
+    cad.span_forward_allowed(dl, cache, t, Nq, torch.from_numpy(top).cuda(), A, argmax_out=am, logits_out=lv)
+    torch.cuda.synchronize()
+    ga = am.cpu().numpy()
+    _check_masked(ga, lv.cpu().numpy().astype(np.float64), top, lg, SMALL.vocab, "top-16")
+    full = np.concatenate([r["argmax"] for r in refs])
+    gap = np.concatenate([r["top2_gap"] for r in refs])
+    assert (ga[gap > 2 * LOGIT_TOL] == full[gap > 2 * LOGIT_TOL]).all()
 
 
 def test_copy_commit_mode_rejects_the_block_mask(small):
