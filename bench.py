@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--ar-steps", type=int, default=64)
     ap.add_argument("--no-pld", action="store_true", help="skip the batched PLD round measurement")
+    ap.add_argument("--no-program", action="store_true",
+                    help="skip the Copy-as-Decode program measurement (op-boundary steps, 7B-shaped layer)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="no timing: a few N = ROOF_N forwards and plain copies of a known size, for a "
                          "hardware-counter run that calibrates and measures the LM head's HBM traffic")
@@ -226,6 +228,9 @@ def main():
     # ---- batched PLD rounds (lookup -> verify forward -> accept, no host sync inside)
     pld = None if a.no_pld else pld_rounds(a, lay0, dev)
 
+    # ---- a whole Copy-as-Decode program with its op-boundary steps (7B-shaped layer)
+    program = None if a.no_program else cad_program(a, dev)
+
     # ---- autoregressive baseline: single-token teacher-forced forwards
     ar_us = timed(ar_graphs, max(2, a.steps // 4)) * 1e3 / a.ar_steps
     for r in per_n:
@@ -265,9 +270,164 @@ def main():
         "roofline": roof,
         "copy_commit_mode": copy_commit,
         "pld_rounds": pld,
+        "cad_program": program,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def cad_program(a, dev):
+    """A whole Copy-as-Decode program on the 7B-shaped layer: after a 4096-token document, 4096
+    output tokens as copy splices and <gen> bodies, with every op-boundary step of the grammar
+    (masked decisions over at most 11 ids, forced-template prefills), enqueued without a host
+    sync and replayed from one HIP graph.  Beside it: the same 4096 output tokens as one-token
+    forwards (autoregressive regeneration, eager), and per-step costs of a masked decision, a
+    free decision and a 3-token forced prefill at the program's mid-point context.  The layer's
+    weights are drawn on the device, N(0, 0.02), bf16 (timing does not depend on their values)."""
+    import numpy as np
+    import torch
+
+    from spec_verify_cad_amd import cad, synth
+    from spec_verify_cad_amd.configs import CONFIGS, cad_program_inputs
+    from spec_verify_cad_amd.program import DeviceProgram
+
+    wl = CONFIGS["qwen7_cad_program"]
+    shp = wl.shape
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    t = {}
+    for name, sh in synth.weight_shapes(shp).items():
+        t[name] = (torch.randn(sh, generator=gen, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+    lay = cad.DeviceLayer.from_tensors(shp, t)
+    doc, ops = cad_program_inputs(wl)
+    fwds = synth.cad_program_forwards(ops)
+    Ld, T = len(doc), wl.extra["total_out"]
+    fed = sum(f.n for f in fwds)
+    cap = ((Ld + max(fed, T) + 64 + 3) // 4) * 4
+    cache = cad.DeviceCache(shp, 1, cap)
+    dt = torch.from_numpy(doc[None].astype(np.int32)).to(dev)
+    cad.span_forward(lay, cache, dt, Ld, flags=cad.KV_ONLY | cad.COMMIT_ALL)
+    torch.cuda.synchronize()
+    assert int(cache.len[0]) == Ld
+    prog = DeviceProgram(lay, cache, doc, fwds, dev)
+
+    def run(st):
+        cache.len.fill_(Ld)
+        prog.enqueue(st)
+
+    stream = torch.cuda.current_stream()
+    run(stream)
+    torch.cuda.synchronize()
+    assert int(cache.len[0]) == Ld + fed
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1)
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(stream)
+    t0 = time.time()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap_stream):
+        run(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    log(f"program graph of {len(fwds)} forwards captured in {time.time() - t0:.1f}s")
+    g.replay()
+    torch.cuda.synchronize()
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    assert int(cache.len[0]) == Ld + fed
+
+    # autoregressive regeneration of the same output (copied and generated tokens), one token
+    # per forward with the full LM head
+    stream_toks = prog.fed_tokens(doc)
+    content, pos = [], 0
+    for f in fwds:
+        if f.role == "splice":
+            content += list(stream_toks[pos + len(f.lits):pos + f.n])
+        elif f.role == "gen_body":
+            content.append(stream_toks[pos])
+        pos += f.n
+    assert len(content) == T
+    ar_tok = torch.from_numpy(np.asarray(content, dtype=np.int32).reshape(-1, 1)).to(dev)
+    ar_out = torch.empty((1, 1), dtype=torch.int32, device=dev)
+    ws1 = cad.alloc_workspace(cad.span_forward_workspace(lay, 1, 1, cad.MASK_CAUSAL, 1, 1, cap, cad.COMMIT_ALL))
+
+    def ar(st):
+        cache.len.fill_(Ld)
+        for i in range(T):
+            cad.span_forward(lay, cache, ar_tok[i:i + 1], 1, flags=cad.COMMIT_ALL, argmax_out=ar_out, workspace=ws1,
+                             stream=st)
+
+    ar(stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    ar(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ar_ms = e0.elapsed_time(e1)
+
+    # per-step costs at the program's mid-point context: 32 steps of each kind from one graph
+    mid = Ld + fed // 2
+    one = torch.full((1, 1), synth.CAD_TOK["LT"], dtype=torch.int32, device=dev)
+    three = torch.tensor([[synth.CAD_TOK["COPY"], synth.CAD_TOK["SPACE_LINES"], synth.CAD_TOK["EQ_QUOTE"]]],
+                         dtype=torch.int32, device=dev)
+    al2 = torch.tensor([[synth.CAD_TOK["COPY"], synth.CAD_TOK["GEN"]]], dtype=torch.int32, device=dev)
+    al10 = torch.tensor([list(synth.CAD_DIGITS)], dtype=torch.int32, device=dev)
+    o1 = torch.empty(1, dtype=torch.int32, device=dev)
+    wsx = cad.alloc_workspace(max(cad.span_forward_workspace(lay, 1, n, cad.MASK_CAUSAL, 1, 1, cap, fl)
+                                  for n, fl in ((1, cad.COMMIT_ALL), (3, cad.COMMIT_ALL | cad.LOGITS_LAST))))
+    kinds = {
+        "masked_step": lambda st: cad.span_forward_allowed(lay, cache, one, 1, al2, 2, flags=cad.COMMIT_ALL,
+                                                           argmax_out=o1, workspace=wsx, stream=st),
+        "free_step": lambda st: cad.span_forward(lay, cache, one, 1, flags=cad.COMMIT_ALL, argmax_out=o1,
+                                                 workspace=wsx, stream=st),
+        "forced_prefill_L3": lambda st: cad.span_forward_allowed(lay, cache, three, 3, al10, 10,
+                                                                 flags=cad.COMMIT_ALL | cad.LOGITS_LAST,
+                                                                 argmax_out=o1, workspace=wsx, stream=st),
+    }
+    per_step = {}
+    for name, fn in kinds.items():
+        def body(st, fn=fn):
+            cache.len.fill_(mid)
+            for _ in range(32):
+                fn(st)
+        body(stream)
+        torch.cuda.synchronize()
+        gk = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gk, stream=cap_stream):
+            body(torch.cuda.current_stream())
+        gk.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(4):
+            gk.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_step[name] = round(e0.elapsed_time(e1) * 1e3 / (4 * 32), 2)
+    roles = {}
+    for f in fwds:
+        roles[f.role] = roles.get(f.role, 0) + 1
+    res = {"workload": f"Copy-as-Decode program: Qwen2.5-7B-shaped layer + LM head 152064, {Ld}-token document, "
+                       f"{T} output tokens in {len(ops)} ops ({sum(1 for o in ops if o[0] == 'copy')} copy splices), "
+                       f"{len(fwds)} forwards feeding {fed} tokens incl. the grammar's structural tokens",
+           "ms": round(ms, 3), "eager_ms": round(eager_ms, 3), "output_tok_s": round(T / (ms * 1e-3), 1),
+           "ar_ms": round(ar_ms, 3), "ar_tok_s": round(T / (ar_ms * 1e-3), 1),
+           "speedup_vs_ar": round(ar_ms / ms, 3), "forwards": roles,
+           "masked_forwards": sum(1 for f in fwds if f.allowed is not None),
+           "per_step_us": per_step,
+           "c_mask_us": round(per_step["masked_step"] - per_step["free_step"], 2),
+           "host_syncs_per_op": 0}
+    log(f"cad program: {ms:.1f} ms (eager {eager_ms:.1f}), AR {ar_ms:.1f} ms -> {ar_ms / ms:.2f}x; "
+        f"steps {per_step}")
+    del g
+    return res
 
 
 def pld_rounds(a, layer, dev):

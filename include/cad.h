@@ -182,12 +182,14 @@ int cad_span_forward(const cad_layer_desc *layer, const cad_kv_desc *kv,
  * the model's logits with the ids its state allows, e.g. {<, </} at an op boundary).  Only the
  * allowed rows of the LM head are read (A of them per row instead of the vocabulary).
  *
- *   allowed     [B*Nq, A] int32 ids; entries outside [0, vocab) are padding
+ *   flags       CAD_COMMIT_ALL and/or CAD_LOGITS_LAST (the decision after each sequence's last row
+ *               only, as at the end of a forced-template prefill or a copy splice); R = B*Nq rows,
+ *               or R = B with CAD_LOGITS_LAST
+ *   allowed     [R, A] int32 ids; entries outside [0, vocab) are padding
  *   A           1 .. CAD_MAX_ALLOWED
- *   flags       0 or CAD_COMMIT_ALL
- *   argmax_out  [B*Nq] int32 out: the allowed id with the largest logit, ties to the lowest id;
+ *   argmax_out  [R] int32 out: the allowed id with the largest logit, ties to the lowest id;
  *               -1 for a row whose set holds no valid id
- *   logits_out  [B*Nq, A] fp32 out, nullable: the logit at each allowed slot, -inf for padding
+ *   logits_out  [R, A] fp32 out, nullable: the logit at each allowed slot, -inf for padding
  *   hidden_out, workspace (cad_span_forward_workspace with the same B, Nq), stream: as for
  *               cad_span_forward; the cache rows are those of a full forward.
  * Errors: CAD_EINVAL, CAD_EUNSUPPORTED (A out of range, and as cad_span_forward), CAD_EWORKSPACE,

@@ -123,6 +123,14 @@ class DeviceLayer:
             self.t[name] = t
         self.desc = self.make_desc()
 
+    @classmethod
+    def from_tensors(cls, shape, tensors: dict) -> "DeviceLayer":
+        """A layer over device tensors the caller already holds (bf16 as int16 bit patterns)."""
+        self = cls.__new__(cls)
+        self.shape, self.t = shape, dict(tensors)
+        self.desc = self.make_desc()
+        return self
+
     def make_desc(self, **override) -> LayerDesc:
         s = self.shape
         t = dict(self.t, **override)

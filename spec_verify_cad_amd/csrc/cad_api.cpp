@@ -309,7 +309,7 @@ int span_forward_impl(const cad_layer_desc* L, const cad_kv_desc* kv, const int3
     if (allowed) {
         // grammar-masked step: logits of the allowed ids only, argmax, commit
         if (stage(ST_ALLOWED, stream, [&] {
-                return launch_allowed_argmax(fd, wb, L->w_lm, allowed, A, argmax_out, logits_out,
+                return launch_allowed_argmax(fd, wb, L->w_lm, allowed, A, last_only, argmax_out, logits_out,
                                              (flags & CAD_COMMIT_ALL) ? kv->len : nullptr, stream);
             }) != hipSuccess)
             return CAD_EHIP;
@@ -348,7 +348,7 @@ int cad_span_forward_allowed(const cad_layer_desc* L, const cad_kv_desc* kv, con
                              void* hidden_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!allowed || !argmax_out) return CAD_EINVAL;
     if (A < 1 || A > CAD_MAX_ALLOWED) return CAD_EUNSUPPORTED;
-    if (flags & ~CAD_COMMIT_ALL) return CAD_EINVAL;
+    if (flags & ~(CAD_COMMIT_ALL | CAD_LOGITS_LAST)) return CAD_EINVAL;
     return span_forward_impl(L, kv, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, argmax_out, hidden_out,
                              logits_out, allowed, A, workspace, workspace_bytes, stream);
 }

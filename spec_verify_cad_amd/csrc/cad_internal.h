@@ -78,7 +78,8 @@ hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, bool last_o
 // argmax over each row's allowed ids (final normed rows wb.u3 against those LM-head rows),
 // with the commit of the cache lengths
 hipError_t launch_allowed_argmax(const FwdDims& fd, const FwdBufs& wb, const void* w_lm, const int32_t* allowed, int A,
-                                 int32_t* argmax_out, float* logits_out, int32_t* kv_len, hipStream_t s);
+                                 bool last_only, int32_t* argmax_out, float* logits_out, int32_t* kv_len,
+                                 hipStream_t s);
 hipError_t launch_resid_norm(const FwdDims& fd, const float* base, const float* part, int slices, float* out_f32,
                              void* out_t, void* normed, bool last_only, float eps, const int32_t* len_snap,
                              hipStream_t s);

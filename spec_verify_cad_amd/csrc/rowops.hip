@@ -206,21 +206,22 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ pa
     }
 }
 
-// Grammar-masked argmax: one workgroup per row.  Each thread accumulates, for every allowed id of
-// the row, its strided share of the dot product of the final normed row with that LM-head row
-// (fp32); the shares are summed per id across the workgroup, then thread 0 takes the largest
-// logit (ties to the lowest id), writes the slot logits and, for the sequence's first row,
-// advances the cache length.
+// Grammar-masked argmax: one workgroup per row of u3 (rps rows per sequence: Nq, or 1 when only
+// each sequence's last row was normed).  Each thread accumulates, for every allowed id of the row,
+// its strided share of the dot product of the final normed row with that LM-head row (fp32); the
+// shares are summed per id across the workgroup, then thread 0 takes the largest logit (ties to
+// the lowest id), writes the slot logits and, for the sequence's first row, advances the cache
+// length by Nq.
 constexpr int AMAX = 16;
 template <typename T>
 __global__ __launch_bounds__(NT) void k_allowed_argmax(const T* __restrict__ u3, const T* __restrict__ wlm, int h,
-                                                       int V, const int32_t* __restrict__ allowed, int A, int Nq,
-                                                       int cap, const int32_t* __restrict__ len_snap,
+                                                       int V, const int32_t* __restrict__ allowed, int A, int rps,
+                                                       int Nq, int cap, const int32_t* __restrict__ len_snap,
                                                        int32_t* __restrict__ out, float* __restrict__ logits,
                                                        int32_t* __restrict__ kv_len) {
     static_assert(NT == 256, "the final sum reads four wave partials");
     __shared__ float red[NT / 64][AMAX];
-    const int r = blockIdx.x, b = r / Nq;
+    const int r = blockIdx.x, b = r / rps;
     if (!seq_ok(len_snap, b, Nq, cap)) return;
     int ids[AMAX];
     float acc[AMAX];
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(NT) void k_allowed_argmax(const T* __restrict__ u3,
         if (logits) logits[(size_t)r * A + a] = v;
     }
     out[r] = bi;
-    if (kv_len && r % Nq == 0) kv_len[b] = len_snap[b] + Nq;
+    if (kv_len && r % rps == 0) kv_len[b] = len_snap[b] + Nq;
 }
 
 // One wave per row.  The LM head ran on rps rows per sequence (Nq, or 1 for the last row only):
@@ -352,15 +353,18 @@ hipError_t launch_qkv_finish(const FwdDims& fd, const float* part, int slices, i
 }
 
 hipError_t launch_allowed_argmax(const FwdDims& fd, const FwdBufs& wb, const void* w_lm, const int32_t* allowed, int A,
-                                 int32_t* argmax_out, float* logits_out, int32_t* kv_len, hipStream_t s) {
+                                 bool last_only, int32_t* argmax_out, float* logits_out, int32_t* kv_len,
+                                 hipStream_t s) {
     if (A < 1 || A > AMAX) return hipErrorInvalidValue;
+    const int rps = last_only ? 1 : fd.Nq;
+    const int rows = fd.B * rps;
     if (fd.dtype == CAD_DTYPE_F32)
-        hipLaunchKernelGGL(k_allowed_argmax<float>, dim3(fd.M), dim3(NT), 0, s, (const float*)wb.u3,
-                           (const float*)w_lm, fd.h, fd.V, allowed, A, fd.Nq, fd.cap, wb.len_snap, argmax_out,
+        hipLaunchKernelGGL(k_allowed_argmax<float>, dim3(rows), dim3(NT), 0, s, (const float*)wb.u3,
+                           (const float*)w_lm, fd.h, fd.V, allowed, A, rps, fd.Nq, fd.cap, wb.len_snap, argmax_out,
                            logits_out, kv_len);
     else
-        hipLaunchKernelGGL(k_allowed_argmax<uint16_t>, dim3(fd.M), dim3(NT), 0, s, (const uint16_t*)wb.u3,
-                           (const uint16_t*)w_lm, fd.h, fd.V, allowed, A, fd.Nq, fd.cap, wb.len_snap, argmax_out,
+        hipLaunchKernelGGL(k_allowed_argmax<uint16_t>, dim3(rows), dim3(NT), 0, s, (const uint16_t*)wb.u3,
+                           (const uint16_t*)w_lm, fd.h, fd.V, allowed, A, rps, fd.Nq, fd.cap, wb.len_snap, argmax_out,
                            logits_out, kv_len);
     return hipGetLastError();
 }

@@ -211,3 +211,83 @@ def cad_program(seed: int, doc_len: int, total_out: int, median: float, sigma: f
         out += n
         copy_turn = not copy_turn
     return ops
+
+
+# Structural literals of the Copy-as-Decode grammar as single token ids (Copy-as-Decode,
+# Appendix A, "Qwen2.5 token identifiers").
+CAD_TOK = {"LT": 27, "LT_SLASH": 522, "GT": 29, "COPY": 8560, "GEN": 4370, "PROGRAM": 14906,
+           "SPACE_LINES": 5128, "EQ_QUOTE": 428, "QUOTE_SLASH": 9685, "SLASH_GT": 2577}
+
+
+def _char_id(c: str) -> int:
+    """Single printable characters in byte order, id = code - 33: the order that puts "<" at 27
+    and ">" at 29 in the table above (digit, hyphen and quote ids are not on the page)."""
+    return ord(c) - 33
+
+
+CAD_DIGITS = tuple(_char_id(c) for c in "0123456789")
+CAD_HYPHEN = _char_id("-")
+CAD_QUOTE = _char_id('"')
+LINE_TOKENS = 10   # document tokens per line, for the line numbers a copy tag carries
+
+
+@dataclass(frozen=True)
+class ProgramForward:
+    """One forward of a Copy-as-Decode program.
+
+    Its input is `lits` followed by the document tokens doc[src:src+n] when `doc` = (src, n),
+    or, when `from_prev`, the single token the previous forward chose.  The decision after its
+    last row is restricted to `allowed` (a masked step) or unrestricted (None)."""
+    role: str
+    lits: tuple = ()
+    doc: tuple | None = None
+    from_prev: bool = False
+    allowed: tuple | None = None
+
+    @property
+    def n(self) -> int:
+        return 1 if self.from_prev else len(self.lits) + (self.doc[1] if self.doc else 0)
+
+
+def cad_program_forwards(ops: list, line_tokens: int = LINE_TOKENS) -> list:
+    """The forwards a Copy-as-Decode program of `ops` runs after its prompt (Copy-as-Decode §2.3
+    step types and Appendix A states), with every choice a trained model would make taken from
+    the op schedule; only the <gen> bodies are the model's own tokens.
+
+    Per op: feed "<" and decide the op type in {copy, gen}.  A copy then feeds the forced
+    template (copy, " lines", '="') and decides the first digit; feeds each character of the
+    line range "i-j" (i, j = 1-based lines of `line_tokens` tokens), deciding the next one
+    (digits; digits or "-" inside the first number; digits or the closing quote inside the
+    second); and finally feeds the closing quote, the forced "/>" and the copied tokens in one
+    splice forward that decides the next op boundary in {"<", "</"}.  A gen feeds the forced
+    (gen, ">"), then its g body tokens, each the previous forward's free choice, then the
+    closing literal "</", gen, ">" one token at a time; the forward that feeds ">" decides the
+    next boundary.  After the last op the forced terminator ("</", program, ">") closes it."""
+    T = CAD_TOK
+    boundary = (T["LT"], T["LT_SLASH"])
+    digits = CAD_DIGITS
+    out = []
+    for op in ops:
+        out.append(ProgramForward("op_type", (T["LT"],), allowed=(T["COPY"], T["GEN"])))
+        if op[0] == "copy":
+            _, src, n = op
+            rng = f"{src // line_tokens + 1}-{(src + n - 1) // line_tokens + 1}"
+            out.append(ProgramForward("copy_open", (T["COPY"], T["SPACE_LINES"], T["EQ_QUOTE"]), allowed=digits))
+            second = False
+            for ch in rng:
+                if ch == "-":
+                    second = True
+                    nxt = digits
+                else:
+                    nxt = digits + ((CAD_QUOTE,) if second else (CAD_HYPHEN,))
+                out.append(ProgramForward("line_char", (_char_id(ch),), allowed=nxt))
+            out.append(ProgramForward("splice", (CAD_QUOTE, T["SLASH_GT"]), doc=(src, n), allowed=boundary))
+        else:
+            g = op[1]
+            out.append(ProgramForward("gen_open", (T["GEN"], T["GT"])))
+            out += [ProgramForward("gen_body", from_prev=True) for _ in range(g)]
+            out.append(ProgramForward("gen_close", (T["LT_SLASH"],)))
+            out.append(ProgramForward("gen_close", (T["GEN"],)))
+            out.append(ProgramForward("gen_close", (T["GT"],), allowed=boundary))
+    out.append(ProgramForward("close", (T["LT_SLASH"], T["PROGRAM"], T["GT"])))
+    return out

@@ -68,7 +68,7 @@ def test_host_argument_errors_return_before_launch():
     assert fa(ctypes.byref(d), ctypes.byref(kv), tok, 1, 1, 0, tok, 0, tok, None, None, tok, 1 << 30, None) == cad.CAD_EUNSUPPORTED
     assert fa(ctypes.byref(d), ctypes.byref(kv), tok, 1, 1, 0, tok, cad.MAX_ALLOWED + 1, tok, None, None, tok, 1 << 30,
               None) == cad.CAD_EUNSUPPORTED
-    assert fa(ctypes.byref(d), ctypes.byref(kv), tok, 1, 1, cad.LOGITS_LAST, tok, 4, tok, None, None, tok, 1 << 30,
+    assert fa(ctypes.byref(d), ctypes.byref(kv), tok, 1, 1, cad.KV_ONLY, tok, 4, tok, None, None, tok, 1 << 30,
               None) == cad.CAD_EINVAL
     assert fa(ctypes.byref(d), ctypes.byref(kv), None, 1, 1, 0, tok, 4, tok, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
     # lookup / accept argument errors

@@ -8,9 +8,10 @@ properties that hold at any size:
     greedy candidate that exercises the acceptance and the K/V compaction;
   * batched PLD rounds, 1.5B-shaped layer, 64 sequences x 32768-token contexts, 32 rounds with no
     host sync, two sequences replayed by the oracle round by round;
-  * Copy-as-Decode program, 7B-shaped layer, 4096-token document, 4096 output tokens: the first
-    256 output tokens replayed by the oracle, and the whole 8192-row cache checked against the
-    oracle's K/V of the emitted stream.
+  * Copy-as-Decode program with its op-boundary steps (masked decisions, forced templates, copy
+    splices, free generation), 7B-shaped layer, 4096-token document, 4096 output tokens: the
+    forwards of the first 256 program tokens replayed by the oracle, and the whole cache checked
+    against the oracle's K/V of the program stream.
 """
 import numpy as np
 import pytest
@@ -18,10 +19,11 @@ import torch
 
 import oracle as O
 from spec_verify_cad_amd import cad, synth
+from spec_verify_cad_amd.program import DeviceProgram
 from spec_verify_cad_amd.configs import (CONFIGS, block_verify_context, cad_program_inputs, copy_sweep_inputs,
                                          pld_contexts)
 
-from gpu_util import (argmax_check, compare, compare_cache, log, logit_tol, prefill, run_forward)
+from gpu_util import (NEAR_TIE, argmax_check, compare, compare_cache, log, logit_tol, prefill, run_forward)
 from helpers import oracle_layer
 
 pytestmark = pytest.mark.gpu
@@ -233,68 +235,61 @@ def test_pld_batch_rounds_full_size(qwen15):
 
 
 # ---------------------------------------------------------------------------------------------
-# config 3: a Copy-as-Decode program (copy spans and greedy gen segments)
+# config 3: a Copy-as-Decode program with its op-boundary steps (masked decisions, forced
+# templates, copy splices, free generation)
 # ---------------------------------------------------------------------------------------------
 def test_cad_program_full_size(qwen7):
     wl = CONFIGS["qwen7_cad_program"]
     _, dl, OL = qwen7
     doc, ops = cad_program_inputs(wl)
-    Ld, T = len(doc), wl.extra["total_out"]
-    cap = Ld + T + 8
+    fwds = synth.cad_program_forwards(ops)
+    Ld = len(doc)
+    fed = sum(f.n for f in fwds)
+    cap = ((Ld + fed + 8 + 3) // 4) * 4
     cache = cad.DeviceCache(wl.shape, 1, cap)
     log("cad program: prefill document")
     prefill(dl, cache, doc[None])
-    # every forward writes its argmax rows into one device buffer; a gen forward reads its input
-    # token straight from the previous forward's last argmax (no host sync in the program)
-    total_rows = sum(o[2] if o[0] == "copy" else o[1] for o in ops)
-    preds = torch.full((total_rows + 1,), -1, dtype=torch.int32, device="cuda")
-    doc_t = T32(doc)
-    ws = {}
-    pos, last = 0, None            # rows written so far; pointer of the last forward's final row
-    stream_src = []                 # per output token: ("doc", index) or ("gen", pred row)
-    log(f"cad program: {len(ops)} ops")
-    for op in ops:
-        if op[0] == "copy":
-            _, src, N = op
-            toks = doc_t[src:src + N].view(1, N)
-            stream_src += [("doc", src + i) for i in range(N)]
-        else:
-            N = 1
-        for rep in range(1 if op[0] == "copy" else op[1]):
-            if op[0] == "gen":
-                toks = preds[last:last + 1].view(1, 1)
-                stream_src.append(("gen", last))
-            if N not in ws:
-                ws[N] = cad.alloc_workspace(cad.span_forward_workspace(dl, 1, N, cad.MASK_CAUSAL, 1, 1, cap,
-                                                                       cad.COMMIT_ALL))
-            cad.span_forward(dl, cache, toks, N, flags=cad.COMMIT_ALL, argmax_out=preds[pos:pos + N].view(1, N),
-                             workspace=ws[N])
-            pos += N
-            last = pos - 1
+    prog = DeviceProgram(dl, cache, doc, fwds)
+    log(f"cad program: {len(ops)} ops, {len(fwds)} forwards, {fed} fed tokens")
+    prog.enqueue()
     torch.cuda.synchronize()
-    assert int(cache.len[0]) == Ld + T
-    pred_h = preds.cpu().numpy()
-    stream = np.array([doc[i] if kind == "doc" else pred_h[i] for kind, i in stream_src])
-    assert len(stream) == T
-    # the whole cache against the oracle's K/V of document + emitted stream (a one-layer
-    # model's cached K/V depend only on token and position)
-    log("cad program: oracle K/V of 8192 rows")
-    full = np.concatenate([doc, stream])
-    oc_all = O.cache_from_tokens(OL, full, cap)
-    for lo in range(0, Ld + T, 512):
-        compare_cache(cache, 0, oc_all, lo, min(lo + 512, Ld + T), "bf16", what=f"cache rows {lo}")
-    # the first 256 output tokens replayed by the oracle, forward by forward
-    log("cad program: oracle replay of the first 256 output tokens")
+    assert int(cache.len[0]) == Ld + fed
+    dec = prog.decisions.cpu().numpy()
+    stream = prog.fed_tokens(doc)
+    assert len(stream) == fed
+    # every masked decision lies in its set; every free one is a vocabulary id
+    for f, pf in enumerate(fwds):
+        if pf.allowed is not None:
+            assert int(dec[f]) in pf.allowed, f"forward {f} ({pf.role}) chose {dec[f]} outside {pf.allowed}"
+        else:
+            assert 0 <= dec[f] < wl.shape.vocab
+    # the whole cache against the oracle's K/V of document + program stream (a one-layer model's
+    # cached K/V depend only on token and position)
+    log(f"cad program: oracle K/V of {Ld + fed} rows")
+    oc_all = O.cache_from_tokens(OL, np.concatenate([doc, stream]), cap)
+    for lo in range(0, Ld + fed, 512):
+        compare_cache(cache, 0, oc_all, lo, min(lo + 512, Ld + fed), "bf16", what=f"cache rows {lo}")
+    # the forwards that feed the first 256 program tokens, replayed by the oracle: each decision
+    # against the oracle's (masked) argmax on its last row
+    log("cad program: oracle replay of the first 256 fed tokens")
+    tol = logit_tol(wl.shape.hidden)
     oc = O.cache_from_tokens(OL, doc, cap)
-    row, out = 0, 0
-    for op in ops:
-        if out >= 256:
+    pos, roles = 0, set()
+    for f, pf in enumerate(fwds):
+        if pos >= 256:
             break
-        N, reps = (op[2], 1) if op[0] == "copy" else (1, op[1])
-        for _ in range(reps):
-            toks = stream[out:out + N]
-            ref = O.span_forward(OL, oc, toks)
-            argmax_check(pred_h[row:row + N], ref, None, what=f"cad forward at output {out}",
-                         tol=logit_tol(wl.shape.hidden))
-            row += N
-            out += N
+        ref = O.span_forward(OL, oc, stream[pos:pos + pf.n])
+        last = {k: ref[k][-1:] for k in ("logits", "argmax", "top2_gap")}
+        if pf.allowed is None:
+            argmax_check(dec[f:f + 1], last, None, what=f"forward {f} ({pf.role})", tol=tol)
+        else:
+            al = np.asarray([pf.allowed], dtype=np.int64)
+            best, _, gap = O.masked_argmax(last["logits"], al, wl.shape.vocab)
+            if gap[0] > max(NEAR_TIE, 2 * tol):
+                assert dec[f] == best[0], f"forward {f} ({pf.role}): masked {dec[f]} vs oracle {best[0]}"
+            else:
+                lg = last["logits"][0]
+                assert lg[list(pf.allowed)].max() - lg[dec[f]] <= 2 * tol
+        roles.add(pf.role)
+        pos += pf.n
+    assert {"op_type", "copy_open", "line_char", "splice", "gen_open", "gen_body", "gen_close"} <= roles

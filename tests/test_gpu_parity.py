@@ -316,37 +316,40 @@ def _check_masked(g_a, g_v, al, ref_logits, vocab, what):
     return int(unique.sum())
 
 
-@pytest.mark.parametrize("Nq,A,commit", [(1, 12, True), (5, 16, True), (3, 1, False)])
-def test_small_bf16_grammar_masked_argmax_matches_oracle(small, Nq, A, commit):
+@pytest.mark.parametrize("Nq,A,commit,last", [(1, 12, True, False), (5, 16, True, False), (3, 1, False, False),
+                                               (4, 11, True, True), (1, 2, False, True)])
+def test_small_bf16_grammar_masked_argmax_matches_oracle(small, Nq, A, commit, last):
     """cad_span_forward_allowed: the argmax over each row's allowed ids equals the oracle's
-    masked argmax on the oracle forward's logits; the cache rows, hidden output and commit are
-    those of the full forward."""
+    masked argmax on the oracle forward's logits (each sequence's last row only, with
+    CAD_LOGITS_LAST); the cache rows, hidden output and commit are those of the full forward."""
     w, dl, OL = small
-    log(f"small bf16 masked argmax Nq={Nq} A={A} commit={commit}")
+    log(f"small bf16 masked argmax Nq={Nq} A={A} commit={commit} last={last}")
     B, L0, cap = 3, 150, 320
     ctx = np.stack([synth.uniform_tokens(50 + b, L0, SMALL.vocab) for b in range(B)])
     span = np.stack([synth.uniform_tokens(110 + b, Nq, SMALL.vocab) for b in range(B)])
     ocs = [O.cache_from_tokens(OL, ctx[b], cap) for b in range(B)]
     refs = [O.span_forward(OL, ocs[b], span[b]) for b in range(B)]       # appends the span rows to ocs[b]
-    ref_logits = np.concatenate([r["logits"] for r in refs])
+    sel = slice(Nq - 1, Nq) if last else slice(0, Nq)
+    ref_logits = np.concatenate([r["logits"][sel] for r in refs])
     ref_hidden = np.concatenate([r["hidden_out"] for r in refs])
-    al = _allowed_sets(7 * Nq + A, B * Nq, A, SMALL.vocab, np.concatenate([r["argmax"] for r in refs]))
+    R = B if last else B * Nq
+    al = _allowed_sets(7 * Nq + A, R, A, SMALL.vocab, np.concatenate([r["argmax"][sel] for r in refs]))
     cache = cad.DeviceCache(SMALL, B, cap)
     prefill(dl, cache, ctx, chunk=64)
     t = torch.from_numpy(np.ascontiguousarray(span, dtype=np.int32)).cuda()
     ta = torch.from_numpy(al).cuda()
-    am = torch.full((B * Nq,), -7, dtype=torch.int32, device="cuda")
-    lv = torch.zeros((B * Nq, A), dtype=torch.float32, device="cuda")
+    am = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    lv = torch.zeros((R, A), dtype=torch.float32, device="cuda")
     hid = torch.zeros((B * Nq, SMALL.hidden), dtype=torch.int16, device="cuda")
-    cad.span_forward_allowed(dl, cache, t, Nq, ta, A, flags=cad.COMMIT_ALL if commit else 0, argmax_out=am,
-                             logits_out=lv, hidden_out=hid)
+    fl = (cad.COMMIT_ALL if commit else 0) | (cad.LOGITS_LAST if last else 0)
+    cad.span_forward_allowed(dl, cache, t, Nq, ta, A, flags=fl, argmax_out=am, logits_out=lv, hidden_out=hid)
     torch.cuda.synchronize()
     assert list(cache.len.cpu().numpy()) == [L0 + Nq if commit else L0] * B
     dh = np.abs(to_f64(hid, "bf16") - ref_hidden)
     assert (dh <= hidden_tol(ref_hidden, SMALL.ffn)).all(), f"hidden {dh.max()}"
     n_unique = _check_masked(am.cpu().numpy(), lv.cpu().numpy().astype(np.float64), al, ref_logits, SMALL.vocab,
                              f"Nq={Nq} A={A}")
-    assert n_unique >= (B * Nq) // 2
+    assert n_unique >= R // 2
     for b in range(B):
         compare_cache(cache, b, ocs[b], L0, L0 + Nq, "bf16", what=f"masked rows b={b}")
 
