@@ -206,53 +206,66 @@ __global__ __launch_bounds__(256) void k_qkv_finish(const float* __restrict__ pa
     }
 }
 
-// Grammar-masked argmax: one workgroup per row of u3 (rps rows per sequence: Nq, or 1 when only
-// each sequence's last row was normed).  Each thread accumulates, for every allowed id of the row,
-// its strided share of the dot product of the final normed row with that LM-head row (fp32); the
-// shares are summed per id across the workgroup, then thread 0 takes the largest logit (ties to
-// the lowest id), writes the slot logits and, for the sequence's first row, advances the cache
-// length by Nq.
+// Grammar-masked argmax: one workgroup of AMAX waves per row of u3 (rps rows per sequence: Nq,
+// or 1 when only each sequence's last row was normed).  Wave a computes the logit of allowed
+// slot a, the dot product of the final normed row with that LM-head row (16-byte vector loads,
+// fp32 sums); then thread 0 takes the largest logit (ties to the lowest id), writes the slot
+// logits and, for the sequence's first row, advances the cache length by Nq.
 constexpr int AMAX = 16;
+__device__ __forceinline__ float dot_vec(uint4 x, uint4 w) {
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ws[4] = {w.x, w.y, w.z, w.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc += __uint_as_float(xs[i] << 16) * __uint_as_float(ws[i] << 16);
+        acc += __uint_as_float(xs[i] & 0xFFFF0000u) * __uint_as_float(ws[i] & 0xFFFF0000u);
+    }
+    return acc;
+}
+__device__ __forceinline__ float dot_vec(float4 x, float4 w) { return x.x * w.x + x.y * w.y + x.z * w.z + x.w * w.w; }
+template <typename T> struct VecOf;
+template <> struct VecOf<uint16_t> { using type = uint4; static constexpr int n = 8; };
+template <> struct VecOf<float> { using type = float4; static constexpr int n = 4; };
+
 template <typename T>
-__global__ __launch_bounds__(NT) void k_allowed_argmax(const T* __restrict__ u3, const T* __restrict__ wlm, int h,
-                                                       int V, const int32_t* __restrict__ allowed, int A, int rps,
-                                                       int Nq, int cap, const int32_t* __restrict__ len_snap,
-                                                       int32_t* __restrict__ out, float* __restrict__ logits,
-                                                       int32_t* __restrict__ kv_len) {
-    static_assert(NT == 256, "the final sum reads four wave partials");
-    __shared__ float red[NT / 64][AMAX];
+__global__ __launch_bounds__(AMAX * 64) void k_allowed_argmax(const T* __restrict__ u3, const T* __restrict__ wlm,
+                                                              int h, int V, const int32_t* __restrict__ allowed,
+                                                              int A, int rps, int Nq, int cap,
+                                                              const int32_t* __restrict__ len_snap,
+                                                              int32_t* __restrict__ out, float* __restrict__ logits,
+                                                              int32_t* __restrict__ kv_len) {
+    using VT = typename VecOf<T>::type;
+    __shared__ float val[AMAX];
+    __shared__ int idv[AMAX];
     const int r = blockIdx.x, b = r / rps;
     if (!seq_ok(len_snap, b, Nq, cap)) return;
-    int ids[AMAX];
-    float acc[AMAX];
-#pragma unroll
-    for (int a = 0; a < AMAX; ++a) {
-        const int id = a < A ? allowed[(size_t)r * A + a] : -1;
-        ids[a] = (id >= 0 && id < V) ? id : -1;
-        acc[a] = 0.f;
-    }
-    for (int j = threadIdx.x; j < h; j += NT) {
-        const float x = Elt<T>::ld(u3, (size_t)r * h + j);
-#pragma unroll
-        for (int a = 0; a < AMAX; ++a)
-            if (ids[a] >= 0) acc[a] += x * Elt<T>::ld(wlm, (size_t)ids[a] * h + j);
-    }
-#pragma unroll
-    for (int a = 0; a < AMAX; ++a) {
-        const float v = wave_sum(acc[a]);
-        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6][a] = v;
+    const int lane = threadIdx.x & 63, a = threadIdx.x >> 6;
+    if (a < A) {
+        const int raw = allowed[(size_t)r * A + a];
+        const int id = (raw >= 0 && raw < V) ? raw : -1;
+        float acc = 0.f;
+        if (id >= 0) {
+            const VT* x = (const VT*)(u3 + (size_t)r * h);
+            const VT* w = (const VT*)(wlm + (size_t)id * h);
+            const int nv = h / VecOf<T>::n;
+#pragma unroll 4
+            for (int v = lane; v < nv; v += 64) acc += dot_vec(x[v], w[v]);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) {
+            val[a] = acc;
+            idv[a] = id;
+        }
     }
     __syncthreads();
     if (threadIdx.x != 0) return;
     float best = -INFINITY;
     int bi = -1;
-    for (int a = 0; a < A; ++a) {
-        float v = -INFINITY;
-        if (ids[a] >= 0) {
-            v = (red[0][a] + red[1][a]) + (red[2][a] + red[3][a]);
-            if (bi < 0 || v > best || (v == best && ids[a] < bi)) { best = v; bi = ids[a]; }
-        }
-        if (logits) logits[(size_t)r * A + a] = v;
+    for (int k = 0; k < A; ++k) {
+        const int id = idv[k];
+        const float v = id >= 0 ? val[k] : -INFINITY;
+        if (id >= 0 && (bi < 0 || v > best || (v == best && id < bi))) { best = v; bi = id; }
+        if (logits) logits[(size_t)r * A + k] = v;
     }
     out[r] = bi;
     if (kv_len && r % rps == 0) kv_len[b] = len_snap[b] + Nq;
@@ -359,11 +372,11 @@ hipError_t launch_allowed_argmax(const FwdDims& fd, const FwdBufs& wb, const voi
     const int rps = last_only ? 1 : fd.Nq;
     const int rows = fd.B * rps;
     if (fd.dtype == CAD_DTYPE_F32)
-        hipLaunchKernelGGL(k_allowed_argmax<float>, dim3(rows), dim3(NT), 0, s, (const float*)wb.u3,
+        hipLaunchKernelGGL(k_allowed_argmax<float>, dim3(rows), dim3(AMAX * 64), 0, s, (const float*)wb.u3,
                            (const float*)w_lm, fd.h, fd.V, allowed, A, rps, fd.Nq, fd.cap, wb.len_snap, argmax_out,
                            logits_out, kv_len);
     else
-        hipLaunchKernelGGL(k_allowed_argmax<uint16_t>, dim3(rows), dim3(NT), 0, s, (const uint16_t*)wb.u3,
+        hipLaunchKernelGGL(k_allowed_argmax<uint16_t>, dim3(rows), dim3(AMAX * 64), 0, s, (const uint16_t*)wb.u3,
                            (const uint16_t*)w_lm, fd.h, fd.V, allowed, A, rps, fd.Nq, fd.cap, wb.len_snap, argmax_out,
                            logits_out, kv_len);
     return hipGetLastError();
