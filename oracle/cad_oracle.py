@@ -203,18 +203,30 @@ def kv_group(L: Layer, h: int) -> int:
     return h // (L.n_q_heads // L.n_kv_heads)
 
 
-def tail(L: Layer, x: np.ndarray, o: np.ndarray) -> dict:
-    """Everything after attention: O projection + residual, SwiGLU MLP + residual, final
-    norm, LM head, argmax.  x: layer input rows [n, hidden]; o: stored attention output."""
+def layer_block(L: Layer, x: np.ndarray, o: np.ndarray) -> dict:
+    """Everything of a layer after attention: O projection + residual, SwiGLU MLP + residual,
+    and the RMSNorm of the result (the next layer's normed input, or the final norm).
+    x: layer input rows [n, hidden]; o: stored attention output."""
     h1 = round_f32(x + o @ L.wo.T)
     u2 = L.rnd(rms_norm(h1, L.eps))                           # R5
     act = L.rnd(silu(u2 @ L.wg.T) * (u2 @ L.wu.T))            # R6
     h2 = round_f32(h1 + act @ L.wd.T)
     hidden_out = L.rnd(h2)                                    # R7
     u3 = L.rnd(rms_norm(h2, L.eps))                           # R8
+    return {"h1": h1, "u2": u2, "act": act, "h2": h2, "hidden_out": hidden_out, "u3": u3}
+
+
+def lm_head(L: Layer, u3: np.ndarray) -> dict:
+    """Logits of the final normed rows, their argmax (ties to the lowest id) and top-2 gap."""
     logits = round_f32(u3 @ L.wlm.T)
-    return {"h1": h1, "u2": u2, "act": act, "h2": h2, "hidden_out": hidden_out, "u3": u3,
-            "logits": logits, "argmax": argmax_lowest(logits), "top2_gap": top2_gap(logits)}
+    return {"logits": logits, "argmax": argmax_lowest(logits), "top2_gap": top2_gap(logits)}
+
+
+def tail(L: Layer, x: np.ndarray, o: np.ndarray) -> dict:
+    """Everything after attention of a one-layer model: the layer block, then the LM head."""
+    out = layer_block(L, x, o)
+    out.update(lm_head(L, out["u3"]))
+    return out
 
 
 def argmax_lowest(logits: np.ndarray) -> np.ndarray:
@@ -309,13 +321,9 @@ def cache_from_tokens(L: Layer, tokens, cap: int, chunk: int = 4096) -> Cache:
 # forwards
 # ---------------------------------------------------------------------------------------
 
-def decode_one(L: Layer, cache: Cache, token: int) -> dict:
-    """One autoregressive step: the token at position len is appended, then attends to
-    slots [0, len] one query head at a time; len grows by one."""
-    p = cache.length
-    if p + 1 > cache.cap:
-        raise ValueError("cache capacity exceeded")
-    x, u = embed_norm(L, [token])
+def _decode_attend(L: Layer, cache: Cache, u: np.ndarray, p: int):
+    """Decode-step attention of one normed row at position p: its K/V are written to slot p,
+    then each query head attends to slots [0, p].  Returns q, k, v and the stored output."""
     q, k, v = qkv_rows(L, u, [p])
     cache.K[:, p] = k[0]
     cache.V[:, p] = v[0]
@@ -325,7 +333,17 @@ def decode_one(L: Layer, cache: Cache, token: int) -> dict:
         keys, vals = cache.K[g, : p + 1], cache.V[g, : p + 1]
         scores = keys @ q[0, h] / math.sqrt(L.head_dim)
         o[h] = softmax_checked(scores) @ vals
-    o = L.rnd(o.reshape(1, -1))                               # R4
+    return q, k, v, L.rnd(o.reshape(1, -1))                  # R4
+
+
+def decode_one(L: Layer, cache: Cache, token: int) -> dict:
+    """One autoregressive step: the token at position len is appended, then attends to
+    slots [0, len] one query head at a time; len grows by one."""
+    p = cache.length
+    if p + 1 > cache.cap:
+        raise ValueError("cache capacity exceeded")
+    x, u = embed_norm(L, [token])
+    q, k, v, o = _decode_attend(L, cache, u, p)
     cache.length = p + 1
     out = tail(L, x, o)
     out.update(q=q, k=k, v=v, o=o, u=u, x=x)
@@ -373,22 +391,89 @@ def span_forward(L: Layer, cache: Cache, tokens, mode: str = "causal", W: int = 
         raise ValueError("cache capacity exceeded")
     slots, pos, mask = span_layout(base, n, mode, W, D)
     x, u = embed_norm(L, tokens)
+    q, k, v, o = _span_attend(L, cache, u, pos, slots, mask)
+    if commit:
+        cache.length = base + n
+    out = tail(L, x, o)
+    out.update(q=q, k=k, v=v, o=o, u=u, x=x, positions=pos, slots=slots)
+    return out
+
+
+def _span_attend(L: Layer, cache: Cache, u: np.ndarray, pos, slots, mask):
+    """Span attention of normed rows u: all rows write K/V to their slots first, then every
+    row attends through the explicit mask.  Returns q, k, v and the stored output."""
+    n = u.shape[0]
     q, k, v = qkv_rows(L, u, pos)
     cache.K[:, slots] = k.transpose(1, 0, 2)
     cache.V[:, slots] = v.transpose(1, 0, 2)
-    S = base + n
+    S = mask.shape[1]
     o = np.zeros((n, L.n_q_heads, L.head_dim))
     for h in range(L.n_q_heads):
         g = kv_group(L, h)
         scores = q[:, h, :] @ cache.K[g, :S].T / math.sqrt(L.head_dim)
         scores = np.where(mask, scores, -np.inf)
         o[:, h, :] = softmax_checked(scores) @ cache.V[g, :S]
-    o = L.rnd(o.reshape(n, -1))                               # R4
+    return q, k, v, L.rnd(o.reshape(n, -1))                   # R4
+
+
+# ---------------------------------------------------------------------------------------
+# full-depth stacks: the same layer repeated with its own weights and cache
+# ---------------------------------------------------------------------------------------
+# Copy-as-Decode §2.4 and Table 11 run the span forward through whole models.  A stack is
+# a list of layers: the embedding of the first and the LM head of the last are used.  Layer
+# l > 0 takes the previous layer's residual output h2 as its input x and that output's RMSNorm
+# u3 as its normed input (every norm has gain 1, so the next layer's input norm and the
+# final norm are the same operation).  All caches of a stack hold the same length.
+
+def stack_span_forward(layers: list, caches: list, tokens, mode: str = "causal", W: int = 1,
+                       D: int = 0, commit: bool = True) -> dict:
+    """One parallel forward of n tokens through every layer of a stack (causal span or
+    block-triangular mask, as `span_forward`); commit=True advances every cache by n."""
+    tokens = np.asarray(tokens)
+    n, base = len(tokens), caches[0].length
+    if any(c.length != base for c in caches):
+        raise ValueError("stack caches disagree in length")
+    if base + n > caches[0].cap:
+        raise ValueError("cache capacity exceeded")
+    slots, pos, mask = span_layout(base, n, mode, W, D)
+    x, u = embed_norm(layers[0], tokens)
+    for L, c in zip(layers, caches):
+        _, _, _, o = _span_attend(L, c, u, pos, slots, mask)
+        blk = layer_block(L, x, o)
+        x, u = blk["h2"], blk["u3"]
     if commit:
-        cache.length = base + n
-    out = tail(L, x, o)
-    out.update(q=q, k=k, v=v, o=o, u=u, x=x, positions=pos, slots=slots)
-    return out
+        for c in caches:
+            c.length = base + n
+    blk.update(lm_head(layers[-1], u))
+    blk.update(positions=pos, slots=slots)
+    return blk
+
+
+def stack_decode_one(layers: list, caches: list, token: int) -> dict:
+    """One autoregressive step through a stack (decode-step attention in every layer)."""
+    p = caches[0].length
+    if any(c.length != p for c in caches):
+        raise ValueError("stack caches disagree in length")
+    if p + 1 > caches[0].cap:
+        raise ValueError("cache capacity exceeded")
+    x, u = embed_norm(layers[0], [token])
+    for L, c in zip(layers, caches):
+        _, _, _, o = _decode_attend(L, c, u, p)
+        blk = layer_block(L, x, o)
+        x, u = blk["h2"], blk["u3"]
+    for c in caches:
+        c.length = p + 1
+    blk.update(lm_head(layers[-1], u))
+    return blk
+
+
+def stack_prefill(layers: list, tokens, cap: int, chunk: int = 512) -> list:
+    """Caches of every layer for a token prefix: causal span forwards over chunks of it."""
+    caches = [Cache(L.n_kv_heads, cap, L.head_dim) for L in layers]
+    tokens = np.asarray(tokens)
+    for s in range(0, len(tokens), chunk):
+        stack_span_forward(layers, caches, tokens[s:s + chunk], "causal")
+    return caches
 
 
 # ---------------------------------------------------------------------------------------
