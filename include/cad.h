@@ -202,6 +202,32 @@ int cad_span_forward_allowed(const cad_layer_desc *layer, const cad_kv_desc *kv,
                              int32_t *argmax_out, float *logits_out, void *hidden_out,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * cad_stack_span_forward — the span forward through a whole stack of n_layers decoder layers
+ * (Copy-as-Decode §2.4 splices a copy span through the full model; its Table 11 times whole
+ * models).  Same arguments and outputs as cad_span_forward, with:
+ *   layers   [n_layers] descriptors of identical shape, dtype, eps and rope base; the embedding
+ *            of layers[0] and the LM head of layers[n_layers-1] are used (those fields of the
+ *            other layers are ignored and may be NULL)
+ *   kvs      [n_layers] caches, one per layer, of identical B and cap; the lengths and error
+ *            flags are those of kvs[0] (every layer's rows are written at kvs[0].len and only
+ *            kvs[0].len is advanced); kvs[l].len / .err are ignored for l > 0
+ * Layer l+1 takes layer l's residual output as its input and that output's RMSNorm (gain 1) as
+ * its normed input.  With CAD_KV_ONLY every layer but the last runs in full (their outputs feed
+ * the next layer's K/V) and the last writes its K/V rows only.
+ * Errors: as cad_span_forward; CAD_EINVAL also for n_layers outside 1..CAD_MAX_LAYERS or layers
+ * that disagree in shape.
+ */
+#define CAD_MAX_LAYERS 256
+int cad_stack_span_forward(const cad_layer_desc *layers, int n_layers, const cad_kv_desc *kvs,
+                           const int32_t *tokens, int B, int Nq, int mode, int W, int D, int flags,
+                           int32_t *argmax_out, void *hidden_out, float *logits_out,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+/* Workspace of cad_stack_span_forward (0 for an invalid shape); the buffers are reused by every
+ * layer, so this is the one-layer size (the full one when n_layers > 1, even with CAD_KV_ONLY). */
+size_t cad_stack_span_forward_workspace(const cad_layer_desc *layers, int n_layers, int B, int Nq, int mode,
+                                        int W, int D, int cap, int flags);
+
 /* Bytes of workspace cad_span_forward needs for these arguments and flags (0 on invalid
  * arguments).  A CAD_KV_ONLY forward needs far less than a full one. */
 size_t cad_span_forward_workspace(const cad_layer_desc *layer, int B, int Nq, int mask_mode,

@@ -56,6 +56,11 @@ def lib() -> ctypes.CDLL:
     L.cad_span_forward.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(KVDesc), vp, i32, i32, i32, i32, i32,
                                    i32, vp, vp, vp, vp, sz, vp]
     L.cad_span_forward.restype = i32
+    L.cad_stack_span_forward.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(KVDesc), vp, i32, i32, i32,
+                                         i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.cad_stack_span_forward.restype = i32
+    L.cad_stack_span_forward_workspace.argtypes = [ctypes.POINTER(LayerDesc), i32, i32, i32, i32, i32, i32, i32, i32]
+    L.cad_stack_span_forward_workspace.restype = ctypes.c_size_t
     L.cad_span_forward_allowed.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(KVDesc), vp, i32, i32, i32, vp,
                                            i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.cad_span_forward_allowed.restype = i32
@@ -159,6 +164,30 @@ class DeviceCache:
                            shape.n_kv_heads, shape.head_dim, DTYPE_BF16 if shape.dtype == "bf16" else DTYPE_F32)
 
 
+class DeviceStack:
+    """A stack of layers of one shape: the embedding of the first and the LM head of the last
+    are used.  `descs` is the descriptor array the stack call takes."""
+
+    def __init__(self, layers: list):
+        self.layers = list(layers)
+        self.shape = self.layers[0].shape
+        self.n = len(self.layers)
+        self.descs = (LayerDesc * self.n)(*[l.desc for l in self.layers])
+
+
+class StackCache:
+    """One KV cache per layer of a stack, all sharing one length tensor (and layer 0's error
+    flags, which the stack call uses)."""
+
+    def __init__(self, shape, n_layers: int, B: int, cap: int, device="cuda"):
+        import torch
+        self.shape, self.B, self.cap, self.n = shape, B, cap, n_layers
+        self.len = torch.zeros(B, dtype=torch.int32, device=device)
+        self.caches = [DeviceCache(shape, B, cap, device=device, len_tensor=self.len) for _ in range(n_layers)]
+        self.err = self.caches[0].err
+        self.descs = (KVDesc * n_layers)(*[c.desc for c in self.caches])
+
+
 # ---------------------------------------------------------------------------------------
 # the three calls
 # ---------------------------------------------------------------------------------------
@@ -202,6 +231,28 @@ def span_forward(layer: DeviceLayer, cache: DeviceCache, tokens, Nq: int, mode: 
     _check(lib().cad_span_forward(ctypes.byref(layer.desc), ctypes.byref(cache.desc), _ptr(tokens), B, Nq, mode, W, D,
                                   flags, _ptr(argmax_out), _ptr(hidden_out), _ptr(logits_out), _ptr(workspace),
                                   workspace.numel(), _stream(stream)), "cad_span_forward")
+    return workspace
+
+
+def stack_span_forward_workspace(stack: DeviceStack, B: int, Nq: int, mode: int = MASK_CAUSAL, W: int = 1,
+                                 D: int = 1, cap: int = 0, flags: int = 0) -> int:
+    n = lib().cad_stack_span_forward_workspace(stack.descs, stack.n, B, Nq, mode, W, D, cap, flags)
+    if n == 0:
+        raise CadError(CAD_EINVAL, "cad_stack_span_forward_workspace")
+    return n
+
+
+def stack_span_forward(stack: DeviceStack, cache: StackCache, tokens, Nq: int, mode: int = MASK_CAUSAL, W: int = 1,
+                       D: int = 1, flags: int = 0, argmax_out=None, hidden_out=None, logits_out=None,
+                       workspace=None, stream=None):
+    if cache.n != stack.n:
+        raise ValueError("one cache per layer")
+    B = cache.B
+    if workspace is None:
+        workspace = alloc_workspace(stack_span_forward_workspace(stack, B, Nq, mode, W, D, cache.cap, flags))
+    _check(lib().cad_stack_span_forward(stack.descs, stack.n, cache.descs, _ptr(tokens), B, Nq, mode, W, D, flags,
+                                        _ptr(argmax_out), _ptr(hidden_out), _ptr(logits_out), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)), "cad_stack_span_forward")
     return workspace
 
 

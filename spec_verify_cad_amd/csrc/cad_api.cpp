@@ -196,138 +196,188 @@ size_t cad_span_forward_workspace(const cad_layer_desc* L, int B, int Nq, int mo
     return fwd_carve(fd, nullptr, (flags & CAD_KV_ONLY) != 0).total;
 }
 
+size_t cad_stack_span_forward_workspace(const cad_layer_desc* layers, int n_layers, int B, int Nq, int mode, int W,
+                                        int D, int cap, int flags) {
+    FwdDims fd;
+    if (!layers || n_layers < 1 || n_layers > CAD_MAX_LAYERS || !fwd_dims(&layers[0], B, Nq, mode, W, D, cap, &fd))
+        return 0;
+    return fwd_carve(fd, nullptr, (flags & CAD_KV_ONLY) != 0 && n_layers == 1).total;
+}
+
 namespace {
 
-// The span forward.  allowed == nullptr: the full LM head and argmax (or the last row's, with
-// CAD_LOGITS_LAST); otherwise the argmax over each row's A allowed ids.
-int span_forward_impl(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
-                      int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
-                      const int32_t* allowed, int A, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!L || !kv || !tokens) return CAD_EINVAL;
+// Layers of one stack must agree in every dimension and in their norm and rotary constants.
+bool same_shape(const cad_layer_desc* a, const cad_layer_desc* b) {
+    return a->hidden == b->hidden && a->n_q_heads == b->n_q_heads && a->n_kv_heads == b->n_kv_heads &&
+           a->head_dim == b->head_dim && a->ffn == b->ffn && a->vocab == b->vocab && a->dtype == b->dtype &&
+           a->rms_eps == b->rms_eps && a->rope_base == b->rope_base;
+}
+
+// The span forward through n_layers layers (1 for the one-layer model).  The embedding is the
+// first layer's and the LM head the last layer's; layer l+1 takes layer l's residual output h2
+// as its input x and that output's RMSNorm u3 as its normed input.  The cache lengths and error
+// flags are those of kvs[0]; kvs[l] holds layer l's K/V.  allowed == nullptr: the full LM head
+// and argmax (or each sequence's last row only, with CAD_LOGITS_LAST); otherwise the argmax over
+// each row's A allowed ids.  CAD_KV_ONLY runs every layer but the last in full (their outputs
+// feed the next layer's K/V) and only the K/V projection of the last.
+int span_forward_impl(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs, const int32_t* tokens,
+                      int B, int Nq, int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out,
+                      float* logits_out, const int32_t* allowed, int A, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    if (!layers || !kvs || !tokens || n_layers < 1) return CAD_EINVAL;
     if (flags & ~(CAD_COMMIT_ALL | CAD_KV_ONLY | CAD_LOGITS_LAST)) return CAD_EINVAL;
     const bool kv_only = (flags & CAD_KV_ONLY) != 0;
     const bool last_only = (flags & CAD_LOGITS_LAST) != 0;
     if (last_only && mode != CAD_MASK_CAUSAL_SPAN) return CAD_EINVAL;
-    if (!kv->k || !kv->v || !kv->len || kv->B != B) return CAD_EINVAL;
+    const cad_layer_desc* L0 = &layers[0];
+    const cad_layer_desc* Lz = &layers[n_layers - 1];
+    const cad_kv_desc* kv0 = &kvs[0];
+    if (!kv0->len) return CAD_EINVAL;
     FwdDims fd;
-    if (!fwd_dims(L, B, Nq, mode, W, D, kv->cap, &fd)) return CAD_EINVAL;
-    if (kv->n_kv_heads != L->n_kv_heads || kv->head_dim != L->head_dim || kv->dtype != L->dtype) return CAD_EINVAL;
-    if (!L->embed || !L->w_qkv) return CAD_EINVAL;
-    if (!kv_only && (!L->w_o || !L->w_gate_up || !L->w_down || !L->w_lm || !argmax_out)) return CAD_EINVAL;
-    if (!layer_supported(L) || kv->cap % 4) return CAD_EUNSUPPORTED;
+    if (!fwd_dims(L0, B, Nq, mode, W, D, kv0->cap, &fd)) return CAD_EINVAL;
+    for (int l = 0; l < n_layers; ++l) {
+        const cad_layer_desc* L = &layers[l];
+        const cad_kv_desc* kv = &kvs[l];
+        const bool full = !kv_only || l < n_layers - 1;
+        if (!same_shape(L, L0) || !L->w_qkv) return CAD_EINVAL;
+        if (full && (!L->w_o || !L->w_gate_up || !L->w_down)) return CAD_EINVAL;
+        if (!kv->k || !kv->v || kv->B != B || kv->cap != kv0->cap) return CAD_EINVAL;
+        if (kv->n_kv_heads != L->n_kv_heads || kv->head_dim != L->head_dim || kv->dtype != L->dtype) return CAD_EINVAL;
+    }
+    if (!L0->embed) return CAD_EINVAL;
+    if (!kv_only && (!Lz->w_lm || !argmax_out)) return CAD_EINVAL;
+    if (!layer_supported(L0) || kv0->cap % 4) return CAD_EUNSUPPORTED;
     if ((long)fd.M * fd.h > (1L << 31) || (long)fd.M * fd.ffn > (1L << 31)) return CAD_EUNSUPPORTED;
+    const bool attends = !kv_only || n_layers > 1;
     const bool simple_attn = fd.dtype == CAD_DTYPE_F32 || (fd.d != 64 && fd.d != 128);
-    if (!kv_only && simple_attn && (size_t)(fd.cap + fd.Nq) * 4 > 64 * 1024) return CAD_EUNSUPPORTED;
-    const FwdBufs wb = fwd_carve(fd, workspace, kv_only);
+    if (attends && simple_attn && (size_t)(fd.cap + fd.Nq) * 4 > 64 * 1024) return CAD_EUNSUPPORTED;
+    const FwdBufs wb = fwd_carve(fd, workspace, kv_only && n_layers == 1);
     if (!workspace || workspace_bytes < wb.total || ((uintptr_t)workspace & 255)) return CAD_EWORKSPACE;
 
     RopeFreqs freqs;
-    for (int i = 0; i < fd.d / 2; ++i) freqs.inv[i] = std::pow(L->rope_base, -2.0 * i / fd.d);
+    for (int i = 0; i < fd.d / 2; ++i) freqs.inv[i] = std::pow(L0->rope_base, -2.0 * i / fd.d);
     if (stage(ST_EMBED_NORM, stream, [&] {
-            return launch_embed_norm(fd, tokens, L->embed, L->rms_eps, freqs, kv->len, kv->err, wb, stream);
+            return launch_embed_norm(fd, tokens, L0->embed, L0->rms_eps, freqs, kv0->len, kv0->err, wb, stream);
         }) != hipSuccess)
         return CAD_EHIP;
 
-    EpiParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.M = fd.M; p.len_snap = wb.len_snap; p.Nq = fd.Nq; p.cap = fd.cap;
-    p.q_out = wb.q; p.kc = kv->k; p.vc = kv->v;
-    p.Hq = fd.Hq; p.Hkv = fd.Hkv; p.d = fd.d; p.rope_cs = wb.rope_cs;
     const size_t h = fd.h;
-    // QKV projection + RoPE + K/V append (K/V rows only for a cache prefill)
-    {
-        EpiParams pq = p;
-        const char* w = (const char*)L->w_qkv;
-        int N = fd.qkv_n;
-        if (kv_only) {
-            pq.head_off = fd.Hq;
-            w += (size_t)fd.Hq * fd.d * h * fd.esz;
-            N = 2 * fd.Hkv * fd.d;
+    EpiParams base;
+    std::memset(&base, 0, sizeof(base));
+    base.M = fd.M; base.len_snap = wb.len_snap; base.Nq = fd.Nq; base.cap = fd.cap;
+    base.Hq = fd.Hq; base.Hkv = fd.Hkv; base.d = fd.d; base.rope_cs = wb.rope_cs;
+    // the residual stream alternates between two buffer pairs: layer l reads (x, u) and writes
+    // (h2, u3) when l is even, the other way round when l is odd
+    FwdBufs lb = wb;
+    for (int l = 0; l < n_layers; ++l) {
+        const cad_layer_desc* L = &layers[l];
+        const cad_kv_desc* kv = &kvs[l];
+        const bool last = l == n_layers - 1;
+        if (l & 1) {
+            lb.x = wb.h2; lb.u = wb.u3; lb.h2 = wb.x; lb.u3 = wb.u;
+        } else {
+            lb.x = wb.x; lb.u = wb.u; lb.h2 = wb.h2; lb.u3 = wb.u3;
         }
-        pq.N = N;
-        if (fd.qkv_slices) {
-            // split form: K-slice partials, then RoPE + K/V append per row
-            const int S = kv_only ? fd.kv_slices : fd.qkv_slices;
-            pq.part = wb.qkv_part;
-            if (stage(ST_QKV, stream, [&] {
-                    return launch_gemm(fd.dtype, EPI_PARTIAL, wb.u, w, fd.M, N, fd.h, S, pq, stream);
-                }) != hipSuccess)
+        EpiParams p = base;
+        p.q_out = lb.q; p.kc = kv->k; p.vc = kv->v;
+        const bool kv_rows_only = kv_only && last;
+        // QKV projection + RoPE + K/V append (K/V rows only for the last layer of a cache prefill)
+        {
+            EpiParams pq = p;
+            const char* w = (const char*)L->w_qkv;
+            int N = fd.qkv_n;
+            if (kv_rows_only) {
+                pq.head_off = fd.Hq;
+                w += (size_t)fd.Hq * fd.d * h * fd.esz;
+                N = 2 * fd.Hkv * fd.d;
+            }
+            pq.N = N;
+            if (fd.qkv_slices) {
+                // split form: K-slice partials, then RoPE + K/V append per row
+                const int S = kv_rows_only ? fd.kv_slices : fd.qkv_slices;
+                pq.part = wb.qkv_part;
+                if (stage(ST_QKV, stream, [&] {
+                        return launch_gemm(fd.dtype, EPI_PARTIAL, lb.u, w, fd.M, N, fd.h, S, pq, stream);
+                    }) != hipSuccess)
+                    return CAD_EHIP;
+                if (stage(ST_QKV_FINISH, stream, [&] {
+                        return launch_qkv_finish(fd, wb.qkv_part, S, N, pq.head_off, lb, kv->k, kv->v, stream);
+                    }) != hipSuccess)
+                    return CAD_EHIP;
+            } else if (stage(ST_QKV, stream, [&] {
+                           return launch_gemm(fd.dtype, EPI_QKV, lb.u, w, fd.M, N, fd.h, 1, pq, stream);
+                       }) != hipSuccess) {
                 return CAD_EHIP;
-            if (stage(ST_QKV_FINISH, stream, [&] {
-                    return launch_qkv_finish(fd, wb.qkv_part, S, N, pq.head_off, wb, kv->k, kv->v, stream);
-                }) != hipSuccess)
-                return CAD_EHIP;
-        } else if (stage(ST_QKV, stream, [&] {
-                       return launch_gemm(fd.dtype, EPI_QKV, wb.u, w, fd.M, N, fd.h, 1, pq, stream);
-                   }) != hipSuccess) {
-            return CAD_EHIP;
+            }
         }
-    }
-    if (kv_only) {
-        if ((flags & CAD_COMMIT_ALL) &&
-            stage(ST_COMMIT, stream, [&] { return launch_commit(fd, wb, kv->len, stream); }) != hipSuccess)
+        if (kv_rows_only) {
+            if ((flags & CAD_COMMIT_ALL) &&
+                stage(ST_COMMIT, stream, [&] { return launch_commit(fd, wb, kv0->len, stream); }) != hipSuccess)
+                return CAD_EHIP;
+            return CAD_OK;
+        }
+        if (stage(ST_ATTN, stream, [&] { return launch_attention(fd, lb, kv->k, kv->v, stream); }) != hipSuccess)
             return CAD_EHIP;
-        return CAD_OK;
+        if (attention_uses_merge(fd) &&
+            stage(ST_ATTN_MERGE, stream, [&] { return launch_attention_merge(fd, lb, stream); }) != hipSuccess)
+            return CAD_EHIP;
+        // O projection (K-slice partials) -> h1 = x + o.Wo^T, u2 = RMSNorm(h1)
+        EpiParams po = p;
+        po.N = fd.h; po.part = wb.part;
+        if (stage(ST_O_PROJ, stream, [&] {
+                return launch_gemm(fd.dtype, EPI_PARTIAL, lb.o, L->w_o, fd.M, fd.h, fd.Hq * fd.d, fd.o_slices, po,
+                                   stream);
+            }) != hipSuccess)
+            return CAD_EHIP;
+        if (stage(ST_NORM2, stream, [&] {
+                return launch_resid_norm(fd, lb.x, wb.part, fd.o_slices, wb.h1, nullptr, wb.u2, false, L->rms_eps,
+                                         wb.len_snap, stream);
+            }) != hipSuccess)
+            return CAD_EHIP;
+        EpiParams pg = p;
+        pg.N = 2 * fd.ffn; pg.act = wb.act; pg.ffn = fd.ffn;
+        if (stage(ST_GATE_UP, stream, [&] {
+                return launch_gemm(fd.dtype, EPI_SWIGLU, wb.u2, L->w_gate_up, fd.M, 2 * fd.ffn, fd.h, 1, pg, stream);
+            }) != hipSuccess)
+            return CAD_EHIP;
+        // down projection (K-slice partials) -> h2 = h1 + act.Wd^T, u3 = RMSNorm(h2); the last
+        // layer also writes hidden_out = rnd(h2), and with CAD_LOGITS_LAST normalises only each
+        // sequence's last row
+        EpiParams pd = p;
+        pd.N = fd.h; pd.part = wb.part;
+        if (stage(ST_DOWN, stream, [&] {
+                return launch_gemm(fd.dtype, EPI_PARTIAL, wb.act, L->w_down, fd.M, fd.h, fd.ffn, fd.down_slices, pd,
+                                   stream);
+            }) != hipSuccess)
+            return CAD_EHIP;
+        if (stage(ST_NORM3, stream, [&] {
+                return launch_resid_norm(fd, wb.h1, wb.part, fd.down_slices, lb.h2, last ? hidden_out : nullptr,
+                                         lb.u3, last && last_only, L->rms_eps, wb.len_snap, stream);
+            }) != hipSuccess)
+            return CAD_EHIP;
     }
-    if (stage(ST_ATTN, stream, [&] { return launch_attention(fd, wb, kv->k, kv->v, stream); }) != hipSuccess)
-        return CAD_EHIP;
-    if (attention_uses_merge(fd) &&
-        stage(ST_ATTN_MERGE, stream, [&] { return launch_attention_merge(fd, wb, stream); }) != hipSuccess)
-        return CAD_EHIP;
-    // O projection (K-slice partials) -> h1 = x + o.Wo^T, u2 = RMSNorm(h1)
-    EpiParams po = p;
-    po.N = fd.h; po.part = wb.part;
-    if (stage(ST_O_PROJ, stream, [&] {
-            return launch_gemm(fd.dtype, EPI_PARTIAL, wb.o, L->w_o, fd.M, fd.h, fd.Hq * fd.d, fd.o_slices, po,
-                               stream);
-        }) != hipSuccess)
-        return CAD_EHIP;
-    if (stage(ST_NORM2, stream, [&] {
-            return launch_resid_norm(fd, wb.x, wb.part, fd.o_slices, wb.h1, nullptr, wb.u2, false, L->rms_eps, wb.len_snap,
-                                     stream);
-        }) != hipSuccess)
-        return CAD_EHIP;
-    EpiParams pg = p;
-    pg.N = 2 * fd.ffn; pg.act = wb.act; pg.ffn = fd.ffn;
-    if (stage(ST_GATE_UP, stream, [&] {
-            return launch_gemm(fd.dtype, EPI_SWIGLU, wb.u2, L->w_gate_up, fd.M, 2 * fd.ffn, fd.h, 1, pg, stream);
-        }) != hipSuccess)
-        return CAD_EHIP;
-    // down projection (K-slice partials) -> h2 = h1 + act.Wd^T, hidden_out = rnd(h2), u3 = RMSNorm(h2)
-    EpiParams pd = p;
-    pd.N = fd.h; pd.part = wb.part;
-    if (stage(ST_DOWN, stream, [&] {
-            return launch_gemm(fd.dtype, EPI_PARTIAL, wb.act, L->w_down, fd.M, fd.h, fd.ffn, fd.down_slices, pd,
-                               stream);
-        }) != hipSuccess)
-        return CAD_EHIP;
-    if (stage(ST_NORM3, stream, [&] {
-            return launch_resid_norm(fd, wb.h1, wb.part, fd.down_slices, wb.h2, hidden_out, wb.u3, last_only, L->rms_eps,
-                                     wb.len_snap, stream);
-        }) != hipSuccess)
-        return CAD_EHIP;
     if (allowed) {
         // grammar-masked step: logits of the allowed ids only, argmax, commit
         if (stage(ST_ALLOWED, stream, [&] {
-                return launch_allowed_argmax(fd, wb, L->w_lm, allowed, A, last_only, argmax_out, logits_out,
-                                             (flags & CAD_COMMIT_ALL) ? kv->len : nullptr, stream);
+                return launch_allowed_argmax(fd, lb, Lz->w_lm, allowed, A, last_only, argmax_out, logits_out,
+                                             (flags & CAD_COMMIT_ALL) ? kv0->len : nullptr, stream);
             }) != hipSuccess)
             return CAD_EHIP;
         return CAD_OK;
     }
     // LM head + argmax partials, then the per-row reduction (+ commit of the cache lengths).
     // Copy-commit mode: u3 holds one row per sequence (row b = the sequence's last row).
-    EpiParams pl = p;
+    EpiParams pl = base;
     const int lm_rows = last_only ? fd.B : fd.M;
     pl.M = lm_rows; pl.Nq = last_only ? 1 : fd.Nq;
     pl.N = fd.V; pl.amax_part = wb.amax_part; pl.amax_slots = last_only ? wb.amax_slots_last : wb.amax_slots;
     pl.logits = logits_out;
     if (stage(ST_LM_HEAD, stream, [&] {
-            return launch_gemm(fd.dtype, EPI_ARGMAX, wb.u3, L->w_lm, lm_rows, fd.V, fd.h, 1, pl, stream);
+            return launch_gemm(fd.dtype, EPI_ARGMAX, lb.u3, Lz->w_lm, lm_rows, fd.V, fd.h, 1, pl, stream);
         }) != hipSuccess)
         return CAD_EHIP;
     if (stage(ST_ARGMAX, stream, [&] {
-            return launch_argmax_final(fd, wb, last_only, argmax_out, (flags & CAD_COMMIT_ALL) ? kv->len : nullptr,
+            return launch_argmax_final(fd, wb, last_only, argmax_out, (flags & CAD_COMMIT_ALL) ? kv0->len : nullptr,
                                        stream);
         }) != hipSuccess)
         return CAD_EHIP;
@@ -339,8 +389,8 @@ int span_forward_impl(const cad_layer_desc* L, const cad_kv_desc* kv, const int3
 int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
                      int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return span_forward_impl(L, kv, tokens, B, Nq, mode, W, D, flags, argmax_out, hidden_out, logits_out, nullptr, 0,
-                             workspace, workspace_bytes, stream);
+    return span_forward_impl(L, 1, kv, tokens, B, Nq, mode, W, D, flags, argmax_out, hidden_out, logits_out, nullptr,
+                             0, workspace, workspace_bytes, stream);
 }
 
 int cad_span_forward_allowed(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
@@ -349,8 +399,17 @@ int cad_span_forward_allowed(const cad_layer_desc* L, const cad_kv_desc* kv, con
     if (!allowed || !argmax_out) return CAD_EINVAL;
     if (A < 1 || A > CAD_MAX_ALLOWED) return CAD_EUNSUPPORTED;
     if (flags & ~(CAD_COMMIT_ALL | CAD_LOGITS_LAST)) return CAD_EINVAL;
-    return span_forward_impl(L, kv, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, argmax_out, hidden_out,
+    if (!L || !kv) return CAD_EINVAL;
+    return span_forward_impl(L, 1, kv, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, argmax_out, hidden_out,
                              logits_out, allowed, A, workspace, workspace_bytes, stream);
+}
+
+int cad_stack_span_forward(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs, const int32_t* tokens,
+                           int B, int Nq, int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out,
+                           float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (n_layers < 1 || n_layers > CAD_MAX_LAYERS) return CAD_EINVAL;
+    return span_forward_impl(layers, n_layers, kvs, tokens, B, Nq, mode, W, D, flags, argmax_out, hidden_out,
+                             logits_out, nullptr, 0, workspace, workspace_bytes, stream);
 }
 
 int cad_ngram_lookup(const int32_t* ctx, int64_t ctx_stride, const int32_t* ctx_len, int B, int n, int W, int D,

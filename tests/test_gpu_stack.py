@@ -1,0 +1,189 @@
+"""GPU parity of the full-depth stack call (cad_stack_span_forward) against the oracle's stack.
+
+Rounding drift between an fp32-accumulating pipeline and the fp64 oracle enters every layer
+independently (bf16 rounding flips of the normed inputs and the SwiGLU product), so the
+one-layer tolerances are widened by sqrt(depth) for outputs after the last layer and by
+sqrt(l + 1) for the K/V rows of layer l."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from spec_verify_cad_amd import cad, synth
+from spec_verify_cad_amd.configs import SMALL
+
+from gpu_util import argmax_check, hidden_tol, log, logit_tol, to_f64
+from helpers import oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+NL = 4
+
+
+def _stack_weights(shape, seed, n):
+    out = []
+    for l in range(n):
+        names = [k for k in synth.weight_shapes(shape)
+                 if not (k == "embed" and l > 0) and not (k == "w_lm" and l < n - 1)]
+        out.append(synth.layer_weights(shape, seed + l, names=names))
+    return out
+
+
+@pytest.fixture(scope="module")
+def small_stack():
+    ws = _stack_weights(SMALL, 300, NL)
+    dst = cad.DeviceStack([cad.DeviceLayer(SMALL, w) for w in ws])
+    ols = [oracle_layer(SMALL, w, only=list(w)) for w in ws]
+    return ws, dst, ols
+
+
+def _prefill(dst, sc, ctx, chunk=64):
+    for s in range(0, ctx.shape[1], chunk):
+        t = torch.from_numpy(np.ascontiguousarray(ctx[:, s:s + chunk], dtype=np.int32)).cuda()
+        cad.stack_span_forward(dst, sc, t, t.shape[1], flags=cad.KV_ONLY | cad.COMMIT_ALL)
+
+
+def _run(dst, sc, toks, mode=cad.MASK_CAUSAL, W=1, D=1, flags=0):
+    B, Nq = toks.shape
+    s = dst.shape
+    t = torch.from_numpy(np.ascontiguousarray(toks, dtype=np.int32)).cuda()
+    last = bool(flags & cad.LOGITS_LAST)
+    R = B if last else B * Nq
+    am = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    hid = torch.zeros((B * Nq, s.hidden), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((R, s.vocab), dtype=torch.float32, device="cuda")
+    cad.stack_span_forward(dst, sc, t, Nq, mode, W, D, flags, am, hid, lg)
+    torch.cuda.synchronize()
+    return am.cpu().numpy(), to_f64(hid, "bf16"), lg.cpu().numpy().astype(np.float64)
+
+
+def _check_out(g_a, g_h, g_l, ref, rows, n_layers, what):
+    href = ref["hidden_out"]
+    dh = np.abs(g_h - href)
+    scale = math.sqrt(n_layers)
+    tol_h = np.maximum(hidden_tol(href, SMALL.ffn) * scale, hidden_tol(href, SMALL.ffn))
+    assert (dh <= tol_h).all(), f"{what} hidden max-abs {dh.max():.3e}"
+    ltol = logit_tol(SMALL.hidden) * scale
+    dl = np.abs(g_l - ref["logits"]).max()
+    assert dl <= ltol, f"{what} logits max-abs {dl:.3e} > {ltol:.3g}"
+    unique = argmax_check(g_a, ref, g_l, what, ltol)
+    log(f"{what}: hidden {dh.max():.3e} logits {dl:.3e} (tol {ltol:.3g}) unique argmax {int(unique.sum())}/{len(g_a)}")
+
+
+def _check_caches(sc, b, ocs, lo, hi, what):
+    for l, oc in enumerate(ocs):
+        k = to_f64(sc.caches[l].k[b, :, lo:hi], "bf16")
+        v = to_f64(sc.caches[l].v[b, :, :, lo:hi], "bf16").transpose(0, 2, 1)
+        for name, got, ref in (("k", k, oc.K[:, lo:hi]), ("v", v, oc.V[:, lo:hi])):
+            d = np.abs(got - ref)
+            tol = hidden_tol(ref) * math.sqrt(l + 1)
+            frac = float(np.mean(d > 0))
+            assert (d <= tol).all(), f"{what} layer {l} {name} max-abs {d.max():.3e}"
+            log(f"{what} layer {l} {name}: max-abs {d.max():.3e}, differing {frac:.4f}")
+
+
+@pytest.mark.parametrize("Nq", [1, 13, 70])
+def test_small_stack_span_matches_oracle(small_stack, Nq):
+    ws, dst, ols = small_stack
+    log(f"stack of {NL} small layers, causal Nq={Nq}")
+    B, L0, cap = 2, 100, 192
+    ctx = np.stack([synth.uniform_tokens(310 + b, L0, SMALL.vocab) for b in range(B)])
+    span = np.stack([synth.uniform_tokens(320 + b, Nq, SMALL.vocab) for b in range(B)])
+    sc = cad.StackCache(SMALL, NL, B, cap)
+    _prefill(dst, sc, ctx)
+    assert list(sc.len.cpu().numpy()) == [L0] * B
+    g_a, g_h, g_l = _run(dst, sc, span, flags=cad.COMMIT_ALL)
+    assert list(sc.len.cpu().numpy()) == [L0 + Nq] * B
+    for b in range(B):
+        ocs = O.stack_prefill(ols, ctx[b], cap, chunk=64)
+        _check_caches(sc, b, ocs, 0, L0, f"prefill b={b}")
+        ref = O.stack_span_forward(ols, ocs, span[b])
+        rows = slice(b * Nq, (b + 1) * Nq)
+        _check_out(g_a[rows], g_h[rows], g_l[rows], ref, rows, NL, f"b={b}")
+        _check_caches(sc, b, ocs, L0, L0 + Nq, f"span b={b}")
+
+
+def test_small_stack_block_verify_and_copy_commit(small_stack):
+    ws, dst, ols = small_stack
+    W, D, B, L0, cap = 3, 4, 2, 80, 128
+    log("stack block W=3 D=4, then copy-commit Nq=9")
+    ctx = np.stack([synth.uniform_tokens(330 + b, L0, SMALL.vocab) for b in range(B)])
+    cand = np.stack([synth.uniform_tokens(340 + b, W * D, SMALL.vocab) for b in range(B)])
+    sc = cad.StackCache(SMALL, NL, B, cap)
+    _prefill(dst, sc, ctx)
+    g_a, g_h, g_l = _run(dst, sc, cand, mode=cad.MASK_BLOCK, W=W, D=D)
+    assert list(sc.len.cpu().numpy()) == [L0] * B                 # verify forward: no commit
+    ocs = [O.stack_prefill(ols, ctx[b], cap, chunk=64) for b in range(B)]
+    for b in range(B):
+        ref = O.stack_span_forward(ols, [c.copy() for c in ocs[b]], cand[b], mode="block", W=W, D=D, commit=False)
+        rows = slice(b * W * D, (b + 1) * W * D)
+        _check_out(g_a[rows], g_h[rows], g_l[rows], ref, rows, NL, f"block b={b}")
+    # copy-commit mode through the stack: the LM head for each sequence's last row only
+    Nq = 9
+    span = np.stack([synth.uniform_tokens(350 + b, Nq, SMALL.vocab) for b in range(B)])
+    g_a, g_h, g_l = _run(dst, sc, span, flags=cad.COMMIT_ALL | cad.LOGITS_LAST)
+    assert list(sc.len.cpu().numpy()) == [L0 + Nq] * B
+    for b in range(B):
+        ref = O.stack_span_forward(ols, ocs[b], span[b])
+        last = {k: ref[k][Nq - 1:Nq] for k in ("logits", "argmax", "top2_gap")}
+        last["hidden_out"] = ref["hidden_out"]
+        dh = np.abs(g_h[b * Nq:(b + 1) * Nq] - ref["hidden_out"])
+        assert (dh <= hidden_tol(ref["hidden_out"], SMALL.ffn) * math.sqrt(NL)).all()
+        dl = np.abs(g_l[b:b + 1] - last["logits"]).max()
+        assert dl <= logit_tol(SMALL.hidden) * math.sqrt(NL)
+        argmax_check(g_a[b:b + 1], last, g_l[b:b + 1], f"copy-commit b={b}", logit_tol(SMALL.hidden) * math.sqrt(NL))
+        _check_caches(sc, b, ocs[b], L0, L0 + Nq, f"copy-commit b={b}")
+
+
+def test_one_layer_stack_is_bitwise_the_one_layer_call(small_stack):
+    ws, dst, ols = small_stack
+    # a one-layer stack: its only layer carries the embedding and the LM head
+    lay = cad.DeviceLayer(SMALL, synth.layer_weights(SMALL, 300))
+    one = cad.DeviceStack([lay])
+    B, L0, cap, Nq = 2, 50, 96, 11
+    ctx = np.stack([synth.uniform_tokens(360 + b, L0, SMALL.vocab) for b in range(B)])
+    span = np.stack([synth.uniform_tokens(370 + b, Nq, SMALL.vocab) for b in range(B)])
+    sc = cad.StackCache(SMALL, 1, B, cap)
+    c1 = cad.DeviceCache(SMALL, B, cap)
+    _prefill(one, sc, ctx)
+    for s in range(0, L0, 64):
+        t = torch.from_numpy(np.ascontiguousarray(ctx[:, s:s + 64], dtype=np.int32)).cuda()
+        cad.span_forward(lay, c1, t, t.shape[1], flags=cad.KV_ONLY | cad.COMMIT_ALL)
+    a = _run(one, sc, span, flags=cad.COMMIT_ALL)
+    t = torch.from_numpy(np.ascontiguousarray(span, dtype=np.int32)).cuda()
+    am = torch.full((B * Nq,), -7, dtype=torch.int32, device="cuda")
+    hid = torch.zeros((B * Nq, SMALL.hidden), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((B * Nq, SMALL.vocab), dtype=torch.float32, device="cuda")
+    cad.span_forward(lay, c1, t, Nq, flags=cad.COMMIT_ALL, argmax_out=am, hidden_out=hid, logits_out=lg)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(a[0], am.cpu().numpy())
+    np.testing.assert_array_equal(a[2], lg.cpu().numpy())
+    np.testing.assert_array_equal(sc.caches[0].k.cpu().numpy(), c1.k.cpu().numpy())
+    np.testing.assert_array_equal(sc.caches[0].v.cpu().numpy(), c1.v.cpu().numpy())
+
+
+def test_stack_argument_errors(small_stack):
+    ws, dst, ols = small_stack
+    sc = cad.StackCache(SMALL, NL, 1, 64)
+    t = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    am = torch.zeros(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        cad.stack_span_forward(dst, cad.StackCache(SMALL, NL - 1, 1, 64), t, 4, argmax_out=am)
+    L = cad.lib()
+    ws_ = cad.alloc_workspace(1 << 24)
+    import ctypes
+    assert L.cad_stack_span_forward(dst.descs, 0, sc.descs, ctypes.c_void_p(t.data_ptr()), 1, 4, 0, 1, 1, 0,
+                                    ctypes.c_void_p(am.data_ptr()), None, None, ctypes.c_void_p(ws_.data_ptr()),
+                                    ws_.numel(), None) == cad.CAD_EINVAL
+    # a layer of another shape in the stack
+    other = cad.DeviceLayer(synth.LayerShape(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=512,
+                                             vocab=SMALL.vocab),
+                            synth.layer_weights(synth.LayerShape(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                                                                 ffn=512, vocab=SMALL.vocab), 9))
+    mixed = cad.DeviceStack(dst.layers[:NL - 1] + [other])
+    with pytest.raises(cad.CadError):
+        cad.stack_span_forward(mixed, sc, t, 4, argmax_out=am, workspace=ws_)
+    torch.cuda.synchronize()
+    assert int(sc.len[0]) == 0
