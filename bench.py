@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--ar-steps", type=int, default=64)
     ap.add_argument("--no-pld", action="store_true", help="skip the batched PLD round measurement")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the full-depth (28-layer) span-forward curve on the 1.5B and 7B shapes")
     ap.add_argument("--no-program", action="store_true",
                     help="skip the Copy-as-Decode program measurement (op-boundary steps, 7B-shaped layer)")
     ap.add_argument("--pmc-pass", action="store_true",
@@ -228,6 +230,11 @@ def main():
     # ---- batched PLD rounds (lookup -> verify forward -> accept, no host sync inside)
     pld = None if a.no_pld else pld_rounds(a, lay0, dev)
 
+    # ---- full-depth stacks: the pages' kernel table (parallel forward vs autoregression) at 28 layers
+    stack = None if a.no_stack else [stack_curve(a, dev, k) for k in ("qwen15_span", "qwen7_cad_program")]
+    if stack:
+        stack_cost_model(stack)
+
     # ---- a whole Copy-as-Decode program with its op-boundary steps (7B-shaped layer)
     program = None if a.no_program else cad_program(a, dev)
 
@@ -271,6 +278,7 @@ def main():
         "copy_commit_mode": copy_commit,
         "pld_rounds": pld,
         "cad_program": program,
+        "full_depth_stacks": stack,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -428,6 +436,161 @@ def cad_program(a, dev):
         f"steps {per_step}")
     del g
     return res
+
+
+STACK_LAYERS = 28
+STACK_PREFIX = 1024
+STACK_SPANS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
+
+
+def stack_curve(a, dev, shape_key: str):
+    """The span forward through a whole 28-layer stack of the given shape (random weights drawn
+    on the device, N(0, 0.02), bf16) after a 1024-token prefix, for N = 1 .. 512: one parallel
+    forward of N tokens (full LM head, and copy-commit mode with the LM head for the last row
+    only) against N autoregressive one-token forwards from the same prefix; s = AR / parallel.
+    Every forward is replayed from a HIP graph.  The autoregressive times are cumulative over
+    one run of 512 steps whose context grows from 1024, read at each N."""
+    import numpy as np
+    import torch
+
+    from spec_verify_cad_amd import cad, synth
+    from spec_verify_cad_amd import roofline as R
+    from spec_verify_cad_amd.configs import CONFIGS
+
+    shp = CONFIGS[shape_key].shape
+    nl, L0 = STACK_LAYERS, STACK_PREFIX
+    cap = L0 + max(STACK_SPANS) + 8
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    layers = []
+    for l in range(nl):
+        t = {}
+        for name, sh in synth.weight_shapes(shp).items():
+            if (name == "embed" and l > 0) or (name == "w_lm" and l < nl - 1):
+                continue
+            t[name] = (torch.randn(sh, generator=gen, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+        layers.append(cad.DeviceLayer.from_tensors(shp, t))
+    st = cad.DeviceStack(layers)
+    sc = cad.StackCache(shp, nl, 1, cap, device=dev)
+    pre = torch.randint(0, shp.vocab, (1, L0), generator=gen, device=dev, dtype=torch.int32)
+    cad.stack_span_forward(st, sc, pre, L0, flags=cad.KV_ONLY | cad.COMMIT_ALL)
+    torch.cuda.synchronize()
+    assert int(sc.len[0]) == L0
+    toks = torch.randint(0, shp.vocab, (1, max(STACK_SPANS)), generator=gen, device=dev, dtype=torch.int32)
+    out = torch.empty(max(STACK_SPANS), dtype=torch.int32, device=dev)
+    ws = cad.alloc_workspace(max(cad.stack_span_forward_workspace(st, 1, N, cad.MASK_CAUSAL, 1, 1, cap, cad.COMMIT_ALL)
+                                 for N in STACK_SPANS), device=dev)
+    stream = torch.cuda.current_stream()
+    cap_stream = torch.cuda.Stream()
+
+    def graph_of(fn):
+        sc.len.fill_(L0)
+        fn(stream)                                         # eager warm-up of the launch shapes
+        torch.cuda.synchronize()
+        cap_stream.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            fn(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return g
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def pp(N, last, st_):
+        sc.len.fill_(L0)
+        cad.stack_span_forward(st, sc, toks[:, :N], N, flags=cad.COMMIT_ALL | (cad.LOGITS_LAST if last else 0),
+                               argmax_out=out[:1] if last else out[:N], workspace=ws, stream=st_)
+
+    rows = []
+    for N in STACK_SPANS:
+        r = {"N": N}
+        for last in (False, True):
+            g = graph_of(lambda s_, N=N, last=last: pp(N, last, s_))
+            g.replay()
+            e0 = ev()
+            for _ in range(3):
+                g.replay()
+            e1 = ev()
+            torch.cuda.synchronize()
+            r["pp_last_ms" if last else "pp_ms"] = round(e0.elapsed_time(e1) / 3, 4)
+            del g
+        rows.append(r)
+    # autoregressive: one-token forwards, 8 per graph replay, from the prefix onwards
+    one = toks[:, :1]
+
+    def steps(k, s_):
+        for _ in range(k):
+            cad.stack_span_forward(st, sc, one, 1, flags=cad.COMMIT_ALL, argmax_out=out[:1], workspace=ws, stream=s_)
+
+    g1 = graph_of(lambda s_: steps(1, s_))
+    g8 = graph_of(lambda s_: steps(8, s_))
+    ar = {}
+    sc.len.fill_(L0)
+    g1.replay()                                            # warm
+    sc.len.fill_(L0)
+    e = [ev()]
+    for _ in range(4):
+        g1.replay()
+        e.append(ev())
+    torch.cuda.synchronize()
+    for N in (1, 2, 4):
+        ar[N] = e[0].elapsed_time(e[N])
+    sc.len.fill_(L0)
+    e = [ev()]
+    for _ in range(max(STACK_SPANS) // 8):
+        g8.replay()
+        e.append(ev())
+    torch.cuda.synchronize()
+    assert int(sc.len[0]) == L0 + max(STACK_SPANS)
+    for N in STACK_SPANS:
+        if N >= 8:
+            ar[N] = e[0].elapsed_time(e[N // 8])
+    for r in rows:
+        N = r["N"]
+        r["ar_ms"] = round(ar[N], 4)
+        r["s"] = round(ar[N] / r["pp_ms"], 2)
+        r["s_copy_commit"] = round(ar[N] / r["pp_last_ms"], 2)
+        nb = R.stack_forward_bytes(shp, nl, 1, N, L0)
+        fl = R.stack_forward_flops(shp, nl, 1, N, L0)
+        floor, bound = R.floor_us(nb, fl)
+        r["floor_ms"] = round(floor / 1e3, 4)
+        r["bound"] = bound
+        r["frac_of_roofline"] = round(floor / 1e3 / r["pp_ms"], 4)
+    log(f"{STACK_LAYERS}-layer {shape_key}: " + ", ".join(f"N={r['N']}: parallel {r['pp_ms']:.3f} ms, AR "
+                                                          f"{r['ar_ms']:.2f} ms, s={r['s']}x" for r in rows))
+    del g1, g8, st, sc, layers
+    torch.cuda.empty_cache()
+    return {"layers": nl, "prefix": L0, "shape": shape_key, "rows": rows}
+
+
+def stack_cost_model(stack):
+    """The Copy-as-Decode cost model on the measured full-depth curves: tau = one autoregressive
+    step, m* (Appendix J) with c = 0 (no host synchronisation per op, and a masked decision costs
+    less than a free one), and the Eq. (3) bounds of the Copy-as-Decode program workload's copy
+    spans on the 7B-shaped stack, with the full LM head and in copy-commit mode."""
+    from spec_verify_cad_amd import costmodel as C
+    from spec_verify_cad_amd.configs import CONFIGS, cad_program_inputs
+
+    for sc in stack:
+        rows = sc["rows"]
+        tau = next(r["ar_ms"] for r in rows if r["N"] == 1)
+        for key, col in (("full_lm_head", "s"), ("copy_commit", "s_copy_commit")):
+            cur = {r["N"]: r[col] for r in rows}
+            sc.setdefault("cost_model", {})[key] = {"tau_ms": tau, "m_star": C.m_star(cur, tau, 0.0),
+                                                     "m_safe": C.m_safe(cur)}
+        if sc["shape"] == "qwen7_cad_program":
+            wl = CONFIGS["qwen7_cad_program"]
+            _, ops = cad_program_inputs(wl)
+            spans = [o[2] for o in ops if o[0] == "copy"]
+            T = wl.extra["total_out"]
+            for key, col in (("full_lm_head", "s"), ("copy_commit", "s_copy_commit")):
+                b = C.bounds(spans, T, {r["N"]: r[col] for r in rows}, m=8)
+                sc["cost_model"][key]["program_bounds"] = {k: round(v, 4) if isinstance(v, float) else v
+                                                           for k, v in b.items()}
+        log(f"cost model {sc['shape']}: {sc['cost_model']}")
 
 
 def pld_rounds(a, layer, dev):

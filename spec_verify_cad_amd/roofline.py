@@ -70,3 +70,19 @@ def pld_round_bytes(s, B: int, k: int, L: int, ctx_len: int) -> float:
 
 def pld_round_flops(s, B: int, k: int, L: int) -> float:
     return forward_flops(s, B, k + 1, L)
+
+
+def stack_forward_bytes(s, n_layers: int, B: int, N: int, L: int, last_only: bool = False) -> float:
+    """One causal span forward through a stack: every layer's weights and the LM head once, the
+    embedding rows, and per layer the visible K/V read once plus the new rows written."""
+    b = (n_layers * s.layer_params() + s.lm_params()) * s.elt_bytes
+    b += B * N * s.hidden * s.elt_bytes
+    b += n_layers * B * ((L + N) + N) * kv_row_bytes(s)
+    b += B * (1 if last_only else N) * 4 + B * N * 4
+    return float(b)
+
+
+def stack_forward_flops(s, n_layers: int, B: int, N: int, L: int, last_only: bool = False) -> float:
+    lm_rows = B * (1 if last_only else N)
+    return (2.0 * B * N * n_layers * s.layer_params() + 2.0 * lm_rows * s.lm_params()
+            + 4.0 * n_layers * B * visible_keys_causal(L, N) * s.n_q_heads * s.head_dim)
