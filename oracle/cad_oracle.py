@@ -590,3 +590,98 @@ def commit_block(cache: Cache, w_star: int, a_star: int, D: int):
 def pld_speedup(f: float, L: float) -> float:
     """Copy-rate speedup of the PLD page: 1 / (f/L + (1 - f))."""
     return 1.0 / (f / L + (1.0 - f))
+
+
+# ---------------------------------------------------------------------------------------
+# stochastic verification (PLD page, "Speculative decoding in one breath": with the proper
+# rejection-sampling correction the accepted text keeps the target's sampling distribution)
+# ---------------------------------------------------------------------------------------
+# The drafter is deterministic (a retrieved continuation), so its proposal distribution q is
+# one-hot on the draft token d.  The standard correction then reads: accept d with probability
+# min(1, p(d) / q(d)) = p(d); on rejection draw from the residual max(0, p - q), renormalised,
+# which is p with d removed; after an accepted draft draw the bonus token from p.  Here p is
+# softmax(logits / temperature) of the row.  Draws use the Gumbel-max form (the argmax of
+# logits / T plus independent Gumbel noise is a sample of p; restricted to x != d it is a sample
+# of the residual) with uniforms from the Philox4x32-10 counter-based generator.
+
+_PHILOX_M0, _PHILOX_M1 = 0xD2511F53, 0xCD9E8D57      # round multipliers (Salmon et al., SC'11)
+_PHILOX_W0, _PHILOX_W1 = 0x9E3779B9, 0xBB67AE85      # key increments (golden ratio, sqrt(3) - 1)
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+    easy as 1, 2, 3", SC'11).  ctr: uint32 array [..., 4]; key: uint32 pair.  Each round
+    multiplies words 0 and 2 by the round multipliers into 64-bit products and mixes:
+    (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1, lo(M0*c0)); the key is bumped by the
+    Weyl increments between rounds.  Returns uint32 [..., 4]."""
+    c = np.asarray(ctr, dtype=np.uint64) & np.uint64(0xFFFFFFFF)
+    c0, c1, c2, c3 = (c[..., i].copy() for i in range(4))
+    k0, k1 = np.uint64(int(key[0]) & 0xFFFFFFFF), np.uint64(int(key[1]) & 0xFFFFFFFF)
+    mask = np.uint64(0xFFFFFFFF)
+    for r in range(10):
+        p0 = np.uint64(_PHILOX_M0) * c0
+        p1 = np.uint64(_PHILOX_M1) * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & mask
+        hi1, lo1 = p1 >> np.uint64(32), p1 & mask
+        c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+        if r < 9:
+            k0 = (k0 + np.uint64(_PHILOX_W0)) & mask
+            k1 = (k1 + np.uint64(_PHILOX_W1)) & mask
+    return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
+
+
+def uniform_from_bits(bits):
+    """(0, 1) uniform from 32 random bits: the top 23 bits k give (2k + 1) / 2^24, exactly
+    representable in fp32 and never 0 or 1."""
+    k = (np.asarray(bits, dtype=np.uint64) >> np.uint64(9)).astype(np.float64)
+    return (2.0 * k + 1.0) / 16777216.0
+
+
+def sample_uniforms(seed: int, b: int, pos, ids, purpose: int):
+    """Uniforms of draw (sequence b, absolute position pos, vocabulary id, purpose): Philox
+    counter (id // 4, pos, b, purpose), key (seed low word, seed high word), output word id % 4.
+    purpose 0 = Gumbel noise of a logit, 1 = the acceptance test of a row (id 0)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    pos = np.broadcast_to(np.asarray(pos, dtype=np.int64), ids.shape)
+    ctr = np.stack([ids // 4, pos, np.full(ids.shape, b), np.full(ids.shape, purpose)], axis=-1)
+    out = philox4x32_10(ctr.astype(np.uint64), (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))
+    word = np.take_along_axis(out, (ids % 4)[..., None], axis=-1)[..., 0]
+    return uniform_from_bits(word)
+
+
+def sampled_predictions(logits, tokens, draft_len: int, temperature: float, seed: int, b: int, base: int):
+    """The per-row tokens a stochastic verifier compares and emits, for one sequence's forward
+    rows over tokens [g, d_1..d_k] at absolute positions base + i.
+
+    Row i < draft_len holds the draft d = tokens[i + 1]: it keeps d with probability p_i(d) (the
+    acceptance test u < p_i(d)), else it is a draw from p_i without d.  Row i >= draft_len is a
+    plain draw from p_i.  With these predictions the greedy left-to-right scan
+    (`accept_causal`) emits exactly the stochastic result: it continues while a row kept its
+    draft and emits the first replacement, or the bonus draw after the last draft.
+    Returns (pred, y, z, p_draft, u): y = plain draws, z = draws without the draft."""
+    logits = np.asarray(logits, dtype=np.float64)
+    n, V = logits.shape
+    s = logits / temperature
+    ids = np.arange(V)
+    pred = np.zeros(n, dtype=np.int64)
+    y = np.zeros(n, dtype=np.int64)
+    z = np.full(n, -1, dtype=np.int64)
+    pd = np.full(n, np.nan)
+    u = np.full(n, np.nan)
+    for i in range(n):
+        g = -np.log(-np.log(sample_uniforms(seed, b, base + i, ids, 0)))
+        pert = s[i] + g
+        y[i] = int(np.argmax(pert))
+        if i < draft_len:
+            d = int(tokens[i + 1])
+            m = np.max(s[i])
+            lse = m + np.log(np.sum(np.exp(s[i] - m)))
+            pd[i] = math.exp(s[i, d] - lse)
+            u[i] = float(sample_uniforms(seed, b, base + i, [0], 1)[0])
+            alt = pert.copy()
+            alt[d] = -np.inf
+            z[i] = int(np.argmax(alt))
+            pred[i] = d if u[i] < pd[i] else z[i]
+        else:
+            pred[i] = y[i]
+    return pred, y, z, pd, u
