@@ -203,6 +203,38 @@ int cad_span_forward_allowed(const cad_layer_desc *layer, const cad_kv_desc *kv,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * cad_span_forward_sampled — a causal span forward whose LM head draws tokens instead of
+ * taking the argmax, for stochastic verification of a retrieved draft (PLD page, speculative
+ * decoding: with the rejection-sampling correction the output keeps the target's sampling
+ * distribution).  The draft is deterministic, so the correction reads: keep the draft token d
+ * with probability p(d), otherwise draw from p without d; after the last draft draw the bonus
+ * token from p.  p = softmax(logits / temperature).
+ *
+ *   tokens      [B, Nq] the forward's input [g, d_1 .. d_k, padding]; row i < draft_len[b]
+ *               (clamped to Nq - 1) holds the draft d = tokens[b, i + 1]
+ *   draft_len   [B] device int32, nullable (then no row holds a draft)
+ *   flags       CAD_COMMIT_ALL and/or CAD_LOGITS_LAST (each sequence's last row only, no drafts)
+ *   pred_out    [R] int32 out (R = B*Nq, or B with CAD_LOGITS_LAST): a drafted row gives d if
+ *               kept, else its replacement draw; a row without a draft gives a plain draw.  Fed
+ *               to cad_accept_scan as pred (causal mode, with_current = 1) it yields exactly the
+ *               stochastic acceptance: the scan runs while drafts were kept and emits the first
+ *               replacement, or the bonus draw.
+ *   logits_out  [R, vocab] fp32 out, nullable
+ * Randomness: Philox4x32-10 (Salmon et al., SC'11) with key (seed low word, seed high word).
+ * The Gumbel noise of vocabulary id x in the row of sequence b at absolute position pos uses
+ * counter (x / 4, pos, b, 0), output word x % 4; the acceptance uniform of that row uses counter
+ * (0, pos, b, 1), word 0.  A word w becomes the uniform (2 * (w >> 9) + 1) / 2^24.  Draws of one
+ * (seed, sequence, position) are therefore the same in every launch shape.
+ * Errors: CAD_EINVAL (temperature not a positive finite number, flags, as cad_span_forward),
+ * CAD_EUNSUPPORTED (fp32 layers), CAD_EWORKSPACE (cad_span_forward_workspace with the same B,
+ * Nq, flags), CAD_EHIP; per sequence CAD_ECAPACITY in kv->err.
+ */
+int cad_span_forward_sampled(const cad_layer_desc *layer, const cad_kv_desc *kv, const int32_t *tokens,
+                             int B, int Nq, int flags, float temperature, uint64_t seed,
+                             const int32_t *draft_len, int32_t *pred_out, float *logits_out,
+                             void *hidden_out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * cad_stack_span_forward — the span forward through a whole stack of n_layers decoder layers
  * (Copy-as-Decode §2.4 splices a copy span through the full model; its Table 11 times whole
  * models).  Same arguments and outputs as cad_span_forward, with:

@@ -685,3 +685,28 @@ def sampled_predictions(logits, tokens, draft_len: int, temperature: float, seed
         else:
             pred[i] = y[i]
     return pred, y, z, pd, u
+
+
+def sampled_margins(logits, tokens, draft_len: int, temperature: float, seed: int, b: int, base: int):
+    """How firmly `sampled_predictions` decides each row: the gap between the best and the
+    second-best Gumbel-perturbed tempered logit over all ids (y_gap) and over the ids other than
+    the draft (z_gap, drafted rows only), and |u - p(d)| / p(d) of the acceptance test."""
+    logits = np.asarray(logits, dtype=np.float64)
+    n, V = logits.shape
+    s = logits / temperature
+    ids = np.arange(V)
+    y_gap = np.zeros(n)
+    z_gap = np.full(n, np.inf)
+    acc_margin = np.full(n, np.inf)
+    _, _, _, pd, u = sampled_predictions(logits, tokens, draft_len, temperature, seed, b, base)
+    for i in range(n):
+        pert = s[i] - np.log(-np.log(sample_uniforms(seed, b, base + i, ids, 0)))
+        top = np.sort(pert)[-2:]
+        y_gap[i] = top[1] - top[0]
+        if i < draft_len:
+            alt = pert.copy()
+            alt[int(tokens[i + 1])] = -np.inf
+            top = np.sort(alt)[-2:]
+            z_gap[i] = top[1] - top[0]
+            acc_margin[i] = abs(u[i] - pd[i]) / pd[i]
+    return y_gap, z_gap, acc_margin

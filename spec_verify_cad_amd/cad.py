@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
     L.cad_stack_span_forward.restype = i32
     L.cad_stack_span_forward_workspace.argtypes = [ctypes.POINTER(LayerDesc), i32, i32, i32, i32, i32, i32, i32, i32]
     L.cad_stack_span_forward_workspace.restype = ctypes.c_size_t
+    L.cad_span_forward_sampled.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(KVDesc), vp, i32, i32, i32,
+                                           ctypes.c_float, ctypes.c_uint64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.cad_span_forward_sampled.restype = i32
     L.cad_span_forward_allowed.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(KVDesc), vp, i32, i32, i32, vp,
                                            i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.cad_span_forward_allowed.restype = i32
@@ -253,6 +256,21 @@ def stack_span_forward(stack: DeviceStack, cache: StackCache, tokens, Nq: int, m
     _check(lib().cad_stack_span_forward(stack.descs, stack.n, cache.descs, _ptr(tokens), B, Nq, mode, W, D, flags,
                                         _ptr(argmax_out), _ptr(hidden_out), _ptr(logits_out), _ptr(workspace),
                                         workspace.numel(), _stream(stream)), "cad_stack_span_forward")
+    return workspace
+
+
+def span_forward_sampled(layer: DeviceLayer, cache: DeviceCache, tokens, Nq: int, temperature: float, seed: int,
+                         draft_len=None, flags: int = 0, pred_out=None, logits_out=None, hidden_out=None,
+                         workspace=None, stream=None):
+    """Causal span forward whose LM head draws (stochastic verification of the drafts in
+    tokens[:, 1:], draft_len [B] per sequence, or plain draws when draft_len is None)."""
+    B = cache.B
+    if workspace is None:
+        workspace = alloc_workspace(span_forward_workspace(layer, B, Nq, MASK_CAUSAL, 1, 1, cache.cap, flags))
+    _check(lib().cad_span_forward_sampled(ctypes.byref(layer.desc), ctypes.byref(cache.desc), _ptr(tokens), B, Nq,
+                                          flags, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(draft_len),
+                                          _ptr(pred_out), _ptr(logits_out), _ptr(hidden_out), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)), "cad_span_forward_sampled")
     return workspace
 
 

@@ -114,6 +114,12 @@ FwdBufs fwd_carve(const FwdDims& fd, void* base, bool kv_only) {
         w.amax_slots_last = gemm_argmax_slots(fd.dtype, fd.B, fd.V, fd.h);
         const size_t sl = std::max(M * (size_t)w.amax_slots, (size_t)fd.B * w.amax_slots_last);
         w.amax_part = (float2*)take(sl * sizeof(float2));
+        if (fd.dtype == CAD_DTYPE_BF16) {
+            w.samp_slots = gemm_argmax_slots(fd.dtype, fd.M, fd.V, fd.h, EPI_SAMPLE);
+            w.samp_slots_last = gemm_argmax_slots(fd.dtype, fd.B, fd.V, fd.h, EPI_SAMPLE);
+            const size_t ss = std::max(M * (size_t)w.samp_slots, (size_t)fd.B * w.samp_slots_last);
+            w.samp_part = (float4*)take(ss * 2 * sizeof(float4));
+        }
         w.x = (float*)take(M * h * 4);
         w.q = take(M * qd * e);
         w.o = take(M * qd * e);
@@ -222,8 +228,8 @@ bool same_shape(const cad_layer_desc* a, const cad_layer_desc* b) {
 // feed the next layer's K/V) and only the K/V projection of the last.
 int span_forward_impl(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs, const int32_t* tokens,
                       int B, int Nq, int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out,
-                      float* logits_out, const int32_t* allowed, int A, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+                      float* logits_out, const int32_t* allowed, int A, const SampleArgs* samp, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
     if (!layers || !kvs || !tokens || n_layers < 1) return CAD_EINVAL;
     if (flags & ~(CAD_COMMIT_ALL | CAD_KV_ONLY | CAD_LOGITS_LAST)) return CAD_EINVAL;
     const bool kv_only = (flags & CAD_KV_ONLY) != 0;
@@ -245,6 +251,10 @@ int span_forward_impl(const cad_layer_desc* layers, int n_layers, const cad_kv_d
         if (kv->n_kv_heads != L->n_kv_heads || kv->head_dim != L->head_dim || kv->dtype != L->dtype) return CAD_EINVAL;
     }
     if (!L0->embed) return CAD_EINVAL;
+    if (samp && (kv_only || mode != CAD_MASK_CAUSAL_SPAN || !(samp->temperature > 0.f) ||
+                 !std::isfinite(samp->temperature)))
+        return CAD_EINVAL;
+    if (samp && L0->dtype != CAD_DTYPE_BF16) return CAD_EUNSUPPORTED;
     if (!kv_only && (!Lz->w_lm || !argmax_out)) return CAD_EINVAL;
     if (!layer_supported(L0) || kv0->cap % 4) return CAD_EUNSUPPORTED;
     if ((long)fd.M * fd.h > (1L << 31) || (long)fd.M * fd.ffn > (1L << 31)) return CAD_EUNSUPPORTED;
@@ -372,6 +382,29 @@ int span_forward_impl(const cad_layer_desc* layers, int n_layers, const cad_kv_d
     pl.M = lm_rows; pl.Nq = last_only ? 1 : fd.Nq;
     pl.N = fd.V; pl.amax_part = wb.amax_part; pl.amax_slots = last_only ? wb.amax_slots_last : wb.amax_slots;
     pl.logits = logits_out;
+    if (samp) {
+        // sampled LM head: the slots hold sampling states; rows know their sequence, position
+        // and draft through the forward's own geometry
+        pl.Nq = fd.Nq;
+        pl.amax_slots = last_only ? wb.samp_slots_last : wb.samp_slots;
+        pl.samp_part = wb.samp_part;
+        pl.inv_temp = 1.0f / samp->temperature;
+        pl.seed_lo = (uint32_t)(samp->seed & 0xFFFFFFFFu);
+        pl.seed_hi = (uint32_t)(samp->seed >> 32);
+        pl.tokens = tokens;
+        pl.draft_len = samp->draft_len;
+        pl.row_pos_last = last_only ? 1 : 0;
+        if (stage(ST_LM_HEAD, stream, [&] {
+                return launch_gemm(fd.dtype, EPI_SAMPLE, lb.u3, Lz->w_lm, lm_rows, fd.V, fd.h, 1, pl, stream);
+            }) != hipSuccess)
+            return CAD_EHIP;
+        if (stage(ST_ARGMAX, stream, [&] {
+                return launch_sample_final(fd, wb, last_only, tokens, *samp, argmax_out,
+                                           (flags & CAD_COMMIT_ALL) ? kv0->len : nullptr, stream);
+            }) != hipSuccess)
+            return CAD_EHIP;
+        return CAD_OK;
+    }
     if (stage(ST_LM_HEAD, stream, [&] {
             return launch_gemm(fd.dtype, EPI_ARGMAX, lb.u3, Lz->w_lm, lm_rows, fd.V, fd.h, 1, pl, stream);
         }) != hipSuccess)
@@ -390,7 +423,7 @@ int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32
                      int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return span_forward_impl(L, 1, kv, tokens, B, Nq, mode, W, D, flags, argmax_out, hidden_out, logits_out, nullptr,
-                             0, workspace, workspace_bytes, stream);
+                             0, nullptr, workspace, workspace_bytes, stream);
 }
 
 int cad_span_forward_allowed(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
@@ -401,7 +434,18 @@ int cad_span_forward_allowed(const cad_layer_desc* L, const cad_kv_desc* kv, con
     if (flags & ~(CAD_COMMIT_ALL | CAD_LOGITS_LAST)) return CAD_EINVAL;
     if (!L || !kv) return CAD_EINVAL;
     return span_forward_impl(L, 1, kv, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, argmax_out, hidden_out,
-                             logits_out, allowed, A, workspace, workspace_bytes, stream);
+                             logits_out, allowed, A, nullptr, workspace, workspace_bytes, stream);
+}
+
+int cad_span_forward_sampled(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
+                             int flags, float temperature, uint64_t seed, const int32_t* draft_len, int32_t* pred_out,
+                             float* logits_out, void* hidden_out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    if (!L || !kv || !pred_out) return CAD_EINVAL;
+    if (flags & ~(CAD_COMMIT_ALL | CAD_LOGITS_LAST)) return CAD_EINVAL;
+    const SampleArgs sa{temperature, seed, draft_len};
+    return span_forward_impl(L, 1, kv, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, pred_out, hidden_out,
+                             logits_out, nullptr, 0, &sa, workspace, workspace_bytes, stream);
 }
 
 int cad_stack_span_forward(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs, const int32_t* tokens,
@@ -409,7 +453,7 @@ int cad_stack_span_forward(const cad_layer_desc* layers, int n_layers, const cad
                            float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (n_layers < 1 || n_layers > CAD_MAX_LAYERS) return CAD_EINVAL;
     return span_forward_impl(layers, n_layers, kvs, tokens, B, Nq, mode, W, D, flags, argmax_out, hidden_out,
-                             logits_out, nullptr, 0, workspace, workspace_bytes, stream);
+                             logits_out, nullptr, 0, nullptr, workspace, workspace_bytes, stream);
 }
 
 int cad_ngram_lookup(const int32_t* ctx, int64_t ctx_stride, const int32_t* ctx_len, int B, int n, int W, int D,

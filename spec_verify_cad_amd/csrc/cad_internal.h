@@ -13,7 +13,7 @@
 //               column tile); a small row kernel reduces the slots and commits the cache length
 //   EPI_PARTIAL fp32 partial sums of one K slice, part[slice][row][feature]; the next row
 //               kernel adds the slices (in slice order) to the residual stream
-enum EpiKind { EPI_QKV = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2, EPI_PARTIAL = 3 };
+enum EpiKind { EPI_QKV = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2, EPI_PARTIAL = 3, EPI_SAMPLE = 4 };
 
 // Everything a GEMM epilogue needs.  Unused fields are ignored by the other kinds.
 struct EpiParams {
@@ -30,6 +30,14 @@ struct EpiParams {
     float2* amax_part;              // [M, slots] (max, index bits)
     int amax_slots;
     float* logits;                  // nullable debug output [M, N]
+    // EPI_SAMPLE (the LM head of a sampled forward): per (row, slot) two float4 of SampleState;
+    // the slot index is that of the argmax slots (amax_slots per row)
+    float4* samp_part;
+    float inv_temp;
+    uint32_t seed_lo, seed_hi;
+    const int32_t* tokens;          // [M] the forward's input tokens (row r's draft is token r + 1)
+    const int32_t* draft_len;       // [B] drafts per sequence, nullable (no drafts)
+    int row_pos_last;               // rows are each sequence's last row (copy-commit mode)
     // EPI_PARTIAL
     float* part;                    // [S, M, N]
     int k_slice;                    // elements of K per slice (multiple of 64)
@@ -58,7 +66,16 @@ struct FwdBufs {
     float* h1; void* u2; void* act; float* h2; void* u3;
     float* part;                    // K-slice partials of the O and down projections
     float* qkv_part;                // K-slice partials of a split QKV projection
+    float4* samp_part;              // sampled LM head: per (row, slot) two float4 (bf16 layers)
+    int samp_slots, samp_slots_last;
     size_t total;
+};
+
+// Arguments of a sampled forward (stochastic verification).
+struct SampleArgs {
+    float temperature;
+    uint64_t seed;
+    const int32_t* draft_len;       // [B], nullable
 };
 
 bool fwd_dims(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, int cap, FwdDims* fd);
@@ -77,6 +94,10 @@ hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, bool last_o
 // normed rows are written for every row, or (last_only) compactly for each sequence's last row
 // argmax over each row's allowed ids (final normed rows wb.u3 against those LM-head rows),
 // with the commit of the cache lengths
+// reduces a sampled LM head's slots per row and writes the row's prediction (kept draft,
+// replacement draw or plain draw), with the commit of the cache lengths
+hipError_t launch_sample_final(const FwdDims& fd, const FwdBufs& wb, bool last_only, const int32_t* tokens,
+                               const SampleArgs& sa, int32_t* pred_out, int32_t* kv_len, hipStream_t s);
 hipError_t launch_allowed_argmax(const FwdDims& fd, const FwdBufs& wb, const void* w_lm, const int32_t* allowed, int A,
                                  bool last_only, int32_t* argmax_out, float* logits_out, int32_t* kv_len,
                                  hipStream_t s);
@@ -95,7 +116,7 @@ bool gemm_qkv_split(int dtype, int M, int K);
 hipError_t launch_qkv_finish(const FwdDims& fd, const float* part, int slices, int N, int head_off,
                              const FwdBufs& wb, void* kc, void* vc, hipStream_t s);
 // (max, index) partial slots per row written by an EPI_ARGMAX launch of this shape
-int gemm_argmax_slots(int dtype, int M, int N, int K);
+int gemm_argmax_slots(int dtype, int M, int N, int K, int kind = EPI_ARGMAX);
 void attention_plan(FwdDims* fd, int cus);
 hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc, const void* vc,
                             hipStream_t s);

@@ -17,7 +17,7 @@ hipError_t launch_skinny(int kind, const void* A, const void* W, int M, int N, i
                          hipStream_t s);
 bool skinny_supports(int kind, int M, int K);
 int skinny_partial_slices(int K);
-int skinny_argmax_slots(int M, int N, int K);
+int skinny_argmax_slots(int kind, int M, int N, int K);
 hipError_t launch_big(int kind, const void* A, const void* W, int M, int N, int K, int slices, const EpiParams& p,
                       hipStream_t s);
 int big_slots(int kind, int M, int N, int K);
@@ -184,10 +184,10 @@ hipError_t dispatch_f32(const void* A, const void* W, int M, int N, int K, int s
 
 // K slices of an EPI_PARTIAL launch (the O and down projections); the workspace holds
 // slices x M x N fp32 partials.
-int gemm_argmax_slots(int dtype, int M, int N, int K) {
+int gemm_argmax_slots(int dtype, int M, int N, int K, int kind) {
     if (dtype == CAD_DTYPE_F32) return tile_plan(EPI_ARGMAX, M, N, K, 1).nnt;
-    if (skinny_supports(EPI_ARGMAX, M, K)) return skinny_argmax_slots(M, N, K);
-    return big_slots(EPI_ARGMAX, M, N, K);
+    if (skinny_supports(kind, M, K)) return skinny_argmax_slots(kind, M, N, K);
+    return big_slots(kind, M, N, K);
 }
 
 // K slices of an EPI_PARTIAL launch (the O and down projections); the workspace holds

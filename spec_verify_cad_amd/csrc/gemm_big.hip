@@ -281,6 +281,47 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
         if (p.d == 128) qkv_epilogue<FT, TT, 4>(acc, p, m0 + wm * C::WTM, fbase, M, N, l16, g4);
         else if (p.d == 64) qkv_epilogue<FT, TT, 2>(acc, p, m0 + wm * C::WTM, fbase, M, N, l16, g4);
         else qkv_epilogue<FT, TT, 1>(acc, p, m0 + wm * C::WTM, fbase, M, N, l16, g4);
+    } else if constexpr (KIND == EPI_SAMPLE) {
+        // per row: Gumbel-perturbed maxima and the log-sum-exp over this tile's ids, merged over
+        // the lane groups of a wave, then over the WN waves that share the rows
+        __shared__ float4 sred[WN][BM][2];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const int tok = m0 + wm * C::WTM + tt * 16 + l16;
+            SampleState st;
+            sample_init(st);
+            if (tok < M) {
+                const SampleRow sr = sample_row(p, tok);
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft) {
+                    const int n0 = fbase + ft * 16 + g4 * 4;
+                    if (n0 >= N) continue;
+                    const uint4 w = sample_bits(p, sr, n0);
+                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int n = n0 + i;
+                        if (n < N) {
+                            const float v = acc[ft][tt][i];
+                            sample_add(st, v * p.inv_temp, gumbel(ws[i]), n, sr.draft);
+                            if (p.logits) p.logits[(size_t)tok * N + n] = v;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) sample_merge(st, sample_shfl_xor(st, o));
+            if (g4 == 0) sample_store(&sred[wn][wm * C::WTM + tt * 16 + l16][0], st);
+        }
+        __syncthreads();
+        for (int r = tid; r < BM; r += NT) {
+            const int tok = m0 + r;
+            if (tok >= M) continue;
+            SampleState st = sample_load(&sred[0][r][0]);
+#pragma unroll
+            for (int w = 1; w < WN; ++w) sample_merge(st, sample_load(&sred[w][r][0]));
+            sample_store(p.samp_part + ((size_t)tok * p.amax_slots + nt) * 2, st);
+        }
     } else {                                                 // EPI_ARGMAX
         __shared__ float2 red[WN][BM];
 #pragma unroll
@@ -353,6 +394,7 @@ BigPlan big_plan(int kind, int M, int N, int K, int slices) {
     t.BN = 256;
     t.BM = M <= 64 ? 64 : M <= 128 ? 128 : 256;
     if (kind == EPI_SWIGLU && M <= 128) t.BM = 64;     // more workgroups for the gate/up pairs
+    if (kind == EPI_SAMPLE && t.BM > 128) t.BM = 128;  // the sampling state of 256 rows spills
     if (kind == EPI_QKV || kind == EPI_PARTIAL || (kind == EPI_SWIGLU && M > 128 && M <= 256)) {
         // narrow outputs: 128 x 64 tiles give more workgroups (and QKV one head per wave); for the
         // K-slice partials they also mean fewer slices, so less partial traffic for the row
@@ -398,6 +440,7 @@ hipError_t launch_big(int kind, const void* A, const void* W, int M, int N, int 
         case EPI_QKV: return big_dispatch<EPI_QKV>(A, W, M, N, K, 1, p, s);
         case EPI_SWIGLU: return big_dispatch<EPI_SWIGLU>(A, W, M, N, K, 1, p, s);
         case EPI_ARGMAX: return big_dispatch<EPI_ARGMAX>(A, W, M, N, K, 1, p, s);
+        case EPI_SAMPLE: return big_dispatch<EPI_SAMPLE>(A, W, M, N, K, 1, p, s);
         default: return big_dispatch<EPI_PARTIAL>(A, W, M, N, K, slices, p, s);
     }
 }

@@ -88,6 +88,13 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
 
     float best = -INFINITY;                           // LM head: this lane's running (max, index)
     int bidx = 0x7fffffff;
+    SampleState sst;                                  // sampled LM head: this lane's running state
+    SampleRow srow;
+    if constexpr (KIND == EPI_SAMPLE) {
+        sample_init(sst);
+        const int tok = wave * 16 + l16;
+        srow = sample_row(p, tok < M && wave < TT ? tok : 0);
+    }
 
     auto compute = [&](int uu, const uint4 (&wf)[SSW][2]) {
         const int tile = uu / S;
@@ -121,6 +128,20 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
                     if (live && n < N) {
                         if (c[i] > best) { best = c[i]; bidx = n; }   // n increases along a lane
                         if (p.logits) p.logits[(size_t)tok * N + n] = c[i];
+                    }
+                }
+            } else if constexpr (KIND == EPI_SAMPLE) {
+                if (live) {
+                    const int n0 = tile * 16 + g4 * 4;
+                    const uint4 w = sample_bits(p, srow, n0);
+                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int n = n0 + i;
+                        if (n < N) {
+                            sample_add(sst, c[i] * p.inv_temp, gumbel(ws[i]), n, srow.draft);
+                            if (p.logits) p.logits[(size_t)tok * N + n] = c[i];
+                        }
                     }
                 }
             } else {
@@ -196,6 +217,14 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
         }
     }
 
+    if constexpr (KIND == EPI_SAMPLE) {
+        if (wave < TT) {
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) sample_merge(sst, sample_shfl_xor(sst, o));
+            const int tok = wave * 16 + l16;
+            if (g4 == 0 && tok < M) sample_store(p.samp_part + ((size_t)tok * p.amax_slots + blockIdx.x) * 2, sst);
+        }
+    }
     if constexpr (KIND == EPI_ARGMAX) {
         if (wave < TT) {
 #pragma unroll
@@ -266,8 +295,12 @@ int full_grid(int K, int ntiles) {
 
 }  // namespace
 
-int skinny_argmax_slots(int M, int N, int K) {
+int skinny_argmax_slots(int kind, int M, int N, int K) {
     const int nt = (N + 15) / 16;
+    if (kind == EPI_SAMPLE) {
+        if (M > 32) return full_grid<EPI_SAMPLE, 4>(K, nt);
+        return M > 16 ? full_grid<EPI_SAMPLE, 2>(K, nt) : full_grid<EPI_SAMPLE, 1>(K, nt);
+    }
     if (M > 32) return full_grid<EPI_ARGMAX, 4>(K, nt);
     return M > 16 ? full_grid<EPI_ARGMAX, 2>(K, nt) : full_grid<EPI_ARGMAX, 1>(K, nt);
 }
@@ -279,7 +312,7 @@ int skinny_partial_slices(int K) { return (K + kSkinnyPartialSlice - 1) / kSkinn
 // Rows 33..64 take the 8-wave, 3-super-step variant (one workgroup per CU); for the LM head that
 // measured slower than the LDS-tiled kernel, so only the layer's projections use it.
 bool skinny_supports(int kind, int M, int K) {
-    if (M > 64 || (M > 32 && kind == EPI_ARGMAX)) return false;
+    if (M > 64 || (M > 32 && (kind == EPI_ARGMAX || kind == EPI_SAMPLE))) return false;
     if (kind == EPI_PARTIAL) return true;
     return K <= (M > 32 ? 8 * 3 * 64 : 8 * 7 * 64);
 }
@@ -298,6 +331,7 @@ hipError_t launch_skinny(int kind, const void* A, const void* W, int M, int N, i
         case EPI_QKV: return full_tt<EPI_QKV>(A, W, M, N, K, N / 16, p, s);
         case EPI_SWIGLU: return full_tt<EPI_SWIGLU>(A, W, M, N, K, (p.ffn + 7) / 8, p, s);
         case EPI_ARGMAX: return full_tt<EPI_ARGMAX>(A, W, M, N, K, (N + 15) / 16, p, s);
+        case EPI_SAMPLE: return full_tt<EPI_SAMPLE>(A, W, M, N, K, (N + 15) / 16, p, s);
         default: {
             const int nt = (N + 15) / 16, S = skinny_partial_slices(K);
             if (M > 32) return go<EPI_PARTIAL, 4, 3, 4>(A, W, M, N, K, nt, S, p, s);

@@ -271,6 +271,43 @@ __global__ __launch_bounds__(AMAX * 64) void k_allowed_argmax(const T* __restric
     if (kv_len && r % rps == 0) kv_len[b] = len_snap[b] + Nq;
 }
 
+// Sampled forward, one wave per row: merges the row's LM-head slots (Gumbel-perturbed maxima y
+// over all ids and z over the ids other than the draft, and the log-sum-exp of the tempered
+// logits), then the prediction: a row holding a draft d keeps it when the row's acceptance
+// uniform is below p(d) = exp(logit_d / T - lse) and otherwise takes z; a row without a draft
+// takes y.  The first row of each sequence advances the cache length.
+__global__ __launch_bounds__(64) void k_sample_final(const float4* __restrict__ part, int slots, int rps, int Nq,
+                                                     int cap, const int32_t* __restrict__ len_snap,
+                                                     const int32_t* __restrict__ tokens,
+                                                     const int32_t* __restrict__ draft_len, uint32_t seed_lo,
+                                                     uint32_t seed_hi, int32_t* __restrict__ out,
+                                                     int32_t* __restrict__ kv_len) {
+    const int r = blockIdx.x, b = r / rps;
+    if (!seq_ok(len_snap, b, Nq, cap)) return;
+    SampleState st;
+    sample_init(st);
+    for (int t = threadIdx.x; t < slots; t += 64) sample_merge(st, sample_load(part + ((size_t)r * slots + t) * 2));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) sample_merge(st, sample_shfl_xor(st, o));
+    if (threadIdx.x != 0) return;
+    const int it = rps == 1 ? Nq - 1 : r % Nq;
+    int d = -1;
+    if (draft_len && rps != 1) {
+        int dl = draft_len[b];
+        dl = dl < Nq - 1 ? dl : Nq - 1;
+        if (it < dl) d = tokens[(size_t)b * Nq + it + 1];
+    }
+    int pred = st.yi;
+    if (d >= 0) {
+        const float lse = st.m + logf(st.s);
+        const float pd = expf(st.dl - lse);
+        const uint4 w = philox4x32_10(make_uint4(0u, (uint32_t)(len_snap[b] + it), (uint32_t)b, 1u), seed_lo, seed_hi);
+        pred = uniform_from_bits(w.x) < pd ? d : st.zi;
+    }
+    out[r] = pred;
+    if (kv_len && r % rps == 0) kv_len[b] = len_snap[b] + Nq;
+}
+
 // One wave per row.  The LM head ran on rps rows per sequence (Nq, or 1 for the last row only):
 // row r belongs to sequence b = r / rps, and the wave of the sequence's first row commits.
 __global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ part, int slots, int rps, int Nq,
@@ -379,5 +416,15 @@ hipError_t launch_allowed_argmax(const FwdDims& fd, const FwdBufs& wb, const voi
         hipLaunchKernelGGL(k_allowed_argmax<uint16_t>, dim3(rows), dim3(AMAX * 64), 0, s, (const uint16_t*)wb.u3,
                            (const uint16_t*)w_lm, fd.h, fd.V, allowed, A, rps, fd.Nq, fd.cap, wb.len_snap, argmax_out,
                            logits_out, kv_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_sample_final(const FwdDims& fd, const FwdBufs& wb, bool last_only, const int32_t* tokens,
+                               const SampleArgs& sa, int32_t* pred_out, int32_t* kv_len, hipStream_t s) {
+    const int rps = last_only ? 1 : fd.Nq;
+    const int slots = last_only ? wb.samp_slots_last : wb.samp_slots;
+    hipLaunchKernelGGL(k_sample_final, dim3(fd.B * rps), dim3(64), 0, s, wb.samp_part, slots, rps, fd.Nq, fd.cap,
+                       wb.len_snap, tokens, sa.draft_len, (uint32_t)(sa.seed & 0xFFFFFFFFu), (uint32_t)(sa.seed >> 32),
+                       pred_out, kv_len);
     return hipGetLastError();
 }
