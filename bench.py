@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--pmc-pass", action="store_true",
                     help="no timing: a few N = ROOF_N forwards and plain copies of a known size, for a "
                          "hardware-counter run that calibrates and measures the LM head's HBM traffic")
+    ap.add_argument("--part", choices=("program", "stack", "pld"), default=None,
+                    help="run one secondary workload alone and print its JSON object (for a profiler run); "
+                         "no headline line")
     return ap.parse_args()
 
 
@@ -69,6 +72,18 @@ def main():
     from spec_verify_cad_amd import cad, synth
     from spec_verify_cad_amd import roofline as R
     from spec_verify_cad_amd.configs import CONFIGS, copy_sweep_inputs
+
+    if a.part in ("program", "stack"):
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        cad.lib()
+        if a.part == "program":
+            out = cad_program(a, dev)
+        else:
+            out = [stack_curve(a, dev, k) for k in ("qwen15_span", "qwen7_cad_program")]
+            stack_cost_model(out)
+        print(json.dumps(out), flush=True)
+        return
 
     wl = CONFIGS["qwen15_span"]
     shp = wl.shape
@@ -94,6 +109,9 @@ def main():
     doc, prefix, span_toks = copy_sweep_inputs(wl, spans)
     if a.pmc_pass:
         pmc_pass(a, shp, layers, prefix, span_toks, spans, L0, cap, dev)
+        return
+    if a.part == "pld":
+        print(json.dumps(pld_rounds(a, lay0, dev)), flush=True)
         return
 
     # one cache per N; their lengths are views of one tensor so a single fill restores them all
