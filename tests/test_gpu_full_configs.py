@@ -174,7 +174,13 @@ def test_block_verify_full_size(qwen7):
 # ---------------------------------------------------------------------------------------------
 # config 5: batched PLD rounds, zero host syncs inside the 32 rounds
 # ---------------------------------------------------------------------------------------------
-def test_pld_batch_rounds_full_size(qwen15):
+PLD_SAMPLE_SEED = 0x5EED_CAD0        # the seed bench.py's sampled rounds use
+
+
+@pytest.mark.parametrize("temperature", [None, 1.0], ids=["greedy", "sampled"])
+def test_pld_batch_rounds_full_size(qwen15, temperature):
+    """Greedy verification, and stochastic verification at T = 1 (the drafts come from the
+    context, so with random weights they are replaced; kept drafts are covered at the small shape)."""
     wl = CONFIGS["qwen15_pld_batch"]
     _, dl, OL = qwen15
     e = wl.extra
@@ -204,7 +210,11 @@ def test_pld_batch_rounds_full_size(qwen15):
     log("pld: 32 rounds")
     for r in range(R):
         cad.ngram_lookup(hist, hlen, n, 1, k, 1, rows, dlen)
-        cad.span_forward(dl, cache, rows, 1 + k, argmax_out=am, workspace=ws)
+        if temperature is None:
+            cad.span_forward(dl, cache, rows, 1 + k, argmax_out=am, workspace=ws)
+        else:
+            cad.span_forward_sampled(dl, cache, rows, 1 + k, temperature, PLD_SAMPLE_SEED, draft_len=dlen,
+                                     pred_out=am, workspace=ws)
         cad.accept_scan(rows, 1, dlen, am, None, B, 1, k, cad.MASK_CAUSAL, acc, None, em, ne, ctx=hist, ctx_len=hlen,
                         ctx_cap=stride, cache=cache)
         rec_rows[r].copy_(rows)
@@ -218,20 +228,40 @@ def test_pld_batch_rounds_full_size(qwen15):
     assert (dlen_h[0] > 0).all()                         # every sequence starts mid-copy
     # the oracle replays two sequences round by round, following the GPU's stream where an
     # argmax was not determined (its choice is then checked to be a near-top one)
-    for b in (0, 41):
+    ltol = logit_tol(wl.shape.hidden)
+    firm_rows = 0
+    for b in ((0, 41) if temperature is None else (17,)):
         log(f"pld: oracle replay of sequence {b}")
         oc = O.cache_from_tokens(OL, ctxs[b][:Lc - 1], cap)
         h = list(ctxs[b])
         for r in range(R):
             d, l, _ = O.ngram_lookup(np.array(h), len(h), n, 1, k)
             assert rows_h[r, b, 0] == h[-1] and list(rows_h[r, b, 1:]) == list(d[0]) and dlen_h[r, b] == l[0], (b, r)
-            ref = O.span_forward(OL, oc, [h[-1]] + list(d[0]), commit=False)
-            argmax_check(pred_h[r, b], ref, None, what=f"pld b={b} r={r}", tol=logit_tol(wl.shape.hidden))
+            toks = [h[-1]] + list(d[0])
+            base = oc.length
+            ref = O.span_forward(OL, oc, toks, commit=False)
+            if temperature is None:
+                argmax_check(pred_h[r, b], ref, None, what=f"pld b={b} r={r}", tol=ltol)
+            else:
+                # decisions the logit error (at most ltol per logit) cannot flip must match
+                dl_ = int(l[0])
+                opred = O.sampled_predictions(ref["logits"], toks, dl_, temperature, PLD_SAMPLE_SEED, b, base)[0]
+                y_gap, z_gap, acc_m = O.sampled_margins(ref["logits"], toks, dl_, temperature, PLD_SAMPLE_SEED, b,
+                                                        base)
+                margin = 2 * ltol / temperature + 1e-6
+                for i in range(1 + k):
+                    firm = (acc_m[i] > np.expm1(margin) and z_gap[i] > margin) if i < dl_ else y_gap[i] > margin
+                    if firm:
+                        firm_rows += 1
+                        assert pred_h[r, b, i] == opred[i], (b, r, i, pred_h[r, b, i], opred[i])
+                    assert 0 <= pred_h[r, b, i] < wl.shape.vocab
             a, emitted = O.accept_causal(d[0], int(l[0]), pred_h[r, b])
             assert a == acc_h[r, b], (b, r)
             h += emitted
             oc.length += a + 1
         np.testing.assert_array_equal(hist_h[b, :len(h)], h)
+    if temperature is not None:
+        assert firm_rows >= 0.9 * R * (1 + k)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -187,3 +187,56 @@ def test_stack_argument_errors(small_stack):
         cad.stack_span_forward(mixed, sc, t, 4, argmax_out=am, workspace=ws_)
     torch.cuda.synchronize()
     assert int(sc.len[0]) == 0
+
+
+def test_full_depth_1p5b_stack_matches_oracle():
+    """The 28-layer stack of the 1.5B shape the full-depth curve times: a 64-token prefix, an
+    8-token span (all rows' logits), then a copy-commit span, against the oracle's stack."""
+    from spec_verify_cad_amd.configs import QWEN15
+    nl, L0, cap, N = 28, 64, 96, 8
+    log("full-depth 1.5B stack: weights")
+    ws = _stack_weights(QWEN15, 900, nl)
+    dst = cad.DeviceStack([cad.DeviceLayer(QWEN15, w) for w in ws])
+    log("full-depth 1.5B stack: oracle weights")
+    ols = [oracle_layer(QWEN15, w, only=list(w)) for w in ws]
+    del ws
+    ctx = synth.uniform_tokens(910, L0, QWEN15.vocab)[None]
+    span = synth.uniform_tokens(911, 2 * N, QWEN15.vocab)[None]
+    sc = cad.StackCache(QWEN15, nl, 1, cap)
+    _prefill(dst, sc, ctx, chunk=64)
+    t = torch.from_numpy(np.ascontiguousarray(span[:, :N], dtype=np.int32)).cuda()
+    am = torch.full((N,), -7, dtype=torch.int32, device="cuda")
+    hid = torch.zeros((N, QWEN15.hidden), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((N, QWEN15.vocab), dtype=torch.float32, device="cuda")
+    cad.stack_span_forward(dst, sc, t, N, flags=cad.COMMIT_ALL, argmax_out=am, hidden_out=hid, logits_out=lg)
+    t2 = torch.from_numpy(np.ascontiguousarray(span[:, N:], dtype=np.int32)).cuda()
+    am2 = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    lg2 = torch.zeros((1, QWEN15.vocab), dtype=torch.float32, device="cuda")
+    cad.stack_span_forward(dst, sc, t2, N, flags=cad.COMMIT_ALL | cad.LOGITS_LAST, argmax_out=am2, logits_out=lg2)
+    torch.cuda.synchronize()
+    assert int(sc.len[0]) == L0 + 2 * N
+    log("full-depth 1.5B stack: oracle prefill and spans")
+    ocs = O.stack_prefill(ols, ctx[0], cap, chunk=64)
+    ref = O.stack_span_forward(ols, ocs, span[0, :N])
+    scale = math.sqrt(nl)
+    g_h = to_f64(hid, "bf16")
+    dh = np.abs(g_h - ref["hidden_out"])
+    tol_h = hidden_tol(ref["hidden_out"], QWEN15.ffn) * scale
+    ltol = logit_tol(QWEN15.hidden) * scale
+    g_l = lg.cpu().numpy().astype(np.float64)
+    dl = np.abs(g_l - ref["logits"]).max()
+    log(f"28 layers: hidden max-abs {dh.max():.3e} (tol from {tol_h.min():.3g}), logits max-abs {dl:.3e} (tol {ltol:.3g})")
+    assert (dh <= tol_h).all()
+    assert dl <= ltol
+    argmax_check(am.cpu().numpy(), ref, g_l, "28-layer span", ltol)
+    ref2 = O.stack_span_forward(ols, ocs, span[0, N:])
+    last = {k: ref2[k][N - 1:N] for k in ("logits", "argmax", "top2_gap")}
+    g_l2 = lg2.cpu().numpy().astype(np.float64)
+    assert np.abs(g_l2 - last["logits"]).max() <= ltol
+    argmax_check(am2.cpu().numpy(), last, g_l2, "28-layer copy-commit", ltol)
+    # the first and last layers' cache rows of the whole sequence
+    for l in (0, nl - 1):
+        k_ = to_f64(sc.caches[l].k[0, :, :L0 + 2 * N], "bf16")
+        d = np.abs(k_ - ocs[l].K[:, :L0 + 2 * N])
+        assert (d <= hidden_tol(ocs[l].K[:, :L0 + 2 * N]) * math.sqrt(l + 1)).all(), f"layer {l} K {d.max()}"
+        log(f"layer {l} K rows: max-abs {d.max():.3e}")
