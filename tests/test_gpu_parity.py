@@ -379,6 +379,39 @@ def test_masked_argmax_over_the_top_ids_equals_the_plain_argmax(small):
     assert (ga[gap > 2 * LOGIT_TOL] == full[gap > 2 * LOGIT_TOL]).all()
 
 
+def test_tiny_fp32_masked_argmax_matches_oracle():
+    """The masked decision on the fp32 layer (the fp32 instance of the allowed-ids kernel)."""
+    wl = CONFIGS["tiny_f32"]
+    w = synth.layer_weights(TINY, wl.seed)
+    OL = oracle_layer(TINY, w)
+    oc = O.cache_from_hidden(OL, synth.hidden_states(wl.seed, wl.cache_len, TINY.hidden), 160)
+    span = synth.uniform_tokens(wl.seed, 8, TINY.vocab, stream=3)
+    ref = O.span_forward(OL, oc.copy(), span)
+    dl = cad.DeviceLayer(TINY, w)
+    cache = cad.DeviceCache(TINY, 1, 160)
+    upload_oracle_cache(cache, 0, oc, "f32")
+    A = 9
+    al = _allowed_sets(21, 8, A, TINY.vocab, ref["argmax"])
+    am = torch.full((8,), -7, dtype=torch.int32, device="cuda")
+    lv = torch.zeros((8, A), dtype=torch.float32, device="cuda")
+    cad.span_forward_allowed(dl, cache, torch.from_numpy(span[None].astype(np.int32)).cuda(), 8,
+                             torch.from_numpy(al).cuda(), A, flags=cad.COMMIT_ALL, argmax_out=am, logits_out=lv)
+    torch.cuda.synchronize()
+    assert int(cache.len[0]) == 128 + 8
+    _check_masked(am.cpu().numpy(), lv.cpu().numpy().astype(np.float64), al, ref["logits"], TINY.vocab, "tiny fp32")
+
+
+def test_sampled_forward_rejects_fp32_layers():
+    wl = CONFIGS["tiny_f32"]
+    dl = cad.DeviceLayer(TINY, synth.layer_weights(TINY, wl.seed))
+    cache = cad.DeviceCache(TINY, 1, 32)
+    t = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    pred = torch.zeros(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(cad.CadError) as e:
+        cad.span_forward_sampled(dl, cache, t, 4, 1.0, 1, pred_out=pred)
+    assert e.value.status == cad.CAD_EUNSUPPORTED
+
+
 def test_copy_commit_mode_rejects_the_block_mask(small):
     w, dl, OL = small
     cache = cad.DeviceCache(SMALL, 1, 64)

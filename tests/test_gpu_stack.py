@@ -240,3 +240,33 @@ def test_full_depth_1p5b_stack_matches_oracle():
         d = np.abs(k_ - ocs[l].K[:, :L0 + 2 * N])
         assert (d <= hidden_tol(ocs[l].K[:, :L0 + 2 * N]) * math.sqrt(l + 1)).all(), f"layer {l} K {d.max()}"
         log(f"layer {l} K rows: max-abs {d.max():.3e}")
+
+
+def test_tiny_fp32_stack_matches_oracle():
+    """A 3-layer stack of the tiny fp32 layer (the simple attention path) against the oracle."""
+    from spec_verify_cad_amd.configs import TINY
+    nl, L0, cap, N = 3, 40, 64, 8
+    ws = _stack_weights(TINY, 500, nl)
+    dst = cad.DeviceStack([cad.DeviceLayer(TINY, w) for w in ws])
+    ols = [oracle_layer(TINY, w, only=list(w)) for w in ws]
+    ctx = synth.uniform_tokens(510, L0, TINY.vocab)[None]
+    span = synth.uniform_tokens(511, N, TINY.vocab)[None]
+    sc = cad.StackCache(TINY, nl, 1, cap)
+    _prefill(dst, sc, ctx)
+    t = torch.from_numpy(np.ascontiguousarray(span, dtype=np.int32)).cuda()
+    am = torch.full((N,), -7, dtype=torch.int32, device="cuda")
+    hid = torch.zeros((N, TINY.hidden), dtype=torch.float32, device="cuda")
+    lg = torch.zeros((N, TINY.vocab), dtype=torch.float32, device="cuda")
+    cad.stack_span_forward(dst, sc, t, N, flags=cad.COMMIT_ALL, argmax_out=am, hidden_out=hid, logits_out=lg)
+    torch.cuda.synchronize()
+    ocs = O.stack_prefill(ols, ctx[0], cap)
+    ref = O.stack_span_forward(ols, ocs, span[0])
+    dh = np.abs(hid.cpu().numpy().astype(np.float64) - ref["hidden_out"]).max()
+    g_l = lg.cpu().numpy().astype(np.float64)
+    dl = np.abs(g_l - ref["logits"]).max()
+    log(f"tiny fp32 stack: hidden {dh:.3e} logits {dl:.3e}")
+    assert dh <= 1e-4 and dl <= 1e-4
+    argmax_check(am.cpu().numpy(), ref, g_l, "tiny fp32 stack", 1e-4)
+    for l in range(nl):
+        k_ = sc.caches[l].k[0, :, :L0 + N].cpu().numpy().astype(np.float64)
+        assert np.abs(k_ - ocs[l].K[:, :L0 + N]).max() <= 1e-4
