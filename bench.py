@@ -80,7 +80,7 @@ def main():
         if a.part == "program":
             out = cad_program(a, dev)
         else:
-            out = [stack_curve(a, dev, k) for k in ("qwen15_span", "qwen7_cad_program")]
+            out = [stack_curve(a, dev, "qwen15_span"), stack_curve(a, dev, "qwen7_cad_program", program=True)]
             stack_cost_model(out)
         print(json.dumps(out), flush=True)
         return
@@ -249,7 +249,8 @@ def main():
     pld = None if a.no_pld else pld_rounds(a, lay0, dev)
 
     # ---- full-depth stacks: the pages' kernel table (parallel forward vs autoregression) at 28 layers
-    stack = None if a.no_stack else [stack_curve(a, dev, k) for k in ("qwen15_span", "qwen7_cad_program")]
+    stack = None if a.no_stack else [stack_curve(a, dev, "qwen15_span"),
+                                     stack_curve(a, dev, "qwen7_cad_program", program=not a.no_program)]
     if stack:
         stack_cost_model(stack)
 
@@ -462,7 +463,7 @@ STACK_PREFIX = 1024
 STACK_SPANS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
 
 
-def stack_curve(a, dev, shape_key: str):
+def stack_curve(a, dev, shape_key: str, program: bool = False):
     """The span forward through a whole 28-layer stack of the given shape (random weights drawn
     on the device, N(0, 0.02), bf16) after a 1024-token prefix, for N = 1 .. 512: one parallel
     forward of N tokens (full LM head, and copy-commit mode with the LM head for the last row
@@ -580,9 +581,75 @@ def stack_curve(a, dev, shape_key: str):
         r["frac_of_roofline"] = round(floor / 1e3 / r["pp_ms"], 4)
     log(f"{STACK_LAYERS}-layer {shape_key}: " + ", ".join(f"N={r['N']}: parallel {r['pp_ms']:.3f} ms, AR "
                                                           f"{r['ar_ms']:.2f} ms, s={r['s']}x" for r in rows))
-    del g1, g8, st, sc, layers
+    del g1, g8, sc
+    out = {"layers": nl, "prefix": L0, "shape": shape_key, "rows": rows}
+    if shape_key == "qwen7_cad_program" and program:
+        out["cad_program"] = stack_program(st, dev, rows)
+    del st, layers
     torch.cuda.empty_cache()
-    return {"layers": nl, "prefix": L0, "shape": shape_key, "rows": rows}
+    return out
+
+
+def stack_program(st, dev, rows):
+    """The Copy-as-Decode program workload through the whole 28-layer 7B-shaped stack, eager
+    (one stack call per forward), with an event after every forward so the time splits into
+    copy splices, free generation and the grammar's structural forwards.  Beside it, the page's
+    cost model on the measured curve: autoregressive regeneration L_AR = tau * T (Eq. (1)), the
+    fixed-cost-free bound (Eq. (3)) and the realised speedup."""
+    import numpy as np
+    import torch
+
+    from spec_verify_cad_amd import cad, synth
+    from spec_verify_cad_amd import costmodel as C
+    from spec_verify_cad_amd.configs import CONFIGS, cad_program_inputs
+    from spec_verify_cad_amd.program import DeviceProgram
+
+    wl = CONFIGS["qwen7_cad_program"]
+    doc, ops = cad_program_inputs(wl)
+    fwds = synth.cad_program_forwards(ops)
+    Ld, T = len(doc), wl.extra["total_out"]
+    fed = sum(f.n for f in fwds)
+    cap = ((Ld + fed + 8 + 3) // 4) * 4
+    sc = cad.StackCache(st.shape, st.n, 1, cap, device=dev)
+    dt = torch.from_numpy(doc[None].astype(np.int32)).to(dev)
+    for s0 in range(0, Ld, 2048):
+        cad.stack_span_forward(st, sc, dt[:, s0:s0 + 2048], min(2048, Ld - s0), flags=cad.KV_ONLY | cad.COMMIT_ALL)
+    torch.cuda.synchronize()
+    prog = DeviceProgram(st, sc, doc, fwds, dev)
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(fwds) + 1)]
+    sc.len.fill_(Ld)
+    prog.enqueue(stream)                                 # warm-up run
+    torch.cuda.synchronize()
+    sc.len.fill_(Ld)
+    evs[0].record(stream)
+    for f in range(len(fwds)):                           # the same forwards, one event after each
+        prog.enqueue_one(f, stream)
+        evs[f + 1].record(stream)
+    torch.cuda.synchronize()
+    assert int(sc.len[0]) == Ld + fed
+    per = [evs[f].elapsed_time(evs[f + 1]) for f in range(len(fwds))]
+    total = evs[0].elapsed_time(evs[-1])
+    by_role = {}
+    for f, pf in enumerate(fwds):
+        by_role[pf.role] = by_role.get(pf.role, 0.0) + per[f]
+    cur = {r["N"]: r["s"] for r in rows}
+    tau = next(r["ar_ms"] for r in rows if r["N"] == 1)
+    spans = [o[2] for o in ops if o[0] == "copy"]
+    b = C.bounds(spans, T, cur, m=8)
+    splice_pred = tau * sum(n / C.interp_s(cur, n) for n in spans)
+    res = {"workload": f"{len(ops)} ops, {len(fwds)} forwards, {fed} fed tokens through {st.n} layers",
+           "ms": round(total, 2), "ms_by_role": {k: round(v, 2) for k, v in by_role.items()},
+           "tau_ms": tau, "ar_ms_eq1": round(tau * T, 2), "realized_speedup": round(tau * T / total, 3),
+           "bnd_exact_eq3": round(b["bnd_exact"], 3),
+           "eq2_terms_ms": {"gen_decode": round(tau * b["T_gen"], 2), "copy_splices": round(splice_pred, 2),
+                            "fixed_per_op_measured": round(total - by_role.get("gen_body", 0.0)
+                                                           - by_role.get("splice", 0.0), 2)},
+           "measured_ms": {"gen_body": round(by_role.get("gen_body", 0.0), 2),
+                           "splices": round(by_role.get("splice", 0.0), 2)}}
+    log(f"full-depth cad program: {res}")
+    del sc, prog
+    return res
 
 
 def stack_cost_model(stack):

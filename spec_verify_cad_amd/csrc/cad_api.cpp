@@ -448,6 +448,18 @@ int cad_span_forward_sampled(const cad_layer_desc* L, const cad_kv_desc* kv, con
                              logits_out, nullptr, 0, &sa, workspace, workspace_bytes, stream);
 }
 
+int cad_stack_span_forward_allowed(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs,
+                                   const int32_t* tokens, int B, int Nq, int flags, const int32_t* allowed, int A,
+                                   int32_t* argmax_out, float* logits_out, void* hidden_out, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    if (n_layers < 1 || n_layers > CAD_MAX_LAYERS) return CAD_EINVAL;
+    if (!allowed || !argmax_out) return CAD_EINVAL;
+    if (A < 1 || A > CAD_MAX_ALLOWED) return CAD_EUNSUPPORTED;
+    if (flags & ~(CAD_COMMIT_ALL | CAD_LOGITS_LAST)) return CAD_EINVAL;
+    return span_forward_impl(layers, n_layers, kvs, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, argmax_out,
+                             hidden_out, logits_out, allowed, A, nullptr, workspace, workspace_bytes, stream);
+}
+
 int cad_stack_span_forward(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs, const int32_t* tokens,
                            int B, int Nq, int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out,
                            float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {

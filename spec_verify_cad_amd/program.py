@@ -20,10 +20,14 @@ class DeviceProgram:
     decisions[f] receives the token forward f chose after its last row (masked forwards: the
     allowed id with the largest logit; the others: the unrestricted argmax)."""
 
-    def __init__(self, layer: cad.DeviceLayer, cache: cad.DeviceCache, doc: np.ndarray, forwards: list,
-                 device=None):
+    def __init__(self, layer, cache, doc: np.ndarray, forwards: list, device=None):
+        """layer / cache: a DeviceLayer with its DeviceCache, or a DeviceStack with its StackCache
+        (the program then runs through every layer)."""
         if cache.B != 1:
             raise ValueError("a program runs on a batch-1 cache")
+        self.stacked = isinstance(layer, cad.DeviceStack)
+        if self.stacked != isinstance(cache, cad.StackCache):
+            raise ValueError("a stack runs on a stack cache")
         dev = device if device is not None else cache.len.device
         self.layer, self.cache, self.forwards = layer, cache, list(forwards)
         F = len(self.forwards)
@@ -54,7 +58,11 @@ class DeviceProgram:
         for pf in self.forwards:
             key = (pf.n, self._flags(pf))
             if key not in sizes:
-                sizes[key] = cad.span_forward_workspace(layer, 1, pf.n, cad.MASK_CAUSAL, 1, 1, cache.cap, key[1])
+                if self.stacked:
+                    sizes[key] = cad.stack_span_forward_workspace(layer, 1, pf.n, cad.MASK_CAUSAL, 1, 1, cache.cap,
+                                                                  key[1])
+                else:
+                    sizes[key] = cad.span_forward_workspace(layer, 1, pf.n, cad.MASK_CAUSAL, 1, 1, cache.cap, key[1])
         self.workspace = cad.alloc_workspace(max(sizes.values()), device=dev)
 
     @staticmethod
@@ -63,22 +71,28 @@ class DeviceProgram:
 
     def enqueue(self, stream=None):
         """Enqueue every forward; the cache grows by `fed` rows."""
-        for f, pf in enumerate(self.forwards):
-            n = pf.n
-            if pf.from_prev:
-                tok = self.decisions[f - 1:f].view(1, 1)
-            else:
-                o = int(self.tok_off[f])
-                tok = self.tokens[o:o + n].view(1, n)
-            out = self.decisions[f:f + 1]
-            if pf.allowed is None:
-                cad.span_forward(self.layer, self.cache, tok, n, flags=self._flags(pf), argmax_out=out,
-                                 workspace=self.workspace, stream=stream)
-            else:
-                A = len(pf.allowed)
-                cad.span_forward_allowed(self.layer, self.cache, tok, n, self.allowed[f:f + 1, :A], A,
-                                         flags=self._flags(pf), argmax_out=out, workspace=self.workspace,
-                                         stream=stream)
+        for f in range(len(self.forwards)):
+            self.enqueue_one(f, stream)
+
+    def enqueue_one(self, f: int, stream=None):
+        """Enqueue forward f (after forward f - 1, whose decision it may read)."""
+        pf = self.forwards[f]
+        n = pf.n
+        if pf.from_prev:
+            tok = self.decisions[f - 1:f].view(1, 1)
+        else:
+            o = int(self.tok_off[f])
+            tok = self.tokens[o:o + n].view(1, n)
+        out = self.decisions[f:f + 1]
+        if pf.allowed is None:
+            fwd = cad.stack_span_forward if self.stacked else cad.span_forward
+            fwd(self.layer, self.cache, tok, n, flags=self._flags(pf), argmax_out=out, workspace=self.workspace,
+                stream=stream)
+        else:
+            A = len(pf.allowed)
+            fwd = cad.stack_span_forward_allowed if self.stacked else cad.span_forward_allowed
+            fwd(self.layer, self.cache, tok, n, self.allowed[f:f + 1, :A], A, flags=self._flags(pf),
+                argmax_out=out, workspace=self.workspace, stream=stream)
 
     def fed_tokens(self, doc: np.ndarray) -> np.ndarray:
         """The program's input stream in cache order (reads the decisions back: synchronises)."""

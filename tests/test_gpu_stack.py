@@ -270,3 +270,49 @@ def test_tiny_fp32_stack_matches_oracle():
     for l in range(nl):
         k_ = sc.caches[l].k[0, :, :L0 + N].cpu().numpy().astype(np.float64)
         assert np.abs(k_ - ocs[l].K[:, :L0 + N]).max() <= 1e-4
+
+
+def test_small_stack_cad_program_matches_oracle():
+    """A short Copy-as-Decode program with its op-boundary steps through a 3-layer stack (the
+    vocabulary holds the grammar's token ids): every decision against the oracle's stack, and
+    every layer's cache at the end."""
+    from spec_verify_cad_amd.program import DeviceProgram
+    shp = synth.LayerShape(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=704, vocab=15013)
+    nl = 3
+    ws = _stack_weights(shp, 700, nl)
+    dst = cad.DeviceStack([cad.DeviceLayer(shp, w) for w in ws])
+    ols = [oracle_layer(shp, w, only=list(w)) for w in ws]
+    doc = synth.uniform_tokens(710, 300, shp.vocab)
+    ops = [("copy", 10, 25), ("gen", 3), ("copy", 150, 40), ("gen", 2), ("copy", 0, 7)]
+    fwds = synth.cad_program_forwards(ops)
+    fed = sum(f.n for f in fwds)
+    cap = ((len(doc) + fed + 8 + 3) // 4) * 4
+    sc = cad.StackCache(shp, nl, 1, cap)
+    _prefill(dst, sc, doc[None], chunk=128)
+    prog = DeviceProgram(dst, sc, doc, fwds)
+    log(f"stack program: {len(fwds)} forwards, {fed} fed tokens")
+    prog.enqueue()
+    torch.cuda.synchronize()
+    assert int(sc.len[0]) == len(doc) + fed
+    dec = prog.decisions.cpu().numpy()
+    stream = prog.fed_tokens(doc)
+    ocs = O.stack_prefill(ols, doc, cap, chunk=128)
+    tol = logit_tol(shp.hidden) * math.sqrt(nl)
+    pos, firm = 0, 0
+    for f, pf in enumerate(fwds):
+        ref = O.stack_span_forward(ols, ocs, stream[pos:pos + pf.n])
+        last = {k: ref[k][-1:] for k in ("logits", "argmax", "top2_gap")}
+        if pf.allowed is None:
+            argmax_check(dec[f:f + 1], last, None, f"forward {f} ({pf.role})", tol)
+        else:
+            assert int(dec[f]) in pf.allowed
+            best, _, gap = O.masked_argmax(last["logits"], np.asarray([pf.allowed]), shp.vocab)
+            if gap[0] > 2 * tol:
+                firm += 1
+                assert dec[f] == best[0], f"forward {f} ({pf.role}): {dec[f]} vs {best[0]}"
+        pos += pf.n
+    log(f"stack program: {firm} masked decisions firm")
+    for l in range(nl):
+        k_ = to_f64(sc.caches[l].k[0, :, :len(doc) + fed], "bf16")
+        d = np.abs(k_ - ocs[l].K[:, :len(doc) + fed])
+        assert (d <= hidden_tol(ocs[l].K[:, :len(doc) + fed]) * math.sqrt(l + 1)).all(), f"layer {l}"
