@@ -263,6 +263,14 @@ int cad_stack_span_forward_allowed(const cad_layer_desc *layers, int n_layers, c
                                    const int32_t *allowed, int A, int32_t *argmax_out, float *logits_out,
                                    void *hidden_out, void *workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+/* The sampled forward (as cad_span_forward_sampled: stochastic verification of the drafts in
+ * tokens[:, 1:], or plain draws) through a stack of layers, with the layers, caches and lengths
+ * of cad_stack_span_forward; the draws are keyed by (seed, sequence, position) as there. */
+int cad_stack_span_forward_sampled(const cad_layer_desc *layers, int n_layers, const cad_kv_desc *kvs,
+                                   const int32_t *tokens, int B, int Nq, int flags, float temperature,
+                                   uint64_t seed, const int32_t *draft_len, int32_t *pred_out,
+                                   float *logits_out, void *hidden_out, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 /* Workspace of cad_stack_span_forward (0 for an invalid shape); the buffers are reused by every
  * layer, so this is the one-layer size (the full one when n_layers > 1, even with CAD_KV_ONLY). */
 size_t cad_stack_span_forward_workspace(const cad_layer_desc *layers, int n_layers, int B, int Nq, int mode,

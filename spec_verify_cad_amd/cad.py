@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.cad_stack_span_forward_allowed.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(KVDesc), vp, i32, i32,
                                                  i32, vp, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.cad_stack_span_forward_allowed.restype = i32
+    L.cad_stack_span_forward_sampled.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(KVDesc), vp, i32, i32,
+                                                 i32, ctypes.c_float, ctypes.c_uint64, vp, vp, vp, vp, vp,
+                                                 ctypes.c_size_t, vp]
+    L.cad_stack_span_forward_sampled.restype = i32
     L.cad_stack_span_forward_workspace.argtypes = [ctypes.POINTER(LayerDesc), i32, i32, i32, i32, i32, i32, i32, i32]
     L.cad_stack_span_forward_workspace.restype = ctypes.c_size_t
     L.cad_span_forward_sampled.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(KVDesc), vp, i32, i32, i32,
@@ -274,6 +278,21 @@ def stack_span_forward_allowed(stack: DeviceStack, cache: StackCache, tokens, Nq
                                                 _ptr(allowed), A, _ptr(argmax_out), _ptr(logits_out),
                                                 _ptr(hidden_out), _ptr(workspace), workspace.numel(),
                                                 _stream(stream)), "cad_stack_span_forward_allowed")
+    return workspace
+
+
+def stack_span_forward_sampled(stack: DeviceStack, cache: StackCache, tokens, Nq: int, temperature: float, seed: int,
+                               draft_len=None, flags: int = 0, pred_out=None, logits_out=None, hidden_out=None,
+                               workspace=None, stream=None):
+    if cache.n != stack.n:
+        raise ValueError("one cache per layer")
+    B = cache.B
+    if workspace is None:
+        workspace = alloc_workspace(stack_span_forward_workspace(stack, B, Nq, MASK_CAUSAL, 1, 1, cache.cap, flags))
+    _check(lib().cad_stack_span_forward_sampled(stack.descs, stack.n, cache.descs, _ptr(tokens), B, Nq, flags,
+                                                float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(draft_len),
+                                                _ptr(pred_out), _ptr(logits_out), _ptr(hidden_out), _ptr(workspace),
+                                                workspace.numel(), _stream(stream)), "cad_stack_span_forward_sampled")
     return workspace
 
 

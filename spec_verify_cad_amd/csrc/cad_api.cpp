@@ -460,6 +460,17 @@ int cad_stack_span_forward_allowed(const cad_layer_desc* layers, int n_layers, c
                              hidden_out, logits_out, allowed, A, nullptr, workspace, workspace_bytes, stream);
 }
 
+int cad_stack_span_forward_sampled(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs,
+                                   const int32_t* tokens, int B, int Nq, int flags, float temperature, uint64_t seed,
+                                   const int32_t* draft_len, int32_t* pred_out, float* logits_out, void* hidden_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (n_layers < 1 || n_layers > CAD_MAX_LAYERS || !pred_out) return CAD_EINVAL;
+    if (flags & ~(CAD_COMMIT_ALL | CAD_LOGITS_LAST)) return CAD_EINVAL;
+    const SampleArgs sa{temperature, seed, draft_len};
+    return span_forward_impl(layers, n_layers, kvs, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, pred_out,
+                             hidden_out, logits_out, nullptr, 0, &sa, workspace, workspace_bytes, stream);
+}
+
 int cad_stack_span_forward(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs, const int32_t* tokens,
                            int B, int Nq, int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out,
                            float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {

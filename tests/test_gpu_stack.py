@@ -316,3 +316,43 @@ def test_small_stack_cad_program_matches_oracle():
         k_ = to_f64(sc.caches[l].k[0, :, :len(doc) + fed], "bf16")
         d = np.abs(k_ - ocs[l].K[:, :len(doc) + fed])
         assert (d <= hidden_tol(ocs[l].K[:, :len(doc) + fed]) * math.sqrt(l + 1)).all(), f"layer {l}"
+
+
+def test_small_stack_sampled_verify_matches_oracle(small_stack):
+    """Stochastic verification through the 4-layer small stack: a greedy-chain draft at a small
+    temperature (drafts kept) and a random draft, against the oracle's stack and draws."""
+    ws, dst, ols = small_stack
+    B, L0, cap, k, T, seed = 2, 70, 128, 6, 0.05, 4242
+    Nq = k + 1
+    ctx = np.stack([synth.uniform_tokens(720 + b, L0, SMALL.vocab) for b in range(B)])
+    g = [int(x) for x in synth.uniform_tokens(730, B, SMALL.vocab)]
+    chain, c = [], O.stack_prefill(ols, ctx[0], cap)
+    t = g[0]
+    for _ in range(k):
+        t = int(O.stack_decode_one(ols, c, t)["argmax"][0])
+        chain.append(t)
+    toks = np.array([[g[0]] + chain, [g[1]] + list(synth.uniform_tokens(731, k, SMALL.vocab))], dtype=np.int32)
+    dls = [k, 4]
+    sc = cad.StackCache(SMALL, NL, B, cap)
+    _prefill(dst, sc, ctx)
+    pred = torch.full((B * Nq,), -7, dtype=torch.int32, device="cuda")
+    lg = torch.zeros((B * Nq, SMALL.vocab), dtype=torch.float32, device="cuda")
+    T32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    cad.stack_span_forward_sampled(dst, sc, T32(toks), Nq, T, seed, draft_len=T32(dls), pred_out=pred, logits_out=lg)
+    torch.cuda.synchronize()
+    g_pred, g_l = pred.cpu().numpy(), lg.cpu().numpy().astype(np.float64)
+    kept = 0
+    for b in range(B):
+        ref = O.stack_span_forward(ols, O.stack_prefill(ols, ctx[b], cap), toks[b], commit=False)
+        rows = slice(b * Nq, (b + 1) * Nq)
+        opred = O.sampled_predictions(ref["logits"], toks[b], dls[b], T, seed, b, L0)[0]
+        y_gap, z_gap, acc_m = O.sampled_margins(ref["logits"], toks[b], dls[b], T, seed, b, L0)
+        e = np.max(np.abs(g_l[rows] - ref["logits"]), axis=1)
+        for i in range(Nq):
+            m = 2 * e[i] / T + 1e-6
+            firm = (acc_m[i] > math.expm1(m) and (opred[i] == toks[b, i + 1] or z_gap[i] > m)) if i < dls[b] \
+                else y_gap[i] > m
+            if firm:
+                assert g_pred[rows][i] == opred[i], (b, i, g_pred[rows][i], opred[i])
+        kept += sum(1 for i in range(dls[b]) if opred[i] == toks[b, i + 1])
+    assert kept >= 1
