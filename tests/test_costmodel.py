@@ -72,3 +72,12 @@ def test_interpolation_and_reductions():
     # Eq. (2) without splices or fixed costs is full regeneration
     assert C.cad_latency(20.0, 300, [], cur, 0, 1.0) == 6000.0
     assert C.cad_latency(20.0, 0, [8], cur, 1, 1.0) == pytest.approx(20.0 * 8 / cur[8] + 1.0)
+
+
+def test_policy_edge_cases():
+    flat = {1: 1.0, 2: 1.0, 4: 1.2, 8: 1.4}
+    assert C.m_star(flat, 1.0, 0.0) == 4                        # s(2) = 1 is no gain
+    assert C.m_safe(flat) is None                               # never above 1.5
+    assert C.m_star(flat, 1.0, 100.0) is None                   # a fixed cost no span clears
+    b = C.bounds([], 100, flat)                                 # no copies: full regeneration
+    assert b["bnd_exact"] == 1.0 and b["bnd_mean"] == 1.0 and b["K"] == 0

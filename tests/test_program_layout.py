@@ -84,3 +84,21 @@ def test_device_program_buffers_on_the_host():
     gb = [f for f, x in enumerate(fwds) if x.role == "gen_body"]
     pos = [sum(x.n for x in fwds[:f]) for f in gb]
     assert [int(s[p]) for p in pos] == [7000 + f - 1 for f in gb]
+
+
+def test_device_program_rejects_bad_layouts():
+    import pytest
+    shp = QWEN7
+    tens = {n: torch.zeros(1, dtype=torch.int16) for n in synth.weight_shapes(shp)}
+    lay = cad.DeviceLayer.from_tensors(shp, tens)
+    doc = np.arange(10, dtype=np.int32)
+    with pytest.raises(ValueError):                       # batch of two
+        DeviceProgram(lay, cad.DeviceCache(shp, 2, 64, device="cpu"), doc, [], device="cpu")
+    c1 = cad.DeviceCache(shp, 1, 64, device="cpu")
+    with pytest.raises(ValueError):                       # nothing before the first fed-back token
+        DeviceProgram(lay, c1, doc, [synth.ProgramForward("gen_body", from_prev=True)], device="cpu")
+    with pytest.raises(ValueError):                       # more allowed ids than the kernel takes
+        DeviceProgram(lay, c1, doc, [synth.ProgramForward("x", (1,), allowed=tuple(range(cad.MAX_ALLOWED + 1)))],
+                      device="cpu")
+    with pytest.raises(ValueError):                       # a stack needs a stack cache
+        DeviceProgram(cad.DeviceStack([lay, lay]), c1, doc, [], device="cpu")
