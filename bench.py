@@ -346,12 +346,19 @@ def cad_program(a, dev):
     run(stream)
     torch.cuda.synchronize()
     assert int(cache.len[0]) == Ld + fed
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    run(stream)
-    e1.record(stream)
+    # eager, one event after every forward: the time of each forward role
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(fwds) + 1)]
+    cache.len.fill_(Ld)
+    evs[0].record(stream)
+    for f in range(len(fwds)):
+        prog.enqueue_one(f, stream)
+        evs[f + 1].record(stream)
     torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1)
+    eager_ms = evs[0].elapsed_time(evs[-1])
+    by_role = {}
+    for f, pf in enumerate(fwds):
+        by_role[pf.role] = by_role.get(pf.role, 0.0) + evs[f].elapsed_time(evs[f + 1])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     cap_stream = torch.cuda.Stream()
     cap_stream.wait_stream(stream)
     t0 = time.time()
@@ -438,6 +445,42 @@ def cad_program(a, dev):
         e1.record(stream)
         torch.cuda.synchronize()
         per_step[name] = round(e0.elapsed_time(e1) * 1e3 / (4 * 32), 2)
+    # this layer's own s(N) at the document's length, the page's way (one parallel forward of N
+    # against N one-token forwards), for the splice forwards as the program runs them (the
+    # decision after the last row masked), and Eq. (2)'s terms from it against the measured roles
+    from spec_verify_cad_amd import costmodel as C
+    spans_n = [n for n in STACK_SPANS if n >= 2] + [514]
+    toks = torch.randint(0, shp.vocab, (1, max(spans_n)), generator=gen, device=dev, dtype=torch.int32)
+    wsc = cad.alloc_workspace(max(cad.span_forward_workspace(lay, 1, n, cad.MASK_CAUSAL, 1, 1, cap,
+                                                             cad.COMMIT_ALL | cad.LOGITS_LAST) for n in spans_n))
+    pp = {}
+    for n in spans_n:
+        def body(st, n=n):
+            cache.len.fill_(Ld)
+            cad.span_forward_allowed(lay, cache, toks[:, :n], n, al2, 2, flags=cad.COMMIT_ALL | cad.LOGITS_LAST,
+                                     argmax_out=o1, workspace=wsc, stream=st)
+        body(stream)
+        torch.cuda.synchronize()
+        gk = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gk, stream=cap_stream):
+            body(torch.cuda.current_stream())
+        gk.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(4):
+            gk.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pp[n] = e0.elapsed_time(e1) / 4
+        del gk
+    tau = per_step["free_step"] / 1e3
+    splice_curve = {n: n * tau / pp[n] for n in spans_n}
+    spans = [o[2] for o in ops if o[0] == "copy"]
+    T_gen = sum(o[1] for o in ops if o[0] == "gen")
+    eq2 = {"gen_decode": round(tau * T_gen, 2),
+           "copy_splices": round(sum((n + 2) * tau / C.interp_s(splice_curve, n + 2) for n in spans), 2)}
+    measured = {"gen_body": round(by_role.get("gen_body", 0.0), 2), "splices": round(by_role.get("splice", 0.0), 2),
+                "fixed_per_op": round(eager_ms - by_role.get("gen_body", 0.0) - by_role.get("splice", 0.0), 2)}
     roles = {}
     for f in fwds:
         roles[f.role] = roles.get(f.role, 0) + 1
@@ -450,7 +493,11 @@ def cad_program(a, dev):
            "masked_forwards": sum(1 for f in fwds if f.allowed is not None),
            "per_step_us": per_step,
            "c_mask_us": round(per_step["masked_step"] - per_step["free_step"], 2),
-           "host_syncs_per_op": 0}
+           "host_syncs_per_op": 0,
+           "ms_by_role": {k: round(v, 2) for k, v in by_role.items()},
+           "splice_s_curve": {n: round(v, 2) for n, v in splice_curve.items()},
+           "ar_ms_eq1": round(tau * T, 2), "eq2_terms_ms": eq2, "measured_ms": measured,
+           "realized_speedup_eq1": round(tau * T / ms, 3)}
     log(f"cad program: {ms:.1f} ms (eager {eager_ms:.1f}), AR {ar_ms:.1f} ms -> {ar_ms / ms:.2f}x; "
         f"steps {per_step}")
     del g
