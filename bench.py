@@ -46,12 +46,13 @@ def parse():
     ap.add_argument("--no-pld", action="store_true", help="skip the batched PLD round measurement")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the full-depth (28-layer) span-forward curve on the 1.5B and 7B shapes")
+    ap.add_argument("--no-block", action="store_true", help="skip the block-triangular verify measurement")
     ap.add_argument("--no-program", action="store_true",
                     help="skip the Copy-as-Decode program measurement (op-boundary steps, 7B-shaped layer)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="no timing: a few N = ROOF_N forwards and plain copies of a known size, for a "
                          "hardware-counter run that calibrates and measures the LM head's HBM traffic")
-    ap.add_argument("--part", choices=("program", "stack", "pld"), default=None,
+    ap.add_argument("--part", choices=("program", "stack", "pld", "block"), default=None,
                     help="run one secondary workload alone and print its JSON object (for a profiler run); "
                          "no headline line")
     return ap.parse_args()
@@ -73,12 +74,14 @@ def main():
     from spec_verify_cad_amd import roofline as R
     from spec_verify_cad_amd.configs import CONFIGS, copy_sweep_inputs
 
-    if a.part in ("program", "stack"):
+    if a.part in ("program", "stack", "block"):
         dev = torch.device("cuda:0")
         torch.cuda.set_device(dev)
         cad.lib()
         if a.part == "program":
             out = cad_program(a, dev)
+        elif a.part == "block":
+            out = block_verify(a, dev)
         else:
             out = [stack_curve(a, dev, "qwen15_span"), stack_curve(a, dev, "qwen7_cad_program", program=True)]
             stack_cost_model(out)
@@ -254,6 +257,9 @@ def main():
     if stack:
         stack_cost_model(stack)
 
+    # ---- block-triangular multi-candidate verify (7B-shaped layer)
+    block = None if a.no_block else block_verify(a, dev)
+
     # ---- a whole Copy-as-Decode program with its op-boundary steps (7B-shaped layer)
     program = None if a.no_program else cad_program(a, dev)
 
@@ -296,6 +302,7 @@ def main():
         "roofline": roof,
         "copy_commit_mode": copy_commit,
         "pld_rounds": pld,
+        "block_verify": block,
         "cad_program": program,
         "full_depth_stacks": stack,
         "cpu_baseline": cpu,
@@ -696,6 +703,93 @@ def stack_program(st, dev, rows):
                            "splices": round(by_role.get("splice", 0.0), 2)}}
     log(f"full-depth cad program: {res}")
     del sc, prog
+    return res
+
+
+def block_verify(a, dev):
+    """The block-triangular multi-candidate verify on the 7B-shaped layer (random weights drawn on
+    the device): a 4096-token context with planted repeats, the kappa = 5 lookup of W = 4
+    recency-ranked candidates of D = 8 tokens, one 32-row block-triangular verify forward and the
+    block accept scan (longest validated candidate, K/V compaction), replayed from a HIP graph.
+    Reported per verify, and the forward alone against its HBM floor."""
+    import numpy as np
+    import torch
+
+    from spec_verify_cad_amd import cad, synth
+    from spec_verify_cad_amd import roofline as R
+    from spec_verify_cad_amd.configs import CONFIGS, block_verify_context
+
+    wl = CONFIGS["qwen7_block_verify"]
+    shp, e = wl.shape, wl.extra
+    W, D, n = e["W"], e["D"], e["kappa"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    t = {}
+    for name, sh in synth.weight_shapes(shp).items():
+        t[name] = (torch.randn(sh, generator=gen, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+    lay = cad.DeviceLayer.from_tensors(shp, t)
+    ctx = block_verify_context(wl)
+    Lc = len(ctx)
+    cap = ((Lc + W * D + 32 + 3) // 4) * 4
+    cache = cad.DeviceCache(shp, 1, cap)
+    ct = torch.from_numpy(ctx[None].astype(np.int32)).to(dev)
+    cad.span_forward(lay, cache, ct[:, :Lc - 1], Lc - 1, flags=cad.KV_ONLY | cad.COMMIT_ALL)
+    anchor = torch.zeros(1, dtype=torch.int32, device=dev)
+    cad.span_forward(lay, cache, ct[:, Lc - 1:], 1, flags=cad.COMMIT_ALL, argmax_out=anchor)
+    torch.cuda.synchronize()
+    assert int(cache.len[0]) == Lc
+    hlen = torch.tensor([Lc], dtype=torch.int32, device=dev)
+    draft = torch.zeros((1, W * D), dtype=torch.int32, device=dev)
+    dlen = torch.zeros((1, W), dtype=torch.int32, device=dev)
+    pred = torch.zeros(W * D, dtype=torch.int32, device=dev)
+    acc, bw, ne = (torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(3))
+    em = torch.zeros((1, D + 1), dtype=torch.int32, device=dev)
+    ws = cad.alloc_workspace(cad.span_forward_workspace(lay, 1, W * D, cad.MASK_BLOCK, W, D, cap, 0), device=dev)
+
+    def forward(st):
+        cad.span_forward(lay, cache, draft, W * D, cad.MASK_BLOCK, W, D, 0, argmax_out=pred, workspace=ws, stream=st)
+
+    def verify(st):
+        cache.len.fill_(Lc)
+        cad.ngram_lookup(ct, hlen, n, W, D, 0, draft, dlen, stream=st)
+        forward(st)
+        cad.accept_scan(draft, 0, dlen, pred, anchor, 1, W, D, cad.MASK_BLOCK, acc, bw, em, ne, cache=cache,
+                        stream=st)
+
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    out = {}
+    for name, fn in (("verify", verify), ("forward", forward)):
+        fn(stream)
+        torch.cuda.synchronize()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(8):
+                fn(torch.cuda.current_stream())
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1e3 / 40
+        del g
+    assert int((dlen > 0).sum()) == W
+    nb = R.forward_bytes(shp, 1, W * D, Lc)
+    floor, bound = R.floor_us(nb, R.forward_flops(shp, 1, W * D, Lc))
+    res = {"workload": f"block-triangular verify, 7B-shaped layer: {Lc}-token context with planted repeats, "
+                       f"kappa = {n} lookup of W = {W} candidates x D = {D}, one {W * D}-row verify forward and "
+                       f"the block accept (K/V compaction), graph-replayed",
+           "us_per_verify": round(out["verify"], 2), "forward_us": round(out["forward"], 2),
+           "verified_positions_per_s": round(W * D / (out["verify"] * 1e-6), 1),
+           "committed_per_verify": int(ne.item()), "alg_bytes": int(nb), "bound": bound,
+           "floor_us": round(floor, 2), "forward_frac_of_roofline": round(floor / out["forward"], 4)}
+    log(f"block verify: {res}")
+    del cache, lay, t
+    torch.cuda.empty_cache()
     return res
 
 
