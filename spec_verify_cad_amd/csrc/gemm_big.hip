@@ -17,11 +17,30 @@
 //   PARTIAL fp32 partial sums of one K slice, 16 bytes per lane store.
 // Workgroups are dealt to XCDs round-robin; the unit order gives each XCD a contiguous run, and
 // consecutive units are the row tiles (then K slices) of one column tile, so they share its W in L2.
+//
+// Balanced LM head (BAL): the vocabulary is cut into one contiguous range of 16-row blocks per
+// CU instead of BN-row column tiles (594 tiles of 256 rows on 256 CUs would run 3 rounds with
+// the last one 30 % full).  A workgroup walks its range in chunks of BN rows with the load
+// pipeline running on across chunk boundaries; a wave whose rows of a chunk all lie past the
+// range end skips its multiplies (the waves of one feature half sit on different SIMDs, so the
+// short last chunk costs about half a chunk).  Each chunk leaves one (max, index) slot per row.
+#include <algorithm>
+
 #include "cad_device.h"
 
 namespace {
 
 constexpr int BK64 = 64;
+constexpr int BAL_MAX_CHUNKS = 4;
+// register stages of the balanced LM head: 3 for 64-token tiles, 2 for 128 (measured; the
+// column-tile schedule uses 2 and 1)
+constexpr int BAL_RS64 = 3, BAL_RS128 = 2;
+
+// chunks of BN rows in the longest of G balanced ranges over N rows (ranges are whole 16-row blocks)
+__host__ __device__ inline int bal_chunks(int N, int G, int BN) {
+    const int NB = (N + 15) / 16, per = (NB + G - 1) / G;
+    return (per * 16 + BN - 1) / BN;
+}
 
 template <int KIND, int BN, int BM, int WN, int WM, int BK>
 struct BigCfg {
@@ -103,7 +122,8 @@ __device__ __forceinline__ void qkv_epilogue(const f32x4_t (&acc)[FT][TT], const
     }
 }
 
-template <int KIND, int BN, int BM, int WN, int WM, int BK, int RS>
+// BAL: 0 = column tiles, 1 = balanced ranges, 2 = balanced ranges that also write the logits
+template <int KIND, int BN, int BM, int WN, int WM, int BK, int RS, int BAL>
 __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                      int M, int N, int K, int nmt, int nnt, int S, int ffn,
                                                      EpiParams p) {
@@ -121,7 +141,9 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
     const int kbeg = ks * p.k_slice, kend = min(K, kbeg + p.k_slice);
     const int nk = (kend - kbeg + BK - 1) / BK;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave % WN, wm = wave / WN;
+    // (balanced ranges: the waves of one wn sit on different SIMDs, so a chunk whose second half
+    // is past the range end still keeps every SIMD busy)
+    const int wn = BAL ? wave / WM : wave % WN, wm = BAL ? wave % WM : wave / WN;
     const int l16 = lane & 15, g4 = lane >> 4;
 
     // per-thread global sources as 32-bit element offsets (row base + chunk offset); invalid rows
@@ -227,10 +249,121 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
     // next; loads are issued unconditionally (a stage past the slice reads valid addresses and
     // is masked to zero), because a load inside a branch makes the compiler's wait counts at the
     // join conservative and drains the pipeline before every LDS write.
+
+    constexpr int UNR = RS % 2 ? 2 * RS : RS;
+    if constexpr (BAL) {
+        // range nt of nnt: vocabulary rows [r0, r1), chunk c = rows r0 + c*BN + (0..BN-1)
+        static_assert(KIND == EPI_ARGMAX, "balanced ranges are an LM-head schedule");
+        __shared__ float2 bred[BAL_MAX_CHUNKS][WN][BM];
+        const int NB = (N + 15) >> 4;
+        const int r0 = (int)((long long)nt * NB / nnt) * 16;
+        const int r1 = min(N, (int)((long long)(nt + 1) * NB / nnt) * 16);
+        const int nch = (r1 - r0 + BN - 1) / BN;
+        const int cpw = bal_chunks(N, nnt, BN);
+        const int T = nch * nk;
+        const int wn_s = __builtin_amdgcn_readfirstlane(wn);               // wave-uniform: scalar branches
+        // W chunk c of this thread: tile row tid / (BK/8) + c * NT / (BK/8), column kchunk
+        static_assert(NT % (BK / 8) == 0, "every W chunk of a thread has the same column");
+        const int wtr0 = tid / (BK / 8);
+        // global step t = chunk t / nk, K step t % nk; steps past the last chunk read valid
+        // addresses and are masked like rows past the range end
+        auto load_bal = [&](int t, Stage& r) {
+            const int cc = t / nk;
+            const int k0 = kbeg + (t - cc * nk) * BK;
+            const int rb = r0 + cc * BN;
+            const bool kin = k0 + kchunk < kend;
+            const int row0 = rb + wtr0;
+            uint32_t wok = 0;
+#pragma unroll
+            for (int c = 0; c < WCH; ++c) wok |= (uint32_t)(kin && row0 + c * (NT / (BK / 8)) < r1) << c;
+            r.wok = wok;
+            r.aok = kin ? amask : 0u;
+#pragma unroll
+            for (int c = 0; c < WCH; ++c) {
+                const bool ok = (wok >> c) & 1;
+                const uint32_t off = (uint32_t)(row0 + c * (NT / (BK / 8))) * (uint32_t)K + (uint32_t)k0;
+                r.w[c] = *(const uint4*)(W + (ok ? off : 0u) + kchunk);
+                if constexpr (RS > 1) __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int c = 0; c < ACH; ++c) {
+                r.a[c] = *(const uint4*)(A + aoff[c] + (((r.aok >> c) & 1) ? k0 : 0));
+                if constexpr (RS > 1) __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // per-chunk (max, lowest index) of each token over this wave's rows, into LDS only (no
+        // global store inside the K loop but the debug logits, which have an instantiation of
+        // their own)
+        auto chunk_argmax = [&](int cc) {
+            const int rb = r0 + cc * BN;
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const int tok = m0 + wm * C::WTM + tt * 16 + l16;
+                float best = -INFINITY;
+                int bi = 0x7fffffff;
+                if (tok < M) {
+#pragma unroll
+                    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int n = rb + wn * C::WTN + ft * 16 + g4 * 4 + i;   // increasing along the lane
+                            if (n < r1) {
+                                const float v = acc[ft][tt][i];
+                                if (v > best) { best = v; bi = n; }
+                                if constexpr (BAL == 2) p.logits[(size_t)tok * N + n] = v;
+                            }
+                        }
+                }
+#pragma unroll
+                for (int o = 16; o <= 32; o <<= 1) {
+                    const float v2 = __shfl_xor(best, o, 64);
+                    const int i2 = __shfl_xor(bi, o, 64);
+                    argmax_merge(best, bi, v2, i2);
+                }
+                if (g4 == 0) bred[cc][wn][wm * C::WTM + tt * 16 + l16] = make_float2(best, __int_as_float(bi));
+            }
+        };
+        Stage r[RS];
+#pragma unroll
+        for (int i = 0; i < RS; ++i) load_bal(i, r[i]);
+        for (int t0 = 0; t0 < T; t0 += UNR) {
+#pragma unroll
+            for (int j = 0; j < UNR; ++j) {
+                const int t = t0 + j;
+                if (t >= T) break;
+                store_lds(j & 1, r[j % RS]);
+                load_bal(t + RS, r[j % RS]);
+                __syncthreads();
+                const int cc = t / nk;
+                // a wave whose rows all lie past the range end skips the multiply
+                if (wn_s * C::WTN < r1 - (r0 + cc * BN)) compute(j & 1);
+                if (t - cc * nk == nk - 1) {
+                    chunk_argmax(cc);
+#pragma unroll
+                    for (int a = 0; a < FT; ++a)
+#pragma unroll
+                        for (int b = 0; b < TT; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+        __syncthreads();
+        // one slot per chunk of every range (cpw per range), empty slots for chunks past its end
+        for (int cc = 0; cc < cpw; ++cc)
+            for (int rr = tid; rr < BM; rr += NT) {
+                const int tok = m0 + rr;
+                if (tok >= M || !seq_ok(p.len_snap, tok / p.Nq, p.Nq, p.cap)) continue;
+                float best = -INFINITY;
+                int bi = 0x7fffffff;
+                if (cc < nch)
+#pragma unroll
+                    for (int w = 0; w < WN; ++w) argmax_merge(best, bi, bred[cc][w][rr].x, __float_as_int(bred[cc][w][rr].y));
+                p.amax_part[(size_t)tok * p.amax_slots + nt * cpw + cc] = make_float2(best, __int_as_float(bi));
+            }
+        return;
+    }
     Stage r[RS];
 #pragma unroll
     for (int i = 0; i < RS; ++i) load_g(kbeg + i * BK, r[i]);
-    constexpr int UNR = RS % 2 ? 2 * RS : RS;
     for (int kt0 = 0; kt0 < nk; kt0 += UNR) {
 #pragma unroll
         for (int j = 0; j < UNR; ++j) {
@@ -363,12 +496,12 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
     }
 }
 
-struct BigPlan { int BN, BM, nmt, nnt, S, k_slice, grid; };
+struct BigPlan { int BN, BM, nmt, nnt, S, k_slice, grid; bool bal; };
 
-template <int KIND, int BN, int BM, int WN, int WM, int BK, int RS>
+template <int KIND, int BN, int BM, int WN, int WM, int BK, int RS, int BAL = 0>
 hipError_t go_big(const void* A, const void* W, int M, int N, int K, int ffn, const BigPlan& t, const EpiParams& p,
                   hipStream_t s) {
-    auto kern = k_gemm_big<KIND, BN, BM, WN, WM, BK, RS>;
+    auto kern = k_gemm_big<KIND, BN, BM, WN, WM, BK, RS, BAL>;
     constexpr size_t smem = BigCfg<KIND, BN, BM, WN, WM, BK>::SMEM;
     static bool attr = false;
     if (!attr) {
@@ -406,17 +539,33 @@ BigPlan big_plan(int kind, int M, int N, int K, int slices) {
     t.nnt = kind == EPI_SWIGLU ? (N / 2 + t.BN / 2 - 1) / (t.BN / 2) : (N + t.BN - 1) / t.BN;
     t.S = kind == EPI_PARTIAL ? slices : 1;
     t.k_slice = ((K + t.S - 1) / t.S + BK64 - 1) / BK64 * BK64;
+    // (only while the LM head is bound by the weight stream: at 256 rows and more the column
+    // tiles' rounds measured faster than balanced ranges)
+    t.bal = kind == EPI_ARGMAX && t.BM <= 128;
+    if (t.bal) {
+        // one range per CU, at least 24 blocks per range (small vocabularies) and at most
+        // BAL_MAX_CHUNKS chunks per range
+        const int NB = (N + 15) / 16, bpc = t.BN / 16;
+        int G = std::min(device_cu_count(), (NB + 23) / 24);
+        G = std::max(G, (NB + BAL_MAX_CHUNKS * bpc - 1) / (BAL_MAX_CHUNKS * bpc));
+        t.nnt = std::max(G, 1);
+    }
     const int total = t.nmt * t.nnt * t.S;
     t.grid = (total + 7) / 8 * 8;
     return t;
 }
 
-int big_slots(int kind, int M, int N, int K) { return big_plan(kind, M, N, K, 1).nnt; }
+int big_slots(int kind, int M, int N, int K) {
+    const BigPlan t = big_plan(kind, M, N, K, 1);
+    return t.bal ? t.nnt * bal_chunks(N, t.nnt, t.BN) : t.nnt;
+}
 
 int big_partial_slices(int M, int N, int K, int cus) {
     const BigPlan t = big_plan(EPI_PARTIAL, M, N, K, 1);
     const int tiles = t.nmt * t.nnt;
-    int S = (cus + tiles - 1) / tiles;                       // about one workgroup per CU
+    // as many slices as two resident workgroups per CU take in one round (the 128 x 64 partial
+    // tile runs two per CU): at 512 rows the down projection took 44 us with one per CU, 33 with two
+    int S = 2 * cus / tiles;
     const int smax = K / 256 > 1 ? K / 256 : 1;              // at least 256 of K per slice
     return S < 1 ? 1 : (S > smax ? smax : S);
 }
@@ -427,6 +576,14 @@ hipError_t big_dispatch(const void* A, const void* W, int M, int N, int K, int s
     p.k_slice = t.k_slice;
     const int ffn = KIND == EPI_SWIGLU ? p.ffn : 0;
     if (t.BN == 128) return go_big<KIND, 128, 64, 1, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
+    if constexpr (KIND == EPI_ARGMAX) {
+        if (t.bal && t.BM == 64)
+            return p.logits ? go_big<KIND, 256, 64, 2, 4, 64, BAL_RS64, 2>(A, W, M, N, K, ffn, t, p, s)
+                            : go_big<KIND, 256, 64, 2, 4, 64, BAL_RS64, 1>(A, W, M, N, K, ffn, t, p, s);
+        if (t.bal)
+            return p.logits ? go_big<KIND, 256, 128, 2, 4, 64, BAL_RS128, 2>(A, W, M, N, K, ffn, t, p, s)
+                            : go_big<KIND, 256, 128, 2, 4, 64, BAL_RS128, 1>(A, W, M, N, K, ffn, t, p, s);
+    }
     switch (t.BM) {
         case 64: return go_big<KIND, 256, 64, 2, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
         case 128: return go_big<KIND, 256, 128, 2, 4, 64, 1>(A, W, M, N, K, ffn, t, p, s);
