@@ -520,15 +520,18 @@ hipError_t go_big(const void* A, const void* W, int M, int N, int K, int ffn, co
 // Tile choice: 256 features per workgroup tile (two waves of 128 across it); 64, 128 or 256
 // tokens.  The narrow QKV projection and the K-slice partial projections take 128 x 64 tiles
 // (one wave of 128 features, so a QKV wave holds whole heads of up to 128 dims) to spread over
-// more workgroups; so does the gate/up projection up to 256 rows (measured on the 1.5B shape:
-// 256 x 64 tiles are best up to 128 rows, 128 x 64 up to 256, 256 x 256 beyond).
+// more workgroups (measured on the 1.5B shape for gate/up: 256 x 64 tiles are best up to 128
+// rows, 256 x 128 up to 256, 256 x 256 beyond).
 BigPlan big_plan(int kind, int M, int N, int K, int slices) {
     BigPlan t;
     t.BN = 256;
     t.BM = M <= 64 ? 64 : M <= 128 ? 128 : 256;
-    if (kind == EPI_SWIGLU && M <= 128) t.BM = 64;     // more workgroups for the gate/up pairs
+    // gate/up: 256 x 64 tiles up to 128 rows (more workgroups), 256 x 128 up to 256 rows (at
+    // 256 rows one round of 140 workgroups took 35 us, 560 128 x 64 tiles in two rounds 44 us)
+    if (kind == EPI_SWIGLU && M <= 128) t.BM = 64;
+    if (kind == EPI_SWIGLU && M > 128 && M <= 256) t.BM = 128;
     if (kind == EPI_SAMPLE && t.BM > 128) t.BM = 128;  // the sampling state of 256 rows spills
-    if (kind == EPI_QKV || kind == EPI_PARTIAL || (kind == EPI_SWIGLU && M > 128 && M <= 256)) {
+    if (kind == EPI_QKV || kind == EPI_PARTIAL) {
         // narrow outputs: 128 x 64 tiles give more workgroups (and QKV one head per wave); for the
         // K-slice partials they also mean fewer slices, so less partial traffic for the row
         // kernel that adds them

@@ -247,6 +247,31 @@ def test_small_bf16_span_matches_oracle(small, Nq):
         compare_cache(cache, b, oc, L0, L0 + Nq, "bf16", what=f"span rows b={b}")
 
 
+@pytest.mark.parametrize("B, Nq", [(3, 12), (3, 40), (1, 97)])
+def test_small_bf16_lm_head_without_logits_matches_oracle(small, B, Nq):
+    # 33..128 LM-head rows run on balanced vocabulary ranges (the 5003-id vocabulary makes short
+    # last chunks); the forward without a logits output is its own kernel instantiation, so its
+    # argmax is checked against the oracle and against the forward that writes the logits
+    w, dl, OL = small
+    log(f"small bf16 LM head without logits B={B} Nq={Nq}")
+    L0, cap = 150, 320
+    ctx = np.stack([synth.uniform_tokens(120 + b, L0, SMALL.vocab) for b in range(B)])
+    span = np.stack([synth.uniform_tokens(130 + b, Nq, SMALL.vocab) for b in range(B)])
+    outs = []
+    for logits in (False, True):
+        cache = cad.DeviceCache(SMALL, B, cap)
+        prefill(dl, cache, ctx, chunk=64)
+        outs.append(run_forward(dl, cache, span, flags=cad.COMMIT_ALL, logits=logits))
+        assert list(cache.len.cpu().numpy()) == [L0 + Nq] * B
+    np.testing.assert_array_equal(outs[0]["argmax"], outs[1]["argmax"])
+    np.testing.assert_array_equal(outs[0]["hidden"], outs[1]["hidden"])
+    for b in range(B):
+        oc = O.cache_from_tokens(OL, ctx[b], cap)
+        ref = O.span_forward(OL, oc, span[b])
+        rows = slice(b * Nq, (b + 1) * Nq)
+        argmax_check(outs[0]["argmax"][rows], ref, outs[1]["logits"][rows], what=f"b={b} without logits")
+
+
 @pytest.mark.parametrize("Nq", [1, 13, 40])
 def test_small_bf16_copy_commit_last_row_matches_oracle(small, Nq):
     """Copy-commit mode (CAD_LOGITS_LAST): the LM head and argmax run for each sequence's last
