@@ -63,7 +63,11 @@ __device__ __forceinline__ int swz_k(int r, int c) {
 }
 __device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r >> 1) & 7); }   // 128-byte rows
 
-template <int DH, int MODE, int NWV>
+// NPH key phases: with NPH = 2 the waves form NWV/2 row blocks twice over, and phase p takes
+// keys 32p .. 32p+31 of every tile (its own running maximum and sums); the two phases' states
+// are combined through LDS at the end.  This halves each wave's chain per tile for groups whose
+// rows fill few waves (the PLD verify: 66 rows, five row blocks).
+template <int DH, int MODE, int NWV, int NPH = 1>
 __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                                    const uint16_t* __restrict__ vc, const int32_t* __restrict__ len_snap,
                                                    int Nq, int Hq, int Hkv, int cap, int Dblk,
@@ -73,9 +77,13 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
     constexpr int DB = DH / 16;                 // 16-wide head_dim blocks of the output
     constexpr int TK = 64;                      // keys per LDS tile (two 32-key MFMA steps)
     constexpr int KCH = DH / 8;                 // 16-byte chunks of a K row
-    constexpr int NT = NWV * 64;                // threads; NWV waves of 16 rows each
-    constexpr int KLD = TK * KCH / NT;          // K chunks each thread copies per tile
-    constexpr int VLD = DH * (TK / 4) / NT;     // 4-key V groups each thread copies per tile
+    constexpr int NT = NWV * 64;                // threads; NWV waves of 16 rows each (per phase)
+    constexpr int NRW = NWV / NPH;              // row blocks
+    constexpr int KB = 4 / NPH;                 // 16-key score blocks of a wave per tile
+    constexpr int KTOT = TK * KCH, VTOT = DH * (TK / 4);     // 16-byte K chunks, 4-key V groups per tile
+    constexpr int KLD = (KTOT + NT - 1) / NT;   // K chunks each thread copies per tile
+    constexpr int VLD = (VTOT + NT - 1) / NT;   // 4-key V groups each thread copies per tile
+    static_assert(NPH == 1 || NPH == 2, "one or two key phases");
     __shared__ u32x4_t ks[2][TK * KCH];
     __shared__ u32x4_t vs[2][DH * (TK / 8)];
 
@@ -84,9 +92,10 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
     const int G = Hq / Hkv, Rg = Nq * G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
+    const int rw = wave % NRW, ph = __builtin_amdgcn_readfirstlane(wave / NRW);   // row block, key phase
 
-    const int wg_row0 = rtile * (NWV * 16);
-    const int wrow0 = wg_row0 + wave * 16;
+    const int wg_row0 = rtile * (NRW * 16);
+    const int wrow0 = wg_row0 + rw * 16;
     const bool wlive = wrow0 < Rg;              // a wave without rows still copies tiles
     const bool ok = seq_ok(len_snap, b, Nq, cap);
     const int len = ok ? len_snap[b] : 0;
@@ -94,7 +103,7 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
     const bool qlive = rho < Rg;
     const int it = qlive ? rho / G : 0, hh = qlive ? rho % G : 0;
     // keys past len + (last token of the workgroup's rows) are masked for all of its rows
-    const int it_max = min(Nq - 1, min(wg_row0 + NWV * 16 - 1, Rg - 1) / G);
+    const int it_max = min(Nq - 1, min(wg_row0 + NRW * 16 - 1, Rg - 1) / G);
     const int chunk = split_chunk(len, Nq, nsplit);
     const int kbeg = split * chunk;
     int kend = min(kbeg + chunk, len + it_max + 1);
@@ -134,16 +143,18 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
     // slot 0 and is zeroed (so masked keys add exactly zero); cap is a multiple of 4, so an 8-byte
     // V group never crosses the end of a row.
     struct Tile { u32x4_t k[KLD]; u32x2_t v[VLD]; };
+    // (when the thread count does not divide a tile, the surplus threads of the last round load
+    // a clamped, valid chunk and store nothing)
     auto load = [&](int t0, Tile& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
-            const int id = tid + NT * i, key = t0 + id / KCH;
+            const int id = min(tid + NT * i, KTOT - 1), key = t0 + id / KCH;
             r.k[i] = *(const u32x4_t*)(kbase + (size_t)(key < kend ? key : 0) * DH + (id % KCH) * 8);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
-            const int id = tid + NT * i, key0 = t0 + 4 * (id % (TK / 4));
+            const int id = min(tid + NT * i, VTOT - 1), key0 = t0 + 4 * (id % (TK / 4));
             r.v[i] = *(const u32x2_t*)(vbase + (size_t)(id / (TK / 4)) * cap + (key0 < kend ? key0 : 0));
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -154,11 +165,12 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
             const int id = tid + NT * i, key = id / KCH;
-            ks[buf][key * KCH + swz_k<DH>(key, id % KCH)] = r.k[i];
+            if (KTOT % NT == 0 || id < KTOT) ks[buf][key * KCH + swz_k<DH>(key, id % KCH)] = r.k[i];
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int id = tid + NT * i, row = id / (TK / 4), grp = id % (TK / 4);
+            if (VTOT % NT != 0 && id >= VTOT) continue;
             const int n = kend - (t0 + 4 * grp);                   // valid keys of the group
             u32x2_t w = r.v[i];
             w.x &= n >= 2 ? 0xFFFFFFFFu : (n == 1 ? 0xFFFFu : 0u);
@@ -171,15 +183,15 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
     // one 64-key step of the wave's 16 rows out of LDS buffer buf (keys k0 .. k0+63): four
     // 16-key score blocks, one softmax update, then two 32-key value products
     auto step = [&](int k0, int buf) __attribute__((always_inline)) {
-        f32x4_t st[4];
+        f32x4_t st[KB];                         // score block kb of the tile is st[kb - ph*KB]
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int key = kb * 16 + l16;
-            st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kbi = 0; kbi < KB; ++kbi) {
+            const int key = (ph * KB + kbi) * 16 + l16;
+            st[kbi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int d = 0; d < DS; ++d) {
                 const u32x4_t kv = ks[buf][key * KCH + swz_k<DH>(key, d * 4 + g4)];
-                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&kv, qf[d], st[kb], 0, 0, 0);
+                st[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&kv, qf[d], st[kbi], 0, 0, 0);
             }
         }
         // S^T[key][query]: lane holds keys kb*16 + 4*g4 + i of query l16.  A step wholly below
@@ -187,13 +199,13 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
         const bool full = k0 + TK <= kend && k0 + TK <= len;
         float lmax = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kbi = 0; kbi < KB; ++kbi)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = k0 + kb * 16 + g4 * 4 + i;
+                const int key = k0 + (ph * KB + kbi) * 16 + g4 * 4 + i;
                 const bool al = full || (qlive && key < kend && key_allowed<MODE>(key, len, it, Dblk));
-                const float sv = al ? st[kb][i] * sl2 : -INFINITY;
-                st[kb][i] = sv;
+                const float sv = al ? st[kbi][i] * sl2 : -INFINITY;
+                st[kbi][i] = sv;
                 lmax = fmaxf(lmax, sv);
             }
         if (__ballot(lmax > m_run + RESCALE) != 0) {      // wave-uniform, rare after the first step
@@ -207,14 +219,15 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
             m_run = m_new;
         }
 #pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
+        for (int kqi = 0; kqi < 2 / NPH; ++kqi) {
             // P^T fragment of keys k0 + 32kq ..: k-slot 8*g4 + i <- key 4*g4 + i (block 2kq),
             // 8*g4 + 4 + i <- key 16 + 4*g4 + i (block 2kq + 1); each weight as bf16 hi + bf16 lo
             // (both round to nearest even, two keys per conversion)
-            bf16x8_t ph, pl;
+            const int kq = ph * (2 / NPH) + kqi;
+            bf16x8_t phi, pl;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int kb = 2 * kq + (j >> 1), i = (j & 1) * 2;
+                const int kb = 2 * kqi + (j >> 1), i = (j & 1) * 2;     // index into st
                 const f32x2_t pv = m_run == -INFINITY
                                        ? f32x2_t{0.f, 0.f}
                                        : f32x2_t{__builtin_amdgcn_exp2f(st[kb][i] - m_run),
@@ -222,14 +235,14 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
                 const bf16x2_t h = __builtin_convertvector(pv, bf16x2_t);
                 const bf16x2_t lo = __builtin_convertvector(pv - __builtin_convertvector(h, f32x2_t), bf16x2_t);
                 l_lane += pv.x + pv.y;
-                ph[2 * j] = h.x; ph[2 * j + 1] = h.y;
+                phi[2 * j] = h.x; phi[2 * j + 1] = h.y;
                 pl[2 * j] = lo.x; pl[2 * j + 1] = lo.y;
             }
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int row = db * 16 + l16;
                 const u32x4_t vv = vs[buf][row * (TK / 8) + swz_v(row, kq * 4 + g4)];
-                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, ph, oacc[db], 0, 0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, phi, oacc[db], 0, 0, 0);
                 oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, pl, oacc[db], 0, 0, 0);
             }
         }
@@ -248,6 +261,33 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
 
     float l_run = l_lane + __shfl_xor(l_lane, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
+    if constexpr (NPH == 2) {
+        // phase 1 hands (m, l, O) to phase 0 of the same row block and lane through the K/V
+        // buffers (free once every wave has left the loop): O = O0 2^(m0-m) + O1 2^(m1-m)
+        __shared__ float2 ml1[NRW * 64];
+        static_assert(NRW * 64 * (DB / 2) * sizeof(f32x4_t) <= sizeof(ks), "O halves fit the K/V buffers");
+        f32x4_t* o_lo = (f32x4_t*)&ks[0][0];
+        f32x4_t* o_hi = (f32x4_t*)&vs[0][0];
+        const int slot = rw * 64 + lane;
+        __syncthreads();
+        if (ph == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                (db < DB / 2 ? o_lo : o_hi)[slot * (DB / 2) + db % (DB / 2)] = oacc[db];
+            ml1[slot] = make_float2(m_run, l_run);
+        }
+        __syncthreads();
+        if (ph == 1) return;
+        const float2 o1ml = ml1[slot];
+        const float m = fmaxf(m_run, o1ml.x);
+        const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+        const float a1 = o1ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o1ml.x - m);
+        l_run = l_run * a0 + o1ml.y * a1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            oacc[db] = oacc[db] * a0 + (db < DB / 2 ? o_lo : o_hi)[slot * (DB / 2) + db % (DB / 2)] * a1;
+        m_run = m;
+    }
     if (!qlive) return;
     // lane holds O^T[dim = db*16 + 4*g4 + i][query l16]
     if (nsplit == 1) {
@@ -469,10 +509,14 @@ void attention_plan(FwdDims* fd, int cus) {
     // 128-row tiles (8 waves) once a GQA group has more than 64 rows: the K/V of a split is then
     // fetched for twice the rows (a 66-row group, 6 heads x 11 positions, is one tile, not two)
     fd->attn_rows_per_wg = Rg > 64 ? 128 : 64;
+    // a group of 65..80 rows (the PLD verify: 6 heads x 11 positions) takes 80-row tiles of five
+    // row blocks in two key phases (ten waves, one workgroup per CU), not an 8-wave tile with
+    // three idle waves
+    if (Rg > 64 && Rg <= 80 && fd->d == 128) fd->attn_rows_per_wg = 80;
     fd->attn_row_tiles = (Rg + fd->attn_rows_per_wg - 1) / fd->attn_rows_per_wg;
     const long units = (long)fd->B * fd->Hkv * fd->attn_row_tiles;
-    // resident workgroups: two 4-wave or one 8-wave workgroup per CU (registers and LDS)
-    const long want = (fd->attn_rows_per_wg == 128 ? 1L : 2L) * cus;
+    // resident workgroups: two 4-wave or one 8- or 10-wave workgroup per CU (registers and LDS)
+    const long want = (fd->attn_rows_per_wg == 64 ? 2L : 1L) * cus;
     long splits = want / units;
     if (splits > 24) {
         // few row tiles (small spans): as many splits as fill the chip, the merge is cheap
@@ -504,14 +548,17 @@ hipError_t launch_attention(const FwdDims& fd, const FwdBufs& wb, const void* kc
     }
     const dim3 grid(fd.attn_splits, fd.attn_row_tiles, fd.B * fd.Hkv);
     const bool tri = fd.mode == CAD_MASK_BLOCK_TRI;
-    const int nt = fd.attn_rows_per_wg / 16 * 64;
+    const int nt = fd.attn_rows_per_wg == 80 ? 640 : fd.attn_rows_per_wg / 16 * 64;
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, dim3(nt), 0, s, (const uint16_t*)wb.q, (const uint16_t*)kc,
                            (const uint16_t*)vc, wb.len_snap, fd.Nq, fd.Hq, fd.Hkv, fd.cap, fd.Dblk, fd.attn_splits,
                            wb.part_o, wb.part_ml, (uint16_t*)wb.o);
     };
     const bool big = fd.attn_rows_per_wg == 128;
-    if (fd.d == 128) {
+    if (fd.d == 128 && fd.attn_rows_per_wg == 80) {
+        if (tri) go(k_attn_bf16<128, CAD_MASK_BLOCK_TRI, 10, 2>);
+        else go(k_attn_bf16<128, CAD_MASK_CAUSAL_SPAN, 10, 2>);
+    } else if (fd.d == 128) {
         if (tri) big ? go(k_attn_bf16<128, CAD_MASK_BLOCK_TRI, 8>) : go(k_attn_bf16<128, CAD_MASK_BLOCK_TRI, 4>);
         else big ? go(k_attn_bf16<128, CAD_MASK_CAUSAL_SPAN, 8>) : go(k_attn_bf16<128, CAD_MASK_CAUSAL_SPAN, 4>);
     } else {

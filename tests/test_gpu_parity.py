@@ -228,8 +228,9 @@ def test_tiny_fp32_corrupted_draft_accepts_four():
     assert cache.len.item() == 128 + 5
 
 
-@pytest.mark.parametrize("Nq", [1, 8, 13, 40, 100])
+@pytest.mark.parametrize("Nq", [1, 8, 13, 17, 20, 40, 100])
 def test_small_bf16_span_matches_oracle(small, Nq):
+    # Nq = 17 and 20: 68 and 80 rows per GQA group (4 query heads), the two-key-phase attention tile
     w, dl, OL = small
     log(f"small bf16 causal Nq={Nq}")
     B, L0, cap = 3, 150, 320
@@ -446,10 +447,12 @@ def test_copy_commit_mode_rejects_the_block_mask(small):
         cad.span_forward(dl, cache, t, 8, mode=cad.MASK_BLOCK, W=2, D=4, flags=cad.LOGITS_LAST, argmax_out=am)
 
 
-def test_small_bf16_block_verify_matches_oracle(small):
+@pytest.mark.parametrize("W, D", [(4, 8), (2, 9)])
+def test_small_bf16_block_verify_matches_oracle(small, W, D):
+    # (W, D) = (2, 9): 18 rows x 4 heads = 72 rows per GQA group, the two-key-phase attention tile
     w, dl, OL = small
-    W, D, B, L0, cap = 4, 8, 2, 200, 260
-    log("small bf16 block W=4 D=8")
+    B, L0, cap = 2, 200, 260
+    log(f"small bf16 block W={W} D={D}")
     ctx = np.stack([synth.uniform_tokens(80 + b, L0, SMALL.vocab) for b in range(B)])
     cand = np.stack([synth.uniform_tokens(90 + b, W * D, SMALL.vocab) for b in range(B)])
     cache = cad.DeviceCache(SMALL, B, cap)
