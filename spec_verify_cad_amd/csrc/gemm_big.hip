@@ -521,7 +521,7 @@ hipError_t go_big(const void* A, const void* W, int M, int N, int K, int ffn, co
 // tokens.  The narrow QKV projection and the K-slice partial projections take 128 x 64 tiles
 // (one wave of 128 features, so a QKV wave holds whole heads of up to 128 dims) to spread over
 // more workgroups (measured on the 1.5B shape for gate/up: 256 x 64 tiles are best up to 128
-// rows, 256 x 128 up to 256, 256 x 256 beyond).
+// rows, 256 x 128 up to 256, 192 x 256 beyond while one round holds them, else 256 x 256).
 BigPlan big_plan(int kind, int M, int N, int K, int slices) {
     BigPlan t;
     t.BN = 256;
@@ -530,6 +530,11 @@ BigPlan big_plan(int kind, int M, int N, int K, int slices) {
     // 256 rows one round of 140 workgroups took 35 us, 560 128 x 64 tiles in two rounds 44 us)
     if (kind == EPI_SWIGLU && M <= 128) t.BM = 64;
     if (kind == EPI_SWIGLU && M > 128 && M <= 256) t.BM = 128;
+    // beyond 256 rows: 192 x 256 tiles while they fit the CUs in one round (at 512 rows, 188
+    // workgroups: 46 us against 52 us for 140 256 x 256 tiles), else 256 x 256 (at 704 rows 282
+    // 192-wide tiles would need a second round)
+    if (kind == EPI_SWIGLU && M > 256 && (long)((M + 255) / 256) * ((N / 2 + 95) / 96) <= device_cu_count())
+        t.BN = 192;
     if (kind == EPI_SAMPLE && t.BM > 128) t.BM = 128;  // the sampling state of 256 rows spills
     if (kind == EPI_QKV || kind == EPI_PARTIAL) {
         // narrow outputs: 128 x 64 tiles give more workgroups (and QKV one head per wave); for the
@@ -579,6 +584,8 @@ hipError_t big_dispatch(const void* A, const void* W, int M, int N, int K, int s
     p.k_slice = t.k_slice;
     const int ffn = KIND == EPI_SWIGLU ? p.ffn : 0;
     if (t.BN == 128) return go_big<KIND, 128, 64, 1, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
+    if constexpr (KIND == EPI_SWIGLU)
+        if (t.BN == 192) return go_big<KIND, 192, 256, 2, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
     if constexpr (KIND == EPI_ARGMAX) {
         if (t.bal && t.BM == 64)
             return p.logits ? go_big<KIND, 256, 64, 2, 4, 64, BAL_RS64, 2>(A, W, M, N, K, ffn, t, p, s)
