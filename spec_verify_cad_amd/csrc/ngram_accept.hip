@@ -2,9 +2,10 @@
 //
 // k_ngram: prompt-lookup draft search (PLD page, "The n-gram match, precisely"; SwitchSD's
 // kappa-gram gate with recency-ranked candidates).  One workgroup of 1024 threads per sequence
-// scans the candidate starts newest-first in chunks of 4096 (four consecutive starts per thread,
-// the chunk's token window staged in LDS so the loads are coalesced), ranks the hits of a chunk
-// by a block-wide prefix count in descending start order and stops as soon as W hits are known.
+// scans the candidate starts newest-first in chunks of 8192 (eight consecutive starts per thread,
+// the chunk's token window staged in LDS so the loads are coalesced, and the next chunk's window
+// fetched into registers while the current one is compared), ranks the hits of a chunk by a
+// block-wide prefix count in descending start order and stops as soon as W hits are known.
 //
 // k_accept: greedy left-to-right acceptance (PLD page, "Verification in a single parallel
 // pass") or the longest validated candidate of a block verify (SwitchSD), then the commit:
@@ -15,9 +16,10 @@
 namespace {
 
 constexpr int NG_NT = 1024;      // threads of the scan workgroup
-constexpr int NG_Q = 4;          // candidate starts per thread per chunk
+constexpr int NG_Q = 8;          // candidate starts per thread per chunk
 constexpr int CH = NG_NT * NG_Q; // candidate starts per scan chunk
 constexpr int MAXN = 64;
+constexpr int NG_L = (CH + MAXN + NG_NT - 1) / NG_NT;   // window tokens each thread fetches per chunk
 
 // Suffix lengths n_hi down to n_lo are tried in turn and the hits of the first length that has
 // any are kept (n_hi == n_lo: the plain lookup); match_n (nullable) gets that length, 0 if none.
@@ -45,16 +47,30 @@ __global__ __launch_bounds__(NG_NT) void k_ngram(const int32_t* __restrict__ ctx
     if (len < n + 1) continue;
     __syncthreads();                                     // the previous length's suffix is no longer read
     for (int k = tid; k < n; k += NG_NT) suf[k] = c[len - n + k];
+    // the window of a chunk (starts lo..hi and their n tokens) is fetched into registers one
+    // chunk ahead, every load in flight at once; positions before 0 read position 0 and become -1
+    int32_t pre[NG_L];
+    auto fetch = [&](int lo_) {
+#pragma unroll
+        for (int i = 0; i < NG_L; ++i) {
+            const int e = min(tid + i * NG_NT, CH + n - 2), pos = lo_ + e;
+            const int32_t v = c[pos > 0 ? pos : 0];
+            pre[i] = pos >= 0 ? v : -1;
+        }
+    };
     int found = 0;
+    fetch(len - n - CH);
     for (int hi = len - n - 1; hi >= 0 && found < W; hi -= CH) {
         const int lo = hi - CH + 1;                      // window covers starts lo..hi and their n tokens
         __syncthreads();                                 // the previous chunk's window is no longer read
-        for (int e = tid; e < CH + n - 1; e += NG_NT) {
-            const int pos = lo + e;
-            win[e] = pos >= 0 ? c[pos] : -1;
+#pragma unroll
+        for (int i = 0; i < NG_L; ++i) {
+            const int e = tid + i * NG_NT;
+            if (e < CH + n - 1) win[e] = pre[i];
         }
+        fetch(lo - CH);                                  // the next chunk's window, in flight meanwhile
         __syncthreads();
-        // thread t takes starts hi - 4t - q, q = 0..3 (descending in thread order, then in q)
+        // thread t takes starts hi - NG_Q*t - q, q < NG_Q (descending in thread order, then in q)
         int hits = 0;
 #pragma unroll
         for (int q = 0; q < NG_Q; ++q) {
