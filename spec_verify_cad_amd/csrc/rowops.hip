@@ -19,6 +19,7 @@
 namespace {
 
 constexpr int NT = 256;
+constexpr int FB = 8;            // slot loads in flight per lane in the final reductions
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
     v = wave_sum(v);
@@ -286,7 +287,17 @@ __global__ __launch_bounds__(64) void k_sample_final(const float4* __restrict__ 
     if (!seq_ok(len_snap, b, Nq, cap)) return;
     SampleState st;
     sample_init(st);
-    for (int t = threadIdx.x; t < slots; t += 64) sample_merge(st, sample_load(part + ((size_t)r * slots + t) * 2));
+    // a lane merges slots lane, lane + 64, ... in that order; the loads of FB of them are issued
+    // before the first is used (clamped addresses, surplus ones not merged)
+    for (int t0 = 0; t0 < slots; t0 += 64 * FB) {
+        SampleState v[FB];
+#pragma unroll
+        for (int u = 0; u < FB; ++u)
+            v[u] = sample_load(part + ((size_t)r * slots + min(t0 + (int)threadIdx.x + 64 * u, slots - 1)) * 2);
+#pragma unroll
+        for (int u = 0; u < FB; ++u)
+            if (t0 + (int)threadIdx.x + 64 * u < slots) sample_merge(st, v[u]);
+    }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) sample_merge(st, sample_shfl_xor(st, o));
     if (threadIdx.x != 0) return;
@@ -317,9 +328,15 @@ __global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ 
     if (!seq_ok(len_snap, b, Nq, cap)) return;
     float best = -INFINITY;
     int bi = 0x7fffffff;
-    for (int t = threadIdx.x; t < slots; t += 64) {
-        const float2 pv = part[(size_t)r * slots + t];
-        argmax_merge(best, bi, pv.x, __float_as_int(pv.y));
+    // slots lane, lane + 64, ... with the loads of FB of them in flight at once (clamped
+    // addresses, surplus ones not merged)
+    for (int t0 = 0; t0 < slots; t0 += 64 * FB) {
+        float2 pv[FB];
+#pragma unroll
+        for (int u = 0; u < FB; ++u) pv[u] = part[(size_t)r * slots + min(t0 + (int)threadIdx.x + 64 * u, slots - 1)];
+#pragma unroll
+        for (int u = 0; u < FB; ++u)
+            if (t0 + (int)threadIdx.x + 64 * u < slots) argmax_merge(best, bi, pv[u].x, __float_as_int(pv[u].y));
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
