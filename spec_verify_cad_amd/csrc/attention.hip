@@ -183,6 +183,7 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
     // one 64-key step of the wave's 16 rows out of LDS buffer buf (keys k0 .. k0+63): four
     // 16-key score blocks, one softmax update, then two 32-key value products
     auto step = [&](int k0, int buf) __attribute__((always_inline)) {
+        __builtin_amdgcn_iglp_opt(0);          // interleave the LDS fragment reads with the MFMAs
         f32x4_t st[KB];                         // score block kb of the tile is st[kb - ph*KB]
 #pragma unroll
         for (int kbi = 0; kbi < KB; ++kbi) {
