@@ -48,6 +48,31 @@ def test_ngram_lookup_matches_oracle_small_alphabets(n, W, D, wc):
             assert d[b, 0] == (c[-1] if len(c) else 0)
 
 
+@pytest.mark.parametrize("n,W", [(3, 1), (5, 4)])
+def test_ngram_lookup_matches_in_the_oldest_chunk(n, W):
+    # histories of several 8192-start scan chunks whose only matches sit at the very start, so the
+    # scan runs to the oldest chunk (window positions before 0, the next window fetched past the
+    # end); plus a history shorter than one chunk and one of exactly n + 1 tokens
+    log(f"ngram oldest-chunk matches n={n} W={W}")
+    rng = np.random.default_rng(300 + n)
+    V = 1 << 30                                        # ids drawn from 2^30: no accidental matches
+    ctxs = []
+    for L in (8192 + n + 1, 8192 + n + 2, 20000, 3 * 8192 + 11, 5000):
+        c = rng.integers(0, V, size=L)
+        c[L - n:] = [7, 8, 9, 10, 11][:n]              # the suffix
+        for j in range(min(W, 3)):                     # planted at starts 0, 1, 2 (overlapping)
+            c[j:j + n] = c[L - n:]
+        ctxs.append(c)
+    ctxs.append(np.array([7, 8, 9, 10, 11, 12][:n + 1]))
+    d, l, m = _lookup_gpu(ctxs, n, W, 6, 0)
+    for b, c in enumerate(ctxs):
+        od, ol, om = O.ngram_lookup(c, len(c), n, W, 6)
+        np.testing.assert_array_equal(l[b], ol, err_msg=f"b={b}")
+        np.testing.assert_array_equal(m[b], om, err_msg=f"b={b}")
+        np.testing.assert_array_equal(d[b].reshape(W, 6), od, err_msg=f"b={b}")
+    assert (m[:5, 0] >= 0).all()                       # the planted starts are found
+
+
 def test_ngram_lookup_planted_contexts():
     # contexts shaped like the batched PLD workload (Zipf background, planted copies), n=3, D=10
     log("ngram planted zipf contexts")
