@@ -13,6 +13,12 @@ from helpers import oracle_layer
 HIDDEN_TOL = 2e-2
 LOGIT_TOL = 1e-2
 NEAR_TIE = 1e-3
+# Cached k/v rows: fraction of elements allowed to differ at all.  fp32-vs-fp64 flips come in
+# bursts: a token whose normed input rounds differently moves up to ~23 % of its k/v elements
+# by an ulp (0.05 % of all elements on average), so over few rows the fraction is one burst row's
+# share; the bound is 1 % plus one such row (test_tolerance_derivation.py measures both).
+CACHE_FLIP_FRAC = 0.01
+ROW_BURST = 0.25
 
 
 def hidden_tol(ref: np.ndarray, ffn: int = 0) -> np.ndarray:
@@ -144,12 +150,14 @@ def compare_cache(cache: cad.DeviceCache, b: int, oc: O.Cache, lo: int, hi: int,
     rounded dot product of a rounded normed input; where the two sides round that input
     differently (fp32 vs fp64 accumulation just below a rounding boundary) a small element can
     move by an ulp of the larger values, so the bound is the hidden-output tolerance (2e-2 or
-    two ulps, for bf16; 1e-5 for fp32) and almost every element must be bit-identical."""
+    two ulps, for bf16; 1e-5 for fp32) and almost every element must be bit-identical: at most
+    CACHE_FLIP_FRAC of them plus one burst row's share (ROW_BURST / rows) may differ."""
     gk, gv = device_cache_rows(cache, b, lo, hi, dtype)
+    limit = CACHE_FLIP_FRAC + ROW_BURST / max(hi - lo, 1)
     for name, got, ref in (("k", gk, oc.K), ("v", gv, oc.V)):
         want = ref[:, lo:hi]
         diff = np.abs(got - want)
         tol = hidden_tol(want) if dtype == "bf16" else 1e-5
         assert (diff <= tol).all(), f"{what} {name} max-abs {np.max(diff)}"
         frac = np.mean(diff > 0)
-        assert frac < 0.01, f"{what} {name} differing fraction {frac}"
+        assert frac < limit, f"{what} {name} differing fraction {frac} (limit {limit:.4f})"

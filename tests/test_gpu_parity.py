@@ -490,6 +490,33 @@ def test_small_bf16_block_verify_matches_oracle(small, W, D):
         compare(g, ref, rows=slice(b * W * D, (b + 1) * W * D), what=f"block b={b}")
 
 
+@pytest.mark.parametrize("mode, W, D, Nq", [("causal", 1, 0, 13), ("causal", 1, 0, 40), ("block", 2, 9, 18)])
+def test_small_bf16_ragged_cache_lengths_match_oracle(small, mode, W, D, Nq):
+    # one forward over sequences whose caches hold 0, 1, 63, 64, 65 and 200 positions: an empty
+    # cache (the rows see only their own span) and lengths on both sides of a 64-key tile edge.
+    # The caches are the oracle's own (exact in bf16), so both sides attend over the same keys.
+    w, dl, OL = small
+    lens = [0, 1, 63, 64, 65, 200]
+    B, cap = len(lens), 320
+    log(f"small bf16 ragged cache lengths {mode} Nq={Nq}")
+    cache = cad.DeviceCache(SMALL, B, cap)
+    ocs = []
+    for b, L0 in enumerate(lens):
+        oc = O.cache_from_tokens(OL, synth.uniform_tokens(140 + b, L0, SMALL.vocab), cap)
+        upload_oracle_cache(cache, b, oc, "bf16")
+        ocs.append(oc)
+    span = np.stack([synth.uniform_tokens(150 + b, Nq, SMALL.vocab) for b in range(B)])
+    commit = mode == "causal"
+    g = run_forward(dl, cache, span, mode=cad.MASK_CAUSAL if commit else cad.MASK_BLOCK, W=W, D=max(D, 1),
+                    flags=cad.COMMIT_ALL if commit else 0)
+    assert list(cache.len.cpu().numpy()) == [L0 + (Nq if commit else 0) for L0 in lens]
+    for b, L0 in enumerate(lens):
+        ref = O.span_forward(OL, ocs[b], span[b], mode=mode, W=W, D=D, commit=commit)
+        compare(g, ref, rows=slice(b * Nq, (b + 1) * Nq), what=f"{mode} b={b} len={L0}")
+        if commit:
+            compare_cache(cache, b, ocs[b], L0, L0 + Nq, "bf16", what=f"span rows b={b} len={L0}")
+
+
 def test_small_bf16_span_equals_decode_steps_on_gpu(small):
     w, dl, OL = small
     log("small bf16 span vs gpu decode steps")
