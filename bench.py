@@ -63,7 +63,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only: --gpus {a.gpus} / WORLD_SIZE {world} is not supported "
-              "(the span forward of one sequence batch is not sharded across GPUs in this build)",
+              "(the span forward of a sequence batch runs on one GPU and is not sharded across GPUs)",
               file=sys.stderr, flush=True)
         sys.exit(2)
 
