@@ -92,7 +92,8 @@ typedef struct {
  * value cache is stored transposed so that attention reads, for one dimension, a contiguous run
  * of slots (the operand layout of the value product).  cap must be a multiple of 4.
  * len: [B] int32, device-resident current lengths.  err: [B] int32, nullable; set to
- * CAD_ECAPACITY for a sequence whose operation would overflow (never cleared by the library).
+ * CAD_ECAPACITY for a sequence whose operation would overflow, and by a forward to CAD_EINVAL for
+ * a sequence whose tokens hold an id outside [0, vocab) (never cleared by the library).
  * n_kv_heads, head_dim and dtype must match the layer the cache is used with.
  */
 typedef struct {
@@ -148,7 +149,8 @@ int cad_ngram_lookup_longest(const int32_t *ctx, int64_t ctx_stride, const int32
  * cad_span_forward — one parallel forward of Nq new tokens per sequence (Copy-as-Decode §2.4
  * and Appendix K; SwitchSD block-triangular verification).
  *
- *   tokens      [B, Nq] int32 token ids (must be < vocab)
+ *   tokens      [B, Nq] int32 token ids; a sequence holding an id outside [0, vocab) is flagged
+ *               CAD_EINVAL in kv->err and its forward is a no-op (nothing written, length kept)
  *   mask_mode   CAD_MASK_CAUSAL_SPAN, or CAD_MASK_BLOCK_TRI with Nq == W*D
  *   flags       CAD_COMMIT_ALL, CAD_KV_ONLY, CAD_LOGITS_LAST (or-ed)
  *   argmax_out  [B, Nq] int32 out: LM-head argmax per row, ties to the lowest id (nullable
@@ -156,6 +158,8 @@ int cad_ngram_lookup_longest(const int32_t *ctx, int64_t ctx_stride, const int32
  *   hidden_out  [B*Nq, hidden] dtype out, nullable: the layer output (residual stream)
  *   logits_out  [B*Nq, vocab] fp32 out, nullable (debug; costs a full logits write);
  *               [B, vocab] with CAD_LOGITS_LAST
+ *   top2_gap    [B*Nq] fp32 out, nullable ([B] with CAD_LOGITS_LAST): largest minus second-largest
+ *               logit of each row (0 for a tie), the margin by which the argmax is decided
  *   workspace   device scratch of at least cad_span_forward_workspace(...) bytes, 256-aligned
  *
  * Every row first appends its K/V at slot len+i (RoPE at the row's position), then attends
@@ -173,7 +177,7 @@ int cad_ngram_lookup_longest(const int32_t *ctx, int64_t ctx_stride, const int32
 int cad_span_forward(const cad_layer_desc *layer, const cad_kv_desc *kv,
                      const int32_t *tokens, int B, int Nq,
                      int mask_mode, int W, int D, int flags,
-                     int32_t *argmax_out, void *hidden_out, float *logits_out,
+                     int32_t *argmax_out, void *hidden_out, float *logits_out, float *top2_gap,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -253,7 +257,7 @@ int cad_span_forward_sampled(const cad_layer_desc *layer, const cad_kv_desc *kv,
 #define CAD_MAX_LAYERS 256
 int cad_stack_span_forward(const cad_layer_desc *layers, int n_layers, const cad_kv_desc *kvs,
                            const int32_t *tokens, int B, int Nq, int mode, int W, int D, int flags,
-                           int32_t *argmax_out, void *hidden_out, float *logits_out,
+                           int32_t *argmax_out, void *hidden_out, float *logits_out, float *top2_gap,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 /* The masked-decision forward (as cad_span_forward_allowed) through a stack of layers, with the
  * layers, caches and lengths of cad_stack_span_forward: a grammar decision point of a program run
@@ -304,7 +308,12 @@ size_t cad_span_forward_workspace(const cad_layer_desc *layer, int B, int Nq, in
  * Causal: a = number of leading i < draft_len with d_{i+1} == pred[i]; bonus = pred[a].
  * Block: a_w = leading run of candidate w checked against first_pred, then against
  * pred[w*D + j - 1]; the largest a_w wins, ties to the lowest w; bonus = first_pred when a* = 0,
- * else pred[w*D + a* - 1].  Errors: CAD_EINVAL, CAD_EUNSUPPORTED (W > 8, D > 64).
+ * else pred[w*D + a* - 1].  Draft lengths are clamped to [0, D].
+ * A skipped sequence (kv->err already set, or its history or cache would overflow; an overflow
+ * is flagged CAD_ECAPACITY in kv->err when kv is given) gets accepted = 0, best_w = 0,
+ * n_emitted = 0 and a zero emitted row, and no length changes: n_emitted[b] == 0 identifies it,
+ * since a sequence that ran always emits at least one token.
+ * Errors: CAD_EINVAL, CAD_EUNSUPPORTED (W > 8, D > 64).
  */
 int cad_accept_scan(const int32_t *draft, int with_current, const int32_t *draft_len,
                     const int32_t *pred, const int32_t *first_pred,
@@ -312,6 +321,25 @@ int cad_accept_scan(const int32_t *draft, int with_current, const int32_t *draft
                     int32_t *accepted, int32_t *best_w, int32_t *emitted, int32_t *n_emitted,
                     int32_t *ctx, int64_t ctx_stride, int32_t *ctx_len, int ctx_cap,
                     const cad_kv_desc *kv, hipStream_t stream);
+
+/*
+ * cad_stack_accept_scan — cad_accept_scan for a verify forward run through a stack of layers
+ * (cad_stack_span_forward; SwitchSD's block verify on the whole model).  Arguments as
+ * cad_accept_scan, with the caches of cad_stack_span_forward:
+ *   kvs        [n_layers] caches (required), lengths and error flags those of kvs[0]
+ *   best_w     required in block mode with n_layers > 1
+ * Causal mode: kvs[0].len += a+1 (every layer's rows are already in place).  Block mode: the
+ * winner's first a* K/V slots move from len + w*D + j to len + j in EVERY layer's cache, then
+ * kvs[0].len += a*.
+ * Errors: as cad_accept_scan; CAD_EINVAL also for n_layers outside 1..CAD_MAX_LAYERS, a missing
+ * best_w, or caches that disagree in B, cap, heads, head_dim or dtype.
+ */
+int cad_stack_accept_scan(const int32_t *draft, int with_current, const int32_t *draft_len,
+                          const int32_t *pred, const int32_t *first_pred,
+                          int B, int W, int D, int mask_mode,
+                          int32_t *accepted, int32_t *best_w, int32_t *emitted, int32_t *n_emitted,
+                          int32_t *ctx, int64_t ctx_stride, int32_t *ctx_len, int ctx_cap,
+                          const cad_kv_desc *kvs, int n_layers, hipStream_t stream);
 
 /*
  * Diagnostics: per-stage GPU time of cad_span_forward.  While enabled, every forward records a

@@ -54,10 +54,10 @@ def lib() -> ctypes.CDLL:
     L.cad_ngram_lookup_longest.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     L.cad_ngram_lookup_longest.restype = i32
     L.cad_span_forward.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(KVDesc), vp, i32, i32, i32, i32, i32,
-                                   i32, vp, vp, vp, vp, sz, vp]
+                                   i32, vp, vp, vp, vp, vp, sz, vp]
     L.cad_span_forward.restype = i32
     L.cad_stack_span_forward.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(KVDesc), vp, i32, i32, i32,
-                                         i32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+                                         i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.cad_stack_span_forward.restype = i32
     L.cad_stack_span_forward_allowed.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(KVDesc), vp, i32, i32,
                                                  i32, vp, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -79,6 +79,9 @@ def lib() -> ctypes.CDLL:
     L.cad_accept_scan.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64, vp, i32,
                                   ctypes.POINTER(KVDesc), vp]
     L.cad_accept_scan.restype = i32
+    L.cad_stack_accept_scan.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64, vp, i32,
+                                        ctypes.POINTER(KVDesc), i32, vp]
+    L.cad_stack_accept_scan.restype = i32
     L.cad_status_string.argtypes = [i32]
     L.cad_status_string.restype = ctypes.c_char_p
     L.cad_version.restype = i32
@@ -234,13 +237,13 @@ def alloc_workspace(nbytes: int, device="cuda"):
 
 def span_forward(layer: DeviceLayer, cache: DeviceCache, tokens, Nq: int, mode: int = MASK_CAUSAL, W: int = 1,
                  D: int = 1, flags: int = 0, argmax_out=None, hidden_out=None, logits_out=None, workspace=None,
-                 stream=None):
+                 stream=None, top2_gap=None):
     B = cache.B
     if workspace is None:
         workspace = alloc_workspace(span_forward_workspace(layer, B, Nq, mode, W, D, cache.cap, flags))
     _check(lib().cad_span_forward(ctypes.byref(layer.desc), ctypes.byref(cache.desc), _ptr(tokens), B, Nq, mode, W, D,
-                                  flags, _ptr(argmax_out), _ptr(hidden_out), _ptr(logits_out), _ptr(workspace),
-                                  workspace.numel(), _stream(stream)), "cad_span_forward")
+                                  flags, _ptr(argmax_out), _ptr(hidden_out), _ptr(logits_out), _ptr(top2_gap),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)), "cad_span_forward")
     return workspace
 
 
@@ -254,15 +257,15 @@ def stack_span_forward_workspace(stack: DeviceStack, B: int, Nq: int, mode: int 
 
 def stack_span_forward(stack: DeviceStack, cache: StackCache, tokens, Nq: int, mode: int = MASK_CAUSAL, W: int = 1,
                        D: int = 1, flags: int = 0, argmax_out=None, hidden_out=None, logits_out=None,
-                       workspace=None, stream=None):
+                       workspace=None, stream=None, top2_gap=None):
     if cache.n != stack.n:
         raise ValueError("one cache per layer")
     B = cache.B
     if workspace is None:
         workspace = alloc_workspace(stack_span_forward_workspace(stack, B, Nq, mode, W, D, cache.cap, flags))
     _check(lib().cad_stack_span_forward(stack.descs, stack.n, cache.descs, _ptr(tokens), B, Nq, mode, W, D, flags,
-                                        _ptr(argmax_out), _ptr(hidden_out), _ptr(logits_out), _ptr(workspace),
-                                        workspace.numel(), _stream(stream)), "cad_stack_span_forward")
+                                        _ptr(argmax_out), _ptr(hidden_out), _ptr(logits_out), _ptr(top2_gap),
+                                        _ptr(workspace), workspace.numel(), _stream(stream)), "cad_stack_span_forward")
     return workspace
 
 
@@ -332,6 +335,17 @@ def accept_scan(draft, with_current: int, draft_len, pred, first_pred, B: int, W
                                  mode, _ptr(accepted), _ptr(best_w), _ptr(emitted), _ptr(n_emitted), _ptr(ctx),
                                  _row_stride(ctx) if ctx is not None else 0, _ptr(ctx_len), ctx_cap, kvp,
                                  _stream(stream)), "cad_accept_scan")
+
+
+def stack_accept_scan(draft, with_current: int, draft_len, pred, first_pred, B: int, W: int, D: int, mode: int,
+                      accepted, best_w, emitted, n_emitted, cache: StackCache, ctx=None, ctx_len=None,
+                      ctx_cap: int = 0, stream=None):
+    """Accept scan after a verify forward through a stack: in block mode the winner's rows move in
+    every layer's cache."""
+    _check(lib().cad_stack_accept_scan(_ptr(draft), with_current, _ptr(draft_len), _ptr(pred), _ptr(first_pred), B, W,
+                                       D, mode, _ptr(accepted), _ptr(best_w), _ptr(emitted), _ptr(n_emitted),
+                                       _ptr(ctx), _row_stride(ctx) if ctx is not None else 0, _ptr(ctx_len), ctx_cap,
+                                       cache.descs, cache.n, _stream(stream)), "cad_stack_accept_scan")
 
 
 # ---------------------------------------------------------------------------------------

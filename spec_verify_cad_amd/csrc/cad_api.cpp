@@ -51,6 +51,8 @@ hipError_t stage(int id, hipStream_t s, F&& launch) {
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr long long kMaxRows = 1LL << 24;          // rows of one forward (B * Nq)
+
 bool layer_ok(const cad_layer_desc* L) {
     if (!L) return false;
     if (L->hidden <= 0 || L->n_q_heads <= 0 || L->n_kv_heads <= 0 || L->head_dim <= 0 || L->ffn <= 0 ||
@@ -72,6 +74,7 @@ bool layer_supported(const cad_layer_desc* L) {
 
 bool fwd_dims(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, int cap, FwdDims* fd) {
     if (!layer_ok(L) || B <= 0 || Nq <= 0 || cap <= 0) return false;
+    if ((long long)B * Nq > kMaxRows) return false;        // M = B * Nq rows stays far inside int
     if (mode != CAD_MASK_CAUSAL_SPAN && mode != CAD_MASK_BLOCK_TRI) return false;
     if (mode == CAD_MASK_BLOCK_TRI && (W <= 0 || D <= 0 || (long)W * D != Nq)) return false;
     std::memset(fd, 0, sizeof(*fd));
@@ -114,6 +117,7 @@ FwdBufs fwd_carve(const FwdDims& fd, void* base, bool kv_only) {
         w.amax_slots_last = gemm_argmax_slots(fd.dtype, fd.B, fd.V, fd.h);
         const size_t sl = std::max(M * (size_t)w.amax_slots, (size_t)fd.B * w.amax_slots_last);
         w.amax_part = (float2*)take(sl * sizeof(float2));
+        w.amax_sec = (float*)take(sl * sizeof(float));
         if (fd.dtype == CAD_DTYPE_BF16) {
             w.samp_slots = gemm_argmax_slots(fd.dtype, fd.M, fd.V, fd.h, EPI_SAMPLE);
             w.samp_slots_last = gemm_argmax_slots(fd.dtype, fd.B, fd.V, fd.h, EPI_SAMPLE);
@@ -228,8 +232,8 @@ bool same_shape(const cad_layer_desc* a, const cad_layer_desc* b) {
 // feed the next layer's K/V) and only the K/V projection of the last.
 int span_forward_impl(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs, const int32_t* tokens,
                       int B, int Nq, int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out,
-                      float* logits_out, const int32_t* allowed, int A, const SampleArgs* samp, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+                      float* logits_out, float* top2_gap, const int32_t* allowed, int A, const SampleArgs* samp,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!layers || !kvs || !tokens || n_layers < 1) return CAD_EINVAL;
     if (flags & ~(CAD_COMMIT_ALL | CAD_KV_ONLY | CAD_LOGITS_LAST)) return CAD_EINVAL;
     const bool kv_only = (flags & CAD_KV_ONLY) != 0;
@@ -381,6 +385,7 @@ int span_forward_impl(const cad_layer_desc* layers, int n_layers, const cad_kv_d
     const int lm_rows = last_only ? fd.B : fd.M;
     pl.M = lm_rows; pl.Nq = last_only ? 1 : fd.Nq;
     pl.N = fd.V; pl.amax_part = wb.amax_part; pl.amax_slots = last_only ? wb.amax_slots_last : wb.amax_slots;
+    pl.amax_sec = top2_gap ? wb.amax_sec : nullptr;
     pl.logits = logits_out;
     if (samp) {
         // sampled LM head: the slots hold sampling states; rows know their sequence, position
@@ -410,8 +415,8 @@ int span_forward_impl(const cad_layer_desc* layers, int n_layers, const cad_kv_d
         }) != hipSuccess)
         return CAD_EHIP;
     if (stage(ST_ARGMAX, stream, [&] {
-            return launch_argmax_final(fd, wb, last_only, argmax_out, (flags & CAD_COMMIT_ALL) ? kv0->len : nullptr,
-                                       stream);
+            return launch_argmax_final(fd, wb, last_only, argmax_out, top2_gap,
+                                       (flags & CAD_COMMIT_ALL) ? kv0->len : nullptr, stream);
         }) != hipSuccess)
         return CAD_EHIP;
     return CAD_OK;
@@ -419,11 +424,22 @@ int span_forward_impl(const cad_layer_desc* layers, int n_layers, const cad_kv_d
 
 }  // namespace
 
+}  // extern "C"
+
+int span_forward_internal(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
+                          int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
+                          float* top2_gap, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return span_forward_impl(L, 1, kv, tokens, B, Nq, mode, W, D, flags, argmax_out, hidden_out, logits_out, top2_gap,
+                             nullptr, 0, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" {
+
 int cad_span_forward(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
                      int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return span_forward_impl(L, 1, kv, tokens, B, Nq, mode, W, D, flags, argmax_out, hidden_out, logits_out, nullptr,
-                             0, nullptr, workspace, workspace_bytes, stream);
+                     float* top2_gap, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return span_forward_impl(L, 1, kv, tokens, B, Nq, mode, W, D, flags, argmax_out, hidden_out, logits_out, top2_gap,
+                             nullptr, 0, nullptr, workspace, workspace_bytes, stream);
 }
 
 int cad_span_forward_allowed(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
@@ -434,7 +450,7 @@ int cad_span_forward_allowed(const cad_layer_desc* L, const cad_kv_desc* kv, con
     if (flags & ~(CAD_COMMIT_ALL | CAD_LOGITS_LAST)) return CAD_EINVAL;
     if (!L || !kv) return CAD_EINVAL;
     return span_forward_impl(L, 1, kv, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, argmax_out, hidden_out,
-                             logits_out, allowed, A, nullptr, workspace, workspace_bytes, stream);
+                             logits_out, nullptr, allowed, A, nullptr, workspace, workspace_bytes, stream);
 }
 
 int cad_span_forward_sampled(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
@@ -445,7 +461,7 @@ int cad_span_forward_sampled(const cad_layer_desc* L, const cad_kv_desc* kv, con
     if (flags & ~(CAD_COMMIT_ALL | CAD_LOGITS_LAST)) return CAD_EINVAL;
     const SampleArgs sa{temperature, seed, draft_len};
     return span_forward_impl(L, 1, kv, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, pred_out, hidden_out,
-                             logits_out, nullptr, 0, &sa, workspace, workspace_bytes, stream);
+                             logits_out, nullptr, nullptr, 0, &sa, workspace, workspace_bytes, stream);
 }
 
 int cad_stack_span_forward_allowed(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs,
@@ -457,7 +473,7 @@ int cad_stack_span_forward_allowed(const cad_layer_desc* layers, int n_layers, c
     if (A < 1 || A > CAD_MAX_ALLOWED) return CAD_EUNSUPPORTED;
     if (flags & ~(CAD_COMMIT_ALL | CAD_LOGITS_LAST)) return CAD_EINVAL;
     return span_forward_impl(layers, n_layers, kvs, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, argmax_out,
-                             hidden_out, logits_out, allowed, A, nullptr, workspace, workspace_bytes, stream);
+                             hidden_out, logits_out, nullptr, allowed, A, nullptr, workspace, workspace_bytes, stream);
 }
 
 int cad_stack_span_forward_sampled(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs,
@@ -468,15 +484,16 @@ int cad_stack_span_forward_sampled(const cad_layer_desc* layers, int n_layers, c
     if (flags & ~(CAD_COMMIT_ALL | CAD_LOGITS_LAST)) return CAD_EINVAL;
     const SampleArgs sa{temperature, seed, draft_len};
     return span_forward_impl(layers, n_layers, kvs, tokens, B, Nq, CAD_MASK_CAUSAL_SPAN, 1, 1, flags, pred_out,
-                             hidden_out, logits_out, nullptr, 0, &sa, workspace, workspace_bytes, stream);
+                             hidden_out, logits_out, nullptr, nullptr, 0, &sa, workspace, workspace_bytes, stream);
 }
 
 int cad_stack_span_forward(const cad_layer_desc* layers, int n_layers, const cad_kv_desc* kvs, const int32_t* tokens,
                            int B, int Nq, int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out,
-                           float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                           float* logits_out, float* top2_gap, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
     if (n_layers < 1 || n_layers > CAD_MAX_LAYERS) return CAD_EINVAL;
     return span_forward_impl(layers, n_layers, kvs, tokens, B, Nq, mode, W, D, flags, argmax_out, hidden_out,
-                             logits_out, nullptr, 0, nullptr, workspace, workspace_bytes, stream);
+                             logits_out, top2_gap, nullptr, 0, nullptr, workspace, workspace_bytes, stream);
 }
 
 int cad_ngram_lookup(const int32_t* ctx, int64_t ctx_stride, const int32_t* ctx_len, int B, int n, int W, int D,
@@ -504,10 +521,15 @@ int cad_ngram_lookup_longest(const int32_t* ctx, int64_t ctx_stride, const int32
                : CAD_EHIP;
 }
 
-int cad_accept_scan(const int32_t* draft, int with_current, const int32_t* draft_len, const int32_t* pred,
-                    const int32_t* first_pred, int B, int W, int D, int mode, int32_t* accepted, int32_t* best_w,
-                    int32_t* emitted, int32_t* n_emitted, int32_t* ctx, int64_t ctx_stride, int32_t* ctx_len,
-                    int ctx_cap, const cad_kv_desc* kv, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks shared by the one-layer and the stack accept scan.
+int accept_args_ok(const int32_t* draft, int with_current, const int32_t* draft_len, const int32_t* pred,
+                   const int32_t* first_pred, int B, int W, int D, int mode, const int32_t* accepted,
+                   const int32_t* emitted, const int32_t* n_emitted, const int32_t* ctx, int64_t ctx_stride,
+                   const int32_t* ctx_len, int ctx_cap, const cad_kv_desc* kv) {
     if (!draft || !draft_len || !pred || !accepted || !emitted || !n_emitted) return CAD_EINVAL;
     if (B <= 0 || W <= 0 || D <= 0) return CAD_EINVAL;
     if (mode == CAD_MASK_CAUSAL_SPAN) {
@@ -524,10 +546,50 @@ int cad_accept_scan(const int32_t* draft, int with_current, const int32_t* draft
                                                       kv->head_dim != 128)))
         return CAD_EINVAL;
     if (W > 8 || D > 64 || (kv && kv->cap % 4)) return CAD_EUNSUPPORTED;
+    return CAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cad_accept_scan(const int32_t* draft, int with_current, const int32_t* draft_len, const int32_t* pred,
+                    const int32_t* first_pred, int B, int W, int D, int mode, int32_t* accepted, int32_t* best_w,
+                    int32_t* emitted, int32_t* n_emitted, int32_t* ctx, int64_t ctx_stride, int32_t* ctx_len,
+                    int ctx_cap, const cad_kv_desc* kv, hipStream_t stream) {
+    const int st = accept_args_ok(draft, with_current, draft_len, pred, first_pred, B, W, D, mode, accepted, emitted,
+                                  n_emitted, ctx, ctx_stride, ctx_len, ctx_cap, kv);
+    if (st != CAD_OK) return st;
     return launch_accept(draft, with_current, draft_len, pred, first_pred, B, W, D, mode, accepted, best_w, emitted,
                          n_emitted, ctx, ctx_stride, ctx_len, ctx_cap, kv, stream) == hipSuccess
                ? CAD_OK
                : CAD_EHIP;
+}
+
+int cad_stack_accept_scan(const int32_t* draft, int with_current, const int32_t* draft_len, const int32_t* pred,
+                          const int32_t* first_pred, int B, int W, int D, int mode, int32_t* accepted,
+                          int32_t* best_w, int32_t* emitted, int32_t* n_emitted, int32_t* ctx, int64_t ctx_stride,
+                          int32_t* ctx_len, int ctx_cap, const cad_kv_desc* kvs, int n_layers, hipStream_t stream) {
+    if (!kvs || n_layers < 1 || n_layers > CAD_MAX_LAYERS) return CAD_EINVAL;
+    const int st = accept_args_ok(draft, with_current, draft_len, pred, first_pred, B, W, D, mode, accepted, emitted,
+                                  n_emitted, ctx, ctx_stride, ctx_len, ctx_cap, &kvs[0]);
+    if (st != CAD_OK) return st;
+    const bool block = mode == CAD_MASK_BLOCK_TRI && n_layers > 1;
+    if (block) {
+        if (!best_w) return CAD_EINVAL;
+        for (int l = 1; l < n_layers; ++l) {
+            const cad_kv_desc& k = kvs[l];
+            if (!k.k || !k.v || k.B != B || k.cap != kvs[0].cap || k.n_kv_heads != kvs[0].n_kv_heads ||
+                k.head_dim != kvs[0].head_dim || k.dtype != kvs[0].dtype)
+                return CAD_EINVAL;
+        }
+    }
+    if (launch_accept(draft, with_current, draft_len, pred, first_pred, B, W, D, mode, accepted, best_w, emitted,
+                      n_emitted, ctx, ctx_stride, ctx_len, ctx_cap, &kvs[0], stream) != hipSuccess)
+        return CAD_EHIP;
+    if (block && launch_compact_layers(kvs, n_layers, B, D, accepted, best_w, n_emitted, stream) != hipSuccess)
+        return CAD_EHIP;
+    return CAD_OK;
 }
 
 }  // extern "C"

@@ -51,6 +51,12 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
     if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
+// runner-up of two (max, second) pairs: the larger of both seconds and of the smaller maximum
+// (equal maxima make the runner-up equal to the maximum, a gap of zero)
+__device__ __forceinline__ float second_merge(float b1, float s1, float b2, float s2) {
+    return fmaxf(fmaxf(s1, s2), fminf(b1, b2));
+}
+
 // Per-sequence state captured by the first kernel of a forward: the cache length every
 // later kernel of the same forward uses, and whether the sequence fits.
 __device__ __forceinline__ bool seq_ok(const int32_t* len_snap, int b, int Nq, int cap) {

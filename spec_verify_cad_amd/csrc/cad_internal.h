@@ -28,6 +28,7 @@ struct EpiParams {
     void* act; int ffn;
     // EPI_ARGMAX
     float2* amax_part;              // [M, slots] (max, index bits)
+    float* amax_sec;                // [M, slots] runner-up value of each slot, nullable (top-2 gap)
     int amax_slots;
     float* logits;                  // nullable debug output [M, N]
     // EPI_SAMPLE (the LM head of a sampled forward): per (row, slot) two float4 of SampleState;
@@ -59,6 +60,7 @@ struct RopeFreqs { double inv[64]; };
 struct FwdBufs {
     int32_t* len_snap;
     float2* amax_part; int amax_slots;
+    float* amax_sec;                // runner-up per (row, slot) for the top-2 gap
     int amax_slots_last;            // slots per row of an LM head over one row per sequence
     float2* rope_cs;
     float* x; void* u; void* q; void* o;
@@ -79,6 +81,10 @@ struct SampleArgs {
 };
 
 bool fwd_dims(const cad_layer_desc* L, int B, int Nq, int mode, int W, int D, int cap, FwdDims* fd);
+// the one-layer span forward of cad_span_forward (argument checks, launches) over a given workspace
+int span_forward_internal(const cad_layer_desc* L, const cad_kv_desc* kv, const int32_t* tokens, int B, int Nq,
+                          int mode, int W, int D, int flags, int32_t* argmax_out, void* hidden_out, float* logits_out,
+                          float* top2_gap, void* workspace, size_t workspace_bytes, hipStream_t stream);
 FwdBufs fwd_carve(const FwdDims& fd, void* base, bool kv_only);
 
 // number of compute units of the current device (cached per device)
@@ -89,8 +95,9 @@ hipError_t launch_embed_norm(const FwdDims& fd, const int32_t* tokens, const voi
                              const RopeFreqs& freqs, const int32_t* kv_len, int32_t* err, const FwdBufs& wb,
                              hipStream_t s);
 // argmax over the LM head's slots of `rows` rows: all M rows, or (last_only) one per sequence
+// (top2_gap, nullable: largest minus second-largest logit of each row, from the runner-up slots)
 hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, bool last_only, int32_t* argmax_out,
-                               int32_t* kv_len, hipStream_t s);
+                               float* top2_gap, int32_t* kv_len, hipStream_t s);
 // normed rows are written for every row, or (last_only) compactly for each sequence's last row
 // argmax over each row's allowed ids (final normed rows wb.u3 against those LM-head rows),
 // with the commit of the cache lengths
@@ -126,6 +133,9 @@ hipError_t launch_commit(const FwdDims& fd, const FwdBufs& wb, int32_t* kv_len, 
 hipError_t launch_ngram(const int32_t* ctx, int64_t stride, const int32_t* ctx_len, int B, int n_hi, int n_lo,
                         int W, int D, int with_current, int32_t* draft, int32_t* draft_len, int32_t* match_pos,
                         int32_t* match_n, hipStream_t s);
+// block-verify commit of layers 1 .. n_layers-1 of a stack after launch_accept committed kvs[0]
+hipError_t launch_compact_layers(const cad_kv_desc* kvs, int n_layers, int B, int D, const int32_t* accepted,
+                                 const int32_t* best_w, const int32_t* n_emitted, hipStream_t s);
 hipError_t launch_accept(const int32_t* draft, int with_current, const int32_t* draft_len, const int32_t* pred,
                          const int32_t* first_pred, int B, int W, int D, int mode, int32_t* accepted,
                          int32_t* best_w, int32_t* emitted, int32_t* n_emitted, int32_t* ctx, int64_t ctx_stride,

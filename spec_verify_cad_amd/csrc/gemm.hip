@@ -76,7 +76,7 @@ __device__ void tile_epilogue(const float* C, int ldc, int m0, int n0, int BM, i
         const int tpr = blockDim.x / BM;         // threads per row (power of two, <= 64)
         const int r = threadIdx.x / tpr, sub = threadIdx.x % tpr;
         const int row = m0 + r;
-        float best = -INFINITY;
+        float best = -INFINITY, second = -INFINITY;
         int bi = 0x7fffffff;
         const bool live = row < p.M && seq_ok(p.len_snap, row / p.Nq, p.Nq, p.cap);
         if (live) {
@@ -84,6 +84,7 @@ __device__ void tile_epilogue(const float* C, int ldc, int m0, int n0, int BM, i
                 const int F = n0 + f;
                 if (F >= p.N) break;
                 const float v = C[r * ldc + f];
+                second = fmaxf(second, fminf(best, v));
                 if (v > best) { best = v; bi = F; }                      // increasing F: first max kept
                 if (p.logits) p.logits[(size_t)row * p.N + F] = v;
             }
@@ -91,9 +92,13 @@ __device__ void tile_epilogue(const float* C, int ldc, int m0, int n0, int BM, i
         for (int o = tpr / 2; o > 0; o >>= 1) {
             const float v2 = __shfl_xor(best, o, 64);
             const int i2 = __shfl_xor(bi, o, 64);
+            second = second_merge(best, second, v2, __shfl_xor(second, o, 64));
             argmax_merge(best, bi, v2, i2);
         }
-        if (live && sub == 0) p.amax_part[(size_t)row * p.amax_slots + n0 / BN] = make_float2(best, __int_as_float(bi));
+        if (live && sub == 0) {
+            p.amax_part[(size_t)row * p.amax_slots + n0 / BN] = make_float2(best, __int_as_float(bi));
+            if (p.amax_sec) p.amax_sec[(size_t)row * p.amax_slots + n0 / BN] = second;
+        }
     }
 }
 

@@ -44,11 +44,7 @@ __host__ __device__ inline int bal_chunks(int N, int G, int BN) {
 
 template <int KIND, int BN, int BM, int WN, int WM, int BK>
 struct BigCfg {
-#ifndef BIG_SWZ
-#define BIG_SWZ 1
-#endif
-    static constexpr int SWZ = BIG_SWZ;
-    static constexpr int LDK = SWZ ? BK : BK + 8;             // LDS row pitch: 16 bytes of padding
+    static constexpr int LDK = BK;                            // LDS row pitch (XOR-swizzled chunks)
     static constexpr int WTN = BN / WN, WTM = BM / WM;        // wave tile (features, tokens)
     static constexpr int FT = WTN / 16, TT = WTM / 16;
     static constexpr int NT = WN * WM * 64;                   // threads
@@ -122,7 +118,8 @@ __device__ __forceinline__ void qkv_epilogue(const f32x4_t (&acc)[FT][TT], const
     }
 }
 
-// BAL: 0 = column tiles, 1 = balanced ranges, 2 = balanced ranges that also write the logits
+// BAL: 0 = column tiles, 1 = balanced ranges, 2 = balanced ranges with the debug outputs (logits
+// and/or the runner-up values of the top-2 gap)
 template <int KIND, int BN, int BM, int WN, int WM, int BK, int RS, int BAL>
 __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                      int M, int N, int K, int nmt, int nnt, int S, int ffn,
@@ -188,13 +185,10 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
             if constexpr (RS > 1) __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // 16-byte chunk position of chunk c of tile row r (rows are 16-aligned in every read, so
-    // r mod 16 is all the swizzle needs)
-    auto sw = [](int r, int c) {
-        if constexpr (C::SWZ == 1) return c ^ (r & 7);
-        else if constexpr (C::SWZ == 2) return c ^ ((r >> 1) & 7);
-        else return c;
-    };
+    // 16-byte chunk position of chunk c of tile row r: the chunk index XOR the row's low three
+    // bits, so the 16 rows an MFMA fragment read touches spread over every bank group (rows are
+    // 16-aligned in every read, so r mod 16 is all the swizzle needs)
+    auto sw = [](int r, int c) { return c ^ (r & 7); };
     auto masked = [](uint4 t, uint32_t ok) {
         const uint32_t m = 0u - ok;
         return make_uint4(t.x & m, t.y & m, t.z & m, t.w & m);
@@ -257,6 +251,7 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
         // range nt of nnt: vocabulary rows [r0, r1), chunk c = rows r0 + c*BN + (0..BN-1)
         static_assert(KIND == EPI_ARGMAX, "balanced ranges are an LM-head schedule");
         __shared__ float2 bred[BAL_MAX_CHUNKS][WN][BM];
+        __shared__ float bsec[BAL == 2 ? BAL_MAX_CHUNKS : 1][WN][BM];   // runner-up values (debug form)
         const int NB = (N + 15) >> 4;
         const int r0 = (int)((long long)nt * NB / nnt) * 16;
         const int r1 = min(N, (int)((long long)(nt + 1) * NB / nnt) * 16);
@@ -301,7 +296,7 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
                 const int tok = m0 + wm * C::WTM + tt * 16 + l16;
-                float best = -INFINITY;
+                float best = -INFINITY, second = -INFINITY;
                 int bi = 0x7fffffff;
                 if (tok < M) {
 #pragma unroll
@@ -311,8 +306,10 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
                             const int n = rb + wn * C::WTN + ft * 16 + g4 * 4 + i;   // increasing along the lane
                             if (n < r1) {
                                 const float v = acc[ft][tt][i];
+                                if constexpr (BAL == 2) second = fmaxf(second, fminf(best, v));
                                 if (v > best) { best = v; bi = n; }
-                                if constexpr (BAL == 2) p.logits[(size_t)tok * N + n] = v;
+                                if constexpr (BAL == 2)
+                                    if (p.logits) p.logits[(size_t)tok * N + n] = v;
                             }
                         }
                 }
@@ -320,9 +317,13 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
                 for (int o = 16; o <= 32; o <<= 1) {
                     const float v2 = __shfl_xor(best, o, 64);
                     const int i2 = __shfl_xor(bi, o, 64);
+                    if constexpr (BAL == 2) second = second_merge(best, second, v2, __shfl_xor(second, o, 64));
                     argmax_merge(best, bi, v2, i2);
                 }
-                if (g4 == 0) bred[cc][wn][wm * C::WTM + tt * 16 + l16] = make_float2(best, __int_as_float(bi));
+                if (g4 == 0) {
+                    bred[cc][wn][wm * C::WTM + tt * 16 + l16] = make_float2(best, __int_as_float(bi));
+                    if constexpr (BAL == 2) bsec[cc][wn][wm * C::WTM + tt * 16 + l16] = second;
+                }
             }
         };
         Stage r[RS];
@@ -354,12 +355,17 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
             for (int rr = tid; rr < BM; rr += NT) {
                 const int tok = m0 + rr;
                 if (tok >= M || !seq_ok(p.len_snap, tok / p.Nq, p.Nq, p.cap)) continue;
-                float best = -INFINITY;
+                float best = -INFINITY, second = -INFINITY;
                 int bi = 0x7fffffff;
                 if (cc < nch)
 #pragma unroll
-                    for (int w = 0; w < WN; ++w) argmax_merge(best, bi, bred[cc][w][rr].x, __float_as_int(bred[cc][w][rr].y));
+                    for (int w = 0; w < WN; ++w) {
+                        if constexpr (BAL == 2) second = second_merge(best, second, bred[cc][w][rr].x, bsec[cc][w][rr]);
+                        argmax_merge(best, bi, bred[cc][w][rr].x, __float_as_int(bred[cc][w][rr].y));
+                    }
                 p.amax_part[(size_t)tok * p.amax_slots + nt * cpw + cc] = make_float2(best, __int_as_float(bi));
+                if constexpr (BAL == 2)
+                    if (p.amax_sec) p.amax_sec[(size_t)tok * p.amax_slots + nt * cpw + cc] = second;
             }
         return;
     }
@@ -459,10 +465,12 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
         }
     } else {                                                 // EPI_ARGMAX
         __shared__ float2 red[WN][BM];
+        __shared__ float rsec[WN][BM];                         // runner-up values (top-2 gap asked)
+        const bool top2 = p.amax_sec != nullptr;
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             const int tok = m0 + wm * C::WTM + tt * 16 + l16;
-            float best = -INFINITY;
+            float best = -INFINITY, second = -INFINITY;
             int bi = 0x7fffffff;
             if (tok < M) {
 #pragma unroll
@@ -472,6 +480,7 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
                         const int n = fbase + ft * 16 + g4 * 4 + i;       // increasing along the lane
                         if (n < N) {
                             const float v = acc[ft][tt][i];
+                            if (top2) second = fmaxf(second, fminf(best, v));
                             if (v > best) { best = v; bi = n; }
                             if (p.logits) p.logits[(size_t)tok * N + n] = v;
                         }
@@ -481,19 +490,27 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
             for (int o = 16; o <= 32; o <<= 1) {
                 const float v2 = __shfl_xor(best, o, 64);
                 const int i2 = __shfl_xor(bi, o, 64);
+                if (top2) second = second_merge(best, second, v2, __shfl_xor(second, o, 64));
                 argmax_merge(best, bi, v2, i2);
             }
-            if (g4 == 0) red[wn][wm * C::WTM + tt * 16 + l16] = make_float2(best, __int_as_float(bi));
+            if (g4 == 0) {
+                red[wn][wm * C::WTM + tt * 16 + l16] = make_float2(best, __int_as_float(bi));
+                if (top2) rsec[wn][wm * C::WTM + tt * 16 + l16] = second;
+            }
         }
         __syncthreads();
         for (int r = tid; r < BM; r += NT) {
             const int tok = m0 + r;
             if (tok >= M || !seq_ok(p.len_snap, tok / p.Nq, p.Nq, p.cap)) continue;
-            float best = red[0][r].x;
+            float best = red[0][r].x, second = top2 ? rsec[0][r] : -INFINITY;
             int bi = __float_as_int(red[0][r].y);
 #pragma unroll
-            for (int w = 1; w < WN; ++w) argmax_merge(best, bi, red[w][r].x, __float_as_int(red[w][r].y));
+            for (int w = 1; w < WN; ++w) {
+                if (top2) second = second_merge(best, second, red[w][r].x, rsec[w][r]);
+                argmax_merge(best, bi, red[w][r].x, __float_as_int(red[w][r].y));
+            }
             p.amax_part[(size_t)tok * p.amax_slots + nt] = make_float2(best, __int_as_float(bi));
+            if (top2) p.amax_sec[(size_t)tok * p.amax_slots + nt] = second;
         }
     }
 }
@@ -598,12 +615,14 @@ hipError_t big_dispatch(const void* A, const void* W, int M, int N, int K, int s
             return go_big<KIND, 192, 256, 2, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
         }
     if constexpr (KIND == EPI_ARGMAX) {
+        // debug outputs (logits, runner-up values) have an instantiation of their own
+        const bool dbg = p.logits || p.amax_sec;
         if (t.bal && t.BM == 64)
-            return p.logits ? go_big<KIND, 256, 64, 2, 4, 64, BAL_RS64, 2>(A, W, M, N, K, ffn, t, p, s)
-                            : go_big<KIND, 256, 64, 2, 4, 64, BAL_RS64, 1>(A, W, M, N, K, ffn, t, p, s);
+            return dbg ? go_big<KIND, 256, 64, 2, 4, 64, BAL_RS64, 2>(A, W, M, N, K, ffn, t, p, s)
+                       : go_big<KIND, 256, 64, 2, 4, 64, BAL_RS64, 1>(A, W, M, N, K, ffn, t, p, s);
         if (t.bal)
-            return p.logits ? go_big<KIND, 256, 128, 2, 4, 64, BAL_RS128, 2>(A, W, M, N, K, ffn, t, p, s)
-                            : go_big<KIND, 256, 128, 2, 4, 64, BAL_RS128, 1>(A, W, M, N, K, ffn, t, p, s);
+            return dbg ? go_big<KIND, 256, 128, 2, 4, 64, BAL_RS128, 2>(A, W, M, N, K, ffn, t, p, s)
+                       : go_big<KIND, 256, 128, 2, 4, 64, BAL_RS128, 1>(A, W, M, N, K, ffn, t, p, s);
     }
     switch (t.BM) {
         case 64: return go_big<KIND, 256, 64, 2, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);

@@ -88,6 +88,7 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
 
     float best = -INFINITY;                           // LM head: this lane's running (max, index)
     int bidx = 0x7fffffff;
+    float second = -INFINITY;                         // and runner-up value
     SampleState sst;                                  // sampled LM head: this lane's running state
     SampleRow srow;
     if constexpr (KIND == EPI_SAMPLE) {
@@ -126,6 +127,7 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
                 for (int i = 0; i < 4; ++i) {
                     const int n = tile * 16 + g4 * 4 + i;
                     if (live && n < N) {
+                        second = fmaxf(second, fminf(best, c[i]));
                         if (c[i] > best) { best = c[i]; bidx = n; }   // n increases along a lane
                         if (p.logits) p.logits[(size_t)tok * N + n] = c[i];
                     }
@@ -231,11 +233,14 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
             for (int o = 16; o <= 32; o <<= 1) {
                 const float v2 = __shfl_xor(best, o, 64);
                 const int i2 = __shfl_xor(bidx, o, 64);
+                second = second_merge(best, second, v2, __shfl_xor(second, o, 64));
                 argmax_merge(best, bidx, v2, i2);
             }
             const int tok = wave * 16 + l16;
-            if (g4 == 0 && tok < M)
+            if (g4 == 0 && tok < M) {
                 p.amax_part[(size_t)tok * p.amax_slots + blockIdx.x] = make_float2(best, __int_as_float(bidx));
+                if (p.amax_sec) p.amax_sec[(size_t)tok * p.amax_slots + blockIdx.x] = second;
+            }
         }
     }
 }

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
         int a_best = 0, w_best = 0;
         if (mode == CAD_MASK_CAUSAL_SPAN) {
             const int32_t* pr = pred + (size_t)b * (1 + D);
-            const int dl = draft_len[b];
+            const int dl = min(max(draft_len[b], 0), D);          // a length past D reads no further
             int a = 0;
             while (a < dl && drow[a] == pr[a]) ++a;
             a_best = a;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
             const int32_t* pr = pred + (size_t)b * W * D;
             const int fp = first_pred[b];
             for (int w = 0; w < W; ++w) {
-                const int dl = draft_len[b * W + w];
+                const int dl = min(max(draft_len[b * W + w], 0), D);
                 int a = 0;
                 while (a < dl && drow[w * D + a] == (a == 0 ? fp : pr[w * D + a - 1])) ++a;
                 if (a > a_best) { a_best = a; w_best = w; }
@@ -170,8 +170,18 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
         slen = kl;
     }
     __syncthreads();
+    if (sskip) {
+        // a skipped sequence reports nothing accepted and nothing emitted (n_emitted = 0 marks it:
+        // a sequence that ran always emits at least one token); its lengths stay unchanged
+        for (int e = tid; e <= D; e += 256) emitted[(size_t)b * (D + 1) + e] = 0;
+        if (tid == 0) {
+            accepted[b] = 0;
+            if (best_w) best_w[b] = 0;
+            n_emitted[b] = 0;
+        }
+        return;
+    }
     const int a = sa, w = sw;
-    if (sskip) return;
     for (int e = tid; e <= D; e += 256) emitted[(size_t)b * (D + 1) + e] = e <= a ? em[e] : 0;
     if (ctx)
         for (int e = tid; e <= a; e += 256) ctx[(size_t)b * ctx_stride + sctx + e] = em[e];
@@ -208,7 +218,58 @@ __global__ __launch_bounds__(256) void k_accept(const int32_t* __restrict__ draf
     }
 }
 
+// Block-verify commit of the other layers of a stack: after k_accept has committed the first
+// layer (accepted[b] = a*, best_w[b] = w*, kv_len[b] = len + a*; n_emitted[b] = 0 for a skipped
+// sequence), the winner's first a* K/V slots of each further layer move from len + w*D + j to
+// len + j, exactly as k_accept moved the first layer's.  Grid: (B, layers of this launch).
+constexpr int CL_MAX = 16;
+struct LayerKV { void* k[CL_MAX]; void* v[CL_MAX]; };
+__global__ __launch_bounds__(256) void k_compact_layers(LayerKV lk, const int32_t* __restrict__ accepted,
+                                                        const int32_t* __restrict__ best_w,
+                                                        const int32_t* __restrict__ n_emitted,
+                                                        const int32_t* __restrict__ kv_len, int D, int Hkv, int d,
+                                                        int esz, int cap) {
+    const int b = blockIdx.x, l = blockIdx.y, tid = threadIdx.x;
+    const int a = accepted[b], w = best_w[b];
+    if (n_emitted[b] == 0 || a <= 0 || w <= 0) return;
+    const int len = kv_len[b] - a;
+    if (len < 0 || len + (size_t)(w + 1) * D > (size_t)cap) return;   // not a length k_accept committed
+    uint4* kb = (uint4*)lk.k[l];
+    const int per_row = d * esz / 16;
+    for (int e = tid; e < Hkv * a * per_row; e += 256) {
+        const int g = e / (a * per_row), j = (e / per_row) % a, ck = e % per_row;
+        const size_t head = ((size_t)b * Hkv + g) * cap;
+        kb[(head + len + j) * per_row + ck] = kb[(head + len + (size_t)w * D + j) * per_row + ck];
+    }
+    for (int e = tid; e < Hkv * d * a; e += 256) {
+        const int g = e / (d * a), dim = (e / a) % d, j = e % a;
+        const size_t row = (((size_t)b * Hkv + g) * d + dim) * cap;
+        if (esz == 2)
+            ((uint16_t*)lk.v[l])[row + len + j] = ((const uint16_t*)lk.v[l])[row + len + (size_t)w * D + j];
+        else
+            ((float*)lk.v[l])[row + len + j] = ((const float*)lk.v[l])[row + len + (size_t)w * D + j];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_compact_layers(const cad_kv_desc* kvs, int n_layers, int B, int D, const int32_t* accepted,
+                                 const int32_t* best_w, const int32_t* n_emitted, hipStream_t s) {
+    const int esz = kvs[0].dtype == CAD_DTYPE_F32 ? 4 : 2;
+    for (int l0 = 1; l0 < n_layers; l0 += CL_MAX) {
+        LayerKV lk;
+        const int n = n_layers - l0 < CL_MAX ? n_layers - l0 : CL_MAX;
+        for (int i = 0; i < CL_MAX; ++i) {
+            lk.k[i] = i < n ? kvs[l0 + i].k : nullptr;
+            lk.v[i] = i < n ? kvs[l0 + i].v : nullptr;
+        }
+        hipLaunchKernelGGL(k_compact_layers, dim3(B, n), dim3(256), 0, s, lk, accepted, best_w, n_emitted, kvs[0].len,
+                           D, kvs[0].n_kv_heads, kvs[0].head_dim, esz, kvs[0].cap);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_ngram(const int32_t* ctx, int64_t stride, const int32_t* ctx_len, int B, int n_hi, int n_lo,
                         int W, int D, int with_current, int32_t* draft, int32_t* draft_len, int32_t* match_pos,

@@ -1,7 +1,8 @@
 // Row-wise kernels of the span forward.
 //
 // k_embed_norm  first kernel of every forward: captures the per-sequence cache length the
-//               rest of the forward uses (flagging sequences that would overflow), gathers the
+//               rest of the forward uses (flagging sequences that would overflow or hold a token
+//               id outside the vocabulary), gathers the
 //               embedding rows, applies RMSNorm and tabulates the (cos, sin) of each row's
 //               rotary angles p * base^(-2i/d) (Copy-as-Decode, Appendix K: the rows take the
 //               absolute positions N sequential decode steps would have).  The angle is formed
@@ -52,11 +53,23 @@ __global__ __launch_bounds__(NT) void k_embed_norm(const int32_t* __restrict__ t
     const int r = blockIdx.x, b = r / Nq, it = r % Nq;
     const int len = kv_len[b];
     const bool ok = len >= 0 && len + Nq <= cap;
-    if (it == 0 && threadIdx.x == 0) {
-        len_snap[b] = ok ? len : -1;
-        if (!ok && err) err[b] = CAD_ECAPACITY;
+    const int t = tokens[r];
+    if (it == 0) {
+        // the sequence's first row also checks every token id of the sequence: one outside
+        // [0, vocab) flags the sequence and makes its whole forward a no-op
+        int bad = 0;
+        for (int j = threadIdx.x; j < Nq; j += NT) {
+            const int tj = tokens[(size_t)b * Nq + j];
+            bad |= tj < 0 || tj >= vocab;
+        }
+        const int bad_tok = __syncthreads_or(bad);
+        if (threadIdx.x == 0) {
+            len_snap[b] = ok && !bad_tok ? len : -1;
+            if (err && !ok) err[b] = CAD_ECAPACITY;
+            else if (err && bad_tok) err[b] = CAD_EINVAL;
+        }
     }
-    if (!ok) return;
+    if (!ok || t < 0 || t >= vocab) return;
     if (rope_cs) {
         const int pos = len + (mode == CAD_MASK_BLOCK_TRI ? it % Dblk : it);
         for (int i = threadIdx.x; i < half; i += NT) {
@@ -69,8 +82,6 @@ __global__ __launch_bounds__(NT) void k_embed_norm(const int32_t* __restrict__ t
             rope_cs[(size_t)r * half + i] = make_float2(cn, sn);
         }
     }
-    int t = tokens[r];
-    t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
     const T* e = embed + (size_t)t * h;
     // the row is read once, four elements per thread per pass, and kept in registers
     constexpr int QMAX = 8;                        // h <= 4 * NT * QMAX
@@ -321,31 +332,45 @@ __global__ __launch_bounds__(64) void k_sample_final(const float4* __restrict__ 
 
 // One wave per row.  The LM head ran on rps rows per sequence (Nq, or 1 for the last row only):
 // row r belongs to sequence b = r / rps, and the wave of the sequence's first row commits.
-__global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ part, int slots, int rps, int Nq,
-                                                     int cap, const int32_t* __restrict__ len_snap,
-                                                     int32_t* __restrict__ out, int32_t* __restrict__ kv_len) {
+// With top2_gap, the runner-up slots (sec) are merged too and the row's largest minus
+// second-largest logit is written.
+template <bool GAP>
+__global__ __launch_bounds__(64) void k_argmax_final(const float2* __restrict__ part, const float* __restrict__ sec,
+                                                     int slots, int rps, int Nq, int cap,
+                                                     const int32_t* __restrict__ len_snap, int32_t* __restrict__ out,
+                                                     float* __restrict__ gap, int32_t* __restrict__ kv_len) {
     const int r = blockIdx.x, b = r / rps;
     if (!seq_ok(len_snap, b, Nq, cap)) return;
-    float best = -INFINITY;
+    float best = -INFINITY, second = -INFINITY;
     int bi = 0x7fffffff;
     // slots lane, lane + 64, ... with the loads of FB of them in flight at once (clamped
     // addresses, surplus ones not merged)
     for (int t0 = 0; t0 < slots; t0 += 64 * FB) {
         float2 pv[FB];
+        float sv[FB];
 #pragma unroll
-        for (int u = 0; u < FB; ++u) pv[u] = part[(size_t)r * slots + min(t0 + (int)threadIdx.x + 64 * u, slots - 1)];
+        for (int u = 0; u < FB; ++u) {
+            const size_t i = (size_t)r * slots + min(t0 + (int)threadIdx.x + 64 * u, slots - 1);
+            pv[u] = part[i];
+            if constexpr (GAP) sv[u] = sec[i];
+        }
 #pragma unroll
         for (int u = 0; u < FB; ++u)
-            if (t0 + (int)threadIdx.x + 64 * u < slots) argmax_merge(best, bi, pv[u].x, __float_as_int(pv[u].y));
+            if (t0 + (int)threadIdx.x + 64 * u < slots) {
+                if constexpr (GAP) second = second_merge(best, second, pv[u].x, sv[u]);
+                argmax_merge(best, bi, pv[u].x, __float_as_int(pv[u].y));
+            }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const float v2 = __shfl_xor(best, o, 64);
         const int i2 = __shfl_xor(bi, o, 64);
+        if constexpr (GAP) second = second_merge(best, second, v2, __shfl_xor(second, o, 64));
         argmax_merge(best, bi, v2, i2);
     }
     if (threadIdx.x == 0) {
         out[r] = bi;
+        if constexpr (GAP) gap[r] = best - second;
         if (kv_len && r % rps == 0) kv_len[b] = len_snap[b] + Nq;
     }
 }
@@ -399,11 +424,15 @@ hipError_t launch_resid_norm(const FwdDims& fd, const float* base, const float* 
 }
 
 hipError_t launch_argmax_final(const FwdDims& fd, const FwdBufs& wb, bool last_only, int32_t* argmax_out,
-                               int32_t* kv_len, hipStream_t s) {
+                               float* top2_gap, int32_t* kv_len, hipStream_t s) {
     const int rps = last_only ? 1 : fd.Nq;
     const int slots = last_only ? wb.amax_slots_last : wb.amax_slots;
-    hipLaunchKernelGGL(k_argmax_final, dim3(fd.B * rps), dim3(64), 0, s, wb.amax_part, slots, rps, fd.Nq, fd.cap,
-                       wb.len_snap, argmax_out, kv_len);
+    if (top2_gap)
+        hipLaunchKernelGGL(k_argmax_final<true>, dim3(fd.B * rps), dim3(64), 0, s, wb.amax_part, wb.amax_sec, slots,
+                           rps, fd.Nq, fd.cap, wb.len_snap, argmax_out, top2_gap, kv_len);
+    else
+        hipLaunchKernelGGL(k_argmax_final<false>, dim3(fd.B * rps), dim3(64), 0, s, wb.amax_part, nullptr, slots,
+                           rps, fd.Nq, fd.cap, wb.len_snap, argmax_out, nullptr, kv_len);
     return hipGetLastError();
 }
 

@@ -86,3 +86,18 @@ def stack_forward_flops(s, n_layers: int, B: int, N: int, L: int, last_only: boo
     lm_rows = B * (1 if last_only else N)
     return (2.0 * B * N * n_layers * s.layer_params() + 2.0 * lm_rows * s.lm_params()
             + 4.0 * n_layers * B * visible_keys_causal(L, N) * s.n_q_heads * s.head_dim)
+
+
+def med_iqr(samples) -> dict:
+    """Median and interquartile range of timing samples (linear-interpolated quartiles), with
+    the sample count."""
+    xs = sorted(float(x) for x in samples)
+    n = len(xs)
+
+    def q(p):
+        t = p * (n - 1)
+        i = int(t)
+        return xs[i] if i + 1 >= n else xs[i] + (xs[i + 1] - xs[i]) * (t - i)
+
+    return {"median": round(q(0.5), 2), "q1": round(q(0.25), 2), "q3": round(q(0.75), 2),
+            "iqr": round(q(0.75) - q(0.25), 2), "n": n}

@@ -10,7 +10,8 @@ from spec_verify_cad_amd import cad
 def test_header_declares_the_three_calls():
     names = cad.header_functions()
     for n in ("cad_ngram_lookup", "cad_span_forward", "cad_accept_scan", "cad_span_forward_workspace",
-              "cad_span_forward_allowed", "cad_ngram_lookup_longest", "cad_status_string", "cad_version"):
+              "cad_span_forward_allowed", "cad_ngram_lookup_longest", "cad_status_string", "cad_version",
+              "cad_stack_accept_scan"):
         assert n in names
 
 
@@ -46,21 +47,21 @@ def test_host_argument_errors_return_before_launch():
     kv = cad.KVDesc(1, 1, 1, 1, 1, 160, 4, 64, cad.DTYPE_BF16)
     tok = ctypes.c_void_p(1)
     # null layer / tokens
-    assert L.cad_span_forward(None, ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, tok, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
-    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), None, 1, 8, 0, 1, 1, 0, tok, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
+    assert L.cad_span_forward(None, ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, tok, None, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
+    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), None, 1, 8, 0, 1, 1, 0, tok, None, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
     # cache geometry that does not match the layer
     bad = cad.KVDesc(1, 1, 1, 1, 1, 160, 2, 64, cad.DTYPE_BF16)
-    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(bad), tok, 1, 8, 0, 1, 1, 0, tok, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
+    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(bad), tok, 1, 8, 0, 1, 1, 0, tok, None, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
     # unsupported head_dim
     d2 = _desc(head_dim=48)
     kv2 = cad.KVDesc(1, 1, 1, 1, 1, 160, 4, 48, cad.DTYPE_BF16)
-    assert L.cad_span_forward(ctypes.byref(d2), ctypes.byref(kv2), tok, 1, 8, 0, 1, 1, 0, tok, None, None, tok, 1 << 30, None) == cad.CAD_EUNSUPPORTED
+    assert L.cad_span_forward(ctypes.byref(d2), ctypes.byref(kv2), tok, 1, 8, 0, 1, 1, 0, tok, None, None, None, tok, 1 << 30, None) == cad.CAD_EUNSUPPORTED
     # workspace too small / misaligned
-    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, tok, None, None, ctypes.c_void_p(256), 16, None) == cad.CAD_EWORKSPACE
-    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, tok, None, None, ctypes.c_void_p(8), 1 << 30, None) == cad.CAD_EWORKSPACE
+    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, tok, None, None, None, ctypes.c_void_p(256), 16, None) == cad.CAD_EWORKSPACE
+    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, tok, None, None, None, ctypes.c_void_p(8), 1 << 30, None) == cad.CAD_EWORKSPACE
     # unknown flag, missing argmax output
-    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 8, tok, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
-    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, None, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
+    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 8, tok, None, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
+    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, None, None, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
     # grammar-masked forward: null set / output, set size, flags it does not take
     fa = L.cad_span_forward_allowed
     assert fa(ctypes.byref(d), ctypes.byref(kv), tok, 1, 1, 0, None, 4, tok, None, None, tok, 1 << 30, None) == cad.CAD_EINVAL
@@ -77,3 +78,20 @@ def test_host_argument_errors_return_before_launch():
     assert L.cad_ngram_lookup(tok, 16, tok, 1, 3, 1, 65, 0, tok, tok, None, None) == cad.CAD_EUNSUPPORTED
     assert L.cad_accept_scan(tok, 1, tok, tok, None, 1, 2, 4, cad.MASK_CAUSAL, tok, None, tok, tok, None, 0, None, 0, None, None) == cad.CAD_EINVAL
     assert L.cad_accept_scan(tok, 0, tok, tok, None, 1, 2, 4, cad.MASK_BLOCK, tok, None, tok, tok, None, 0, None, 0, None, None) == cad.CAD_EINVAL
+    # stack accept: no caches, no layers, block mode through several layers without best_w,
+    # caches of another geometry
+    sa = L.cad_stack_accept_scan
+    kvs = (cad.KVDesc * 2)(cad.KVDesc(1, 1, 1, 1, 1, 160, 4, 64, cad.DTYPE_BF16),
+                           cad.KVDesc(1, 1, 1, 1, 1, 160, 4, 64, cad.DTYPE_BF16))
+    assert sa(tok, 0, tok, tok, tok, 1, 2, 4, cad.MASK_BLOCK, tok, tok, tok, tok, None, 0, None, 0, None, 2,
+              None) == cad.CAD_EINVAL
+    assert sa(tok, 0, tok, tok, tok, 1, 2, 4, cad.MASK_BLOCK, tok, tok, tok, tok, None, 0, None, 0, kvs, 0,
+              None) == cad.CAD_EINVAL
+    assert sa(tok, 0, tok, tok, tok, 1, 2, 4, cad.MASK_BLOCK, tok, None, tok, tok, None, 0, None, 0, kvs, 2,
+              None) == cad.CAD_EINVAL
+    kvs[1].head_dim = 32
+    assert sa(tok, 0, tok, tok, tok, 1, 2, 4, cad.MASK_BLOCK, tok, tok, tok, tok, None, 0, None, 0, kvs, 2,
+              None) == cad.CAD_EINVAL
+    kvs[1].head_dim = 64
+    assert sa(tok, 1, tok, tok, None, 1, 2, 4, cad.MASK_CAUSAL, tok, None, tok, tok, None, 0, None, 0, kvs, 2,
+              None) == cad.CAD_EINVAL                            # causal mode takes W = 1

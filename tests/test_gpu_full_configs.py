@@ -2,7 +2,9 @@
 
 Each test runs a workload at its configured size in the launch configuration bench.py uses
 (same caches, capacities, spans and batch), then checks sampled outputs against the oracle and
-properties that hold at any size:
+properties that hold at any size.  Floating-point outputs are bounded by the distance of an ideal
+fp32-accumulating pipeline (tests/ideal_fp32.py) to the oracle on the same inputs; decisions made
+without written logits use the largest such distance over the replayed rows of the workload:
   * copy-span sweep, 1.5B-shaped layer, L = 2048, N in {8 .. 512} (every committed row);
   * block-triangular verify, 7B-shaped layer, L = 4096, W = 4 candidates of D = 8, plus a planted
     greedy candidate that exercises the acceptance and the K/V compaction;
@@ -23,7 +25,9 @@ from spec_verify_cad_amd.program import DeviceProgram
 from spec_verify_cad_amd.configs import (CONFIGS, block_verify_context, cad_program_inputs, copy_sweep_inputs,
                                          pld_contexts)
 
-from gpu_util import (NEAR_TIE, argmax_check, compare, compare_cache, log, logit_tol, prefill, run_forward)
+import ideal_fp32 as IF
+from gpu_util import (IDEAL_FACTOR, LOGIT_TOL, NEAR_TIE, argmax_check, compare, compare_cache, ideal_tols, log,
+                      logit_tol, prefill, run_forward)
 from helpers import oracle_layer
 
 pytestmark = pytest.mark.gpu
@@ -63,6 +67,7 @@ def test_copy_span_sweep_full_size(qwen15):
     cad.span_forward(dl, cache, T32(prefix[None]), L0, flags=cad.KV_ONLY | cad.COMMIT_ALL)
     torch.cuda.synchronize()
     oc = O.cache_from_tokens(OL, prefix, cap)
+    ic = IF.cache_from_tokens(OL, prefix, cap)
     rows = np.r_[0:8, 1000:1008, L0 - 8:L0]
     for lo in rows[::8]:
         compare_cache(cache, 0, oc, int(lo), int(lo) + 8, "bf16", what=f"prefill rows {lo}")
@@ -72,7 +77,8 @@ def test_copy_span_sweep_full_size(qwen15):
         g = run_forward(dl, cache, toks[None], flags=cad.COMMIT_ALL)
         assert int(cache.len[0]) == L0 + N
         ref = O.span_forward(OL, oc.copy(), toks)
-        compare(g, ref, what=f"N={N}")
+        ideal = IF.span_forward(OL, ic.copy(), toks)
+        compare(g, ref, what=f"N={N}", ideal=ideal)
         # the bench's forward writes no logits (a kernel instantiation of its own at 33-128 rows)
         cache.len.fill_(L0)
         g0 = run_forward(dl, cache, toks[None], flags=cad.COMMIT_ALL, logits=False)
@@ -90,21 +96,23 @@ def test_copy_span_sweep_full_size(qwen15):
         assert int(cache.len[0]) == L0 + N
         last = {k: ref[k][N - 1:N] for k in ("logits", "argmax", "top2_gap")}
         g_l = lg.cpu().numpy().astype(np.float64)
-        assert np.max(np.abs(g_l - last["logits"])) <= logit_tol(wl.shape.hidden), f"N={N} copy-commit logits"
-        argmax_check(am.cpu().numpy(), last, g_l, what=f"N={N} copy-commit", tol=logit_tol(wl.shape.hidden))
+        ltol = ideal_tols(ref, ideal)[1]
+        assert np.max(np.abs(g_l - last["logits"])) <= ltol, f"N={N} copy-commit logits"
+        argmax_check(am.cpu().numpy(), last, g_l, what=f"N={N} copy-commit", tol=ltol)
         compare_cache(cache, 0, c2, L0, L0 + N, "bf16", what=f"N={N} copy-commit rows")
 
 
 # ---------------------------------------------------------------------------------------------
 # config 4: block-triangular multi-candidate verify
 # ---------------------------------------------------------------------------------------------
-def _block_round(dl, OL, cache, oc, hist, cands, dlen, first_pred, W, D, what):
+def _block_round(dl, OL, cache, oc, ic, hist, cands, dlen, first_pred, W, D, what):
     """One block verify forward + accept on the GPU, checked against the oracle."""
     L = int(cache.len[0])
     g = run_forward(dl, cache, cands.reshape(1, -1), mode=cad.MASK_BLOCK, W=W, D=D)
     assert int(cache.len[0]) == L                        # a verify forward does not commit
     ref = O.span_forward(OL, oc.copy(), cands.reshape(-1), mode="block", W=W, D=D, commit=False)
-    compare(g, ref, what=what)
+    ideal = IF.span_forward(OL, ic.copy(), cands.reshape(-1), mode="block", W=W, D=D, commit=False)
+    compare(g, ref, what=what, ideal=ideal)
     pred = g["argmax"]
     acc, bw, ne = (torch.full((1,), -1, dtype=torch.int32, device="cuda") for _ in range(3))
     em = torch.full((1, D + 1), -1, dtype=torch.int32, device="cuda")
@@ -135,11 +143,12 @@ def test_block_verify_full_size(qwen7):
     cache = cad.DeviceCache(wl.shape, 1, cap)
     log("block verify: prefill 4095 + anchor")
     prefill(dl, cache, ctx[None, :Lc - 1])
-    anchor = run_forward(dl, cache, ctx[None, Lc - 1:], flags=cad.COMMIT_ALL, logits=False)
+    anchor = run_forward(dl, cache, ctx[None, Lc - 1:], flags=cad.COMMIT_ALL)
     first_pred = int(anchor["argmax"][0])
     oc = O.cache_from_tokens(OL, ctx[:Lc - 1], cap)
+    ic = IF.cache_from_tokens(OL, ctx[:Lc - 1], cap)
     oa = O.span_forward(OL, oc, ctx[Lc - 1:])
-    argmax_check(anchor["argmax"], oa, what="anchor", tol=logit_tol(wl.shape.hidden))
+    compare(anchor, oa, what="anchor", ideal=IF.span_forward(OL, ic, ctx[Lc - 1:]))
     compare_cache(cache, 0, oc, Lc - 64, Lc, "bf16", what="anchor rows")
     # kappa-gram lookup of W recency-ranked candidates (bit-exact)
     hist = T32(ctx[None])
@@ -155,7 +164,7 @@ def test_block_verify_full_size(qwen7):
     assert (ol > 0).sum() == W
     cands = od.copy()
     log("block verify: retrieved candidates")
-    _block_round(dl, OL, cache, oc, hist, cands, ol, first_pred, W, D, "block retrieved")
+    _block_round(dl, OL, cache, oc, ic, hist, cands, ol, first_pred, W, D, "block retrieved")
     # planted agreement: candidate 2 becomes the oracle's greedy continuation from the anchor
     greedy, c = [first_pred], oc.copy()
     for _ in range(D - 1):
@@ -165,7 +174,7 @@ def test_block_verify_full_size(qwen7):
     ol2[2] = D
     cache.len.fill_(Lc)                                  # undo the first round's acceptance, if any
     log("block verify: planted greedy candidate")
-    ref, a, w = _block_round(dl, OL, cache, oc, hist, cands, ol2, first_pred, W, D, "block planted")
+    ref, a, w = _block_round(dl, OL, cache, oc, ic, hist, cands, ol2, first_pred, W, D, "block planted")
     # the planted candidate is accepted as far as the GPU's argmaxes are determined: its first
     # token is first_pred, and token j agrees with the oracle's (greedy) argmax of row (2, j-1)
     unique = ref["top2_gap"][2 * D:2 * D + D - 1] > 2 * logit_tol(wl.shape.hidden)
@@ -231,24 +240,40 @@ def test_pld_batch_rounds_full_size(qwen15, temperature):
     assert (hlen_h == Lc + (acc_h + 1).sum(0)).all() and (kv_h == hlen_h - 1).all()
     assert (dlen_h[0] > 0).all()                         # every sequence starts mid-copy
     # the oracle replays two sequences round by round, following the GPU's stream where an
-    # argmax was not determined (its choice is then checked to be a near-top one)
-    ltol = logit_tol(wl.shape.hidden)
-    firm_rows = 0
-    for b in ((0, 41) if temperature is None else (17,)):
-        log(f"pld: oracle replay of sequence {b}")
+    # argmax was not determined (its choice is then checked to be a near-top one).  The verify
+    # forwards write no logits, so the logit bound is the largest distance of the ideal fp32
+    # pipeline to the oracle over every replayed row, with the usual margin.
+    seqs = (0, 41) if temperature is None else (17,)
+    replay, worst = {}, 0.0
+    for b in seqs:
+        log(f"pld: oracle and ideal fp32 replay of sequence {b}")
         oc = O.cache_from_tokens(OL, ctxs[b][:Lc - 1], cap)
-        h = list(ctxs[b])
+        ic = IF.cache_from_tokens(OL, ctxs[b][:Lc - 1], cap)
+        h, rounds = list(ctxs[b]), []
         for r in range(R):
             d, l, _ = O.ngram_lookup(np.array(h), len(h), n, 1, k)
             assert rows_h[r, b, 0] == h[-1] and list(rows_h[r, b, 1:]) == list(d[0]) and dlen_h[r, b] == l[0], (b, r)
             toks = [h[-1]] + list(d[0])
             base = oc.length
             ref = O.span_forward(OL, oc, toks, commit=False)
+            worst = max(worst, float(np.max(np.abs(IF.span_forward(OL, ic, toks, commit=False)["logits"] -
+                                                   ref["logits"]))))
+            a = int(acc_h[r, b])
+            rounds.append((toks, base, ref, int(l[0]), d[0]))
+            h += list(d[0][:a]) + [int(pred_h[r, b, a])]
+            oc.length += a + 1
+            ic.length += a + 1
+        replay[b] = rounds
+    ltol = max(LOGIT_TOL, IDEAL_FACTOR * worst)
+    log(f"pld: ideal fp32 pipeline's largest logit distance {worst:.3e}; bound {ltol:.3e}")
+    firm_rows = 0
+    for b in seqs:
+        h = list(ctxs[b])
+        for r, (toks, base, ref, dl_, drow) in enumerate(replay[b]):
             if temperature is None:
                 argmax_check(pred_h[r, b], ref, None, what=f"pld b={b} r={r}", tol=ltol)
             else:
                 # decisions the logit error (at most ltol per logit) cannot flip must match
-                dl_ = int(l[0])
                 opred = O.sampled_predictions(ref["logits"], toks, dl_, temperature, PLD_SAMPLE_SEED, b, base)[0]
                 y_gap, z_gap, acc_m = O.sampled_margins(ref["logits"], toks, dl_, temperature, PLD_SAMPLE_SEED, b,
                                                         base)
@@ -259,10 +284,9 @@ def test_pld_batch_rounds_full_size(qwen15, temperature):
                         firm_rows += 1
                         assert pred_h[r, b, i] == opred[i], (b, r, i, pred_h[r, b, i], opred[i])
                     assert 0 <= pred_h[r, b, i] < wl.shape.vocab
-            a, emitted = O.accept_causal(d[0], int(l[0]), pred_h[r, b])
+            a, emitted = O.accept_causal(drow, dl_, pred_h[r, b])
             assert a == acc_h[r, b], (b, r)
             h += emitted
-            oc.length += a + 1
         np.testing.assert_array_equal(hist_h[b, :len(h)], h)
     if temperature is not None:
         assert firm_rows >= 0.9 * R * (1 + k)
@@ -305,14 +329,22 @@ def test_cad_program_full_size(qwen7):
         compare_cache(cache, 0, oc_all, lo, min(lo + 512, Ld + fed), "bf16", what=f"cache rows {lo}")
     # the forwards that feed the first 256 program tokens, replayed by the oracle: each decision
     # against the oracle's (masked) argmax on its last row
-    log("cad program: oracle replay of the first 256 fed tokens")
-    tol = logit_tol(wl.shape.hidden)
+    log("cad program: oracle and ideal fp32 replay of the first 256 fed tokens")
     oc = O.cache_from_tokens(OL, doc, cap)
-    pos, roles = 0, set()
+    ic = IF.cache_from_tokens(OL, doc, cap)
+    pos, replay, worst = 0, [], 0.0
     for f, pf in enumerate(fwds):
         if pos >= 256:
             break
         ref = O.span_forward(OL, oc, stream[pos:pos + pf.n])
+        il = IF.span_forward(OL, ic, stream[pos:pos + pf.n])["logits"]
+        worst = max(worst, float(np.max(np.abs(il - ref["logits"]))))
+        replay.append((f, pf, ref))
+        pos += pf.n
+    tol = max(LOGIT_TOL, IDEAL_FACTOR * worst)
+    log(f"cad program: ideal fp32 pipeline's largest logit distance {worst:.3e}; bound {tol:.3e}")
+    roles = set()
+    for f, pf, ref in replay:
         last = {k: ref[k][-1:] for k in ("logits", "argmax", "top2_gap")}
         if pf.allowed is None:
             argmax_check(dec[f:f + 1], last, None, what=f"forward {f} ({pf.role})", tol=tol)
@@ -325,5 +357,4 @@ def test_cad_program_full_size(qwen7):
                 lg = last["logits"][0]
                 assert lg[list(pf.allowed)].max() - lg[dec[f]] <= 2 * tol
         roles.add(pf.role)
-        pos += pf.n
     assert {"op_type", "copy_open", "line_char", "splice", "gen_open", "gen_body", "gen_close"} <= roles

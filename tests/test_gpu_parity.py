@@ -658,3 +658,125 @@ def test_forward_replays_from_a_hip_graph(small):
         for a, b in zip((am, hid, lg, cache.k, cache.v), eager):
             assert torch.equal(a, b), f"replay {rep}"
         assert int(cache.len[0]) == L0 + N
+
+
+# ------------------------------------------------------------------------- top-2 gap, bad ids, skipped accepts
+@pytest.mark.parametrize("B,Nq,last", [(1, 8, False), (3, 13, False), (1, 40, False), (1, 100, False),
+                                       (2, 150, False), (3, 13, True)])
+def test_top2_gap_matches_oracle(small, B, Nq, last):
+    """The top-2 gap output against the oracle's (largest minus second-largest logit).  Each logit
+    is within the row's measured error e of the oracle's, so the two largest are too and the gap
+    is within 2e; the rows cover the weight-streaming LM head (<= 32 rows), the balanced-range
+    tiled one (33-128) and the column-tile one (300 rows)."""
+    w, dl, OL = small
+    log(f"top2 gap B={B} Nq={Nq} last={last}")
+    L0, cap = 60, (60 + Nq + 4 + 3) // 4 * 4
+    ctx = np.stack([synth.uniform_tokens(700 + b, L0, SMALL.vocab) for b in range(B)])
+    span = np.stack([synth.uniform_tokens(710 + b, Nq, SMALL.vocab) for b in range(B)])
+    cache = cad.DeviceCache(SMALL, B, cap)
+    prefill(dl, cache, ctx, chunk=64)
+    R = B if last else B * Nq
+    t = torch.from_numpy(span.astype(np.int32)).cuda()
+    am = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    gap = torch.full((R,), -7.0, dtype=torch.float32, device="cuda")
+    lg = torch.zeros((R, SMALL.vocab), dtype=torch.float32, device="cuda")
+    flags = cad.COMMIT_ALL | (cad.LOGITS_LAST if last else 0)
+    cad.span_forward(dl, cache, t, Nq, flags=flags, argmax_out=am, logits_out=lg, top2_gap=gap)
+    # the same forward without logits (the hot instantiations) gives the same gap bits
+    cache.len.fill_(L0)
+    am2 = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    gap2 = torch.full((R,), -7.0, dtype=torch.float32, device="cuda")
+    cad.span_forward(dl, cache, t, Nq, flags=flags, argmax_out=am2, top2_gap=gap2)
+    torch.cuda.synchronize()
+    g_gap, g_l = gap.cpu().numpy().astype(np.float64), lg.cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(gap2.cpu().numpy(), gap.cpu().numpy())
+    np.testing.assert_array_equal(am2.cpu().numpy(), am.cpu().numpy())
+    # the gap is exactly the one the GPU's own logits give (an fp32 difference)
+    srt = np.sort(lg.cpu().numpy(), axis=1)
+    np.testing.assert_array_equal(gap.cpu().numpy(), srt[:, -1] - srt[:, -2])
+    for b in range(B):
+        ref = O.span_forward(OL, O.cache_from_tokens(OL, ctx[b], cap), span[b])
+        rows = slice(b, b + 1) if last else slice(b * Nq, (b + 1) * Nq)
+        ref_gap = ref["top2_gap"][Nq - 1:Nq] if last else ref["top2_gap"]
+        ref_l = ref["logits"][Nq - 1:Nq] if last else ref["logits"]
+        e = np.max(np.abs(g_l[rows] - ref_l), axis=1)
+        assert (np.abs(g_gap[rows] - ref_gap) <= 2 * e + 1e-12).all()
+
+
+def test_tiny_fp32_top2_gap_matches_oracle():
+    wl = CONFIGS["tiny_f32"]
+    w = synth.layer_weights(TINY, wl.seed)
+    OL, dl = oracle_layer(TINY, w), cad.DeviceLayer(TINY, w)
+    log("tiny fp32 top2 gap")
+    ctx = synth.uniform_tokens(720, 40, TINY.vocab)
+    span = synth.uniform_tokens(721, 8, TINY.vocab)
+    cache = cad.DeviceCache(TINY, 1, 64)
+    prefill(dl, cache, ctx[None], chunk=64)
+    t = torch.from_numpy(span[None].astype(np.int32)).cuda()
+    am = torch.zeros(8, dtype=torch.int32, device="cuda")
+    gap = torch.zeros(8, dtype=torch.float32, device="cuda")
+    lg = torch.zeros((8, TINY.vocab), dtype=torch.float32, device="cuda")
+    cad.span_forward(dl, cache, t, 8, argmax_out=am, logits_out=lg, top2_gap=gap)
+    torch.cuda.synchronize()
+    ref = O.span_forward(OL, O.cache_from_tokens(OL, ctx, 64), span)
+    e = np.max(np.abs(lg.cpu().numpy() - ref["logits"]), axis=1)
+    assert (np.abs(gap.cpu().numpy() - ref["top2_gap"]) <= 2 * e + 1e-9).all()
+
+
+def test_out_of_range_token_ids_flag_only_their_sequence(small):
+    """A sequence holding an id outside [0, vocab) is flagged CAD_EINVAL and left untouched (no
+    cache rows, no outputs, no commit); the other sequences of the batch are computed as usual."""
+    w, dl, OL = small
+    log("out-of-range token ids")
+    B, Nq, L0, cap = 3, 12, 50, 72
+    ctx = np.stack([synth.uniform_tokens(730 + b, L0, SMALL.vocab) for b in range(B)])
+    span = np.stack([synth.uniform_tokens(740 + b, Nq, SMALL.vocab) for b in range(B)]).astype(np.int64)
+    span[1, 5] = SMALL.vocab
+    span[2, 0] = -1
+    cache = cad.DeviceCache(SMALL, B, cap)
+    prefill(dl, cache, ctx, chunk=64)
+    k_before = cache.k.clone()
+    g = run_forward(dl, cache, span, flags=cad.COMMIT_ALL)
+    assert list(cache.len.cpu().numpy()) == [L0 + Nq, L0, L0]
+    assert list(cache.err.cpu().numpy()) == [0, cad.CAD_EINVAL, cad.CAD_EINVAL]
+    assert (g["argmax"][Nq:] == -7).all()
+    assert torch.equal(cache.k[1:], k_before[1:])
+    ref = O.span_forward(OL, O.cache_from_tokens(OL, ctx[0], cap), span[0])
+    compare(g, ref, rows=slice(0, Nq), what="valid sequence beside flagged ones")
+
+
+def test_accept_scan_skipped_sequences_report_nothing():
+    """Sequences the scan skips (error flag already set; history overflow without a cache) get
+    accepted = 0, n_emitted = 0, a zero emitted row and unchanged lengths."""
+    log("accept skipped sequences")
+    B, D = 4, 6
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    rows = np.arange(B * (1 + D)).reshape(B, 1 + D) % 7
+    pred = rows[:, 1:].copy()
+    pred = np.concatenate([pred, np.full((B, 1), 3)], axis=1)          # every draft agrees: a = D
+    dl = np.full((B, 1), D)
+    cache = cad.DeviceCache(SMALL, B, 64)
+    cache.len.copy_(torch.tensor([10, 10, 10, 10], dtype=torch.int32))
+    cache.err.copy_(torch.tensor([0, cad.CAD_ECAPACITY, 0, 0], dtype=torch.int32))
+    acc, bw, ne = (torch.full((B,), -1, dtype=torch.int32, device="cuda") for _ in range(3))
+    em = torch.full((B, D + 1), -1, dtype=torch.int32, device="cuda")
+    ctx = torch.zeros((B, 32), dtype=torch.int32, device="cuda")
+    clen = T([0, 0, 30, 0])                                            # sequence 2's history is full
+    cad.accept_scan(T(rows), 1, T(dl), T(pred), None, B, 1, D, cad.MASK_CAUSAL, acc, bw, em, ne,
+                    ctx=ctx, ctx_len=clen, ctx_cap=32, cache=cache)
+    torch.cuda.synchronize()
+    assert list(acc.cpu().numpy()) == [D, 0, 0, D]
+    assert list(ne.cpu().numpy()) == [D + 1, 0, 0, D + 1]
+    assert list(bw.cpu().numpy()) == [0, 0, 0, 0]
+    assert not em[1:3].any()
+    assert list(cache.len.cpu().numpy()) == [10 + D + 1, 10, 10, 10 + D + 1]
+    assert list(clen.cpu().numpy()) == [D + 1, 0, 30, D + 1]
+    assert list(cache.err.cpu().numpy()) == [0, cad.CAD_ECAPACITY, cad.CAD_ECAPACITY, 0]
+    # without a cache a history overflow is still visible: n_emitted = 0
+    clen2 = T([0, 30, 0, 0])
+    ne.fill_(-1)
+    cad.accept_scan(T(rows), 1, T(dl), T(pred), None, B, 1, D, cad.MASK_CAUSAL, acc, None, em, ne,
+                    ctx=ctx, ctx_len=clen2, ctx_cap=32)
+    torch.cuda.synchronize()
+    assert list(ne.cpu().numpy()) == [D + 1, 0, D + 1, D + 1]
+    assert list(clen2.cpu().numpy()) == [D + 1, 30, D + 1, D + 1]

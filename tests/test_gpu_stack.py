@@ -1,9 +1,10 @@
 """GPU parity of the full-depth stack call (cad_stack_span_forward) against the oracle's stack.
 
 Rounding drift between an fp32-accumulating pipeline and the fp64 oracle enters every layer
-independently (bf16 rounding flips of the normed inputs and the SwiGLU product), so the
-one-layer tolerances are widened by sqrt(depth) for outputs after the last layer and by
-sqrt(l + 1) for the K/V rows of layer l."""
+independently (bf16 rounding flips of the normed inputs and the SwiGLU product).  Each test runs
+the ideal fp32 pipeline (tests/ideal_fp32.py) through the same stack on the same inputs and
+bounds the GPU's distance to the oracle by its distance with a 1.25 margin, never below the
+one-layer contract values, for the outputs and for every layer's cache rows."""
 import math
 
 import numpy as np
@@ -14,7 +15,8 @@ import oracle as O
 from spec_verify_cad_amd import cad, synth
 from spec_verify_cad_amd.configs import SMALL
 
-from gpu_util import argmax_check, hidden_tol, log, logit_tol, to_f64
+import ideal_fp32 as IF
+from gpu_util import IDEAL_FACTOR, argmax_check, hidden_tol, ideal_tols, log, to_f64
 from helpers import oracle_layer
 
 pytestmark = pytest.mark.gpu
@@ -59,29 +61,47 @@ def _run(dst, sc, toks, mode=cad.MASK_CAUSAL, W=1, D=1, flags=0):
     return am.cpu().numpy(), to_f64(hid, "bf16"), lg.cpu().numpy().astype(np.float64)
 
 
-def _check_out(g_a, g_h, g_l, ref, rows, n_layers, what):
+def _check_out(g_a, g_h, g_l, ref, ideal, what):
+    """Outputs after the last layer against the oracle's stack, bounded by the ideal fp32
+    pipeline's distance on the same inputs (gpu_util.ideal_tols)."""
+    tol_h, ltol, min_unique, ih, il, iu = ideal_tols(ref, ideal)
     href = ref["hidden_out"]
     dh = np.abs(g_h - href)
-    scale = math.sqrt(n_layers)
-    tol_h = np.maximum(hidden_tol(href, SMALL.ffn) * scale, hidden_tol(href, SMALL.ffn))
-    assert (dh <= tol_h).all(), f"{what} hidden max-abs {dh.max():.3e}"
-    ltol = logit_tol(SMALL.hidden) * scale
+    assert (dh <= tol_h).all(), f"{what} hidden max-abs {dh.max():.3e} (ideal {ih:.3e})"
     dl = np.abs(g_l - ref["logits"]).max()
-    assert dl <= ltol, f"{what} logits max-abs {dl:.3e} > {ltol:.3g}"
-    unique = argmax_check(g_a, ref, g_l, what, ltol)
-    log(f"{what}: hidden {dh.max():.3e} logits {dl:.3e} (tol {ltol:.3g}) unique argmax {int(unique.sum())}/{len(g_a)}")
+    assert dl <= ltol, f"{what} logits max-abs {dl:.3e} > {ltol:.3g} (ideal {il:.3e})"
+    argmax_check(g_a, ref, g_l, what, ltol, min_unique if len(g_a) >= 16 else None)
+    log(f"{what}: hidden {dh.max():.3e} (ideal {ih:.3e}) logits {dl:.3e} (ideal {il:.3e}, tol {ltol:.3g}); "
+        f"ideal decides {iu:.3f} of the argmax rows")
 
 
-def _check_caches(sc, b, ocs, lo, hi, what):
-    for l, oc in enumerate(ocs):
+CACHE_MAX_FACTOR = 1.5        # the largest of ~10^5-10^6 cached elements is a noisy extreme
+CACHE_FRAC_FACTOR, CACHE_FRAC_SLACK = 2.0, 0.002
+
+
+def _check_caches(sc, b, ocs, ics, lo, hi, what, layers=None):
+    """Cache rows [lo, hi) of every layer (or of `layers`) against the oracle's.  Each layer's
+    elements are bounded by max(the one-layer bound, 1.5 x the ideal pipeline's largest distance
+    on that layer's rows).  For the first layer, whose K/V come straight from the embedding, the
+    fraction of elements that differ at all is also bounded, by 2 x the ideal's fraction + 0.002
+    (a stored element differs where the two sides round differently: rare there).  Deeper layers'
+    inputs already differ by rounding flips in tens of percent of their elements on either side,
+    so there the fraction only is logged."""
+    for l in (range(len(ocs)) if layers is None else layers):
+        oc, ic = ocs[l], ics[l]
         k = to_f64(sc.caches[l].k[b, :, lo:hi], "bf16")
         v = to_f64(sc.caches[l].v[b, :, :, lo:hi], "bf16").transpose(0, 2, 1)
-        for name, got, ref in (("k", k, oc.K[:, lo:hi]), ("v", v, oc.V[:, lo:hi])):
+        for name, got, ref, idl in (("k", k, oc.K[:, lo:hi], ic.K[:, lo:hi]), ("v", v, oc.V[:, lo:hi], ic.V[:, lo:hi])):
             d = np.abs(got - ref)
-            tol = hidden_tol(ref) * math.sqrt(l + 1)
+            de = np.abs(idl.astype(np.float64) - ref)
+            di, fi = float(de.max()), float(np.mean(de > 0))
+            tol = np.maximum(hidden_tol(ref), CACHE_MAX_FACTOR * di)
             frac = float(np.mean(d > 0))
-            assert (d <= tol).all(), f"{what} layer {l} {name} max-abs {d.max():.3e}"
-            log(f"{what} layer {l} {name}: max-abs {d.max():.3e}, differing {frac:.4f}")
+            log(f"{what} layer {l} {name}: max-abs {d.max():.3e} (ideal {di:.3e}), differing {frac:.4f} "
+                f"(ideal {fi:.4f})")
+            assert (d <= tol).all(), f"{what} layer {l} {name} max-abs {d.max():.3e} (ideal {di:.3e})"
+            if l == 0:
+                assert frac <= CACHE_FRAC_FACTOR * fi + CACHE_FRAC_SLACK, f"{what} layer 0 {name} differing {frac:.4f}"
 
 
 @pytest.mark.parametrize("Nq", [1, 13, 70])
@@ -98,11 +118,13 @@ def test_small_stack_span_matches_oracle(small_stack, Nq):
     assert list(sc.len.cpu().numpy()) == [L0 + Nq] * B
     for b in range(B):
         ocs = O.stack_prefill(ols, ctx[b], cap, chunk=64)
-        _check_caches(sc, b, ocs, 0, L0, f"prefill b={b}")
+        ics = IF.stack_prefill(ols, ctx[b], cap, chunk=64)
+        _check_caches(sc, b, ocs, ics, 0, L0, f"prefill b={b}")
         ref = O.stack_span_forward(ols, ocs, span[b])
+        ideal = IF.stack_span_forward(ols, ics, span[b])
         rows = slice(b * Nq, (b + 1) * Nq)
-        _check_out(g_a[rows], g_h[rows], g_l[rows], ref, rows, NL, f"b={b}")
-        _check_caches(sc, b, ocs, L0, L0 + Nq, f"span b={b}")
+        _check_out(g_a[rows], g_h[rows], g_l[rows], ref, ideal, f"b={b}")
+        _check_caches(sc, b, ocs, ics, L0, L0 + Nq, f"span b={b}")
 
 
 def test_small_stack_block_verify_and_copy_commit(small_stack):
@@ -116,10 +138,12 @@ def test_small_stack_block_verify_and_copy_commit(small_stack):
     g_a, g_h, g_l = _run(dst, sc, cand, mode=cad.MASK_BLOCK, W=W, D=D)
     assert list(sc.len.cpu().numpy()) == [L0] * B                 # verify forward: no commit
     ocs = [O.stack_prefill(ols, ctx[b], cap, chunk=64) for b in range(B)]
+    ics = [IF.stack_prefill(ols, ctx[b], cap, chunk=64) for b in range(B)]
     for b in range(B):
         ref = O.stack_span_forward(ols, [c.copy() for c in ocs[b]], cand[b], mode="block", W=W, D=D, commit=False)
+        ideal = IF.stack_span_forward(ols, [c.copy() for c in ics[b]], cand[b], mode="block", W=W, D=D, commit=False)
         rows = slice(b * W * D, (b + 1) * W * D)
-        _check_out(g_a[rows], g_h[rows], g_l[rows], ref, rows, NL, f"block b={b}")
+        _check_out(g_a[rows], g_h[rows], g_l[rows], ref, ideal, f"block b={b}")
     # copy-commit mode through the stack: the LM head for each sequence's last row only
     Nq = 9
     span = np.stack([synth.uniform_tokens(350 + b, Nq, SMALL.vocab) for b in range(B)])
@@ -127,14 +151,15 @@ def test_small_stack_block_verify_and_copy_commit(small_stack):
     assert list(sc.len.cpu().numpy()) == [L0 + Nq] * B
     for b in range(B):
         ref = O.stack_span_forward(ols, ocs[b], span[b])
+        ideal = IF.stack_span_forward(ols, ics[b], span[b])
+        tol_h, ltol = ideal_tols(ref, ideal)[:2]
         last = {k: ref[k][Nq - 1:Nq] for k in ("logits", "argmax", "top2_gap")}
-        last["hidden_out"] = ref["hidden_out"]
         dh = np.abs(g_h[b * Nq:(b + 1) * Nq] - ref["hidden_out"])
-        assert (dh <= hidden_tol(ref["hidden_out"], SMALL.ffn) * math.sqrt(NL)).all()
+        assert (dh <= tol_h).all()
         dl = np.abs(g_l[b:b + 1] - last["logits"]).max()
-        assert dl <= logit_tol(SMALL.hidden) * math.sqrt(NL)
-        argmax_check(g_a[b:b + 1], last, g_l[b:b + 1], f"copy-commit b={b}", logit_tol(SMALL.hidden) * math.sqrt(NL))
-        _check_caches(sc, b, ocs[b], L0, L0 + Nq, f"copy-commit b={b}")
+        assert dl <= ltol
+        argmax_check(g_a[b:b + 1], last, g_l[b:b + 1], f"copy-commit b={b}", ltol)
+        _check_caches(sc, b, ocs[b], ics[b], L0, L0 + Nq, f"copy-commit b={b}")
 
 
 def test_one_layer_stack_is_bitwise_the_one_layer_call(small_stack):
@@ -175,7 +200,7 @@ def test_stack_argument_errors(small_stack):
     ws_ = cad.alloc_workspace(1 << 24)
     import ctypes
     assert L.cad_stack_span_forward(dst.descs, 0, sc.descs, ctypes.c_void_p(t.data_ptr()), 1, 4, 0, 1, 1, 0,
-                                    ctypes.c_void_p(am.data_ptr()), None, None, ctypes.c_void_p(ws_.data_ptr()),
+                                    ctypes.c_void_p(am.data_ptr()), None, None, None, ctypes.c_void_p(ws_.data_ptr()),
                                     ws_.numel(), None) == cad.CAD_EINVAL
     # a layer of another shape in the stack
     other = cad.DeviceLayer(synth.LayerShape(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=512,
@@ -189,57 +214,62 @@ def test_stack_argument_errors(small_stack):
     assert int(sc.len[0]) == 0
 
 
-def test_full_depth_1p5b_stack_matches_oracle():
-    """The 28-layer stack of the 1.5B shape the full-depth curve times: a 64-token prefix, an
-    8-token span (all rows' logits), then a copy-commit span, against the oracle's stack."""
-    from spec_verify_cad_amd.configs import QWEN15
-    nl, L0, cap, N = 28, 64, 96, 8
-    log("full-depth 1.5B stack: weights")
-    ws = _stack_weights(QWEN15, 900, nl)
-    dst = cad.DeviceStack([cad.DeviceLayer(QWEN15, w) for w in ws])
-    log("full-depth 1.5B stack: oracle weights")
-    ols = [oracle_layer(QWEN15, w, only=list(w)) for w in ws]
+def _full_depth_case(shape, nl, seed, L0, spans, what):
+    """A stack of nl layers of `shape` (weights drawn per layer), a prefix of L0 random tokens
+    (the curve's 1024-token prefix), then for each N of `spans` a span forward with all rows'
+    logits from the same cache state, and a copy-commit span after the first; every output and
+    the first and last layers' cache rows against the oracle's stack, bounded by the ideal fp32
+    pipeline through the same stack."""
+    cap = (L0 + max(spans) + max(spans[0], 8) + 8 + 3) // 4 * 4
+    log(f"{what}: weights")
+    ws = _stack_weights(shape, seed, nl)
+    dst = cad.DeviceStack([cad.DeviceLayer(shape, w) for w in ws])
+    log(f"{what}: oracle weights")
+    ols = [oracle_layer(shape, w, only=list(w)) for w in ws]
     del ws
-    ctx = synth.uniform_tokens(910, L0, QWEN15.vocab)[None]
-    span = synth.uniform_tokens(911, 2 * N, QWEN15.vocab)[None]
-    sc = cad.StackCache(QWEN15, nl, 1, cap)
-    _prefill(dst, sc, ctx, chunk=64)
-    t = torch.from_numpy(np.ascontiguousarray(span[:, :N], dtype=np.int32)).cuda()
-    am = torch.full((N,), -7, dtype=torch.int32, device="cuda")
-    hid = torch.zeros((N, QWEN15.hidden), dtype=torch.int16, device="cuda")
-    lg = torch.zeros((N, QWEN15.vocab), dtype=torch.float32, device="cuda")
-    cad.stack_span_forward(dst, sc, t, N, flags=cad.COMMIT_ALL, argmax_out=am, hidden_out=hid, logits_out=lg)
-    t2 = torch.from_numpy(np.ascontiguousarray(span[:, N:], dtype=np.int32)).cuda()
-    am2 = torch.full((1,), -7, dtype=torch.int32, device="cuda")
-    lg2 = torch.zeros((1, QWEN15.vocab), dtype=torch.float32, device="cuda")
-    cad.stack_span_forward(dst, sc, t2, N, flags=cad.COMMIT_ALL | cad.LOGITS_LAST, argmax_out=am2, logits_out=lg2)
+    ctx = synth.uniform_tokens(seed + 10, L0, shape.vocab)[None]
+    sc = cad.StackCache(shape, nl, 1, cap)
+    _prefill(dst, sc, ctx, chunk=256)
     torch.cuda.synchronize()
-    assert int(sc.len[0]) == L0 + 2 * N
-    log("full-depth 1.5B stack: oracle prefill and spans")
-    ocs = O.stack_prefill(ols, ctx[0], cap, chunk=64)
-    ref = O.stack_span_forward(ols, ocs, span[0, :N])
-    scale = math.sqrt(nl)
-    g_h = to_f64(hid, "bf16")
-    dh = np.abs(g_h - ref["hidden_out"])
-    tol_h = hidden_tol(ref["hidden_out"], QWEN15.ffn) * scale
-    ltol = logit_tol(QWEN15.hidden) * scale
-    g_l = lg.cpu().numpy().astype(np.float64)
-    dl = np.abs(g_l - ref["logits"]).max()
-    log(f"28 layers: hidden max-abs {dh.max():.3e} (tol from {tol_h.min():.3g}), logits max-abs {dl:.3e} (tol {ltol:.3g})")
-    assert (dh <= tol_h).all()
-    assert dl <= ltol
-    argmax_check(am.cpu().numpy(), ref, g_l, "28-layer span", ltol)
-    ref2 = O.stack_span_forward(ols, ocs, span[0, N:])
-    last = {k: ref2[k][N - 1:N] for k in ("logits", "argmax", "top2_gap")}
-    g_l2 = lg2.cpu().numpy().astype(np.float64)
-    assert np.abs(g_l2 - last["logits"]).max() <= ltol
-    argmax_check(am2.cpu().numpy(), last, g_l2, "28-layer copy-commit", ltol)
-    # the first and last layers' cache rows of the whole sequence
-    for l in (0, nl - 1):
-        k_ = to_f64(sc.caches[l].k[0, :, :L0 + 2 * N], "bf16")
-        d = np.abs(k_ - ocs[l].K[:, :L0 + 2 * N])
-        assert (d <= hidden_tol(ocs[l].K[:, :L0 + 2 * N]) * math.sqrt(l + 1)).all(), f"layer {l} K {d.max()}"
-        log(f"layer {l} K rows: max-abs {d.max():.3e}")
+    log(f"{what}: oracle and ideal fp32 prefill of {L0} tokens")
+    ocs = O.stack_prefill(ols, ctx[0], cap, chunk=256)
+    ics = IF.stack_prefill(ols, ctx[0], cap, chunk=256)
+    _check_caches(sc, 0, ocs, ics, 0, L0, f"{what} prefill", layers=(0, nl - 1))
+    for N in spans:
+        span = synth.uniform_tokens(seed + 20 + N, N, shape.vocab)
+        sc.len.fill_(L0)
+        g_a, g_h, g_l = _run(dst, sc, span[None], flags=cad.COMMIT_ALL)
+        assert int(sc.len[0]) == L0 + N
+        oc2, ic2 = [c.copy() for c in ocs], [c.copy() for c in ics]
+        ref = O.stack_span_forward(ols, oc2, span)
+        ideal = IF.stack_span_forward(ols, ic2, span)
+        _check_out(g_a, g_h, g_l, ref, ideal, f"{what} N={N}")
+        _check_caches(sc, 0, oc2, ic2, L0, L0 + N, f"{what} N={N}", layers=(0, nl - 1))
+        if N == spans[0]:
+            # copy-commit mode after it: the LM head for the last row only
+            span2 = synth.uniform_tokens(seed + 30, 8, shape.vocab)
+            g_a2, _, g_l2 = _run(dst, sc, span2[None], flags=cad.COMMIT_ALL | cad.LOGITS_LAST)
+            assert int(sc.len[0]) == L0 + N + 8
+            ref2 = O.stack_span_forward(ols, oc2, span2)
+            ltol = ideal_tols(ref2, IF.stack_span_forward(ols, ic2, span2))[1]
+            last = {k: ref2[k][-1:] for k in ("logits", "argmax", "top2_gap")}
+            assert np.abs(g_l2 - last["logits"]).max() <= ltol
+            argmax_check(g_a2, last, g_l2, f"{what} copy-commit", ltol)
+    for L in ols:
+        IF.release(L)
+
+
+def test_full_depth_1p5b_stack_matches_oracle():
+    """The 28-layer stack of the 1.5B shape the full-depth curve times, at its 1024-token prefix,
+    with an 8-token span, a copy-commit span and a 512-token span."""
+    from spec_verify_cad_amd.configs import QWEN15
+    _full_depth_case(QWEN15, 28, 900, 1024, (8, 512), "28-layer 1.5B stack")
+
+
+def test_7b_stack_matches_oracle():
+    """A 4-layer stack of the 7B shape at the curve's 1024-token prefix, N = 8 and N = 512."""
+    from spec_verify_cad_amd.configs import QWEN7
+    _full_depth_case(QWEN7, 4, 950, 1024, (8, 512), "4-layer 7B stack")
 
 
 def test_tiny_fp32_stack_matches_oracle():
@@ -297,10 +327,19 @@ def test_small_stack_cad_program_matches_oracle():
     dec = prog.decisions.cpu().numpy()
     stream = prog.fed_tokens(doc)
     ocs = O.stack_prefill(ols, doc, cap, chunk=128)
-    tol = logit_tol(shp.hidden) * math.sqrt(nl)
-    pos, firm = 0, 0
+    ics = IF.stack_prefill(ols, doc, cap, chunk=128)
+    pos, replay, worst = 0, [], 0.0
     for f, pf in enumerate(fwds):
         ref = O.stack_span_forward(ols, ocs, stream[pos:pos + pf.n])
+        il = IF.stack_span_forward(ols, ics, stream[pos:pos + pf.n])["logits"]
+        worst = max(worst, float(np.abs(il - ref["logits"]).max()))
+        replay.append((f, pf, ref))
+        pos += pf.n
+    # the decisions write no logits: the bound is the ideal pipeline's largest distance over the
+    # replayed rows, with the usual margin
+    tol = max(1e-2, IDEAL_FACTOR * worst)
+    firm = 0
+    for f, pf, ref in replay:
         last = {k: ref[k][-1:] for k in ("logits", "argmax", "top2_gap")}
         if pf.allowed is None:
             argmax_check(dec[f:f + 1], last, None, f"forward {f} ({pf.role})", tol)
@@ -310,12 +349,8 @@ def test_small_stack_cad_program_matches_oracle():
             if gap[0] > 2 * tol:
                 firm += 1
                 assert dec[f] == best[0], f"forward {f} ({pf.role}): {dec[f]} vs {best[0]}"
-        pos += pf.n
-    log(f"stack program: {firm} masked decisions firm")
-    for l in range(nl):
-        k_ = to_f64(sc.caches[l].k[0, :, :len(doc) + fed], "bf16")
-        d = np.abs(k_ - ocs[l].K[:, :len(doc) + fed])
-        assert (d <= hidden_tol(ocs[l].K[:, :len(doc) + fed]) * math.sqrt(l + 1)).all(), f"layer {l}"
+    log(f"stack program: {firm} masked decisions firm (logit bound {tol:.3e})")
+    _check_caches(sc, 0, ocs, ics, 0, len(doc) + fed, "stack program")
 
 
 def test_small_stack_sampled_verify_matches_oracle(small_stack):
@@ -356,3 +391,53 @@ def test_small_stack_sampled_verify_matches_oracle(small_stack):
                 assert g_pred[rows][i] == opred[i], (b, i, g_pred[rows][i], opred[i])
         kept += sum(1 for i in range(dls[b]) if opred[i] == toks[b, i + 1])
     assert kept >= 1
+
+
+def test_small_stack_block_commit_moves_every_layer(small_stack):
+    """Block verify through the stack, then cad_stack_accept_scan: a planted candidate (w* = 2,
+    the oracle stack's own greedy continuation of the context) wins, and its accepted K/V rows
+    land at len .. len + a* - 1 in EVERY layer's cache (SwitchSD: the longest validated
+    continuation is kept; the other candidates' rows are discarded)."""
+    ws, dst, ols = small_stack
+    W, D, B, L0, cap, w_plant = 4, 6, 2, 70, 128, 2
+    log("stack block commit w*=2")
+    ctx = np.stack([synth.uniform_tokens(360 + b, L0, SMALL.vocab) for b in range(B)])
+    sc = cad.StackCache(SMALL, NL, B, cap)
+    _prefill(dst, sc, ctx)
+    cand = np.stack([synth.uniform_tokens(370 + b, W * D, SMALL.vocab) for b in range(B)]).reshape(B, W, D)
+    first = np.zeros(B, dtype=np.int64)
+    ocs = []
+    ics = []
+    for b in range(B):
+        # the anchor's prediction, then the greedy continuation, from the oracle stack
+        oc = O.stack_prefill(ols, ctx[b][:-1], cap, chunk=64)
+        first[b] = O.stack_span_forward(ols, oc, ctx[b][-1:])["argmax"][0]
+        ic = IF.stack_prefill(ols, ctx[b][:-1], cap, chunk=64)
+        IF.stack_span_forward(ols, ic, ctx[b][-1:])
+        ics.append(ic)
+        greedy, c2, tok = [], [c.copy() for c in oc], int(first[b])
+        for _ in range(D):
+            greedy.append(tok)
+            tok = int(O.stack_decode_one(ols, c2, tok)["argmax"][0])
+        cand[b, w_plant] = greedy
+        ocs.append(oc)
+    g_a, _, _ = _run(dst, sc, cand.reshape(B, W * D), mode=cad.MASK_BLOCK, W=W, D=D)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    acc, bw, ne = (torch.full((B,), -1, dtype=torch.int32, device="cuda") for _ in range(3))
+    em = torch.full((B, D + 1), -1, dtype=torch.int32, device="cuda")
+    cad.stack_accept_scan(T(cand.reshape(B, W * D)), 0, T(np.full((B, W), D)), T(g_a), T(first), B, W, D,
+                          cad.MASK_BLOCK, acc, bw, em, ne, sc)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = O.stack_span_forward(ols, ocs[b], cand[b].reshape(-1), mode="block", W=W, D=D, commit=False)
+        IF.stack_span_forward(ols, ics[b], cand[b].reshape(-1), mode="block", W=W, D=D, commit=False)
+        a, w, e, _ = O.accept_block(cand[b], np.full(W, D), ref["argmax"], int(first[b]), D)
+        assert w == w_plant and a == D, (a, w)
+        assert acc[b].item() == a and bw[b].item() == w and ne[b].item() == a + 1
+        assert list(em[b, :a + 1].cpu().numpy()) == e
+        for oc, ic in zip(ocs[b], ics[b]):
+            O.commit_block(oc, w, a, D)
+            ic.K[:, L0:L0 + a] = ic.K[:, L0 + w * D:L0 + w * D + a]
+            ic.V[:, L0:L0 + a] = ic.V[:, L0 + w * D:L0 + w * D + a]
+        _check_caches(sc, b, ocs[b], ics[b], L0, L0 + a, f"committed winner rows b={b}")
+    assert list(sc.len.cpu().numpy()) == [L0 + D] * B
