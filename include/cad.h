@@ -181,6 +181,27 @@ int cad_span_forward(const cad_layer_desc *layer, const cad_kv_desc *kv,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * cad_span_forward_noalloc — cad_span_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The same
+ * forward with the same arguments, except that its workspace is a static device array of
+ * CAD_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library: every device the library runs on holds
+ * one from the library's load until the process ends.  The call allocates nothing.
+ *   Limit: forwards whose cad_span_forward_workspace(...) exceeds CAD_NOALLOC_SCRATCH_BYTES return
+ *   CAD_EWORKSPACE (at the 1.5B shape up to 64 rows fit, at the 7B shape up to 32).
+ *   Sharing: every call on one device uses that device's one array, which keeps the last call's
+ *   contents (nothing in it needs to start at zero).  Calls on one stream are ordered; calls that
+ *   overlap on one device (several streams, or host threads) race on the array.
+ * Errors: as cad_span_forward; CAD_EWORKSPACE (too large, see above); CAD_EHIP when the array's
+ * device address cannot be obtained.
+ */
+#define CAD_NOALLOC_SCRATCH_BYTES (32 << 20)
+int cad_span_forward_noalloc(const cad_layer_desc *layer, const cad_kv_desc *kv,
+                             const int32_t *tokens, int B, int Nq,
+                             int mask_mode, int W, int D, int flags,
+                             int32_t *argmax_out, void *hidden_out, float *logits_out, float *top2_gap,
+                             hipStream_t stream);
+
+/*
  * cad_span_forward_allowed — a causal span forward whose argmax is restricted to a per-row set
  * of allowed token ids (Copy-as-Decode §2.3: at the grammar's decision points the FSM intersects
  * the model's logits with the ids its state allows, e.g. {<, </} at an op boundary).  Only the

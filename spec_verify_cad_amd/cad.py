@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
     L.cad_stack_span_forward.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(KVDesc), vp, i32, i32, i32,
                                          i32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.cad_stack_span_forward.restype = i32
+    L.cad_span_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(KVDesc), vp, i32, i32, i32, i32,
+                                           i32, i32, vp, vp, vp, vp, vp]
+    L.cad_span_forward_noalloc.restype = i32
     L.cad_stack_span_forward_allowed.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(KVDesc), vp, i32, i32,
                                                  i32, vp, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.cad_stack_span_forward_allowed.restype = i32
@@ -245,6 +248,20 @@ def span_forward(layer: DeviceLayer, cache: DeviceCache, tokens, Nq: int, mode: 
                                   flags, _ptr(argmax_out), _ptr(hidden_out), _ptr(logits_out), _ptr(top2_gap),
                                   _ptr(workspace), workspace.numel(), _stream(stream)), "cad_span_forward")
     return workspace
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def span_forward_noalloc(layer: DeviceLayer, cache: DeviceCache, tokens, Nq: int, mode: int = MASK_CAUSAL, W: int = 1,
+                         D: int = 1, flags: int = 0, argmax_out=None, hidden_out=None, logits_out=None, top2_gap=None,
+                         stream=None):
+    """cad_span_forward with the library's static device workspace (for callers that cannot
+    allocate, e.g. under graph capture); forwards needing more than 32 MiB of workspace raise."""
+    _check(lib().cad_span_forward_noalloc(ctypes.byref(layer.desc), ctypes.byref(cache.desc), _ptr(tokens), cache.B,
+                                          Nq, mode, W, D, flags, _ptr(argmax_out), _ptr(hidden_out),
+                                          _ptr(logits_out), _ptr(top2_gap), _stream(stream)),
+           "cad_span_forward_noalloc")
 
 
 def stack_span_forward_workspace(stack: DeviceStack, B: int, Nq: int, mode: int = MASK_CAUSAL, W: int = 1,
