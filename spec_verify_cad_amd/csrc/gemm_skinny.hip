@@ -9,9 +9,9 @@
 // in sub-step j, and the token operand is loaded from A with the same offsets.  Workgroups are
 // persistent and walk the units with a grid stride that is a multiple of the slice count, so a
 // workgroup always works on the same K slice: its token fragments are loaded into registers
-// once, and only W streams.  (A two-buffer variant issues the next unit's W loads before the
-// current unit is finished; on the 1.5B shapes it measured slower than the single-buffer form
-// with two resident workgroups per CU, which the launchers use.)  The waves' partial tiles are
+// once, and only W streams.  The LM head, whose workgroups walk many units, keeps two W buffers:
+// the next unit's loads are in flight while the current one is multiplied and finished.  The
+// waves' partial tiles are
 // summed through LDS and the wave that owns a 16-token tile runs the epilogue from registers:
 // lane (r, g) then holds features 4g..4g+3 of token r.
 //
@@ -69,8 +69,10 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
             }
     }
 
-    // W fragments of one unit; every load reads a valid address and masked ones are zeroed
-    // afterwards, so all loads are plain global loads and their count never depends on data
+    // W fragments of one unit.  Every load is unconditional from a valid address: a row past N
+    // reads row 0 and a column past K column 0.  Their values are not masked: a column past K
+    // meets a zero token fragment (finite weights times zero add nothing) and a row past N is never
+    // stored, so no load sits in a branch and the wait counts stay exact across units.
     auto load_w = [&](int uu, uint4 (&wf)[SSW][2]) {
         bool wv;
         const int wr = w_row<KIND>(uu / S, l16, N, p, wv);
@@ -80,11 +82,15 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int k = kb + s * 64 + j * 8;
-                const bool ok = wv && k < K;
-                const uint4 t = *(const uint4*)(wrow + (ok ? k : 0));
-                wf[s][j] = ok ? t : make_uint4(0, 0, 0, 0);
+                wf[s][j] = *(const uint4*)(wrow + (k < K ? k : 0));
             }
+        // every load of the unit is issued before anything that uses one (left to itself the
+        // scheduler interleaves them with the multiplies and keeps two in flight)
+        __builtin_amdgcn_sched_barrier(0);
     };
+    // the epilogue row of this lane and whether its sequence runs (read once, not per unit)
+    const int my_tok = wave * 16 + l16;
+    const bool my_live = wave < TT && my_tok < M && seq_ok(p.len_snap, my_tok / p.Nq, p.Nq, p.cap);
 
     float best = -INFINITY;                           // LM head: this lane's running (max, index)
     int bidx = 0x7fffffff;
@@ -117,8 +123,8 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
             f32x4_t c = red[0][wave][lane];
 #pragma unroll
             for (int w = 1; w < NW; ++w) c += red[w][wave][lane];
-            const int tok = wave * 16 + l16;
-            const bool live = tok < M && seq_ok(p.len_snap, tok / p.Nq, p.Nq, p.cap);
+            const int tok = my_tok;
+            const bool live = my_live;
             if constexpr (KIND == EPI_PARTIAL) {
                 const int n = tile * 16 + g4 * 4;
                 if (tok < M && n < N) *(f32x4_t*)(p.part + ((size_t)ks * M + tok) * N + n) = c;
@@ -264,7 +270,15 @@ int skinny_grid(int units, int S) {
     return g < S ? S : g;
 }
 
-template <int KIND, int TT, int SSW, int NW, bool DB = false>
+// Two W buffers (the next unit's loads in flight while this one is multiplied and finished) for
+// the LM head, whose workgroups walk many units: 79.6 / 85.2 us at 8 / 32 rows against 82.8 / 90.7
+// single-buffered.  The layer's projections have one or two units per workgroup, where the second
+// buffer only re-reads a unit (gate/up at 8 rows 15.5 -> 17.1 us), and the 7-super-step two-tile
+// form of the 7B shape spills with it, so those keep one buffer.
+template <int KIND, int TT, int SSW>
+constexpr bool two_buffers() { return KIND == EPI_ARGMAX && TT * SSW <= 12; }
+
+template <int KIND, int TT, int SSW, int NW, bool DB = two_buffers<KIND, TT, SSW>()>
 hipError_t go(const void* A, const void* W, int M, int N, int K, int ntiles, int S, const EpiParams& p,
               hipStream_t s) {
     const int grid = skinny_grid<KIND, TT, SSW, NW, DB>(ntiles * S, S);
@@ -291,10 +305,10 @@ hipError_t go_full(const void* A, const void* W, int M, int N, int K, int ntiles
 template <int KIND, int TT>
 int full_grid(int K, int ntiles) {
     if constexpr (TT == 4) {
-        return skinny_grid<KIND, 4, 3, 8, false>(ntiles, 1);
+        return skinny_grid<KIND, 4, 3, 8, two_buffers<KIND, 4, 3>()>(ntiles, 1);
     } else {
-        if (K <= 4 * 6 * 64) return skinny_grid<KIND, TT, 6, 4, false>(ntiles, 1);
-        return skinny_grid<KIND, TT, 7, 8, false>(ntiles, 1);
+        if (K <= 4 * 6 * 64) return skinny_grid<KIND, TT, 6, 4, two_buffers<KIND, TT, 6>()>(ntiles, 1);
+        return skinny_grid<KIND, TT, 7, 8, two_buffers<KIND, TT, 7>()>(ntiles, 1);
     }
 }
 
