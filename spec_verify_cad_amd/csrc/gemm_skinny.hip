@@ -328,10 +328,13 @@ constexpr int kSkinnyPartialSlice = 4 * 3 * 64;   // K per slice of the partial-
 
 int skinny_partial_slices(int K) { return (K + kSkinnyPartialSlice - 1) / kSkinnyPartialSlice; }
 
-// Rows 33..64 take the 8-wave, 3-super-step variant (one workgroup per CU); for the LM head that
-// measured slower than the LDS-tiled kernel, so only the layer's projections use it.
+// Rows 33..64 take the 8-wave, 3-super-step variant (one workgroup per CU), the argmax LM head
+// included (85.5 us at 64 rows against 101.5 us on the LDS-tiled balanced-range kernel).  Beyond 64
+// rows the LM head stays on the tiled kernel: two workgroups of 64 rows walking the same W units
+// on one XCD took 131.8 us at 128 rows against 109.6 us (a CU pulls ~27 GB/s in this form, and
+// each then reads the whole 3.6 MB of its stream).
 bool skinny_supports(int kind, int M, int K) {
-    if (M > 64 || (M > 32 && (kind == EPI_ARGMAX || kind == EPI_SAMPLE))) return false;
+    if (M > 64 || (M > 32 && kind == EPI_SAMPLE)) return false;
     if (kind == EPI_PARTIAL) return true;
     return K <= (M > 32 ? 8 * 3 * 64 : 8 * 7 * 64);
 }
