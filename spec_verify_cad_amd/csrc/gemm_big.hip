@@ -118,6 +118,159 @@ __device__ __forceinline__ void qkv_epilogue(const f32x4_t (&acc)[FT][TT], const
     }
 }
 
+// Epilogue of one BN x BM column tile from the accumulators: wave (wn, wm)
+// holds features wn*WTN + ft*16 + 4*g4 + i of tokens m0 + wm*WTM + tt*16 + l16.
+template <int KIND, int BN, int BM, int WN, int WM, int FT, int TT>
+__device__ __forceinline__ void big_epilogue(const f32x4_t (&acc)[FT][TT], const EpiParams& p, int M, int N,
+                                                int ffn, int m0, int nt, int ks, int tid, int wn, int wm, int l16,
+                                                int g4) {
+    constexpr int WTN = BN / WN, WTM = BM / WM, NT = WN * WM * 64;
+    const int fbase = nt * BN + wn * WTN;                 // first feature (plain layouts)
+    if constexpr (KIND == EPI_PARTIAL) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const int tok = m0 + wm * WTM + tt * 16 + l16;
+            if (tok >= M) continue;
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) {
+                const int n = fbase + ft * 16 + g4 * 4;
+                if (n < N) *(f32x4_t*)(p.part + ((size_t)ks * M + tok) * N + n) = acc[ft][tt];
+            }
+        }
+    } else if constexpr (KIND == EPI_SWIGLU) {
+        constexpr int H = FT / 2;
+        const int F0 = nt * (BN / 2) + wn * (WTN / 2);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const int tok = m0 + wm * WTM + tt * 16 + l16;
+            if (tok >= M || !seq_ok(p.len_snap, tok / p.Nq, p.Nq, p.cap)) continue;
+#pragma unroll
+            for (int ft = 0; ft < H; ++ft) {
+                const int F = F0 + ft * 16 + g4 * 4;
+                if (F >= ffn) continue;
+                f32x4_t a;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float g = acc[ft][tt][i];
+                    a[i] = g / (1.0f + __expf(-g)) * acc[ft + H][tt][i];
+                }
+                st4((uint16_t*)p.act + (size_t)tok * ffn + F, a);
+            }
+        }
+    } else if constexpr (KIND == EPI_QKV) {
+        // the pair offset d/32 (blocks) must be a compile-time index into acc
+        if (p.d == 128) qkv_epilogue<FT, TT, 4>(acc, p, m0 + wm * WTM, fbase, M, N, l16, g4);
+        else if (p.d == 64) qkv_epilogue<FT, TT, 2>(acc, p, m0 + wm * WTM, fbase, M, N, l16, g4);
+        else qkv_epilogue<FT, TT, 1>(acc, p, m0 + wm * WTM, fbase, M, N, l16, g4);
+    } else if constexpr (KIND == EPI_SAMPLE) {
+        // per row: Gumbel-perturbed maxima and the log-sum-exp over this tile's ids, merged over
+        // the lane groups of a wave, then over the WN waves that share the rows
+        __shared__ float4 sred[WN][BM][2];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const int tok = m0 + wm * WTM + tt * 16 + l16;
+            SampleState st;
+            sample_init(st);
+            if (tok < M) {
+                const SampleRow sr = sample_row(p, tok);
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft) {
+                    const int n0 = fbase + ft * 16 + g4 * 4;
+                    if (n0 >= N) continue;
+                    const uint4 w = sample_bits(p, sr, n0);
+                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int n = n0 + i;
+                        if (n < N) {
+                            const float v = acc[ft][tt][i];
+                            sample_add(st, v * p.inv_temp, gumbel(ws[i]), n, sr.draft);
+                            if (p.logits) p.logits[(size_t)tok * N + n] = v;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) sample_merge(st, sample_shfl_xor(st, o));
+            if (g4 == 0) sample_store(&sred[wn][wm * WTM + tt * 16 + l16][0], st);
+        }
+        __syncthreads();
+        for (int r = tid; r < BM; r += NT) {
+            const int tok = m0 + r;
+            if (tok >= M) continue;
+            SampleState st = sample_load(&sred[0][r][0]);
+#pragma unroll
+            for (int w = 1; w < WN; ++w) sample_merge(st, sample_load(&sred[w][r][0]));
+            sample_store(p.samp_part + ((size_t)tok * p.amax_slots + nt) * 2, st);
+        }
+    } else {                                                 // EPI_ARGMAX
+        __shared__ float2 red[WN][BM];
+        __shared__ float rsec[WN][BM];                         // runner-up values (top-2 gap asked)
+        const bool top2 = p.amax_sec != nullptr;
+        // wave-uniform: this wave's columns all lie inside the vocabulary and no debug output is
+        // asked for.  Then each lane scans its values with one compare and two selects apiece and
+        // no branches (rows past M are scanned too; their results are never stored).  The general
+        // scan below costs several times that in branches per value, which at 128 values per lane
+        // weighed as much as a fifth of the whole launch.
+        const bool plain = !top2 && !p.logits && fbase + WTN <= N;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const int tok = m0 + wm * WTM + tt * 16 + l16;
+            float best = -INFINITY, second = -INFINITY;
+            int bi = 0x7fffffff;
+            if (plain) {
+                int off = -1;                                  // first column of the maximum
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float v = acc[ft][tt][i];
+                        if (v > best) { best = v; off = ft * 16 + i; }
+                    }
+                if (off >= 0) bi = fbase + g4 * 4 + off;
+            } else if (tok < M) {
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int n = fbase + ft * 16 + g4 * 4 + i;       // increasing along the lane
+                        if (n < N) {
+                            const float v = acc[ft][tt][i];
+                            if (top2) second = fmaxf(second, fminf(best, v));
+                            if (v > best) { best = v; bi = n; }
+                            if (p.logits) p.logits[(size_t)tok * N + n] = v;
+                        }
+                    }
+            }
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) {
+                const float v2 = __shfl_xor(best, o, 64);
+                const int i2 = __shfl_xor(bi, o, 64);
+                if (top2) second = second_merge(best, second, v2, __shfl_xor(second, o, 64));
+                argmax_merge(best, bi, v2, i2);
+            }
+            if (g4 == 0) {
+                red[wn][wm * WTM + tt * 16 + l16] = make_float2(best, __int_as_float(bi));
+                if (top2) rsec[wn][wm * WTM + tt * 16 + l16] = second;
+            }
+        }
+        __syncthreads();
+        for (int r = tid; r < BM; r += NT) {
+            const int tok = m0 + r;
+            if (tok >= M || !seq_ok(p.len_snap, tok / p.Nq, p.Nq, p.cap)) continue;
+            float best = red[0][r].x, second = top2 ? rsec[0][r] : -INFINITY;
+            int bi = __float_as_int(red[0][r].y);
+#pragma unroll
+            for (int w = 1; w < WN; ++w) {
+                if (top2) second = second_merge(best, second, red[w][r].x, rsec[w][r]);
+                argmax_merge(best, bi, red[w][r].x, __float_as_int(red[w][r].y));
+            }
+            p.amax_part[(size_t)tok * p.amax_slots + nt] = make_float2(best, __int_as_float(bi));
+            if (top2) p.amax_sec[(size_t)tok * p.amax_slots + nt] = second;
+        }
+    }
+}
+
 // BAL: 0 = column tiles, 1 = balanced ranges, 2 = balanced ranges with the debug outputs (logits
 // and/or the runner-up values of the top-2 gap)
 template <int KIND, int BN, int BM, int WN, int WM, int BK, int RS, int BAL>
@@ -293,12 +446,25 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
         // their own)
         auto chunk_argmax = [&](int cc) {
             const int rb = r0 + cc * BN;
+            // wave-uniform: all of this wave's rows of the chunk lie inside the range (and no debug
+            // output): the branch-free scan of the column-tile epilogue
+            const bool plain = BAL == 1 && rb + (wn_s + 1) * C::WTN <= r1;
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
                 const int tok = m0 + wm * C::WTM + tt * 16 + l16;
                 float best = -INFINITY, second = -INFINITY;
                 int bi = 0x7fffffff;
-                if (tok < M) {
+                if (plain) {
+                    int off = -1;
+#pragma unroll
+                    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float v = acc[ft][tt][i];
+                            if (v > best) { best = v; off = ft * 16 + i; }
+                        }
+                    if (off >= 0) bi = rb + wn * C::WTN + g4 * 4 + off;
+                } else if (tok < M) {
 #pragma unroll
                     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
@@ -385,134 +551,7 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
     }
 
     // ---------------------------------------------------------------- epilogues from registers
-    const int fbase = nt * BN + wn * C::WTN;                 // first feature (plain layouts)
-    if constexpr (KIND == EPI_PARTIAL) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            const int tok = m0 + wm * C::WTM + tt * 16 + l16;
-            if (tok >= M) continue;
-#pragma unroll
-            for (int ft = 0; ft < FT; ++ft) {
-                const int n = fbase + ft * 16 + g4 * 4;
-                if (n < N) *(f32x4_t*)(p.part + ((size_t)ks * M + tok) * N + n) = acc[ft][tt];
-            }
-        }
-    } else if constexpr (KIND == EPI_SWIGLU) {
-        constexpr int H = FT / 2;
-        const int F0 = nt * (BN / 2) + wn * (C::WTN / 2);
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            const int tok = m0 + wm * C::WTM + tt * 16 + l16;
-            if (tok >= M || !seq_ok(p.len_snap, tok / p.Nq, p.Nq, p.cap)) continue;
-#pragma unroll
-            for (int ft = 0; ft < H; ++ft) {
-                const int F = F0 + ft * 16 + g4 * 4;
-                if (F >= ffn) continue;
-                f32x4_t a;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float g = acc[ft][tt][i];
-                    a[i] = g / (1.0f + __expf(-g)) * acc[ft + H][tt][i];
-                }
-                st4((uint16_t*)p.act + (size_t)tok * ffn + F, a);
-            }
-        }
-    } else if constexpr (KIND == EPI_QKV) {
-        // the pair offset d/32 (blocks) must be a compile-time index into acc
-        if (p.d == 128) qkv_epilogue<FT, TT, 4>(acc, p, m0 + wm * C::WTM, fbase, M, N, l16, g4);
-        else if (p.d == 64) qkv_epilogue<FT, TT, 2>(acc, p, m0 + wm * C::WTM, fbase, M, N, l16, g4);
-        else qkv_epilogue<FT, TT, 1>(acc, p, m0 + wm * C::WTM, fbase, M, N, l16, g4);
-    } else if constexpr (KIND == EPI_SAMPLE) {
-        // per row: Gumbel-perturbed maxima and the log-sum-exp over this tile's ids, merged over
-        // the lane groups of a wave, then over the WN waves that share the rows
-        __shared__ float4 sred[WN][BM][2];
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            const int tok = m0 + wm * C::WTM + tt * 16 + l16;
-            SampleState st;
-            sample_init(st);
-            if (tok < M) {
-                const SampleRow sr = sample_row(p, tok);
-#pragma unroll
-                for (int ft = 0; ft < FT; ++ft) {
-                    const int n0 = fbase + ft * 16 + g4 * 4;
-                    if (n0 >= N) continue;
-                    const uint4 w = sample_bits(p, sr, n0);
-                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int n = n0 + i;
-                        if (n < N) {
-                            const float v = acc[ft][tt][i];
-                            sample_add(st, v * p.inv_temp, gumbel(ws[i]), n, sr.draft);
-                            if (p.logits) p.logits[(size_t)tok * N + n] = v;
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int o = 16; o <= 32; o <<= 1) sample_merge(st, sample_shfl_xor(st, o));
-            if (g4 == 0) sample_store(&sred[wn][wm * C::WTM + tt * 16 + l16][0], st);
-        }
-        __syncthreads();
-        for (int r = tid; r < BM; r += NT) {
-            const int tok = m0 + r;
-            if (tok >= M) continue;
-            SampleState st = sample_load(&sred[0][r][0]);
-#pragma unroll
-            for (int w = 1; w < WN; ++w) sample_merge(st, sample_load(&sred[w][r][0]));
-            sample_store(p.samp_part + ((size_t)tok * p.amax_slots + nt) * 2, st);
-        }
-    } else {                                                 // EPI_ARGMAX
-        __shared__ float2 red[WN][BM];
-        __shared__ float rsec[WN][BM];                         // runner-up values (top-2 gap asked)
-        const bool top2 = p.amax_sec != nullptr;
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            const int tok = m0 + wm * C::WTM + tt * 16 + l16;
-            float best = -INFINITY, second = -INFINITY;
-            int bi = 0x7fffffff;
-            if (tok < M) {
-#pragma unroll
-                for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int n = fbase + ft * 16 + g4 * 4 + i;       // increasing along the lane
-                        if (n < N) {
-                            const float v = acc[ft][tt][i];
-                            if (top2) second = fmaxf(second, fminf(best, v));
-                            if (v > best) { best = v; bi = n; }
-                            if (p.logits) p.logits[(size_t)tok * N + n] = v;
-                        }
-                    }
-            }
-#pragma unroll
-            for (int o = 16; o <= 32; o <<= 1) {
-                const float v2 = __shfl_xor(best, o, 64);
-                const int i2 = __shfl_xor(bi, o, 64);
-                if (top2) second = second_merge(best, second, v2, __shfl_xor(second, o, 64));
-                argmax_merge(best, bi, v2, i2);
-            }
-            if (g4 == 0) {
-                red[wn][wm * C::WTM + tt * 16 + l16] = make_float2(best, __int_as_float(bi));
-                if (top2) rsec[wn][wm * C::WTM + tt * 16 + l16] = second;
-            }
-        }
-        __syncthreads();
-        for (int r = tid; r < BM; r += NT) {
-            const int tok = m0 + r;
-            if (tok >= M || !seq_ok(p.len_snap, tok / p.Nq, p.Nq, p.cap)) continue;
-            float best = red[0][r].x, second = top2 ? rsec[0][r] : -INFINITY;
-            int bi = __float_as_int(red[0][r].y);
-#pragma unroll
-            for (int w = 1; w < WN; ++w) {
-                if (top2) second = second_merge(best, second, red[w][r].x, rsec[w][r]);
-                argmax_merge(best, bi, red[w][r].x, __float_as_int(red[w][r].y));
-            }
-            p.amax_part[(size_t)tok * p.amax_slots + nt] = make_float2(best, __int_as_float(bi));
-            if (top2) p.amax_sec[(size_t)tok * p.amax_slots + nt] = second;
-        }
-    }
+    big_epilogue<KIND, BN, BM, WN, WM>(acc, p, M, N, ffn, m0, nt, ks, tid, wn, wm, l16, g4);
 }
 
 struct BigPlan { int BN, BM, nmt, nnt, S, k_slice, grid; bool bal; };
