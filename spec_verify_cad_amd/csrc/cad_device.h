@@ -102,18 +102,25 @@ __device__ __forceinline__ void sample_init(SampleState& st) {
     st.yi = st.zi = 0x7fffffff;
 }
 
-// one logit v of id n (tempered value sv = v * inv_temp, Gumbel noise g)
+// one logit v of id n (tempered value sv = v * inv_temp, Gumbel noise g).  A state takes its
+// ids in increasing order, so a strict comparison keeps the lowest id among equal values.  No
+// branches: the log-sum-exp update uses the one weight exp(-|sv - m|), which is exp(m - sv) when
+// sv raises the maximum (s = s * w + 1) and exp(sv - m) otherwise (s = s + w).
 __device__ __forceinline__ void sample_add(SampleState& st, float sv, float g, int n, int draft) {
     const float pv = sv + g;
-    argmax_merge(st.yv, st.yi, pv, n);
-    if (n != draft) argmax_merge(st.zv, st.zi, pv, n);
-    else st.dl = sv;
-    if (sv > st.m) {
-        st.s = st.s * __expf(st.m - sv) + 1.f;
-        st.m = sv;
-    } else {
-        st.s += __expf(sv - st.m);
-    }
+    const bool ty = pv > st.yv;
+    st.yv = ty ? pv : st.yv;
+    st.yi = ty ? n : st.yi;
+    const bool nd = n != draft;
+    const bool tz = nd && pv > st.zv;
+    st.zv = tz ? pv : st.zv;
+    st.zi = tz ? n : st.zi;
+    st.dl = nd ? st.dl : sv;
+    const float d = sv - st.m;
+    const float w = __expf(-fabsf(d));
+    const bool up = d > 0.f;
+    st.s = up ? fmaf(st.s, w, 1.f) : st.s + w;
+    st.m = up ? sv : st.m;
 }
 
 __device__ __forceinline__ void sample_merge(SampleState& a, const SampleState& b) {

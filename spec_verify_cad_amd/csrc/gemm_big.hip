@@ -166,12 +166,27 @@ __device__ __forceinline__ void big_epilogue(const f32x4_t (&acc)[FT][TT], const
         // per row: Gumbel-perturbed maxima and the log-sum-exp over this tile's ids, merged over
         // the lane groups of a wave, then over the WN waves that share the rows
         __shared__ float4 sred[WN][BM][2];
+        // wave-uniform: this wave's columns all inside the vocabulary and no debug logits.  Then
+        // every row is scanned without per-value tests (a row past M takes row 0's draft and
+        // position; its state is never stored).
+        const bool plain = !p.logits && fbase + WTN <= N;
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             const int tok = m0 + wm * WTM + tt * 16 + l16;
             SampleState st;
             sample_init(st);
-            if (tok < M) {
+            if (plain) {
+                const SampleRow sr = sample_row(p, tok < M ? tok : 0);
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft) {
+                    const int n0 = fbase + ft * 16 + g4 * 4;
+                    const uint4 w = sample_bits(p, sr, n0);
+                    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sample_add(st, acc[ft][tt][i] * p.inv_temp, gumbel(ws[i]), n0 + i, sr.draft);
+                }
+            } else if (tok < M) {
                 const SampleRow sr = sample_row(p, tok);
 #pragma unroll
                 for (int ft = 0; ft < FT; ++ft) {
@@ -180,19 +195,23 @@ __device__ __forceinline__ void big_epilogue(const f32x4_t (&acc)[FT][TT], const
                     const uint4 w = sample_bits(p, sr, n0);
                     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int n = n0 + i;
-                        if (n < N) {
-                            const float v = acc[ft][tt][i];
-                            sample_add(st, v * p.inv_temp, gumbel(ws[i]), n, sr.draft);
-                            if (p.logits) p.logits[(size_t)tok * N + n] = v;
-                        }
-                    }
+                    for (int i = 0; i < 4; ++i)
+                        if (n0 + i < N) sample_add(st, acc[ft][tt][i] * p.inv_temp, gumbel(ws[i]), n0 + i, sr.draft);
                 }
+                if (p.logits)
+#pragma unroll
+                    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int n = fbase + ft * 16 + g4 * 4 + i;
+                            if (n < N) p.logits[(size_t)tok * N + n] = acc[ft][tt][i];
+                        }
             }
 #pragma unroll
             for (int o = 16; o <= 32; o <<= 1) sample_merge(st, sample_shfl_xor(st, o));
             if (g4 == 0) sample_store(&sred[wn][wm * WTM + tt * 16 + l16][0], st);
+            // one token tile's sampling state live at a time (the 256-row tile fits its registers)
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
         for (int r = tid; r < BM; r += NT) {
@@ -598,7 +617,6 @@ BigPlan big_plan(int kind, int M, int N, int K, int slices) {
     // on the 1.5B shape: 27.9 -> 24.7 us at 128 rows, 33.3 -> 29.1 us at 256)
     if (kind == EPI_SWIGLU && M <= 256 && (long)((M + t.BM - 1) / t.BM) * ((N / 2 + 95) / 96) <= device_cu_count())
         t.BN = 192;
-    if (kind == EPI_SAMPLE && t.BM > 128) t.BM = 128;  // the sampling state of 256 rows spills
     if (kind == EPI_QKV || kind == EPI_PARTIAL) {
         // narrow outputs: 128 x 64 tiles give more workgroups (and QKV one head per wave); for the
         // K-slice partials they also mean fewer slices, so less partial traffic for the row
