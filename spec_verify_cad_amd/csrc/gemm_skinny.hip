@@ -203,19 +203,34 @@ __global__ __launch_bounds__(NW * 64) void k_skinny(const uint16_t* __restrict__
 
     if constexpr (DB) {
         // two W buffers: the loads of the next unit are in flight while this one is reduced and
-        // finished (a finished workgroup re-reads its last unit once, from L2)
+        // finished (a finished workgroup re-reads a unit once, from L2).  One exit, at the top:
+        // with exits between the halves the compiler's wait counts at the loop head were merged
+        // conservatively and drained the prefetch before issuing the next one.
+        // (the 64-row form, 8 waves of 3 super-steps, measured 1.5 us slower in this shape at 64
+        // rows and keeps the loop with exits between the halves)
         uint4 wa[SSW][2], wb[SSW][2];
-        load_w(u, wa);
-        while (true) {
-            const int u1 = u + G;
-            load_w(u1 < units ? u1 : u, wb);
-            compute(u, wa);
-            if (u1 >= units) break;
-            const int u2 = u1 + G;
-            load_w(u2 < units ? u2 : u1, wa);
-            compute(u1, wb);
-            if (u2 >= units) break;
-            u = u2;
+        load_w(u, wa);                              // wa: unit u
+        if constexpr (TT <= 2) {
+            for (; u + G < units; u += 2 * G) {
+                load_w(u + G, wb);
+                compute(u, wa);
+                const int u2 = u + 2 * G;
+                load_w(u2 < units ? u2 : u + G, wa);
+                compute(u + G, wb);
+            }
+            if (u < units) compute(u, wa);
+        } else {
+            while (true) {
+                const int u1 = u + G;
+                load_w(u1 < units ? u1 : u, wb);
+                compute(u, wa);
+                if (u1 >= units) break;
+                const int u2 = u1 + G;
+                load_w(u2 < units ? u2 : u1, wa);
+                compute(u1, wb);
+                if (u2 >= units) break;
+                u = u2;
+            }
         }
     } else {
         uint4 wa[SSW][2];
@@ -272,11 +287,14 @@ int skinny_grid(int units, int S) {
 
 // Two W buffers (the next unit's loads in flight while this one is multiplied and finished) for
 // the LM head, whose workgroups walk many units: 79.6 / 85.2 us at 8 / 32 rows against 82.8 / 90.7
-// single-buffered.  The layer's projections have one or two units per workgroup, where the second
-// buffer only re-reads a unit (gate/up at 8 rows 15.5 -> 17.1 us), and the 7-super-step two-tile
-// form of the 7B shape spills with it, so those keep one buffer.
+// single-buffered (and 78.8 / 82.8 us once the loop lost its mid-loop exits), and for gate/up at
+// 33-64 rows (23.7 -> 21.0 us).  At fewer rows the projections have one or two units per
+// workgroup, where the second buffer mostly re-reads a unit (gate/up at 8 rows 15.0 -> 16.0 us),
+// and the 7-super-step two-tile form of the 7B shape spills with it, so those keep one buffer.
 template <int KIND, int TT, int SSW>
-constexpr bool two_buffers() { return KIND == EPI_ARGMAX && TT * SSW <= 12; }
+constexpr bool two_buffers() {
+    return (KIND == EPI_ARGMAX && TT * SSW <= 12) || (KIND == EPI_SWIGLU && TT == 4);
+}
 
 template <int KIND, int TT, int SSW, int NW, bool DB = two_buffers<KIND, TT, SSW>()>
 hipError_t go(const void* A, const void* W, int M, int N, int K, int ntiles, int S, const EpiParams& p,
