@@ -5,7 +5,8 @@
 // = W rows, B operand = token rows; lane (r, g) holds features 4g..4g+3 of token r of each block).
 // K advances 64 at a time through two LDS buffers: while the waves multiply out of one buffer,
 // the next stage sits in registers on its way to the other and the stage after that is being
-// fetched from HBM, so there is one barrier per stage.  Eight waves share a tile, two per SIMD,
+// fetched from HBM, so there is one barrier per stage; the column-tile loop splits each stage
+// into two MFMA halves around the barrier so that every LDS read and write overlaps multiplies.  Eight waves share a tile, two per SIMD,
 // so one wave's LDS and MFMA latencies hide behind the other's work.  Every epilogue runs from
 // registers:
 //   QKV     the wave's features are whole heads, a rotation pair (i, i + d/2) sits in the same
@@ -30,7 +31,12 @@
 
 namespace {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int BK64 = 64;
+// column tiles read their operands through buffer resources of byte offsets: every operand must
+// stay below this size
+constexpr size_t kPipeMaxBytes = 0x7FFFFFF0u;
 constexpr int BAL_MAX_CHUNKS = 4;
 // register stages of the balanced LM head: 3 for 64-token tiles, 2 for 128 (measured; the
 // column-tile schedule uses 2 and 1)
@@ -299,6 +305,7 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
     using C = BigCfg<KIND, BN, BM, WN, WM, BK>;
     constexpr int LDK = C::LDK;
     constexpr int FT = C::FT, TT = C::TT, WCH = C::WCH, ACH = C::ACH, NT = C::NT;
+    static_assert(BAL || BK == 64, "the column-tile pipeline takes K steps of 64 (two MFMA halves)");
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];   // 2 stages of [BN + BM][LDK]
 
     const int total = nmt * nnt * S;
@@ -335,28 +342,11 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
         aoff[c] = (uint32_t)(v ? m0 + r : 0) * (uint32_t)K + (ch % (BK / 8)) * 8;
     }
     const int kchunk = (tid % (BK / 8)) * 8;                  // same k offset for every chunk of a thread
-    // A stage in registers: raw loads plus their validity bits.  Every load is unconditional from
-    // a valid address (no load sits in a branch, so the wait counts stay exact) and the masking
-    // happens when the stage is written to LDS, so the loads of a stage stay in flight until then.
+    // A stage of the balanced schedule in registers: raw loads plus their validity bits.  Every
+    // load is unconditional from a valid address (no load sits in a branch, so the wait counts stay
+    // exact) and the masking happens when the stage is written to LDS, so the loads of a stage
+    // stay in flight until then.
     struct Stage { uint4 w[WCH], a[ACH]; uint32_t wok, aok; };
-    auto load_g = [&](int k0, Stage& r) {
-        const bool kin = k0 + kchunk < kend;
-        r.wok = kin ? wmask : 0u;
-        r.aok = kin ? amask : 0u;
-        // With several register stages every load stays in program order (a scheduling barrier
-        // after each): the compiler's wait counts at the loop head merge the loads' issue order
-        // from the prologue and from the previous step, and stay exact only if the orders agree.
-#pragma unroll
-        for (int c = 0; c < WCH; ++c) {
-            r.w[c] = *(const uint4*)(W + woff[c] + (((r.wok >> c) & 1) ? k0 : 0));
-            if constexpr (RS > 1) __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int c = 0; c < ACH; ++c) {
-            r.a[c] = *(const uint4*)(A + aoff[c] + (((r.aok >> c) & 1) ? k0 : 0));
-            if constexpr (RS > 1) __builtin_amdgcn_sched_barrier(0);
-        }
-    };
     // 16-byte chunk position of chunk c of tile row r: the chunk index XOR the row's low three
     // bits, so the 16 rows an MFMA fragment read touches spread over every bank group (rows are
     // 16-aligned in every read, so r mod 16 is all the swizzle needs)
@@ -409,14 +399,15 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
         }
     };
 
-    // RS register stages in a ring: stage kt is loaded into slot kt % RS, RS stages ahead, and
-    // at step kt written to LDS buffer kt & 1, then (after the barrier) multiplied.  Buffer kt & 1
-    // was last read at step kt - 2, and every wave has passed step kt - 1's barrier since, so one
-    // barrier per step suffices.  The loop is unrolled over a multiple of RS and of 2 so every
-    // slot and buffer index is a constant and the oldest loads always sit in the slot written
-    // next; loads are issued unconditionally (a stage past the slice reads valid addresses and
-    // is masked to zero), because a load inside a branch makes the compiler's wait counts at the
-    // join conservative and drains the pipeline before every LDS write.
+    // Balanced schedule: RS register stages in a ring.  Stage kt is loaded into slot kt % RS, RS
+    // stages ahead, and at step kt written to LDS buffer kt & 1, then (after the barrier)
+    // multiplied.  Buffer kt & 1 was last read at step kt - 2, and every wave has passed step
+    // kt - 1's barrier since, so one barrier per step suffices.  The loop is unrolled over a
+    // multiple of RS and of 2 so every slot and buffer index is a constant and the oldest loads
+    // always sit in the slot written next; loads are issued unconditionally (a stage past the
+    // slice reads valid addresses and is masked to zero), because a load inside a branch makes
+    // the compiler's wait counts at the join conservative and drains the pipeline before every
+    // LDS write.
 
     constexpr int UNR = RS % 2 ? 2 * RS : RS;
     if constexpr (BAL) {
@@ -554,23 +545,113 @@ __global__ __launch_bounds__(WN * WM * 64) void k_gemm_big(const uint16_t* __res
             }
         return;
     }
-    Stage r[RS];
+    {
+        // Column tiles: one register stage, pipelined across the K halves of a step.  Step t
+        // multiplies K half 0 out of registers while it reads half 1's fragments from LDS buffer
+        // t & 1, writes stage t + 1 to buffer (t + 1) & 1 and fetches stage t + 2; after the
+        // step's one barrier it multiplies half 1 while it reads half 0 of step t + 1 from the
+        // buffer just written.  Every LDS read and write thus overlaps the multiplies.  Buffer
+        // (t + 1) & 1 was last read in step t - 1's first half, before that step's barrier, and
+        // buffer t & 1 is written again only after step t's barrier, so one barrier per step is
+        // enough.  A fragment register is read again as soon as its last multiply is issued.
+        // Global loads go through buffer resources whose range check returns zero, so rows past
+        // the operand and K past the slice cost no traffic and need no masking.
+        constexpr uint32_t OOB = 0x7FFFFFF0u;           // buffer size; offsets from here read zero
+        const auto wres = __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)OOB, 0x00020000);
+        const auto ares = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)OOB, 0x00020000);
+        uint32_t wb[WCH], ab[ACH];                      // byte offsets at k = 0, OOB for rows outside
 #pragma unroll
-    for (int i = 0; i < RS; ++i) load_g(kbeg + i * BK, r[i]);
-    for (int kt0 = 0; kt0 < nk; kt0 += UNR) {
+        for (int c = 0; c < WCH; ++c) wb[c] = ((wmask >> c) & 1) ? 2u * woff[c] : OOB;
 #pragma unroll
-        for (int j = 0; j < UNR; ++j) {
-            const int kt = kt0 + j;
-            if (kt >= nk) break;
-            store_lds(j & 1, r[j % RS]);
-            load_g(kbeg + (kt + RS) * BK, r[j % RS]);
-            __syncthreads();
-            compute(j & 1);
+        for (int c = 0; c < ACH; ++c) ab[c] = ((amask >> c) & 1) ? 2u * aoff[c] : OOB;
+        u32x4_t sw_[WCH], sa_[ACH];                     // the stage in flight
+        auto fetch = [&](int k0) {
+            const uint32_t kb = k0 + kchunk < kend ? 2u * (uint32_t)k0 : OOB;
+#pragma unroll
+            for (int c = 0; c < WCH; ++c) sw_[c] = __builtin_amdgcn_raw_buffer_load_b128(wres, wb[c] + kb, 0, 0);
+#pragma unroll
+            for (int c = 0; c < ACH; ++c) sa_[c] = __builtin_amdgcn_raw_buffer_load_b128(ares, ab[c] + kb, 0, 0);
+        };
+        // this thread's stage chunks: tile row tid / 8 + c * NT / 8, chunk tid % 8; the swizzle
+        // depends on the row's low three bits only, the same for every c
+        const int srow = tid / (BK / 8), sch = tid % (BK / 8);
+        const int soff = srow * LDK + sw(srow, sch) * 8;
+        constexpr int RSTEP = NT / (BK / 8) * LDK;      // elements between a thread's chunks
+        auto put = [&](uint16_t* Ws, int c) {
+            if (c < WCH) *(u32x4_t*)(Ws + soff + c * RSTEP) = sw_[c];
+            else *(u32x4_t*)(Ws + BN * LDK + soff + (c - WCH) * RSTEP) = sa_[c - WCH];
+        };
+        auto rd_a = [&](const uint16_t* Ws, int kq, int ft) {
+            return *(const bf16x8_t*)(Ws + (wn * C::WTN + ft * 16 + l16) * LDK + sw(l16, kq * 4 + g4) * 8);
+        };
+        auto rd_b = [&](const uint16_t* Ws, int kq, int tt) {
+            return *(const bf16x8_t*)(Ws + BN * LDK + (wm * C::WTM + tt * 16 + l16) * LDK + sw(l16, kq * 4 + g4) * 8);
+        };
+        constexpr int NS = WCH + ACH;                   // stage chunks per thread
+        bf16x8_t fa[FT], fb0[TT], fb1[TT];              // W fragments; token fragments of the two halves
+        // the multiplies of one K half out of fa / fu; fa is refilled from (Rs, rkq) block by block
+        // as it frees up and the other half's token fragments go to fn; with STORE the stage is
+        // written to Ws and the next one fetched from k0n meanwhile (Rs and Ws are different buffers)
+        auto half = [&](const uint16_t* __restrict__ Rs, int rkq, const bf16x8_t(&fu)[TT], bf16x8_t(&fn)[TT],
+                        bool store, uint16_t* __restrict__ Ws, int k0n) {
+            if (store) {
+#pragma unroll
+                for (int c = 0; c < NS; ++c) put(Ws, c);
+                fetch(k0n);
+            }
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) {
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt)
+                    acc[ft][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ft], fu[tt], acc[ft][tt], 0, 0, 0);
+                fa[ft] = rd_a(Rs, rkq, ft);
+                if (ft < TT) fn[ft] = rd_b(Rs, rkq, ft);
+            }
+            // issue pattern: per feature block its multiplies with the block's share of stage chunks
+            // (write, then refetch of that register) between them, then the block's fragment reads
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) {
+                const int c0 = ft * NS / FT, c1 = (ft + 1) * NS / FT;   // stage chunks of this block
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+                    if (store && tt < c1 - c0) {
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // LDS write
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // global load
+                    }
+                }
+                if (store)
+                    for (int c = TT; c < c1 - c0; ++c) {
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    }
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // LDS reads
+                if (ft < TT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        };
+        // prologue: stage 0 in LDS buffer 0, stage 1 in flight, half 0 of step 0 in registers
+        fetch(kbeg);
+#pragma unroll
+        for (int c = 0; c < NS; ++c) put(smem, c);
+        fetch(kbeg + BK);
+        __syncthreads();
+        // (in the order the loop reads them, so the wait counts at the loop head agree)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+            fa[ft] = rd_a(smem, 0, ft);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ft < TT) fb0[ft] = rd_b(smem, 0, ft);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        for (int kt = 0; kt < nk; ++kt) {
+            uint16_t* cur = smem + (kt & 1) * C::STAGE;
+            uint16_t* nxt = smem + ((kt + 1) & 1) * C::STAGE;
+            half(cur, 1, fb0, fb1, true, nxt, kbeg + (kt + 2) * BK);
+            __syncthreads();
+            half(nxt, 0, fb1, fb0, false, nullptr, 0);
+        }
+        big_epilogue<KIND, BN, BM, WN, WM>(acc, p, M, N, ffn, m0, nt, ks, tid, wn, wm, l16, g4);
     }
-
-    // ---------------------------------------------------------------- epilogues from registers
-    big_epilogue<KIND, BN, BM, WN, WM>(acc, p, M, N, ffn, m0, nt, ks, tid, wn, wm, l16, g4);
 }
 
 struct BigPlan { int BN, BM, nmt, nnt, S, k_slice, grid; bool bal; };
@@ -580,6 +661,10 @@ hipError_t go_big(const void* A, const void* W, int M, int N, int K, int ffn, co
                   hipStream_t s) {
     auto kern = k_gemm_big<KIND, BN, BM, WN, WM, BK, RS, BAL>;
     constexpr size_t smem = BigCfg<KIND, BN, BM, WN, WM, BK>::SMEM;
+    if (!BAL) {
+        const size_t wrows = KIND == EPI_SWIGLU ? 2 * (size_t)ffn : (size_t)N;
+        if (wrows * K * 2 >= kPipeMaxBytes || (size_t)M * K * 2 >= kPipeMaxBytes) return hipErrorInvalidValue;
+    }
     static bool attr = false;
     if (!attr) {
         const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -664,12 +749,12 @@ hipError_t big_dispatch(const void* A, const void* W, int M, int N, int K, int s
     const BigPlan t = big_plan(KIND, M, N, K, slices);
     p.k_slice = t.k_slice;
     const int ffn = KIND == EPI_SWIGLU ? p.ffn : 0;
-    if (t.BN == 128) return go_big<KIND, 128, 64, 1, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
+    if (t.BN == 128) return go_big<KIND, 128, 64, 1, 4, 64, 1>(A, W, M, N, K, ffn, t, p, s);
     if constexpr (KIND == EPI_SWIGLU)
         if (t.BN == 192) {
-            if (t.BM == 64) return go_big<KIND, 192, 64, 2, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
-            if (t.BM == 128) return go_big<KIND, 192, 128, 2, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
-            return go_big<KIND, 192, 256, 2, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
+            if (t.BM == 64) return go_big<KIND, 192, 64, 2, 4, 64, 1>(A, W, M, N, K, ffn, t, p, s);
+            if (t.BM == 128) return go_big<KIND, 192, 128, 2, 4, 64, 1>(A, W, M, N, K, ffn, t, p, s);
+            return go_big<KIND, 192, 256, 2, 4, 64, 1>(A, W, M, N, K, ffn, t, p, s);
         }
     if constexpr (KIND == EPI_ARGMAX) {
         // debug outputs (logits, runner-up values) have an instantiation of their own
@@ -682,7 +767,7 @@ hipError_t big_dispatch(const void* A, const void* W, int M, int N, int K, int s
                        : go_big<KIND, 256, 128, 2, 4, 64, BAL_RS128, 1>(A, W, M, N, K, ffn, t, p, s);
     }
     switch (t.BM) {
-        case 64: return go_big<KIND, 256, 64, 2, 4, 64, 2>(A, W, M, N, K, ffn, t, p, s);
+        case 64: return go_big<KIND, 256, 64, 2, 4, 64, 1>(A, W, M, N, K, ffn, t, p, s);
         case 128: return go_big<KIND, 256, 128, 2, 4, 64, 1>(A, W, M, N, K, ffn, t, p, s);
         default: return go_big<KIND, 256, 256, 2, 4, 64, 1>(A, W, M, N, K, ffn, t, p, s);
     }
