@@ -68,7 +68,8 @@ __device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r >> 1) & 7); 
 // are combined through LDS at the end.  This halves each wave's chain per tile for groups whose
 // rows fill few waves (the PLD verify: 66 rows, five row blocks).
 template <int DH, int MODE, int NWV, int NPH = 1>
-__global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+// (4-wave tiles run two workgroups per CU: the register budget must leave two waves per SIMD)
+__global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                                    const uint16_t* __restrict__ vc, const int32_t* __restrict__ len_snap,
                                                    int Nq, int Hq, int Hkv, int cap, int Dblk,
                                                    int nsplit, float* __restrict__ part_o,
@@ -124,140 +125,280 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
     const float sl2 = 1.4426950408889634f / sqrtf((float)DH);   // log2(e)/sqrt(d)
     // m_run: the query's reference maximum (log2 units), shared by its 4 lanes; it may trail the
     // running maximum by up to RESCALE, so weights stay <= 2^RESCALE and the accumulators are
-    // rescaled only when some lane of the wave exceeds that.  l_lane: this lane's share of the
-    // weight sum (its 8 keys of every step), summed over the 4 lanes at the end.
-    constexpr float RESCALE = 8.f;
-    float m_run = -INFINITY, l_lane = 0.f;
+    // rescaled only when some lane of the wave exceeds that.  It starts at a finite M_NONE (below
+    // any score), so a weight exp2(s - m_run) needs no guard: a masked score (-inf) gives 0, and
+    // the first visible score triggers a rescale; M_NONE is reported as -inf.  l_lane: this
+    // lane's share of the weight sum (its 8 keys of every step), summed over the 4 lanes at the end.
+    constexpr float RESCALE = 8.f, M_NONE = -1e30f;
+    float m_run = M_NONE, l_lane = 0.f;
     f32x4_t oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // keys this lane's query sees, below kend: [0, vis_a) and [vis_lo, vis_hi] (causal: the
+    // cached prefix and the span up to the query's own position; block mode: the prefix and the
+    // query's candidate block up to its position in it); none for a lane without a query
+    int vis_a, vis_lo, vis_hi;
+    if constexpr (MODE == CAD_MASK_BLOCK_TRI) {
+        const int w = it / Dblk, j = it % Dblk;
+        vis_a = min(kend, len);
+        vis_lo = len + w * Dblk;
+        vis_hi = min(kend - 1, len + w * Dblk + j);
+    } else {
+        vis_a = min(kend, len + it + 1);
+        vis_lo = 1;
+        vis_hi = 0;
+    }
+    if (!qlive) { vis_a = INT_MIN / 2; vis_lo = 1; vis_hi = 0; }
 
     const size_t head = (size_t)b * Hkv + g;
     const uint16_t* kbase = kc + head * cap * DH;
     const uint16_t* vbase = vc + head * DH * cap;          // dim-major: row = one dim over all slots
 
-    // One tile in registers on its way to LDS.  The loads stay in program order (a scheduling
-    // barrier after each), so the compiler's wait counts at the loop head, which merge the issue
-    // order of the prologue and of the previous step, wait for the oldest tile only.  Every load
-    // is issued unconditionally from a valid address: a K row past kend reads slot 0 (its scores are masked), a V group past kend reads
-    // slot 0 and is zeroed (so masked keys add exactly zero); cap is a multiple of 4, so an 8-byte
-    // V group never crosses the end of a row.
+    // K/V in registers on their way to LDS.  K runs one tile ahead of V: during step t the K rows
+    // of tile t + 2 and the V rows of tile t + 1 are fetched, so that step t can multiply tile
+    // t + 1's scores while it turns tile t's scores into weights.  The loads stay in program order
+    // (a scheduling barrier after each), so the compiler's wait counts at the loop head, which
+    // merge the issue order of the prologue and of the previous step, wait for the oldest loads
+    // only.  Every load is issued unconditionally from a valid address: a K row past kend reads
+    // slot 0 (its scores are masked), a V group past kend reads slot 0 and is zeroed (so masked
+    // keys add exactly zero); cap is a multiple of 4, so an 8-byte V group never crosses the end
+    // of a row.
     struct Tile { u32x4_t k[KLD]; u32x2_t v[VLD]; };
     // (when the thread count does not divide a tile, the surplus threads of the last round load
     // a clamped, valid chunk and store nothing)
-    auto load = [&](int t0, Tile& r) __attribute__((always_inline)) {
+    auto load_k = [&](int tk0, Tile& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
-            const int id = min(tid + NT * i, KTOT - 1), key = t0 + id / KCH;
+            const int id = min(tid + NT * i, KTOT - 1), key = tk0 + id / KCH;
             r.k[i] = *(const u32x4_t*)(kbase + (size_t)(key < kend ? key : 0) * DH + (id % KCH) * 8);
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    auto load_v = [&](int tv0, Tile& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
-            const int id = min(tid + NT * i, VTOT - 1), key0 = t0 + 4 * (id % (TK / 4));
+            const int id = min(tid + NT * i, VTOT - 1), key0 = tv0 + 4 * (id % (TK / 4));
             r.v[i] = *(const u32x2_t*)(vbase + (size_t)(id / (TK / 4)) * cap + (key0 < kend ? key0 : 0));
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    auto load = [&](int tk0, int tv0, Tile& r) __attribute__((always_inline)) {
+        load_k(tk0, r);
+        load_v(tv0, r);
+    };
     // V tile layout: the 8 keys an MFMA lane needs (4g..4g+3 and 16+4g..16+4g+3 of a 32-key step)
-    // form one 16-byte chunk, chunk kq*4 + g of the dim row.
-    auto store = [&](int t0, int buf, const Tile& r) __attribute__((always_inline)) {
+    // form one 16-byte chunk, chunk kq*4 + g of the dim row.  (K into buffer kb, V of the tile at
+    // tv0 into buffer vb.)
+    auto store_k = [&](int kb, const Tile& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
             const int id = tid + NT * i, key = id / KCH;
-            if (KTOT % NT == 0 || id < KTOT) ks[buf][key * KCH + swz_k<DH>(key, id % KCH)] = r.k[i];
+            if (KTOT % NT == 0 || id < KTOT) ks[kb][key * KCH + swz_k<DH>(key, id % KCH)] = r.k[i];
         }
+    };
+    auto store_v = [&](int tv0, int vb, const Tile& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int id = tid + NT * i, row = id / (TK / 4), grp = id % (TK / 4);
             if (VTOT % NT != 0 && id >= VTOT) continue;
-            const int n = kend - (t0 + 4 * grp);                   // valid keys of the group
+            const int n = kend - (tv0 + 4 * grp);                  // valid keys of the group
             u32x2_t w = r.v[i];
             w.x &= n >= 2 ? 0xFFFFFFFFu : (n == 1 ? 0xFFFFu : 0u);
             w.y &= n >= 4 ? 0xFFFFFFFFu : (n == 3 ? 0xFFFFu : 0u);
             const int kq = grp >> 3, gq = grp & 7;
             const int c = swz_v(row, kq * 4 + (gq & 3));
-            ((u32x2_t*)vs[buf])[(row * (TK / 8) + c) * 2 + (gq >> 2)] = w;
+            ((u32x2_t*)vs[vb])[(row * (TK / 8) + c) * 2 + (gq >> 2)] = w;
         }
     };
-    // one 64-key step of the wave's 16 rows out of LDS buffer buf (keys k0 .. k0+63): four
-    // 16-key score blocks, one softmax update, then two 32-key value products
-    auto step = [&](int k0, int buf) __attribute__((always_inline)) {
-        __builtin_amdgcn_iglp_opt(0);          // interleave the LDS fragment reads with the MFMAs
-        f32x4_t st[KB];                         // score block kb of the tile is st[kb - ph*KB]
+    auto store = [&](int tv0, int kb, int vb, const Tile& r) __attribute__((always_inline)) {
+        store_k(kb, r);
+        store_v(tv0, vb, r);
+    };
+    // this wave's four (two with two key phases) 16-key score blocks of the K tile in buffer kb:
+    // S^T = K . Q^T, score block kb of the tile is st[kb - ph*KB]
+    auto scores = [&](int kb, f32x4_t(&st)[KB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kbi = 0; kbi < KB; ++kbi) {
             const int key = (ph * KB + kbi) * 16 + l16;
             st[kbi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int d = 0; d < DS; ++d) {
-                const u32x4_t kv = ks[buf][key * KCH + swz_k<DH>(key, d * 4 + g4)];
+                const u32x4_t kv = ks[kb][key * KCH + swz_k<DH>(key, d * 4 + g4)];
                 st[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&kv, qf[d], st[kbi], 0, 0, 0);
             }
         }
-        // S^T[key][query]: lane holds keys kb*16 + 4*g4 + i of query l16.  A step wholly below
-        // the cached length and kend needs no mask (every cached key is visible to every row).
-        const bool full = k0 + TK <= kend && k0 + TK <= len;
+    };
+    // mask the scores of the tile at keys k0.. (S^T[key][query]: lane holds keys
+    // k0 + (ph*KB + kb)*16 + 4*g4 + i of query l16) to -inf outside the lane's visible keys and
+    // return the lane's maximum in log2 units; the scores stay unscaled (the weights fold the
+    // 1/sqrt(d) scale into their exponent).  One compare per score against per-tile bounds
+    // (bitwise: short-circuit tests made the compiler branch per score).
+    auto mask_max = [&](int k0, f32x4_t(&st)[KB]) __attribute__((always_inline)) {
+        const int base = k0 + ph * KB * 16 + g4 * 4;
+        const int A = vis_a - base, L = vis_lo - base, H = vis_hi - base;
         float lmax = -INFINITY;
 #pragma unroll
         for (int kbi = 0; kbi < KB; ++kbi)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = k0 + (ph * KB + kbi) * 16 + g4 * 4 + i;
-                const bool al = full || (qlive && key < kend && key_allowed<MODE>(key, len, it, Dblk));
-                const float sv = al ? st[kbi][i] * sl2 : -INFINITY;
+                const int c = kbi * 16 + i;
+                bool al = c < A;
+                if constexpr (MODE == CAD_MASK_BLOCK_TRI) al = al | ((c >= L) & (c <= H));
+                const float sv = al ? st[kbi][i] : -INFINITY;
                 st[kbi][i] = sv;
                 lmax = fmaxf(lmax, sv);
             }
-        if (__ballot(lmax > m_run + RESCALE) != 0) {      // wave-uniform, rare after the first step
+        return lmax * sl2;
+    };
+    // lazy rescale: only when some lane of the wave exceeds the reference maximum by RESCALE
+    auto rescale = [&](float lmax) __attribute__((always_inline)) {
+        if (__ballot(lmax > m_run + RESCALE) != 0) {      // wave-uniform, rare after the first tile
             float tmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
             const float m_new = fmaxf(m_run, tmax);
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             l_lane *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
             m_run = m_new;
         }
+    };
+    // P^T fragment of keys 32kq ..: k-slot 8*g4 + i <- key 4*g4 + i (block 2kq), 8*g4 + 4 + i <-
+    // key 16 + 4*g4 + i (block 2kq + 1); each weight as bf16 hi + bf16 lo (both round to nearest
+    // even, two keys per conversion)
+    auto weights = [&](int kqi, const f32x4_t(&st)[KB], bf16x8_t& phi, bf16x8_t& pl) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kqi = 0; kqi < 2 / NPH; ++kqi) {
-            // P^T fragment of keys k0 + 32kq ..: k-slot 8*g4 + i <- key 4*g4 + i (block 2kq),
-            // 8*g4 + 4 + i <- key 16 + 4*g4 + i (block 2kq + 1); each weight as bf16 hi + bf16 lo
-            // (both round to nearest even, two keys per conversion)
-            const int kq = ph * (2 / NPH) + kqi;
+        for (int j = 0; j < 4; ++j) {
+            const int kb = 2 * kqi + (j >> 1), i = (j & 1) * 2;     // index into st
+            const f32x2_t pv = f32x2_t{__builtin_amdgcn_exp2f(fmaf(st[kb][i], sl2, -m_run)),
+                                       __builtin_amdgcn_exp2f(fmaf(st[kb][i + 1], sl2, -m_run))};
+            const bf16x2_t h = __builtin_convertvector(pv, bf16x2_t);
+            const bf16x2_t lo = __builtin_convertvector(pv - __builtin_convertvector(h, f32x2_t), bf16x2_t);
+            l_lane += pv.x + pv.y;
+            phi[2 * j] = h.x; phi[2 * j + 1] = h.y;
+            pl[2 * j] = lo.x; pl[2 * j + 1] = lo.y;
+        }
+    };
+    auto values = [&](int kqi, int vb, const bf16x8_t& phi, const bf16x8_t& pl) __attribute__((always_inline)) {
+        const int kq = ph * (2 / NPH) + kqi;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int row = db * 16 + l16;
+            const u32x4_t vv = vs[vb][row * (TK / 8) + swz_v(row, kq * 4 + g4)];
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, phi, oacc[db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, pl, oacc[db], 0, 0, 0);
+        }
+    };
+    // One 64-key step of tile t at keys k0 (its scores in cur, masked, the reference maximum
+    // already updated; its V in buffer vb), with tile t + 1's scores (K in buffer kbn) going to
+    // nxt: the weights of tile t are formed while tile t + 1's score MFMAs run, and tile t + 1's
+    // mask and maximum while tile t's value MFMAs run; the issue order is pinned below.
+    auto step = [&](int k0, int kbn, int vb, f32x4_t(&cur)[KB], f32x4_t(&nxt)[KB]) __attribute__((always_inline)) {
+        constexpr int NKQ = 2 / NPH;
+        bf16x8_t phi[NKQ], pl[NKQ];
+#pragma unroll
+        for (int kqi = 0; kqi < NKQ; ++kqi) weights(kqi, cur, phi[kqi], pl[kqi]);
+        scores(kbn, nxt);
+#pragma unroll
+        for (int kqi = 0; kqi < NKQ; ++kqi) values(kqi, vb, phi[kqi], pl[kqi]);
+        const float lmax = mask_max(k0 + TK, nxt);
+        // issue pattern: the score reads, then each score MFMA with a share of the weight
+        // arithmetic; then each value MFMA (its V read ahead) with a share of the masking
+        constexpr int NS = KB * DS, NV = 2 * NKQ * DB;         // score and value MFMAs
+#pragma unroll
+        for (int i = 0; i < NS; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K reads
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                          // VALU
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // V read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                          // VALU
+        }
+        rescale(lmax);
+    };
+
+    // tile t's weights and value products only (the last tile of a split)
+    auto last = [&](int vb, const f32x4_t(&cur)[KB]) __attribute__((always_inline)) {
+        constexpr int NKQ = 2 / NPH;
+#pragma unroll
+        for (int kqi = 0; kqi < NKQ; ++kqi) {
             bf16x8_t phi, pl;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int kb = 2 * kqi + (j >> 1), i = (j & 1) * 2;     // index into st
-                const f32x2_t pv = m_run == -INFINITY
-                                       ? f32x2_t{0.f, 0.f}
-                                       : f32x2_t{__builtin_amdgcn_exp2f(st[kb][i] - m_run),
-                                                 __builtin_amdgcn_exp2f(st[kb][i + 1] - m_run)};
-                const bf16x2_t h = __builtin_convertvector(pv, bf16x2_t);
-                const bf16x2_t lo = __builtin_convertvector(pv - __builtin_convertvector(h, f32x2_t), bf16x2_t);
-                l_lane += pv.x + pv.y;
-                phi[2 * j] = h.x; phi[2 * j + 1] = h.y;
-                pl[2 * j] = lo.x; pl[2 * j + 1] = lo.y;
-            }
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int row = db * 16 + l16;
-                const u32x4_t vv = vs[buf][row * (TK / 8) + swz_v(row, kq * 4 + g4)];
-                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, phi, oacc[db], 0, 0, 0);
-                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, pl, oacc[db], 0, 0, 0);
-            }
+            weights(kqi, cur, phi, pl);
+            values(kqi, vb, phi, pl);
         }
     };
 
-    // tile t is copied to LDS buffer t & 1 at the start of its step (buffer t & 1 was last read
-    // two steps earlier, before the previous barrier), and tile t + 1 is fetched meanwhile
-    Tile r;
-    load(kbeg, r);
-    for (int t0 = kbeg, t = 0; t0 < kend; t0 += TK, ++t) {
-        store(t0, t & 1, r);
-        load(t0 + TK, r);
+    f32x4_t st0[KB], st1[KB];
+    Tile r, r1;
+    if (NPH == 1 && kend - kbeg <= TK) {
+        // one tile (every split of a short span): fetched, copied, scored and multiplied in turn
+        // (the two-phase tile serves long histories only)
+        load(kbeg, kbeg, r);
+        store(kbeg, 0, 0, r);
         __syncthreads();
-        if (wlive) step(t0, t & 1);
+        if (wlive) {
+            scores(0, st0);
+            rescale(mask_max(kbeg, st0));
+            last(0, st0);
+        }
+    } else {
+        // Prologue: tiles 0 and 1 fetched together (one memory round trip); tile 0's K through
+        // buffer 0, its scores, mask and reference maximum; then tile 1's K to buffer 1 and tile
+        // 0's V to buffer 0, with tile 2's K fetched behind tile 1's V.  Step t runs on K buffer
+        // (t + 1) & 1 and V buffer t & 1; after it the K of tile t + 2 goes to buffer t & 1 (last
+        // read by tile t's scores, in step t - 1) and the V of tile t + 1 to buffer (t + 1) & 1
+        // (last read in step t - 1), both before the barrier that opens step t + 1.  The last
+        // tile takes its weights and values only (one-phase tiles).  The loop is unrolled by two
+        // so the score sets and buffers are constants.
+        load(kbeg, kbeg, r);
+        load(kbeg + TK, kbeg + TK, r1);
+        store_k(0, r);
+        __syncthreads();
+        if (wlive) {
+            scores(0, st0);
+            rescale(mask_max(kbeg, st0));
+        }
+        store_k(1, r1);                                    // K of tile 1
+        store_v(kbeg, 0, r);                               // V of tile 0
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) r.v[i] = r1.v[i];   // tile 1's V, in flight
+        load_k(kbeg + 2 * TK, r);
+        __syncthreads();
+        // (the two-phase tile keeps a full step for its last tile: the peeled form spilled
+        // registers there, and its splits hold hundreds of tiles)
+        for (int t0 = kbeg;;) {
+            if constexpr (NPH == 1) {
+                if (t0 + TK >= kend) {
+                    if (wlive) last(0, st0);
+                    break;
+                }
+            } else if (t0 >= kend) {
+                break;
+            }
+            if (wlive) step(t0, 1, 0, st0, st1);
+            store(t0 + TK, 0, 1, r);
+            load(t0 + 3 * TK, t0 + 2 * TK, r);
+            __syncthreads();
+            t0 += TK;
+            if constexpr (NPH == 1) {
+                if (t0 + TK >= kend) {
+                    if (wlive) last(1, st1);
+                    break;
+                }
+            } else if (t0 >= kend) {
+                break;
+            }
+            if (wlive) step(t0, 0, 1, st1, st0);
+            store(t0 + TK, 1, 0, r);
+            load(t0 + 3 * TK, t0 + 2 * TK, r);
+            __syncthreads();
+            t0 += TK;
+        }
     }
 
     float l_run = l_lane + __shfl_xor(l_lane, 16, 64);
@@ -281,8 +422,9 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
         if (ph == 1) return;
         const float2 o1ml = ml1[slot];
         const float m = fmaxf(m_run, o1ml.x);
-        const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-        const float a1 = o1ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o1ml.x - m);
+        // (both maxima are finite, M_NONE at the least)
+        const float a0 = __builtin_amdgcn_exp2f(m_run - m);
+        const float a1 = __builtin_amdgcn_exp2f(o1ml.x - m);
         l_run = l_run * a0 + o1ml.y * a1;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -303,7 +445,7 @@ __global__ __launch_bounds__(NWV * 64) void k_attn_bf16(const uint16_t* __restri
 #pragma unroll
     for (int db = 0; db < DB; ++db) *(f32x4_t*)(part_o + pidx * DH + db * 16 + g4 * 4) = oacc[db];
     if (g4 == 0) {
-        part_ml[pidx * 2 + 0] = m_run;
+        part_ml[pidx * 2 + 0] = m_run == M_NONE ? -INFINITY : m_run;   // no visible key: -inf
         part_ml[pidx * 2 + 1] = l_run;
     }
 }
