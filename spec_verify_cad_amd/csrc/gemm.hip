@@ -211,8 +211,11 @@ int gemm_partial_slices(int dtype, int M, int N, int K) {
 
 // A bf16 QKV projection the weight-streaming kernel does not take runs as K-slice partials plus
 // a row kernel for RoPE and the K/V append: its output is too narrow to fill the chip otherwise.
+// (the unsplit tiled QKV projection takes ~21 us at any row count; split into K-slice partials
+// plus the finishing row kernel it is faster up to 256 rows, and no faster beyond: at 704 rows
+// the unsplit form measured 5-10 us faster per batched PLD round)
 bool gemm_qkv_split(int dtype, int M, int K) {
-    return dtype == CAD_DTYPE_BF16 && !skinny_supports(EPI_QKV, M, K);
+    return dtype == CAD_DTYPE_BF16 && !skinny_supports(EPI_QKV, M, K) && M <= 256;
 }
 
 hipError_t launch_gemm(int dtype, int kind, const void* A, const void* W, int M, int N, int K, int slices,
