@@ -517,6 +517,30 @@ def test_small_bf16_ragged_cache_lengths_match_oracle(small, mode, W, D, Nq):
             compare_cache(cache, b, ocs[b], L0, L0 + Nq, "bf16", what=f"span rows b={b} len={L0}")
 
 
+def test_small_bf16_multi_tile_splits_match_oracle(small):
+    # 96-row spans over caches of 0..920 positions: three 128-row attention tiles per GQA group
+    # and 7 key splits, so the longer sequences give each split two or three 64-key tiles (the
+    # attention's cross-tile pipeline, its last tile ragged) while the short ones keep one-tile
+    # splits
+    w, dl, OL = small
+    lens = [0, 200, 450, 700, 850, 920]
+    B, Nq, cap = len(lens), 96, 1024
+    log("small bf16 multi-tile attention splits")
+    cache = cad.DeviceCache(SMALL, B, cap)
+    ocs = []
+    for b, L0 in enumerate(lens):
+        oc = O.cache_from_tokens(OL, synth.uniform_tokens(170 + b, L0, SMALL.vocab), cap)
+        upload_oracle_cache(cache, b, oc, "bf16")
+        ocs.append(oc)
+    span = np.stack([synth.uniform_tokens(180 + b, Nq, SMALL.vocab) for b in range(B)])
+    g = run_forward(dl, cache, span, flags=cad.COMMIT_ALL)
+    assert list(cache.len.cpu().numpy()) == [L0 + Nq for L0 in lens]
+    for b, L0 in enumerate(lens):
+        ref = O.span_forward(OL, ocs[b], span[b])
+        compare(g, ref, rows=slice(b * Nq, (b + 1) * Nq), what=f"multi-tile b={b} len={L0}")
+        compare_cache(cache, b, ocs[b], L0, L0 + Nq, "bf16", what=f"span rows b={b} len={L0}")
+
+
 def test_small_bf16_span_equals_decode_steps_on_gpu(small):
     w, dl, OL = small
     log("small bf16 span vs gpu decode steps")
