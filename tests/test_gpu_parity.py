@@ -273,11 +273,13 @@ def test_small_bf16_span_matches_oracle(small, Nq):
         compare_cache(cache, b, oc, L0, L0 + Nq, "bf16", what=f"span rows b={b}")
 
 
-@pytest.mark.parametrize("B, Nq", [(3, 12), (3, 40), (1, 97)])
+@pytest.mark.parametrize("B, Nq", [(3, 12), (3, 40), (1, 97), (3, 100)])
 def test_small_bf16_lm_head_without_logits_matches_oracle(small, B, Nq):
     # 33..128 LM-head rows run on balanced vocabulary ranges (the 5003-id vocabulary makes short
-    # last chunks); the forward without a logits output is its own kernel instantiation, so its
-    # argmax is checked against the oracle and against the forward that writes the logits
+    # last chunks), 300 rows on 256 x 256 column tiles (a ragged last column and row tile); the
+    # forward without a logits output is its own kernel instantiation (and the column tiles' scan
+    # without bounds tests), so its argmax is checked against the oracle and against the forward
+    # that writes the logits
     w, dl, OL = small
     log(f"small bf16 LM head without logits B={B} Nq={Nq}")
     L0, cap = 150, 320
