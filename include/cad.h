@@ -171,8 +171,8 @@ int cad_ngram_lookup_longest(const int32_t *ctx, int64_t ctx_stride, const int32
  * CAD_LOGITS_LAST runs the final norm, LM head and argmax for row Nq-1 of each sequence; the
  * cache rows and hidden_out are those of a full forward.
  * Errors: CAD_EINVAL (also: CAD_LOGITS_LAST with the block mask), CAD_EUNSUPPORTED (also: cap
- * not a multiple of 4), CAD_EWORKSPACE, CAD_EHIP; per sequence CAD_ECAPACITY in kv->err when
- * len + Nq > cap.
+ * not a multiple of 4, or one head's bf16 K cache, cap * head_dim * 2 bytes, of 2 GiB or more),
+ * CAD_EWORKSPACE, CAD_EHIP; per sequence CAD_ECAPACITY in kv->err when len + Nq > cap.
  */
 int cad_span_forward(const cad_layer_desc *layer, const cad_kv_desc *kv,
                      const int32_t *tokens, int B, int Nq,

@@ -18,6 +18,8 @@
 // writes (m, l, O) partials and a merge kernel combines them.
 //
 // fp32 path: one workgroup per (row, q head), plain two-pass softmax over all keys.
+#include <type_traits>
+
 #include "cad_device.h"
 
 namespace {
@@ -63,6 +65,11 @@ __device__ __forceinline__ int swz_k(int r, int c) {
 }
 __device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r >> 1) & 7); }   // 128-byte rows
 
+// 16 bytes per lane from a buffer straight into LDS: lane i's bytes at voff land at lds + 16 i
+__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t res, uint32_t lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voff, 0, 0, 0);
+}
+
 // NPH key phases: with NPH = 2 the waves form NWV/2 row blocks twice over, and phase p takes
 // keys 32p .. 32p+31 of every tile (its own running maximum and sums); the two phases' states
 // are combined through LDS at the end.  This halves each wave's chain per tile for groups whose
@@ -85,9 +92,20 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
     constexpr int KLD = (KTOT + NT - 1) / NT;   // K chunks each thread copies per tile
     constexpr int VLD = (VTOT + NT - 1) / NT;   // 4-key V groups each thread copies per tile
     static_assert(NPH == 1 || NPH == 2, "one or two key phases");
-    __shared__ u32x4_t ks[2][TK * KCH];
+    // K tiles land in LDS straight from memory, two steps ahead of their scores (three buffers);
+    // V tiles come through registers, also two steps ahead (two register sets).  The K buffers
+    // are separate variables: the compiler then tells a read of one from a copy still landing
+    // in another and waits only where they meet.
+    constexpr bool DEEP = NWV >= 8;
+    constexpr int KSZ = TK * KCH;
+    __shared__ u32x4_t ks0[DEEP ? KSZ : 1], ks1[DEEP ? KSZ : 1], ks2[DEEP ? KSZ : 1];
+    __shared__ u32x4_t ksr[DEEP ? 1 : 2][DEEP ? 1 : KSZ];     // (the one-tile lead's two buffers)
     __shared__ u32x4_t vs[2][DH * (TK / 8)];
 
+    auto KS = [&](int i) __attribute__((always_inline)) -> u32x4_t* {
+        if constexpr (DEEP) return i == 0 ? ks0 : (i == 1 ? ks1 : ks2);
+        else return ksr[i];
+    };
     const int split = blockIdx.x, rtile = blockIdx.y;
     const int bg = blockIdx.z, b = bg / Hkv, g = bg % Hkv;
     const int G = Hq / Hkv, Rg = Nq * G;
@@ -109,6 +127,7 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
     const int kbeg = split * chunk;
     int kend = min(kbeg + chunk, len + it_max + 1);
     if (!ok) kend = kbeg;
+    if constexpr (DEEP) kend = __builtin_amdgcn_readfirstlane(kend);   // (uniform loop exits)
 
     bf16x8_t qf[DS];
     {
@@ -175,7 +194,7 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto load_v = [&](int tv0, Tile& r) __attribute__((always_inline)) {
+    auto load_v = [&](int tv0, auto& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int id = min(tid + NT * i, VTOT - 1), key0 = tv0 + 4 * (id % (TK / 4));
@@ -194,10 +213,10 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
             const int id = tid + NT * i, key = id / KCH;
-            if (KTOT % NT == 0 || id < KTOT) ks[kb][key * KCH + swz_k<DH>(key, id % KCH)] = r.k[i];
+            if (KTOT % NT == 0 || id < KTOT) KS(kb)[key * KCH + swz_k<DH>(key, id % KCH)] = r.k[i];
         }
     };
-    auto store_v = [&](int tv0, int vb, const Tile& r) __attribute__((always_inline)) {
+    auto store_v = [&](int tv0, int vb, const auto& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int id = tid + NT * i, row = id / (TK / 4), grp = id % (TK / 4);
@@ -215,6 +234,52 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
         store_k(kb, r);
         store_v(tv0, vb, r);
     };
+    // Loads of the two-tile lead (below): each goes through a buffer resource whose base is the
+    // tile's first key, with per-lane byte offsets that stay fixed for the whole loop, so no
+    // address register of a load in flight is ever rewritten (the compiler would wait for the
+    // load before reusing one).  K rows of the tile at tk0 go straight into LDS buffer kb: each
+    // wave copies 1 KB blocks of the swizzled tile, lane i the 16 bytes at block offset 16 i,
+    // i.e. the logical chunk the swizzle puts there (it is its own inverse); with more waves than
+    // blocks some repeat a block.  Rows past kend hold whatever the cache holds (their scores
+    // are masked) and rows past the cache's end read zero.  V groups are loaded into registers
+    // the same way; past kend they are zeroed when stored to LDS.
+    constexpr int KBLK = TK * KCH / 64, KD = (KBLK + NWV - 1) / NWV;
+    uint32_t koff[KD], voff[VLD];
+#pragma unroll
+    for (int j = 0; j < KD; ++j) {
+        const int e = ((__builtin_amdgcn_readfirstlane(wave) * KD + j) % KBLK) * 64 + lane, key = e / KCH;
+        koff[j] = (key * DH + swz_k<DH>(key, e % KCH) * 8) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+        const int id = min(tid + NT * i, VTOT - 1);
+        voff[i] = ((id / (TK / 4)) * cap + 4 * (id % (TK / 4))) * 2;
+    }
+    auto kdirect = [&](int tk0, int kb) __attribute__((always_inline)) {
+        const auto res = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (size_t)tk0 * DH), (short)0,
+                                                           max(0, cap - tk0) * DH * 2, 0x00020000);
+#pragma unroll
+        for (int j = 0; j < KD; ++j) {
+            const int blk = (__builtin_amdgcn_readfirstlane(wave) * KD + j) % KBLK;
+            // the LDS address passes through an integer: the compiler then does not tie the copy
+            // to the K buffer it fills, and does not make later reads of the other buffers wait
+            // for it (the explicit counts before each barrier order them)
+            buf_to_lds16(res, __builtin_amdgcn_readfirstlane(
+                                  (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&KS(kb)[blk * 64]),
+                         koff[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    struct VT { u32x2_t v[VLD]; };
+    auto vload = [&](int tv0, VT& r) __attribute__((always_inline)) {
+        const auto res = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + tv0), (short)0,
+                                                           max(0, DH * cap - tv0) * 2, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) {
+            r.v[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(res, voff[i], 0, 0));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
     // this wave's four (two with two key phases) 16-key score blocks of the K tile in buffer kb:
     // S^T = K . Q^T, score block kb of the tile is st[kb - ph*KB]
     auto scores = [&](int kb, f32x4_t(&st)[KB]) __attribute__((always_inline)) {
@@ -224,7 +289,7 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
             st[kbi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int d = 0; d < DS; ++d) {
-                const u32x4_t kv = ks[kb][key * KCH + swz_k<DH>(key, d * 4 + g4)];
+                const u32x4_t kv = KS(kb)[key * KCH + swz_k<DH>(key, d * 4 + g4)];
                 st[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&kv, qf[d], st[kbi], 0, 0, 0);
             }
         }
@@ -346,6 +411,83 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
             rescale(mask_max(kbeg, st0));
             last(0, st0);
         }
+    } else if constexpr (DEEP) {
+        // Two tiles of lead.  Prologue: the K of tiles 0, 1, 2 into K buffers 0, 1, 2 and the V of
+        // tiles 0, 1 into register sets 0, 1 (tile j's V in set j & 1), all fetched together;
+        // tile 0's scores once its K has landed; tile 0's V to V buffer 0 and tile 2's V fetched.
+        // Step t opens by fetching tile t + 3's K into K buffer t % 3 (last read by tile t's
+        // scores, in step t - 1), scores tile t + 1 out of K buffer (t + 1) % 3 and multiplies
+        // tile t's V out of V buffer t & 1; after it tile t + 1's V goes to V buffer (t + 1) & 1
+        // (last read in step t - 1) and tile t + 3's V is fetched into the register set tile
+        // t + 1's V just left.  A K copy thus has two steps to land and a V load two steps to
+        // reach its registers.  Before the barrier that closes step t each wave waits for its
+        // LDS writes and for its share of tile t + 2's K, not for the loads issued after it (tile
+        // t + 2's V, tile t + 3's K and V): the count is explicit and the barrier carries no
+        // memory fence (a fence would wait for every copy into LDS); empty asm statements keep
+        // the compiler from moving LDS accesses across it.  The loop is unrolled six times so
+        // that every buffer and register set is fixed in each copy.
+        constexpr int WN = 2 * VLD + KD;
+        constexpr int WN0 = 2 * KD + 2 * VLD;
+        static_assert(WN0 < 64, "vmcnt range");
+        // s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt left open)
+        constexpr int WAITK = (WN & 15) | (7 << 4) | ((WN >> 4) << 14);
+        constexpr int WAIT0 = (WN0 & 15) | (7 << 4) | ((WN0 >> 4) << 14);
+        auto bar = [&]() __attribute__((always_inline)) {
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            __asm__ volatile("" ::: "memory");
+        };
+        VT va, vb;
+        kdirect(kbeg, 0);
+        kdirect(kbeg + TK, 1);
+        kdirect(kbeg + 2 * TK, 2);
+        vload(kbeg, va);
+        vload(kbeg + TK, vb);
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(WAIT0);                 // tile 0's K
+        bar();
+        if (wlive) {
+            scores(0, st0);
+            rescale(mask_max(kbeg, st0));
+        }
+        store_v(kbeg, 0, va);                              // (its wait covers tiles 1 and 2's K)
+        vload(kbeg + 2 * TK, va);
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((VLD & 15) | (7 << 4) | ((VLD >> 4) << 14));
+        bar();
+        // one step at t0 = kbeg + (6i + P) TK; true once the split is done
+        auto body = [&](auto pc, int t0) __attribute__((always_inline)) -> bool {
+            constexpr int P = decltype(pc)::value;
+            f32x4_t(&cur)[KB] = (P & 1) ? st1 : st0;
+            f32x4_t(&nxt)[KB] = (P & 1) ? st0 : st1;
+            VT& vn = (P & 1) ? va : vb;                    // tile t + 1's V, then tile t + 3's
+            if constexpr (NPH == 1) {
+                if (t0 + TK >= kend) {
+                    if (wlive) last(P & 1, cur);
+                    return true;
+                }
+            } else if (t0 >= kend) {
+                return true;
+            }
+            kdirect(t0 + 3 * TK, P % 3);
+            if (wlive) step(t0, (P + 1) % 3, P & 1, cur, nxt);
+            store_v(t0 + TK, (P + 1) & 1, vn);
+            vload(t0 + 3 * TK, vn);
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(WAITK);
+            bar();
+            return false;
+        };
+        using std::integral_constant;
+        for (int t0 = kbeg;; t0 += 6 * TK) {
+            if (body(integral_constant<int, 0>{}, t0)) break;
+            if (body(integral_constant<int, 1>{}, t0 + TK)) break;
+            if (body(integral_constant<int, 2>{}, t0 + 2 * TK)) break;
+            if (body(integral_constant<int, 3>{}, t0 + 3 * TK)) break;
+            if (body(integral_constant<int, 4>{}, t0 + 4 * TK)) break;
+            if (body(integral_constant<int, 5>{}, t0 + 5 * TK)) break;
+        }
+        __builtin_amdgcn_s_waitcnt(0);                     // no copy may still write LDS below
     } else {
         // Prologue: tiles 0 and 1 fetched together (one memory round trip); tile 0's K through
         // buffer 0, its scores, mask and reference maximum; then tile 1's K to buffer 1 and tile
@@ -405,17 +547,19 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
     l_run += __shfl_xor(l_run, 32, 64);
     if constexpr (NPH == 2) {
         // phase 1 hands (m, l, O) to phase 0 of the same row block and lane through the K/V
-        // buffers (free once every wave has left the loop): O = O0 2^(m0-m) + O1 2^(m1-m)
+        // buffers (free once every wave has left the loop), a quarter of O in each of four:
+        // O = O0 2^(m0-m) + O1 2^(m1-m)
         __shared__ float2 ml1[NRW * 64];
-        static_assert(NRW * 64 * (DB / 2) * sizeof(f32x4_t) <= sizeof(ks), "O halves fit the K/V buffers");
-        f32x4_t* o_lo = (f32x4_t*)&ks[0][0];
-        f32x4_t* o_hi = (f32x4_t*)&vs[0][0];
+        constexpr int DQ = DB / 4;
+        static_assert(DB % 4 == 0 && NRW * 64 * DQ * sizeof(f32x4_t) <= KSZ * sizeof(u32x4_t) &&
+                      NRW * 64 * DQ * sizeof(f32x4_t) <= sizeof(vs[0]), "O quarters fit the K/V buffers");
+        f32x4_t* const oq[4] = {(f32x4_t*)KS(0), (f32x4_t*)KS(1), (f32x4_t*)vs[0], (f32x4_t*)vs[1]};
         const int slot = rw * 64 + lane;
         __syncthreads();
         if (ph == 1) {
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                (db < DB / 2 ? o_lo : o_hi)[slot * (DB / 2) + db % (DB / 2)] = oacc[db];
+                oq[db / DQ][slot * DQ + db % DQ] = oacc[db];
             ml1[slot] = make_float2(m_run, l_run);
         }
         __syncthreads();
@@ -428,7 +572,7 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
         l_run = l_run * a0 + o1ml.y * a1;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            oacc[db] = oacc[db] * a0 + (db < DB / 2 ? o_lo : o_hi)[slot * (DB / 2) + db % (DB / 2)] * a1;
+            oacc[db] = oacc[db] * a0 + oq[db / DQ][slot * DQ + db % DQ] * a1;
         m_run = m;
     }
     if (!qlive) return;

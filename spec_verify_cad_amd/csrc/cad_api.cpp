@@ -265,6 +265,8 @@ int span_forward_impl(const cad_layer_desc* layers, int n_layers, const cad_kv_d
     const bool attends = !kv_only || n_layers > 1;
     const bool simple_attn = fd.dtype == CAD_DTYPE_F32 || (fd.d != 64 && fd.d != 128);
     if (attends && simple_attn && (size_t)(fd.cap + fd.Nq) * 4 > 64 * 1024) return CAD_EUNSUPPORTED;
+    // the tiled attention addresses one head's K or V cache with 32-bit byte offsets
+    if (attends && !simple_attn && (size_t)fd.cap * fd.d * 2 > 0x7FFFFFFFu) return CAD_EUNSUPPORTED;
     const FwdBufs wb = fwd_carve(fd, workspace, kv_only && n_layers == 1);
     if (!workspace || workspace_bytes < wb.total || ((uintptr_t)workspace & 255)) return CAD_EWORKSPACE;
 
