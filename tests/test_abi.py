@@ -56,6 +56,11 @@ def test_host_argument_errors_return_before_launch():
     d2 = _desc(head_dim=48)
     kv2 = cad.KVDesc(1, 1, 1, 1, 1, 160, 4, 48, cad.DTYPE_BF16)
     assert L.cad_span_forward(ctypes.byref(d2), ctypes.byref(kv2), tok, 1, 8, 0, 1, 1, 0, tok, None, None, None, tok, 1 << 30, None) == cad.CAD_EUNSUPPORTED
+    # one head's K cache of 2 GiB or more (the tiled attention addresses it with 32-bit offsets)
+    huge = cad.KVDesc(1, 1, 1, 1, 1, 1 << 24, 4, 64, cad.DTYPE_BF16)
+    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(huge), tok, 1, 8, 0, 1, 1, 0, tok, None, None, None, tok, 1 << 30, None) == cad.CAD_EUNSUPPORTED
+    ok_cap = cad.KVDesc(1, 1, 1, 1, 1, (1 << 24) - 4, 4, 64, cad.DTYPE_BF16)
+    assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(ok_cap), tok, 1, 8, 0, 1, 1, 0, tok, None, None, None, ctypes.c_void_p(8), 1 << 30, None) == cad.CAD_EWORKSPACE
     # workspace too small / misaligned
     assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, tok, None, None, None, ctypes.c_void_p(256), 16, None) == cad.CAD_EWORKSPACE
     assert L.cad_span_forward(ctypes.byref(d), ctypes.byref(kv), tok, 1, 8, 0, 1, 1, 0, tok, None, None, None, ctypes.c_void_p(8), 1 << 30, None) == cad.CAD_EWORKSPACE
