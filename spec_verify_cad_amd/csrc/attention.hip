@@ -64,6 +64,13 @@ __device__ __forceinline__ int swz_k(int r, int c) {
     else return c ^ ((r >> 1) & 7);                     // 128-byte rows
 }
 __device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r >> 1) & 7); }   // 128-byte rows
+// K swizzle for the permuted score order of the two-tile-lead tiles (below): the 16 rows one
+// 16-lane group reads, keys 8q + 4h + r (q, r = 0..3, h fixed), land in 16 distinct bank groups
+template <int DH>
+__device__ __forceinline__ int swz_kp(int r, int c) {
+    if constexpr (DH == 128) return c ^ ((r & 3) | ((r >> 1) & 12));
+    else return c ^ (((r >> 1) & 1) | ((r >> 2) & 6));
+}
 
 // 16 bytes per lane from a buffer straight into LDS: lane i's bytes at voff land at lds + 16 i
 __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t res, uint32_t lds, uint32_t voff) {
@@ -92,19 +99,24 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
     constexpr int KLD = (KTOT + NT - 1) / NT;   // K chunks each thread copies per tile
     constexpr int VLD = (VTOT + NT - 1) / NT;   // 4-key V groups each thread copies per tile
     static_assert(NPH == 1 || NPH == 2, "one or two key phases");
-    // K tiles land in LDS straight from memory, two steps ahead of their scores (three buffers);
-    // V tiles come through registers, also two steps ahead (two register sets).  The K buffers
-    // are separate variables: the compiler then tells a read of one from a copy still landing
-    // in another and waits only where they meet.
+    // DEEP (8- and 10-wave tiles, one workgroup per CU): K and V tiles land in LDS straight from
+    // memory, two steps ahead of their use, in three buffers each (separate variables, each a
+    // compile-time choice in every copy of the unrolled loop); otherwise K and V come through
+    // registers one tile ahead into two buffers each.
     constexpr bool DEEP = NWV >= 8;
-    constexpr int KSZ = TK * KCH;
+    constexpr int KSZ = TK * KCH, VSZ = DH * (TK / 8);
     __shared__ u32x4_t ks0[DEEP ? KSZ : 1], ks1[DEEP ? KSZ : 1], ks2[DEEP ? KSZ : 1];
-    __shared__ u32x4_t ksr[DEEP ? 1 : 2][DEEP ? 1 : KSZ];     // (the one-tile lead's two buffers)
-    __shared__ u32x4_t vs[2][DH * (TK / 8)];
+    __shared__ u32x4_t vs0[DEEP ? VSZ : 1], vs1[DEEP ? VSZ : 1], vs2[DEEP ? VSZ : 1];
+    __shared__ u32x4_t ksr[DEEP ? 1 : 2][DEEP ? 1 : KSZ];
+    __shared__ u32x4_t vsr[DEEP ? 1 : 2][DEEP ? 1 : VSZ];
 
     auto KS = [&](int i) __attribute__((always_inline)) -> u32x4_t* {
         if constexpr (DEEP) return i == 0 ? ks0 : (i == 1 ? ks1 : ks2);
         else return ksr[i];
+    };
+    auto VS = [&](int i) __attribute__((always_inline)) -> u32x4_t* {
+        if constexpr (DEEP) return i == 0 ? vs0 : (i == 1 ? vs1 : vs2);
+        else return vsr[i];
     };
     const int split = blockIdx.x, rtile = blockIdx.y;
     const int bg = blockIdx.z, b = bg / Hkv, g = bg % Hkv;
@@ -227,57 +239,72 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
             w.y &= n >= 4 ? 0xFFFFFFFFu : (n == 3 ? 0xFFFFu : 0u);
             const int kq = grp >> 3, gq = grp & 7;
             const int c = swz_v(row, kq * 4 + (gq & 3));
-            ((u32x2_t*)vs[vb])[(row * (TK / 8) + c) * 2 + (gq >> 2)] = w;
+            ((u32x2_t*)VS(vb))[(row * (TK / 8) + c) * 2 + (gq >> 2)] = w;
         }
     };
     auto store = [&](int tv0, int kb, int vb, const Tile& r) __attribute__((always_inline)) {
         store_k(kb, r);
         store_v(tv0, vb, r);
     };
-    // Loads of the two-tile lead (below): each goes through a buffer resource whose base is the
-    // tile's first key, with per-lane byte offsets that stay fixed for the whole loop, so no
-    // address register of a load in flight is ever rewritten (the compiler would wait for the
-    // load before reusing one).  K rows of the tile at tk0 go straight into LDS buffer kb: each
-    // wave copies 1 KB blocks of the swizzled tile, lane i the 16 bytes at block offset 16 i,
-    // i.e. the logical chunk the swizzle puts there (it is its own inverse); with more waves than
-    // blocks some repeat a block.  Rows past kend hold whatever the cache holds (their scores
-    // are masked) and rows past the cache's end read zero.  V groups are loaded into registers
-    // the same way; past kend they are zeroed when stored to LDS.
-    constexpr int KBLK = TK * KCH / 64, KD = (KBLK + NWV - 1) / NWV;
-    uint32_t koff[KD], voff[VLD];
+    // Copies of the two-tile lead (DEEP, below): 1 KB blocks of a tile go from the cache straight
+    // into an LDS buffer, one buffer load per wave and block, lane i's 16 bytes at block offset
+    // 16 i; each lane fetches the logical chunk that the swizzle places at its slot (the
+    // swizzles are their own inverses).  Each copy reads through a buffer resource based at the
+    // tile's first key, with per-lane byte offsets fixed for the whole loop (the compiler waits
+    // for a load in flight before its address register is rewritten).  With more waves than
+    // blocks some waves repeat a block.  K rows past kend hold whatever the cache holds (their
+    // scores are masked); V keys past kend are zeroed in LDS before the tile's value product
+    // (vzero); whatever lies past the cache's end reads zero.  V is dim-major: a 64-key tile is
+    // DH rows of 128 bytes, chunk c holding keys 8c .. 8c + 7 (the permuted score order makes
+    // these a lane's eight weights).
+    constexpr int KBLK = KSZ / 64, KD = (KBLK + NWV - 1) / NWV;
+    constexpr int VBLK = VSZ / 64, VD = (VBLK + NWV - 1) / NWV;
+    uint32_t koff[KD], voff[VD];
 #pragma unroll
     for (int j = 0; j < KD; ++j) {
         const int e = ((__builtin_amdgcn_readfirstlane(wave) * KD + j) % KBLK) * 64 + lane, key = e / KCH;
-        koff[j] = (key * DH + swz_k<DH>(key, e % KCH) * 8) * 2;
+        koff[j] = (key * DH + swz_kp<DH>(key, e % KCH) * 8) * 2;
     }
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-        const int id = min(tid + NT * i, VTOT - 1);
-        voff[i] = ((id / (TK / 4)) * cap + 4 * (id % (TK / 4))) * 2;
+    for (int j = 0; j < VD; ++j) {
+        const int e = ((__builtin_amdgcn_readfirstlane(wave) * VD + j) % VBLK) * 64 + lane, row = e / (TK / 8);
+        voff[j] = (row * cap + swz_v(row, e % (TK / 8)) * 8) * 2;
     }
+    // (the LDS address passes through readfirstlane, an integer: the compiler then does not tie
+    // the copy to the buffer it fills and does not make reads of the other buffers wait for it;
+    // the explicit counts before each barrier order them)
+    auto lds_addr = [&](u32x4_t* p) __attribute__((always_inline)) -> uint32_t {
+        return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p);
+    };
     auto kdirect = [&](int tk0, int kb) __attribute__((always_inline)) {
         const auto res = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (size_t)tk0 * DH), (short)0,
                                                            max(0, cap - tk0) * DH * 2, 0x00020000);
 #pragma unroll
         for (int j = 0; j < KD; ++j) {
-            const int blk = (__builtin_amdgcn_readfirstlane(wave) * KD + j) % KBLK;
-            // the LDS address passes through an integer: the compiler then does not tie the copy
-            // to the K buffer it fills, and does not make later reads of the other buffers wait
-            // for it (the explicit counts before each barrier order them)
-            buf_to_lds16(res, __builtin_amdgcn_readfirstlane(
-                                  (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&KS(kb)[blk * 64]),
-                         koff[j]);
+            buf_to_lds16(res, lds_addr(&KS(kb)[((__builtin_amdgcn_readfirstlane(wave) * KD + j) % KBLK) * 64]), koff[j]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    struct VT { u32x2_t v[VLD]; };
-    auto vload = [&](int tv0, VT& r) __attribute__((always_inline)) {
+    auto vdirect = [&](int tv0, int vb) __attribute__((always_inline)) {
         const auto res = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + tv0), (short)0,
                                                            max(0, DH * cap - tv0) * 2, 0x00020000);
 #pragma unroll
-        for (int i = 0; i < VLD; ++i) {
-            r.v[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(res, voff[i], 0, 0));
+        for (int j = 0; j < VD; ++j) {
+            buf_to_lds16(res, lds_addr(&VS(vb)[((__builtin_amdgcn_readfirstlane(wave) * VD + j) % VBLK) * 64]), voff[j]);
             __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // zero the keys >= kend of the V tile at tv0 in buffer vb (the tile that holds kend)
+    auto vzero = [&](int tv0, int vb) __attribute__((always_inline)) {
+        const int nv = kend - tv0;
+        for (int id = tid; id < VSZ; id += NT) {
+            const int row = id / (TK / 8), c = id % (TK / 8), n = nv - 8 * c;   // valid keys of the chunk
+            if (n >= 8) continue;
+            u32x4_t& w = VS(vb)[row * (TK / 8) + swz_v(row, c)];
+            u32x4_t m;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m[q] = n >= 2 * q + 2 ? 0xFFFFFFFFu : (n == 2 * q + 1 ? 0xFFFFu : 0u);
+            w &= m;
         }
     };
     // this wave's four (two with two key phases) 16-key score blocks of the K tile in buffer kb:
@@ -285,11 +312,15 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
     auto scores = [&](int kb, f32x4_t(&st)[KB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kbi = 0; kbi < KB; ++kbi) {
-            const int key = (ph * KB + kbi) * 16 + l16;
+            const int bk = ph * KB + kbi;
+            // DEEP: output row 4 g + i of blocks 2 kq, 2 kq + 1 is key 32 kq + 8 g + i, + 4 + i, so
+            // each lane's eight weights of a 32-key step are eight consecutive keys
+            const int key = DEEP ? (bk >> 1) * 32 + 8 * (l16 >> 2) + 4 * (bk & 1) + (l16 & 3) : bk * 16 + l16;
             st[kbi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int d = 0; d < DS; ++d) {
-                const u32x4_t kv = KS(kb)[key * KCH + swz_k<DH>(key, d * 4 + g4)];
+                const int ch = DEEP ? swz_kp<DH>(key, d * 4 + g4) : swz_k<DH>(key, d * 4 + g4);
+                const u32x4_t kv = KS(kb)[key * KCH + ch];
                 st[kbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&kv, qf[d], st[kbi], 0, 0, 0);
             }
         }
@@ -300,14 +331,14 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
     // 1/sqrt(d) scale into their exponent).  One compare per score against per-tile bounds
     // (bitwise: short-circuit tests made the compiler branch per score).
     auto mask_max = [&](int k0, f32x4_t(&st)[KB]) __attribute__((always_inline)) {
-        const int base = k0 + ph * KB * 16 + g4 * 4;
+        const int base = DEEP ? k0 + ph * (KB / 2) * 32 + g4 * 8 : k0 + ph * KB * 16 + g4 * 4;
         const int A = vis_a - base, L = vis_lo - base, H = vis_hi - base;
         float lmax = -INFINITY;
 #pragma unroll
         for (int kbi = 0; kbi < KB; ++kbi)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int c = kbi * 16 + i;
+                const int c = DEEP ? (kbi >> 1) * 32 + (kbi & 1) * 4 + i : kbi * 16 + i;
                 bool al = c < A;
                 if constexpr (MODE == CAD_MASK_BLOCK_TRI) al = al | ((c >= L) & (c <= H));
                 const float sv = al ? st[kbi][i] : -INFINITY;
@@ -350,7 +381,7 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const int row = db * 16 + l16;
-            const u32x4_t vv = vs[vb][row * (TK / 8) + swz_v(row, kq * 4 + g4)];
+            const u32x4_t vv = VS(vb)[row * (TK / 8) + swz_v(row, kq * 4 + g4)];
             oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, phi, oacc[db], 0, 0, 0);
             oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)&vv, pl, oacc[db], 0, 0, 0);
         }
@@ -403,9 +434,20 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
     if (NPH == 1 && kend - kbeg <= TK) {
         // one tile (every split of a short span): fetched, copied, scored and multiplied in turn
         // (the two-phase tile serves long histories only)
-        load(kbeg, kbeg, r);
-        store(kbeg, 0, 0, r);
-        __syncthreads();
+        if constexpr (DEEP) {
+            kdirect(kbeg, 0);
+            vdirect(kbeg, 0);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (kend - kbeg < TK) {
+                vzero(kbeg, 0);
+                __syncthreads();
+            }
+        } else {
+            load(kbeg, kbeg, r);
+            store(kbeg, 0, 0, r);
+            __syncthreads();
+        }
         if (wlive) {
             scores(0, st0);
             rescale(mask_max(kbeg, st0));
@@ -413,72 +455,76 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
         }
     } else if constexpr (DEEP) {
         // Two tiles of lead.  Prologue: the K of tiles 0, 1, 2 into K buffers 0, 1, 2 and the V of
-        // tiles 0, 1 into register sets 0, 1 (tile j's V in set j & 1), all fetched together;
-        // tile 0's scores once its K has landed; tile 0's V to V buffer 0 and tile 2's V fetched.
-        // Step t opens by fetching tile t + 3's K into K buffer t % 3 (last read by tile t's
-        // scores, in step t - 1), scores tile t + 1 out of K buffer (t + 1) % 3 and multiplies
-        // tile t's V out of V buffer t & 1; after it tile t + 1's V goes to V buffer (t + 1) & 1
-        // (last read in step t - 1) and tile t + 3's V is fetched into the register set tile
-        // t + 1's V just left.  A K copy thus has two steps to land and a V load two steps to
-        // reach its registers.  Before the barrier that closes step t each wave waits for its
-        // LDS writes and for its share of tile t + 2's K, not for the loads issued after it (tile
-        // t + 2's V, tile t + 3's K and V): the count is explicit and the barrier carries no
-        // memory fence (a fence would wait for every copy into LDS); empty asm statements keep
-        // the compiler from moving LDS accesses across it.  The loop is unrolled six times so
-        // that every buffer and register set is fixed in each copy.
-        constexpr int WN = 2 * VLD + KD;
-        constexpr int WN0 = 2 * KD + 2 * VLD;
+        // tiles 0, 1 into V buffers 0, 1, all issued together; tile 0's scores once its K has
+        // landed.  Step t opens by copying tile t + 3's K into K buffer t % 3 (last read by tile
+        // t's scores, in step t - 1) and tile t + 2's V into V buffer (t + 2) % 3 (last read by
+        // tile t - 1's value product), then scores tile t + 1 out of K buffer (t + 1) % 3 and
+        // multiplies tile t's V out of V buffer t % 3: every copy has two steps to land.  Before
+        // the barrier that closes step t each wave waits for its LDS writes and for its share of
+        // tile t + 2's K and tile t + 1's V, not for the copies issued after them (tile t + 3's K
+        // and tile t + 2's V): the count is explicit and the barrier carries no memory fence (a
+        // fence would wait for every copy into LDS); empty asm statements keep the compiler from
+        // moving LDS accesses across it.  The tile that holds kend has its V keys past kend
+        // zeroed before its value product.  The loop is unrolled six times (three buffers, two
+        // score register sets), so every buffer is a compile-time choice in each copy.
+        constexpr int WN = KD + VD, WN0 = 2 * KD + 2 * VD;
         static_assert(WN0 < 64, "vmcnt range");
         // s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt left open)
         constexpr int WAITK = (WN & 15) | (7 << 4) | ((WN >> 4) << 14);
         constexpr int WAIT0 = (WN0 & 15) | (7 << 4) | ((WN0 >> 4) << 14);
+        constexpr int WAIT1 = (VD & 15) | (7 << 4) | ((VD >> 4) << 14);
+        constexpr int WAITL = 15 | (7 << 4) | (3 << 14);                  // lgkmcnt(0) only
         auto bar = [&]() __attribute__((always_inline)) {
             __asm__ volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();
             __asm__ volatile("" ::: "memory");
         };
-        VT va, vb;
+        auto wait_bar = [&](auto w) __attribute__((always_inline)) {
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(decltype(w)::value);
+            bar();
+        };
+        using std::integral_constant;
         kdirect(kbeg, 0);
         kdirect(kbeg + TK, 1);
         kdirect(kbeg + 2 * TK, 2);
-        vload(kbeg, va);
-        vload(kbeg + TK, vb);
-        __asm__ volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(WAIT0);                 // tile 0's K
-        bar();
+        vdirect(kbeg, 0);
+        vdirect(kbeg + TK, 1);
+        wait_bar(integral_constant<int, WAIT0>{});         // tile 0's K
         if (wlive) {
             scores(0, st0);
             rescale(mask_max(kbeg, st0));
         }
-        store_v(kbeg, 0, va);                              // (its wait covers tiles 1 and 2's K)
-        vload(kbeg + 2 * TK, va);
-        __asm__ volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt((VLD & 15) | (7 << 4) | ((VLD >> 4) << 14));
-        bar();
+        wait_bar(integral_constant<int, WAIT1>{});         // tiles 1 and 2's K, tile 0's V
         // one step at t0 = kbeg + (6i + P) TK; true once the split is done
         auto body = [&](auto pc, int t0) __attribute__((always_inline)) -> bool {
             constexpr int P = decltype(pc)::value;
             f32x4_t(&cur)[KB] = (P & 1) ? st1 : st0;
             f32x4_t(&nxt)[KB] = (P & 1) ? st0 : st1;
-            VT& vn = (P & 1) ? va : vb;                    // tile t + 1's V, then tile t + 3's
             if constexpr (NPH == 1) {
                 if (t0 + TK >= kend) {
-                    if (wlive) last(P & 1, cur);
+                    if (t0 + TK > kend) {
+                        vzero(t0, P % 3);
+                        wait_bar(integral_constant<int, WAITL>{});
+                    }
+                    if (wlive) last(P % 3, cur);
                     return true;
                 }
             } else if (t0 >= kend) {
                 return true;
             }
             kdirect(t0 + 3 * TK, P % 3);
-            if (wlive) step(t0, (P + 1) % 3, P & 1, cur, nxt);
-            store_v(t0 + TK, (P + 1) & 1, vn);
-            vload(t0 + 3 * TK, vn);
-            __asm__ volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(WAITK);
-            bar();
+            vdirect(t0 + 2 * TK, (P + 2) % 3);
+            if constexpr (NPH == 2) {
+                if (t0 + TK > kend) {
+                    vzero(t0, P % 3);
+                    wait_bar(integral_constant<int, WAITL>{});
+                }
+            }
+            if (wlive) step(t0, (P + 1) % 3, P % 3, cur, nxt);
+            wait_bar(integral_constant<int, WAITK>{});
             return false;
         };
-        using std::integral_constant;
         for (int t0 = kbeg;; t0 += 6 * TK) {
             if (body(integral_constant<int, 0>{}, t0)) break;
             if (body(integral_constant<int, 1>{}, t0 + TK)) break;
@@ -552,8 +598,8 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
         __shared__ float2 ml1[NRW * 64];
         constexpr int DQ = DB / 4;
         static_assert(DB % 4 == 0 && NRW * 64 * DQ * sizeof(f32x4_t) <= KSZ * sizeof(u32x4_t) &&
-                      NRW * 64 * DQ * sizeof(f32x4_t) <= sizeof(vs[0]), "O quarters fit the K/V buffers");
-        f32x4_t* const oq[4] = {(f32x4_t*)KS(0), (f32x4_t*)KS(1), (f32x4_t*)vs[0], (f32x4_t*)vs[1]};
+                      NRW * 64 * DQ * sizeof(f32x4_t) <= VSZ * sizeof(u32x4_t), "O quarters fit the K/V buffers");
+        f32x4_t* const oq[4] = {(f32x4_t*)KS(0), (f32x4_t*)KS(1), (f32x4_t*)VS(0), (f32x4_t*)VS(1)};
         const int slot = rw * 64 + lane;
         __syncthreads();
         if (ph == 1) {

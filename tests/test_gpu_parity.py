@@ -519,6 +519,45 @@ def test_small_bf16_ragged_cache_lengths_match_oracle(small, mode, W, D, Nq):
             compare_cache(cache, b, ocs[b], L0, L0 + Nq, "bf16", what=f"span rows b={b} len={L0}")
 
 
+BF16_NAN = 0x7FC0   # a quiet NaN's bf16 bits (the device caches hold bf16 as int16)
+
+# head_dim 64 with 4 query heads per KV head: spans of more than 16 positions take the 8-wave tile
+SMALL_D64 = LayerShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64, ffn=1376, vocab=5003)
+
+
+@pytest.fixture(scope="module")
+def small_d64():
+    w = synth.layer_weights(SMALL_D64, 78)
+    return w, cad.DeviceLayer(SMALL_D64, w), oracle_layer(SMALL_D64, w)
+
+
+@pytest.mark.parametrize("shape, Nq", [("d128", 8), ("d128", 17), ("d128", 40), ("d64", 40)])
+def test_cache_slots_past_the_span_never_reach_the_output(small, small_d64, shape, Nq):
+    # every cache slot at or past len + Nq holds NaN: the attention tiles read whole 64-key tiles
+    # (K rows and V keys past the split's end), which must not reach any output.  Nq = 8, 17 and
+    # 40 with head_dim 128 take the 4-, 10- and 8-wave tiles; head_dim 64 at Nq = 40 the 8-wave
+    # tile.  Lengths on both sides of a tile edge, and 250 + Nq near the end of a 320-slot cache.
+    shp = SMALL if shape == "d128" else SMALL_D64
+    w, dl, OL = small if shape == "d128" else small_d64
+    lens = [0, 1, 63, 64, 65, 250]
+    B, cap = len(lens), 320
+    log(f"NaN past the span {shape} Nq={Nq}")
+    cache = cad.DeviceCache(shp, B, cap)
+    ocs = []
+    for b, L0 in enumerate(lens):
+        oc = O.cache_from_tokens(OL, synth.uniform_tokens(190 + b, L0, shp.vocab), cap)
+        upload_oracle_cache(cache, b, oc, "bf16")
+        cache.k[b, :, L0 + Nq:] = BF16_NAN
+        cache.v[b, :, :, L0 + Nq:] = BF16_NAN
+        ocs.append(oc)
+    span = np.stack([synth.uniform_tokens(200 + b, Nq, shp.vocab) for b in range(B)])
+    g = run_forward(dl, cache, span, flags=cad.COMMIT_ALL)
+    assert list(cache.len.cpu().numpy()) == [L0 + Nq for L0 in lens]
+    for b, L0 in enumerate(lens):
+        ref = O.span_forward(OL, ocs[b], span[b])
+        compare(g, ref, rows=slice(b * Nq, (b + 1) * Nq), what=f"NaN past span b={b} len={L0}")
+
+
 def test_small_bf16_multi_tile_splits_match_oracle(small):
     # 96-row spans over caches of 0..920 positions: three 128-row attention tiles per GQA group
     # and 7 key splits, so the longer sequences give each split two or three 64-key tiles (the
