@@ -3,15 +3,19 @@
 // grouped-query heads sharing one K/V stream.
 //
 // bf16 path (gfx950 MFMA, head_dim 64 or 128): split-L flash decoding with LDS-staged K/V
-// tiles.  A workgroup owns one (sequence, KV head, key split, 64-row tile); the rows of a tile
-// are the (token, q head) pairs of the GQA group, so the K/V of a split is fetched once for all
-// of them.  The 256 threads copy 64-key tiles (K rows, and the dim-major V rows with each
-// lane's 8 keys gathered into one 16-byte chunk) into two swizzled LDS buffers, the next tile
-// in flight while the current one is multiplied; each wave takes 16 rows in 32-key steps:
+// tiles.  A workgroup owns one (sequence, KV head, key split, row tile); the rows of a tile are
+// the (token, q head) pairs of the GQA group, so the K/V of a split is fetched once for all of
+// them.  64-row tiles (4 waves) copy 64-key tiles through registers (K rows, and the dim-major
+// V rows with each lane's 8 keys gathered into one 16-byte chunk) into two swizzled LDS
+// buffers, the next tile in flight while the current one is multiplied; 80- and 128-row tiles
+// (10 and 8 waves) copy K and V straight from the cache into three LDS buffers each, two tiles
+// ahead.  Each wave takes 16 rows in 32-key steps:
 //   S^T = K . Q^T   A = 16 keys x 32 dims of the K tile, B = the wave's query fragments;
 //   O^T += V^T . P^T  A = 16 dims x 32 keys of the V tile, B = P^T taken from the score
-//                   registers: MFMA k-slots 8g+i / 8g+4+i carry keys 4g+i / 16+4g+i, exactly
-//                   the scores lane (g, r) holds, so P never moves between lanes.
+//                   registers: MFMA k-slots 8g+i / 8g+4+i carry the keys of the scores lane
+//                   (g, r) holds, so P never moves between lanes (4g+i / 16+4g+i on the
+//                   register-staged tiles; 8g+i / 8g+4+i, the K rows taken in a permuted order,
+//                   on the direct-copy tiles, whose V chunks are then plain runs of 8 keys).
 // Online softmax runs in registers with exp2 and wavefront max/sum reductions; P enters the PV
 // product as bf16 hi + bf16 lo (the rounding remainder), two MFMAs, so the weights keep about
 // 16 significant bits.  With one split the wave writes the normalised output; otherwise it
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
     const uint16_t* kbase = kc + head * cap * DH;
     const uint16_t* vbase = vc + head * DH * cap;          // dim-major: row = one dim over all slots
 
-    // K/V in registers on their way to LDS.  K runs one tile ahead of V: during step t the K rows
+    // (4-wave tiles) K/V in registers on their way to LDS.  K runs one tile ahead of V: during step t the K rows
     // of tile t + 2 and the V rows of tile t + 1 are fetched, so that step t can multiply tile
     // t + 1's scores while it turns tile t's scores into weights.  The loads stay in program order
     // (a scheduling barrier after each), so the compiler's wait counts at the loop head, which
@@ -326,7 +330,8 @@ __global__ __launch_bounds__(NWV * 64, NWV == 4 ? 2 : 1) void k_attn_bf16(const 
         }
     };
     // mask the scores of the tile at keys k0.. (S^T[key][query]: lane holds keys
-    // k0 + (ph*KB + kb)*16 + 4*g4 + i of query l16) to -inf outside the lane's visible keys and
+    // k0 + (ph*KB + kb)*16 + 4*g4 + i of query l16, or with the permuted order (DEEP) keys
+    // k0 + 32*(bk >> 1) + 8*g4 + 4*(bk & 1) + i, bk = ph*KB + kb) to -inf outside the lane's visible keys and
     // return the lane's maximum in log2 units; the scores stay unscaled (the weights fold the
     // 1/sqrt(d) scale into their exponent).  One compare per score against per-tile bounds
     // (bitwise: short-circuit tests made the compiler branch per score).
