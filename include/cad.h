@@ -88,7 +88,9 @@ typedef struct {
  * KV cache of B sequences, in `dtype`:
  *   k: [B, n_kv_heads, cap, head_dim]  slot-major: k[b][g][s][i]
  *   v: [B, n_kv_heads, head_dim, cap]  dim-major:  v[b][g][i][s]
- * Slot s of sequence b holds the key/value of the token at position s (after acceptance).  The
+ * Slot s of sequence b holds the key/value of the token at position s (after acceptance); slots
+ * at or past len + Nq may hold anything, NaN included (the attention reads whole 64-slot tiles
+ * but no such value reaches a result).  The
  * value cache is stored transposed so that attention reads, for one dimension, a contiguous run
  * of slots (the operand layout of the value product).  cap must be a multiple of 4.
  * len: [B] int32, device-resident current lengths.  err: [B] int32, nullable; set to
