@@ -536,11 +536,12 @@ def test_cache_slots_past_the_span_never_reach_the_output(small, small_d64, shap
     # every cache slot at or past len + Nq holds NaN: the attention tiles read whole 64-key tiles
     # (K rows and V keys past the split's end), which must not reach any output.  Nq = 8, 17 and
     # 40 with head_dim 128 take the 4-, 10- and 8-wave tiles; head_dim 64 at Nq = 40 the 8-wave
-    # tile.  Lengths on both sides of a tile edge, and 250 + Nq near the end of a 320-slot cache.
+    # tile.  Lengths on both sides of a tile edge, and 900 + Nq, whose splits hold several tiles
+    # (the direct-copy tiles' loop and its ragged last tile).
     shp = SMALL if shape == "d128" else SMALL_D64
     w, dl, OL = small if shape == "d128" else small_d64
-    lens = [0, 1, 63, 64, 65, 250]
-    B, cap = len(lens), 320
+    lens = [0, 1, 63, 64, 65, 250, 900]
+    B, cap = len(lens), 1024
     log(f"NaN past the span {shape} Nq={Nq}")
     cache = cad.DeviceCache(shp, B, cap)
     ocs = []
@@ -558,22 +559,24 @@ def test_cache_slots_past_the_span_never_reach_the_output(small, small_d64, shap
         compare(g, ref, rows=slice(b * Nq, (b + 1) * Nq), what=f"NaN past span b={b} len={L0}")
 
 
-def test_small_bf16_multi_tile_splits_match_oracle(small):
+@pytest.mark.parametrize("shape", ["d128", "d64"])
+def test_small_bf16_multi_tile_splits_match_oracle(small, small_d64, shape):
     # 96-row spans over caches of 0..920 positions: three 128-row attention tiles per GQA group
     # and 7 key splits, so the longer sequences give each split two or three 64-key tiles (the
     # attention's cross-tile pipeline, its last tile ragged) while the short ones keep one-tile
-    # splits
-    w, dl, OL = small
+    # splits; at head_dim 128 and 64 (one K and one V copy per wave and tile)
+    shp = SMALL if shape == "d128" else SMALL_D64
+    w, dl, OL = small if shape == "d128" else small_d64
     lens = [0, 200, 450, 700, 850, 920]
     B, Nq, cap = len(lens), 96, 1024
-    log("small bf16 multi-tile attention splits")
-    cache = cad.DeviceCache(SMALL, B, cap)
+    log(f"small bf16 multi-tile attention splits {shape}")
+    cache = cad.DeviceCache(shp, B, cap)
     ocs = []
     for b, L0 in enumerate(lens):
-        oc = O.cache_from_tokens(OL, synth.uniform_tokens(170 + b, L0, SMALL.vocab), cap)
+        oc = O.cache_from_tokens(OL, synth.uniform_tokens(170 + b, L0, shp.vocab), cap)
         upload_oracle_cache(cache, b, oc, "bf16")
         ocs.append(oc)
-    span = np.stack([synth.uniform_tokens(180 + b, Nq, SMALL.vocab) for b in range(B)])
+    span = np.stack([synth.uniform_tokens(180 + b, Nq, shp.vocab) for b in range(B)])
     g = run_forward(dl, cache, span, flags=cad.COMMIT_ALL)
     assert list(cache.len.cpu().numpy()) == [L0 + Nq for L0 in lens]
     for b, L0 in enumerate(lens):
