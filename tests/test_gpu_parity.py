@@ -531,18 +531,21 @@ def small_d64():
     return w, cad.DeviceLayer(SMALL_D64, w), oracle_layer(SMALL_D64, w)
 
 
-@pytest.mark.parametrize("shape, Nq", [("d128", 8), ("d128", 17), ("d128", 40), ("d64", 40)])
-def test_cache_slots_past_the_span_never_reach_the_output(small, small_d64, shape, Nq):
+@pytest.mark.parametrize("shape, Nq, W, D", [("d128", 8, 1, 0), ("d128", 17, 1, 0), ("d128", 40, 1, 0),
+                                         ("d64", 40, 1, 0), ("d128", 18, 2, 9), ("d128", 32, 4, 8)])
+def test_cache_slots_past_the_span_never_reach_the_output(small, small_d64, shape, Nq, W, D):
     # every cache slot at or past len + Nq holds NaN: the attention tiles read whole 64-key tiles
-    # (K rows and V keys past the split's end), which must not reach any output.  Nq = 8, 17 and
-    # 40 with head_dim 128 take the 4-, 10- and 8-wave tiles; head_dim 64 at Nq = 40 the 8-wave
-    # tile.  Lengths on both sides of a tile edge, and 900 + Nq, whose splits hold several tiles
+    # (K rows and V keys past the split's end), which must not reach any output.  Causal spans of
+    # Nq = 8, 17 and 40 with head_dim 128 take the 4-, 10- and 8-wave tiles; head_dim 64 at
+    # Nq = 40 the 8-wave tile; block verifies of 2 x 9 and 4 x 8 candidates the 10- and 8-wave
+    # tiles.  Lengths on both sides of a tile edge, and 900 + Nq, whose splits hold several tiles
     # (the direct-copy tiles' loop and its ragged last tile).
+    block = D > 0
     shp = SMALL if shape == "d128" else SMALL_D64
     w, dl, OL = small if shape == "d128" else small_d64
     lens = [0, 1, 63, 64, 65, 250, 900]
     B, cap = len(lens), 1024
-    log(f"NaN past the span {shape} Nq={Nq}")
+    log(f"NaN past the span {shape} Nq={Nq} {'block' if block else 'causal'}")
     cache = cad.DeviceCache(shp, B, cap)
     ocs = []
     for b, L0 in enumerate(lens):
@@ -552,10 +555,15 @@ def test_cache_slots_past_the_span_never_reach_the_output(small, small_d64, shap
         cache.v[b, :, :, L0 + Nq:] = BF16_NAN
         ocs.append(oc)
     span = np.stack([synth.uniform_tokens(200 + b, Nq, shp.vocab) for b in range(B)])
-    g = run_forward(dl, cache, span, flags=cad.COMMIT_ALL)
-    assert list(cache.len.cpu().numpy()) == [L0 + Nq for L0 in lens]
+    if block:
+        g = run_forward(dl, cache, span, mode=cad.MASK_BLOCK, W=W, D=D)
+        assert list(cache.len.cpu().numpy()) == lens
+    else:
+        g = run_forward(dl, cache, span, flags=cad.COMMIT_ALL)
+        assert list(cache.len.cpu().numpy()) == [L0 + Nq for L0 in lens]
     for b, L0 in enumerate(lens):
-        ref = O.span_forward(OL, ocs[b], span[b])
+        ref = (O.span_forward(OL, ocs[b], span[b], mode="block", W=W, D=D, commit=False) if block
+               else O.span_forward(OL, ocs[b], span[b]))
         compare(g, ref, rows=slice(b * Nq, (b + 1) * Nq), what=f"NaN past span b={b} len={L0}")
 
 
